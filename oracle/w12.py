@@ -1,0 +1,308 @@
+"""W12 oracle: plain numpy encode / decode / validate / float64 GEMMs.
+
+Test infrastructure only (see the package docstring): the product path never
+imports this module.
+
+Sources (SpecPilot, arXiv 2611.02501):
+* figure-captions page, Fig. 5(a): every BF16 weight becomes three 4-bit
+  planes -- A = sign and the top three mantissa bits, E = a 4-bit exponent
+  offset inside a 16-binade window chosen per output channel, B = the low
+  mantissa bits; weights outside the window go to an exact escape list.
+* figure-captions page, Fig. 5(a) and Fig. 7: A and E together are the 8-bit
+  view, nested in each record, that the low-precision Q pass reads.
+* summary page, "Main Findings": 12.01-12.02 bits per weight on average and an
+  escape fraction of 7.3e-5 on Qwen3.8-27B; the format is lossless.
+
+The pages give no bit layout, window rule, tie rule, zero handling or escape
+layout.  The readings used here (numbered as in the design notes):
+* R1  AE byte = s<<7 | E<<3 | m[6:4] (one byte per weight, row-major [n, k]).
+      B plane: per aligned group of 8 weights k = 8g+i, the nibble m[3:0]
+      lives in byte 4g + (i % 4) of the row, low nibble for i < 4, high nibble
+      for i >= 4.
+* R2  E = e - base, with base the window's lowest biased exponent, 1..239, so
+      the window [base, base+15] stays inside the normal range 1..254.
+* R3  base minimises the number of escapes; ties go to the smallest base; a
+      row with no normal value gets base 1.
+* R4  e = 0 (zeros, subnormals) and e = 255 (Inf, NaN) are never inside a
+      window: they are always escapes.
+* R5  an escaped slot holds AE = 0 and B = 0.
+* R6  escapes are a row CSR: esc_ptr u32 [n+1], esc_col u32 and esc_val u16
+      (raw bits), ascending k within each row.
+* R8  the Q pass weight is the 8-bit view with B taken as 0 (for an
+      in-window weight that is bits & 0xFFF0); escapes stay exact.
+* R11 argmax ties go to the lowest index.
+
+Parity status: every function below is pinned by the CPU tests against
+values fixed independently of this file (exhaustive round trip over all 65536
+bfloat16 patterns, brute-force window search, hand-worked examples of the
+readings, exact rational GEMMs, an arithmetic formulation of the truncated
+view, the bits-per-weight closed form).  The readings themselves (bit order,
+tie rule, placeholder) cannot be pinned to the pages, which print no layout
+or worked example.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+WINDOW = 16                       # binades per window (Fig. 5a)
+BASE_MIN = 1                      # R2: lowest normal biased exponent
+BASE_MAX = 254 - WINDOW + 1       # 239: window top stays at 254
+U32_MAX = 0xFFFFFFFF
+
+
+class ValidationError(ValueError):
+    pass
+
+
+@dataclass
+class W12Record:
+    """A W12 tensor as numpy arrays (layout R1, R6)."""
+    n: int
+    k: int
+    base: np.ndarray      # uint8  [n]
+    ae: np.ndarray        # uint8  [n, k]          the 8-bit view (A + E)
+    lo: np.ndarray        # uint8  [n, lo_row_bytes(k)]   the B plane
+    esc_ptr: np.ndarray   # uint32 [n + 1]
+    esc_col: np.ndarray   # uint32 [n_esc]
+    esc_val: np.ndarray   # uint16 [n_esc]
+
+    @property
+    def n_esc(self) -> int:
+        return int(self.esc_col.shape[0])
+
+    def rows(self, r0: int, r1: int) -> "W12Record":
+        """The sub-record of rows [r0, r1), with esc_ptr rebased to 0."""
+        e0, e1 = int(self.esc_ptr[r0]), int(self.esc_ptr[r1])
+        return W12Record(r1 - r0, self.k, self.base[r0:r1].copy(), self.ae[r0:r1].copy(),
+                         self.lo[r0:r1].copy(),
+                         (self.esc_ptr[r0:r1 + 1].astype(np.int64) - e0).astype(np.uint32),
+                         self.esc_col[e0:e1].copy(), self.esc_val[e0:e1].copy())
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 fields
+# ----------------------------------------------------------------------------
+def bf16_fields(bits):
+    """Sign, biased exponent and 7-bit mantissa of raw bfloat16 bits (int64 arrays)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    return u >> 15, (u >> 7) & 0xFF, u & 0x7F
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact float64 value of raw bfloat16 bits (NaN payloads become some NaN)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Window choice (Fig. 5a; readings R2, R3, R4)
+# ----------------------------------------------------------------------------
+def exponent_histogram(w_bits) -> np.ndarray:
+    """hist[n, e] = number of weights of row n with biased exponent e, for e in 1..254.
+
+    Bins 0 and 255 (zeros/subnormals, Inf/NaN) stay 0: those values are never
+    inside a window (R4).
+    """
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    n = w.shape[0]
+    _, e, _ = bf16_fields(w)
+    counted = (e >= 1) & (e <= 254)
+    row = np.broadcast_to(np.arange(n, dtype=np.int64)[:, None], e.shape)
+    idx = (row * 256 + e)[counted]
+    return np.bincount(idx, minlength=n * 256).reshape(n, 256)
+
+
+def window_coverage(hist: np.ndarray) -> np.ndarray:
+    """cov[n, b] = sum of hist[n, b .. b+15] for b in 1..239 (entries b=0 and b>239 unused)."""
+    hist = np.asarray(hist, dtype=np.int64)
+    cov = np.zeros((hist.shape[0], 256), dtype=np.int64)
+    b = np.arange(BASE_MIN, BASE_MAX + 1)
+    for j in range(WINDOW):
+        cov[:, b] += hist[:, b + j]
+    return cov
+
+
+def choose_window(w_bits):
+    """(base [n] uint8, escapes per row [n] int64): fewest escapes, ties to the smallest base (R3)."""
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    cov = window_coverage(exponent_histogram(w))[:, BASE_MIN:BASE_MAX + 1]
+    pick = np.argmax(cov, axis=1)                 # first maximum = smallest base
+    best = cov[np.arange(w.shape[0]), pick]
+    return (pick + BASE_MIN).astype(np.uint8), w.shape[1] - best
+
+
+# ----------------------------------------------------------------------------
+# B-plane nibble placement (R1)
+# ----------------------------------------------------------------------------
+def lo_row_bytes(k: int) -> int:
+    """Bytes of B plane per row: 4 per started group of 8 weights (= k/2 when 8 | k)."""
+    return 4 * ((k + 7) // 8)
+
+
+def lo_position(k_index):
+    """(byte offset within the row, bit shift) of weight k's B nibble (R1)."""
+    k_index = np.asarray(k_index, dtype=np.int64)
+    g, i = k_index // 8, k_index % 8
+    return 4 * g + (i % 4), 4 * (i // 4)
+
+
+def _pack_lo(nib: np.ndarray) -> np.ndarray:
+    n, k = nib.shape
+    lo = np.zeros((n, lo_row_bytes(k)), dtype=np.int64)
+    byte, shift = lo_position(np.arange(k))
+    for kk in range(8):                       # place each of the 8 group positions in turn
+        sel = np.arange(kk, k, 8)
+        if sel.size:
+            lo[:, byte[sel]] |= nib[:, sel] << shift[sel]
+    return lo.astype(np.uint8)
+
+
+def _unpack_lo(lo: np.ndarray, k: int) -> np.ndarray:
+    byte, shift = lo_position(np.arange(k))
+    return (lo.astype(np.int64)[:, byte] >> shift) & 0xF
+
+
+# ----------------------------------------------------------------------------
+# Encode / decode (Fig. 5a; R1-R6)
+# ----------------------------------------------------------------------------
+def encode(w_bits) -> W12Record:
+    """Split every weight into the A/E/B planes, escaping those outside the row window."""
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    n, k = w.shape
+    s, e, m = bf16_fields(w)
+    base, n_esc_row = choose_window(w)
+    b = base.astype(np.int64)[:, None]
+    inside = (e >= b) & (e <= b + WINDOW - 1)
+    E = e - b
+    ae = np.where(inside, (s << 7) | (E << 3) | (m >> 4), 0).astype(np.uint8)
+    nib = np.where(inside, m & 0xF, 0)
+    rows, cols = np.nonzero(~inside)              # row-major: rows ascending, k ascending
+    counts = np.bincount(rows, minlength=n)
+    assert np.array_equal(counts, n_esc_row)
+    total = int(counts.sum())
+    if total > U32_MAX:
+        raise OverflowError("escape total does not fit the u32 CSR")
+    esc_ptr = np.zeros(n + 1, dtype=np.uint64)
+    esc_ptr[1:] = np.cumsum(counts)
+    return W12Record(n, k, base, ae, _pack_lo(nib), esc_ptr.astype(np.uint32),
+                     cols.astype(np.uint32), w[rows, cols].astype(np.uint16))
+
+
+def _escape_rows(rec: W12Record) -> np.ndarray:
+    return np.repeat(np.arange(rec.n), np.diff(rec.esc_ptr.astype(np.int64)))
+
+
+def _assemble(rec: W12Record, nib: np.ndarray) -> np.ndarray:
+    a = rec.ae.astype(np.int64)
+    s, E, mh = a >> 7, (a >> 3) & 0xF, a & 0x7
+    e = rec.base.astype(np.int64)[:, None] + E
+    u = (s << 15) | (e << 7) | (mh << 4) | nib
+    u[_escape_rows(rec), rec.esc_col.astype(np.int64)] = rec.esc_val
+    return u.astype(np.uint16)
+
+
+def decode(rec: W12Record) -> np.ndarray:
+    """Exact bfloat16 bits back from the planes, then every escape overwritten (lossless)."""
+    return _assemble(rec, _unpack_lo(rec.lo, rec.k))
+
+
+def q8_view_bits(rec: W12Record) -> np.ndarray:
+    """Weights the Q pass sees: the 8-bit view with B = 0, escapes exact (R8)."""
+    return _assemble(rec, np.zeros((rec.n, rec.k), dtype=np.int64))
+
+
+def validate(rec: W12Record) -> None:
+    """Raise ValidationError unless ``rec`` is in canonical form."""
+    n, k = rec.n, rec.k
+
+    def need(cond, msg):
+        if not cond:
+            raise ValidationError(msg)
+
+    need(rec.base.shape == (n,) and rec.base.dtype == np.uint8, "base shape/dtype")
+    need(rec.ae.shape == (n, k) and rec.ae.dtype == np.uint8, "ae shape/dtype")
+    need(rec.lo.shape == (n, lo_row_bytes(k)) and rec.lo.dtype == np.uint8, "lo shape/dtype")
+    need(rec.esc_ptr.shape == (n + 1,) and rec.esc_ptr.dtype == np.uint32, "esc_ptr shape/dtype")
+    need(rec.esc_col.dtype == np.uint32 and rec.esc_val.dtype == np.uint16, "escape dtypes")
+    ptr = rec.esc_ptr.astype(np.int64)
+    need(ptr[0] == 0, "esc_ptr[0] != 0")
+    need(bool(np.all(np.diff(ptr) >= 0)), "esc_ptr not monotone")
+    need(ptr[-1] == rec.esc_col.shape[0] == rec.esc_val.shape[0], "escape array lengths")
+    need(bool(np.all((rec.base >= BASE_MIN) & (rec.base <= BASE_MAX))), "base outside 1..239")
+    col = rec.esc_col.astype(np.int64)
+    need(bool(np.all(col < k)), "escape column out of range")
+    rows = _escape_rows(rec)
+    if col.size > 1:
+        same_row = rows[1:] == rows[:-1]
+        need(bool(np.all(col[1:][same_row] > col[:-1][same_row])), "escape columns not ascending")
+    need(bool(np.all(rec.ae[rows, col] == 0)), "escaped slot has nonzero AE")
+    need(bool(np.all(_unpack_lo(rec.lo, k)[rows, col] == 0)), "escaped slot has nonzero B")
+    if k % 8:
+        byte, shift = lo_position(np.arange(k, 8 * ((k + 7) // 8)))
+        pad = (rec.lo.astype(np.int64)[:, byte] >> shift) & 0xF
+        need(bool(np.all(pad == 0)), "B padding nibbles nonzero")
+    _, ev, _ = bf16_fields(rec.esc_val)
+    b = rec.base.astype(np.int64)[rows]
+    need(bool(np.all((ev < b) | (ev > b + WINDOW - 1))), "escaped value lies inside the window")
+    base2, _ = choose_window(decode(rec))
+    need(bool(np.array_equal(base2, rec.base)), "base is not the window rule's choice")
+
+
+# ----------------------------------------------------------------------------
+# float64 GEMMs (y = x W^T, PyTorch Linear shapes) and the error bound
+# ----------------------------------------------------------------------------
+ROW_CHUNK = 8192
+
+
+def gemm64(x_bits, w_bits) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * W[n, k] in float64 (every bf16 x bf16 product is exact)."""
+    x = bf16_to_f64(np.atleast_2d(x_bits))
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    y = np.empty((x.shape[0], w.shape[0]), dtype=np.float64)
+    for r0 in range(0, w.shape[0], ROW_CHUNK):
+        y[:, r0:r0 + ROW_CHUNK] = x @ bf16_to_f64(w[r0:r0 + ROW_CHUNK]).T
+    return y
+
+
+def abs_bound64(x_bits, w_bits) -> np.ndarray:
+    """sum_k |x[m, k] * W[n, k]| in float64: the scale of the error bound."""
+    x = np.abs(bf16_to_f64(np.atleast_2d(x_bits)))
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    y = np.empty((x.shape[0], w.shape[0]), dtype=np.float64)
+    for r0 in range(0, w.shape[0], ROW_CHUNK):
+        y[:, r0:r0 + ROW_CHUNK] = x @ np.abs(bf16_to_f64(w[r0:r0 + ROW_CHUNK])).T
+    return y
+
+
+def _by_rows(rec: W12Record, fn):
+    parts = [fn(rec.rows(r0, min(rec.n, r0 + ROW_CHUNK))) for r0 in range(0, rec.n, ROW_CHUNK)]
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0, rec.k), np.uint16)
+
+
+def w12_gemm64(x_bits, rec: W12Record) -> np.ndarray:
+    """The exact pass: x times the decoded (= original) weights, float64."""
+    return gemm64(x_bits, _by_rows(rec, decode))
+
+
+def q8_gemm64(x_bits, rec: W12Record) -> np.ndarray:
+    """The Q pass: x times the 8-bit-view weights (B = 0, escapes exact), float64."""
+    return gemm64(x_bits, _by_rows(rec, q8_view_bits))
+
+
+def top1(y) -> np.ndarray:
+    """argmax over n for each row m; ties go to the lowest n (R11)."""
+    return np.argmax(np.asarray(y), axis=1)
+
+
+# ----------------------------------------------------------------------------
+# Size accounting (summary page, Main Findings: 12.01-12.02 bits per weight)
+# ----------------------------------------------------------------------------
+def record_nbytes(rec: W12Record) -> int:
+    return int(rec.base.nbytes + rec.ae.nbytes + rec.lo.nbytes + rec.esc_ptr.nbytes
+               + rec.esc_col.nbytes + rec.esc_val.nbytes)
+
+
+def bits_per_weight(rec: W12Record) -> float:
+    return 8.0 * record_nbytes(rec) / (rec.n * rec.k)
