@@ -1,0 +1,140 @@
+/*
+ * w12.h -- C ABI of libw12.so: the W12 lossless 12-bit weight format and the skinny GEMMs
+ * that read it on AMD Instinct MI355X (gfx950).
+ *
+ * The format (SpecPilot, arXiv 2611.02501, figure-captions page, Fig. 5(a)): every bfloat16
+ * weight of W [n, k] (PyTorch Linear layout, n = output channels) is split into three 4-bit
+ * planes -- A (sign and mantissa bits 6..4), E (exponent offset inside a 16-binade window
+ * chosen per output channel) and B (mantissa bits 3..0).  Weights outside their row's window
+ * go to an exact escape list.  A and E together are the 8-bit view that a low-precision
+ * "Q pass" reads without touching B (same page, Fig. 5(a) and Fig. 7).
+ *
+ * Byte layout of a record (the pages fix only the plane contents; this layout is ours):
+ *   base[n]      u8   lowest biased exponent of row n's window, 1..239 (window = base..base+15)
+ *   ae[n][k]     u8   s<<7 | E<<3 | m[6:4],  E = e - base       (the 8-bit view, row-major)
+ *   lo[n][k/2]   u8   B plane.  For weights k = 8g+i (i = 0..7) the nibble m[3:0] is in byte
+ *                     4g + (i % 4) of the row: low nibble for i < 4, high nibble for i >= 4
+ *   esc_ptr[n+1] u32  row CSR offsets into the escape arrays, esc_ptr[0] = 0
+ *   esc_col[]    u32  column k of each escape, strictly ascending within a row
+ *   esc_val[]    u16  exact bfloat16 bits of each escape
+ * Window rule: the window holds as many of the row's weights as possible; ties go to the
+ * smallest base; a row with no normal weight gets base 1.  Zeros, subnormals, Inf and NaN
+ * (exponent field 0 or 255) are never inside a window, so they are always escapes.  An
+ * escaped slot holds ae = 0 and a zero nibble.  Decoding reproduces every input bit (NaN
+ * payloads and -0 included).
+ *
+ * Conventions for every call:
+ *   - Pointers named as device memory must be device memory of the current HIP device,
+ *     16-byte aligned; the caller owns every buffer and keeps it alive until the stream work
+ *     is finished.  The library allocates nothing on the device and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return
+ *     without synchronising, except w12_encode (see there).
+ *   - Arguments are checked on the host before anything is launched; on a non-zero status
+ *     nothing has been enqueued unless stated, and w12_last_error() returns a message
+ *     (thread-local, valid until the next call on the same thread).  Faults inside kernels
+ *     surface at the caller's next synchronisation, as usual in HIP.
+ *   - The GPU kernels need k % 32 == 0 (W12_ERR_SHAPE otherwise).
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W12_ABI_VERSION 1
+
+/* status codes */
+#define W12_OK            0
+#define W12_ERR_ARG      (-1)  /* null pointer, n, k or m <= 0, unknown flag */
+#define W12_ERR_SHAPE    (-2)  /* k % 32 != 0 */
+#define W12_ERR_ALIGN    (-3)  /* a device pointer is not 16-byte aligned */
+#define W12_ERR_CAPACITY (-4)  /* esc_cap smaller than the escape total (w12_encode) */
+#define W12_ERR_RANGE    (-5)  /* escape total >= 2^32 - 1, or a size overflows */
+#define W12_ERR_HIP      (-6)  /* HIP runtime or launch error; message from hipGetErrorString */
+
+/* flags for the GEMM calls: which kernel family runs */
+#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 8, bf16 MFMA for m >= 9 */
+#define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
+#define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
+
+/* A W12 tensor: a non-owning view.  Every pointer is device memory owned by the caller. */
+typedef struct w12_weight {
+    int64_t   n;        /* output channels (rows of W)  */
+    int64_t   k;        /* input features (columns of W) */
+    uint8_t  *base;     /* [n]                           */
+    uint8_t  *ae;       /* [n * k]                       */
+    uint8_t  *lo;       /* [n * k / 2]                   */
+    uint32_t *esc_ptr;  /* [n + 1]                       */
+    uint32_t *esc_col;  /* [esc_cap]                     */
+    uint16_t *esc_val;  /* [esc_cap]                     */
+    uint64_t  esc_cap;  /* entries available in esc_col / esc_val */
+} w12_weight;
+
+/*
+ * w12_encode -- bfloat16 W [n, k] (device, row-major) -> W12 record `out`.
+ * Implements the plane split, window choice and escape list of Fig. 5(a) (figure-captions
+ * page) under the rules above.  The result is byte-identical to a canonical CPU encoder.
+ * Steps: per-row exponent histogram and window choice (writes base and per-row escape
+ * counts), an in-place scan into esc_ptr, one synchronisation of `stream` to read the
+ * escape total into *n_esc (host pointer), then the pack kernel writes ae, lo and the
+ * escapes.  If out->esc_cap < *n_esc the call returns W12_ERR_CAPACITY after the sync:
+ * base, esc_ptr and *n_esc are valid, ae/lo/escapes are not written; allocate and call
+ * again.  out->n, out->k must be set by the caller.  n_esc may not be NULL.
+ */
+int w12_encode(const uint16_t *w, w12_weight *out, uint64_t *n_esc, void *stream);
+
+/*
+ * w12_decode -- W12 record -> bfloat16 bits W [n, k] (device).  Bit-exact inverse of
+ * w12_encode (the format is lossless: figure-captions page, Fig. 5(a) "exact escape list";
+ * summary page, "Key Contributions" 3).  Reads 1.5 bytes per weight plus metadata, writes 2.
+ */
+int w12_decode(const w12_weight *wt, uint16_t *w_out, void *stream);
+
+/*
+ * w12_gemm -- the exact pass: y[m][n] = sum_k x[m][k] * W[n][k], fp32 accumulate, fp32 y.
+ * x is bfloat16 [m, k] (device, row-major), y is float [m, n] (device, row-major, fully
+ * overwritten).  W is read only through its record: the planes are decoded to bfloat16 in
+ * registers (figure-captions page, Fig. 5(b)) and each escape is patched exactly.
+ * Error bound: |y - y_exact| <= 1e-3 * sum_k |x[m][k] * W[n][k]| per element.
+ */
+int w12_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint32_t flags,
+             void *stream);
+
+/*
+ * w12_q8_gemm -- the Q pass of two-level verification (figure-captions page, Fig. 7):
+ * the same product with every in-window weight taken from the 8-bit view alone (A + E, the
+ * B nibble read as 0, i.e. the bfloat16 bits & 0xFFF0) and escapes exact.  Reads base, ae
+ * and the escape arrays only; wt->lo may be NULL.  Same shapes and error bound as
+ * w12_gemm, against that truncated weight.
+ */
+int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint32_t flags,
+                void *stream);
+
+/*
+ * w12_bf16_gemm -- same-build dense baseline: y = x * W^T with W as plain bfloat16 [n, k]
+ * (device), same kernel structure and flags as w12_gemm, 2 bytes per weight.
+ */
+int w12_bf16_gemm(const uint16_t *x, int64_t m, const uint16_t *w, int64_t n, int64_t k,
+                  float *y, uint32_t flags, void *stream);
+
+/*
+ * w12_read_probe -- bandwidth probe: streams `bytes` bytes of `buf` (device, 16-byte
+ * aligned, bytes % 16 == 0) with 128-bit loads and writes one word per workgroup of a
+ * checksum to `sink` (device, at least 4096 u32).  Measures the achievable HBM read rate.
+ */
+int w12_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char *w12_last_error(void);
+
+/* W12_ABI_VERSION of the loaded library. */
+int w12_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W12_H */

@@ -1,0 +1,191 @@
+// C ABI of libw12.so (declared in include/w12.h): argument checks, path choice, launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "w12.h"
+#include "w12_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return W12_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(W12_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // n, k, m each below 2^31; n*k below 2^62
+
+int check_nk(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return fail(W12_ERR_ARG, "n and k must be positive (n=%lld, k=%lld)",
+                                    (long long)n, (long long)k);
+  if (n >= kMaxDim || k >= kMaxDim) return fail(W12_ERR_RANGE, "n or k too large");
+  if (k % 32 != 0) return fail(W12_ERR_SHAPE, "k must be a multiple of 32 (k=%lld)", (long long)k);
+  return W12_OK;
+}
+
+int check_record(const w12_weight* wt, bool need_lo) {
+  if (!wt) return fail(W12_ERR_ARG, "weight record is NULL");
+  int rc = check_nk(wt->n, wt->k);
+  if (rc) return rc;
+  if (!wt->base || !wt->ae || !wt->esc_ptr || (need_lo && !wt->lo))
+    return fail(W12_ERR_ARG, "a plane pointer of the record is NULL");
+  if (wt->esc_cap > 0 && (!wt->esc_col || !wt->esc_val))
+    return fail(W12_ERR_ARG, "escape arrays are NULL but esc_cap > 0");
+  if (!aligned16(wt->ae) || (need_lo && !aligned16(wt->lo)))
+    return fail(W12_ERR_ALIGN, "ae and lo must be 16-byte aligned");
+  if (!aligned4(wt->esc_ptr) || (wt->esc_col && !aligned4(wt->esc_col)) ||
+      (wt->esc_val && (reinterpret_cast<uintptr_t>(wt->esc_val) & 1u)))
+    return fail(W12_ERR_ALIGN, "escape arrays must be naturally aligned");
+  return W12_OK;
+}
+
+w12::Planes planes_of(const w12_weight* wt) {
+  w12::Planes p;
+  p.base = wt->base;
+  p.ae = wt->ae;
+  p.lo = wt->lo;
+  p.esc_ptr = wt->esc_ptr;
+  p.esc_col = wt->esc_col;
+  p.esc_val = wt->esc_val;
+  return p;
+}
+
+int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n, int64_t k,
+             float* y, uint32_t flags, void* stream) {
+  if (!x || !y) return fail(W12_ERR_ARG, "x or y is NULL");
+  if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
+  if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
+  if (flags > W12_PATH_MFMA) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
+  if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned4(y)) return fail(W12_ERR_ALIGN, "y must be 4-byte aligned");
+  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && m <= 8);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, y, s) : w12::launch_mfma(f, x, m, p, n, k, y, s);
+  if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
+  return ok();
+}
+
+}  // namespace
+
+namespace w12 {
+
+hipError_t dev_info(DevInfo* out) {
+  static std::mutex mu;
+  static DevInfo cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev].device != dev) {
+    DevInfo d;
+    d.device = dev;
+    e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&d.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    cache[dev] = d;
+  }
+  *out = cache[dev];
+  return hipSuccess;
+}
+
+}  // namespace w12
+
+extern "C" {
+
+int w12_abi_version(void) { return W12_ABI_VERSION; }
+
+const char* w12_last_error(void) { return g_err; }
+
+int w12_encode(const uint16_t* w, w12_weight* out, uint64_t* n_esc, void* stream) {
+  if (!w || !out || !n_esc) return fail(W12_ERR_ARG, "w, out or n_esc is NULL");
+  int rc = check_record(out, true);
+  if (rc) return rc;
+  if (!aligned16(w)) return fail(W12_ERR_ALIGN, "w must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n = out->n, k = out->k;
+  hipError_t e = w12::launch_analyze(w, n, k, out->base, out->esc_ptr, s);
+  if (e != hipSuccess) return hip_fail(e, "analyze launch");
+  e = w12::launch_scan(out->esc_ptr, n, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  uint32_t total = 0;
+  e = hipMemcpyAsync(&total, out->esc_ptr + n, sizeof total, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "escape total copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "encode synchronisation");
+  if (total == 0xFFFFFFFFu) {
+    *n_esc = total;
+    return fail(W12_ERR_RANGE, "escape total does not fit the 32-bit CSR");
+  }
+  *n_esc = total;
+  if (out->esc_cap < total)
+    return fail(W12_ERR_CAPACITY, "esc_cap %llu < escape total %u", (unsigned long long)out->esc_cap, total);
+  e = w12::launch_pack(w, n, k, out->base, out->esc_ptr, out->ae, out->lo, out->esc_col, out->esc_val, s);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
+int w12_decode(const w12_weight* wt, uint16_t* w_out, void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  if (!w_out) return fail(W12_ERR_ARG, "w_out is NULL");
+  if (!aligned16(w_out)) return fail(W12_ERR_ALIGN, "w_out must be 16-byte aligned");
+  hipError_t e = w12::launch_decode(planes_of(wt), wt->n, wt->k, w_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int w12_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint32_t flags, void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  return run_gemm(w12::kFmtW12, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream);
+}
+
+int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint32_t flags, void* stream) {
+  int rc = check_record(wt, false);
+  if (rc) return rc;
+  return run_gemm(w12::kFmtQ8, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream);
+}
+
+int w12_bf16_gemm(const uint16_t* x, int64_t m, const uint16_t* w, int64_t n, int64_t k, float* y,
+                  uint32_t flags, void* stream) {
+  if (!w) return fail(W12_ERR_ARG, "w is NULL");
+  int rc = check_nk(n, k);
+  if (rc) return rc;
+  if (!aligned16(w)) return fail(W12_ERR_ALIGN, "w must be 16-byte aligned");
+  w12::Planes p;
+  p.w = w;
+  return run_gemm(w12::kFmtBF16, x, m, p, n, k, y, flags, stream);
+}
+
+int w12_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(W12_ERR_ARG, "buf or sink is NULL");
+  if (bytes == 0 || bytes % 16) return fail(W12_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned16(buf) || !aligned4(sink)) return fail(W12_ERR_ALIGN, "buf must be 16-byte aligned");
+  hipError_t e = w12::launch_read_probe(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return ok();
+}
+
+}  // extern "C"

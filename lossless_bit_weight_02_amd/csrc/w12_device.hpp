@@ -1,0 +1,117 @@
+// Device-side helpers shared by the W12 kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w12 {
+
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 waves per workgroup for every kernel here
+
+// Selectors for v_perm_b32 (bytes 0-3 come from the second source, 4-7 from the first,
+// 0x0C yields a zero byte).  Each builds a pair of 16-bit halves, one per weight, whose high
+// byte is the weight's AE byte and whose low byte carries its B nibble in bits 7..4.
+constexpr uint32_t kSelPair01 = 0x05010400u;  // AE bytes 0,1 over source bytes 0,1
+constexpr uint32_t kSelPair23 = 0x07030602u;  // AE bytes 2,3 over source bytes 2,3
+constexpr uint32_t kSelQ01 = 0x050C040Cu;     // AE bytes 0,1, zero low bytes (B := 0)
+constexpr uint32_t kSelQ23 = 0x070C060Cu;     // AE bytes 2,3, zero low bytes
+
+// An opaque copy of 0x38003800 held in a VGPR.  With the AND mask in an SGPR this lets the
+// compiler fold mask-and-insert into one v_and_or_b32 (gfx9 VOP3 takes no literals and one
+// scalar operand).
+__device__ __forceinline__ uint32_t exp112_pair() {
+  uint32_t v = 0x38003800u;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Two weights of one row -> two bfloat16 "window" values w' in one dword.
+// Input half (per weight): AE byte in bits 15..8 = s | E(4) | m6..4, B nibble in bits 7..4.
+// An arithmetic shift by 4 gives s s s s s | E | m6..4 | B; clearing bit 14 and setting bits
+// 13..11 turns the five sign copies into s 0 1 1 1, i.e. exponent field 0111 EEEE = 112 + E.
+// So w' = (-1)^s * 2^(E - 15) * (1 + m/128): the weight divided by 2^(base - 112).
+__device__ __forceinline__ uint32_t window_pair(uint32_t ae_word, uint32_t lo_word, uint32_t sel,
+                                                uint32_t exp112) {
+  uint32_t u = __builtin_amdgcn_perm(ae_word, lo_word, sel);
+  short2v s = __builtin_bit_cast(short2v, u) >> (short2v){4, 4};
+  return (__builtin_bit_cast(uint32_t, s) & 0xBFFFBFFFu) | exp112;
+}
+
+// Eight consecutive weights (AE words a0: k0..3, a1: k4..7; B word lo for the group) ->
+// four dwords of w' pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7).  The B word holds nibble i of the
+// group at bit 8*(i%4) + 4*(i/4), so the low nibbles (weights 0..3) need one shift by 4 and
+// the high nibbles (weights 4..7) none.
+__device__ __forceinline__ void window_group8(uint32_t a0, uint32_t a1, uint32_t lo, uint32_t exp112,
+                                              uint32_t out[4]) {
+  const uint32_t lo4 = lo << 4;
+  out[0] = window_pair(a0, lo4, kSelPair01, exp112);
+  out[1] = window_pair(a0, lo4, kSelPair23, exp112);
+  out[2] = window_pair(a1, lo, kSelPair01, exp112);
+  out[3] = window_pair(a1, lo, kSelPair23, exp112);
+}
+
+// The 8-bit view alone (Q pass): same as window_group8 with every B nibble 0.
+__device__ __forceinline__ void window_group8_q(uint32_t a0, uint32_t a1, uint32_t exp112,
+                                                uint32_t out[4]) {
+  out[0] = window_pair(a0, a0, kSelQ01, exp112);
+  out[1] = window_pair(a0, a0, kSelQ23, exp112);
+  out[2] = window_pair(a1, a1, kSelQ01, exp112);
+  out[3] = window_pair(a1, a1, kSelQ23, exp112);
+}
+
+// 2^(base - 112) as a float: the factor from w' back to the true weight.  base is 1..239,
+// so the exponent field base + 15 is 16..254 (always a normal float).
+__device__ __forceinline__ float window_scale(uint32_t base) {
+  return __uint_as_float((base + 15u) << 23);
+}
+
+// w' of an escaped slot (AE = 0, B = 0): exponent 112, mantissa 0 -> 2^-15.
+constexpr float kPlaceholder = 3.0517578125e-05f;
+
+__device__ __forceinline__ float bf16_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+// DPP move of a float with row/bank masks; lanes not written keep `old`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWMASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; the total lands in lane 63.
+//  quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: every lane of a row
+//  of 16 holds the row sum; row_bcast:15 (rows 1,3) and row_bcast:31 (rows 2,3) then fold the
+//  four row sums into row 3.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp_f<0xB1, 0xF>(0.0f, v);
+  v += dpp_f<0x4E, 0xF>(0.0f, v);
+  v += dpp_f<0x141, 0xF>(0.0f, v);
+  v += dpp_f<0x140, 0xF>(0.0f, v);
+  v += dpp_f<0x142, 0xA>(0.0f, v);
+  v += dpp_f<0x143, 0xC>(0.0f, v);
+  return v;
+}
+
+// Non-temporal 128-bit load: weight planes are streamed once, keep them out of the caches'
+// reuse set.
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+}  // namespace w12

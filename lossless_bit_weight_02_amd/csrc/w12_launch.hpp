@@ -1,0 +1,50 @@
+// Host-side launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w12 {
+
+enum Fmt : int { kFmtW12 = 0, kFmtQ8 = 1, kFmtBF16 = 2 };
+
+struct DevInfo {
+  int device = -1;
+  int cus = 0;          // compute units
+  int max_lds = 0;      // bytes of LDS one workgroup may use
+};
+// Properties of the current device (cached per device id).
+hipError_t dev_info(DevInfo* out);
+
+struct Planes {
+  const uint8_t* base = nullptr;
+  const uint8_t* ae = nullptr;
+  const uint8_t* lo = nullptr;
+  const uint32_t* esc_ptr = nullptr;
+  const uint32_t* esc_col = nullptr;
+  const uint16_t* esc_val = nullptr;
+  const uint16_t* w = nullptr;  // kFmtBF16 only: the dense bfloat16 weight
+};
+
+// encoder: window choice per row (writes base[n] and the escape count of row i to esc_ptr[i+1])
+hipError_t launch_analyze(const uint16_t* w, int64_t n, int64_t k, uint8_t* base, uint32_t* esc_ptr,
+                          hipStream_t s);
+// encoder: in-place inclusive scan of esc_ptr[1..n], esc_ptr[0] = 0; totals >= 2^32-1 saturate
+hipError_t launch_scan(uint32_t* esc_ptr, int64_t n, hipStream_t s);
+// encoder: planes and escapes
+hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* base,
+                       const uint32_t* esc_ptr, uint8_t* ae, uint8_t* lo, uint32_t* esc_col,
+                       uint16_t* esc_val, hipStream_t s);
+// decoder: planes -> bfloat16 bits, then every escape written over its slot
+hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
+// bandwidth probe
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
+
+// GEMV family (wave-reduction kernel), any m (passes of <= 8 rows of x)
+hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
+                       float* y, hipStream_t s);
+// MFMA family (bf16 v_mfma_f32_16x16x32), any m (blocks of <= 64 rows of x)
+hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
+                       float* y, hipStream_t s);
+
+}  // namespace w12

@@ -1,0 +1,233 @@
+"""Python binding of libw12.so (ctypes): argument marshalling over torch device tensors.
+
+Every step runs in the HIP library; this module only allocates the output tensors with torch,
+passes raw device pointers and the current stream, and turns non-zero statuses into W12Error.
+If the library is missing, loading fails loudly: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw12.so")
+
+W12_OK = 0
+W12_ERR_ARG = -1
+W12_ERR_SHAPE = -2
+W12_ERR_ALIGN = -3
+W12_ERR_CAPACITY = -4
+W12_ERR_RANGE = -5
+W12_ERR_HIP = -6
+
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+_PATHS = {None: PATH_AUTO, "auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
+
+
+class W12Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"w12 status {status}: {msg}")
+        self.status = status
+
+
+class _W12Weight(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("base", ctypes.c_void_p), ("ae", ctypes.c_void_p), ("lo", ctypes.c_void_p),
+                ("esc_ptr", ctypes.c_void_p), ("esc_col", ctypes.c_void_p),
+                ("esc_val", ctypes.c_void_p), ("esc_cap", ctypes.c_uint64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+# name -> (restype, argtypes)
+EXPORTS = {
+    "w12_abi_version": (ctypes.c_int, []),
+    "w12_last_error": (ctypes.c_char_p, []),
+    "w12_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_W12Weight),
+                                  ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]),
+    "w12_decode": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_void_p, ctypes.c_void_p]),
+    "w12_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_q8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                   ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_bf16_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded library (raises if it was never built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m lossless_bit_weight_02_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in EXPORTS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            if L.w12_abi_version() != 1:
+                raise RuntimeError("libw12.so ABI version mismatch")
+            _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != W12_OK:
+        raise W12Error(status, lib().w12_last_error().decode(errors="replace"))
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected bfloat16 (or 16-bit raw bits), got {t.dtype}")
+
+
+class W12Weight:
+    """A W12 record held as torch device tensors (layout of include/w12.h)."""
+
+    def __init__(self, n, k, base, ae, lo, esc_ptr, esc_col, esc_val):
+        self.n, self.k = int(n), int(k)
+        self.base, self.ae, self.lo = base, ae, lo
+        self.esc_ptr, self.esc_col, self.esc_val = esc_ptr, esc_col, esc_val
+
+    @property
+    def n_esc(self) -> int:
+        return int(self.esc_col.numel())
+
+    @property
+    def device(self):
+        return self.ae.device
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.base, self.ae, self.lo, self.esc_ptr, self.esc_col, self.esc_val))
+
+    def bits_per_weight(self) -> float:
+        return 8.0 * self.nbytes() / (self.n * self.k)
+
+    def c_struct(self) -> _W12Weight:
+        return _W12Weight(self.n, self.k, _ptr(self.base), _ptr(self.ae), _ptr(self.lo),
+                          _ptr(self.esc_ptr), _ptr(self.esc_col), _ptr(self.esc_val),
+                          self.esc_col.numel())
+
+    def clone(self) -> "W12Weight":
+        return W12Weight(self.n, self.k, *(t.clone() for t in
+                                           (self.base, self.ae, self.lo, self.esc_ptr,
+                                            self.esc_col, self.esc_val)))
+
+    def to_numpy(self) -> dict:
+        """Host copies of every array (uint8/uint32/uint16 numpy arrays)."""
+        def host(t, dt):
+            return t.cpu().numpy().view(dt)
+        import numpy as np
+        return dict(n=self.n, k=self.k, base=host(self.base, np.uint8),
+                    ae=host(self.ae, np.uint8).reshape(self.n, self.k),
+                    lo=host(self.lo, np.uint8).reshape(self.n, self.k // 2),
+                    esc_ptr=host(self.esc_ptr, np.uint32), esc_col=host(self.esc_col, np.uint32),
+                    esc_val=host(self.esc_val, np.uint16))
+
+
+def encode(w: torch.Tensor, esc_guess: int | None = None) -> W12Weight:
+    """bfloat16 W [n, k] on the GPU -> W12Weight (one host synchronisation for the escape total)."""
+    w = _bits16(w)
+    if w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D CUDA tensor")
+    w = w.contiguous()
+    n, k = w.shape
+    dev = w.device
+    u8, i32, i16 = torch.uint8, torch.int32, torch.int16
+    base = torch.empty(n, dtype=u8, device=dev)
+    ae = torch.empty(n * k, dtype=u8, device=dev)
+    lo = torch.empty(n * k // 2, dtype=u8, device=dev)
+    esc_ptr = torch.empty(n + 1, dtype=i32, device=dev)
+    cap = max(1024, (n * k) // 256) if esc_guess is None else max(1, int(esc_guess))
+    esc_col = torch.empty(cap, dtype=i32, device=dev)
+    esc_val = torch.empty(cap, dtype=i16, device=dev)
+    n_esc = ctypes.c_uint64(0)
+    L = lib()
+    def run():
+        s = _W12Weight(n, k, base.data_ptr(), ae.data_ptr(), lo.data_ptr(),
+                       esc_ptr.data_ptr(), esc_col.data_ptr(), esc_val.data_ptr(), esc_col.numel())
+        return L.w12_encode(w.data_ptr(), ctypes.byref(s), ctypes.byref(n_esc), _stream_handle(dev))
+
+    st = run()
+    if st == W12_ERR_CAPACITY:  # the first guess was too small: size exactly and encode again
+        esc_col = torch.empty(max(1, n_esc.value), dtype=i32, device=dev)
+        esc_val = torch.empty(max(1, n_esc.value), dtype=i16, device=dev)
+        st = run()
+    _check(st)
+    ne = n_esc.value
+    return W12Weight(n, k, base, ae, lo, esc_ptr, esc_col[:ne], esc_val[:ne])
+
+
+def decode(wt: W12Weight) -> torch.Tensor:
+    """W12Weight -> bfloat16 W [n, k] (bit-exact)."""
+    out = torch.empty((wt.n, wt.k), dtype=torch.bfloat16, device=wt.device)
+    s = wt.c_struct()
+    _check(lib().w12_decode(ctypes.byref(s), out.data_ptr(), _stream_handle(wt.device)))
+    return out
+
+
+def _gemm_out(x, n):
+    x = _bits16(x)
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D CUDA tensor")
+    return x.contiguous(), torch.empty((x.shape[0], n), dtype=torch.float32, device=x.device)
+
+
+def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None):
+    """Exact pass: y = x W^T (fp32) with W read from its W12 record."""
+    if out is None:
+        x, out = _gemm_out(x, wt.n)
+    s = wt.c_struct()
+    _check(lib().w12_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
+                          _PATHS[path], _stream_handle(x.device)))
+    return out
+
+
+def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None):
+    """Q pass: y = x W_q^T with W_q the 8-bit view (B plane taken as 0), escapes exact."""
+    if out is None:
+        x, out = _gemm_out(x, wt.n)
+    s = wt.c_struct()
+    s.lo = None
+    _check(lib().w12_q8_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
+                             _PATHS[path], _stream_handle(x.device)))
+    return out
+
+
+def bf16_gemm(x: torch.Tensor, w: torch.Tensor, path: str | None = None, out: torch.Tensor | None = None):
+    """Same-build dense baseline: y = x W^T with W plain bfloat16."""
+    w = _bits16(w).contiguous()
+    if out is None:
+        x, out = _gemm_out(x, w.shape[0])
+    _check(lib().w12_bf16_gemm(x.data_ptr(), x.shape[0], w.data_ptr(), w.shape[0], w.shape[1],
+                               out.data_ptr(), _PATHS[path], _stream_handle(x.device)))
+    return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None):
+    """Stream every byte of ``buf`` through the read-bandwidth probe kernel."""
+    if sink is None:
+        sink = torch.zeros(4096, dtype=torch.int32, device=buf.device)
+    _check(lib().w12_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                _stream_handle(buf.device)))
+    return sink

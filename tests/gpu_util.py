@@ -1,0 +1,63 @@
+"""Helpers for the GPU parity tests: device transfer and the element-wise bound check."""
+import sys
+
+import numpy as np
+
+import oracle
+
+
+def say(msg: str):
+    """Print what is about to run on the GPU (flushed, so a crash still names the case)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray, device="cuda:0"):
+    import torch
+    a = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+def to_host_bits(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def record_numpy(rec) -> oracle.W12Record:
+    d = rec.to_numpy()
+    return oracle.W12Record(d["n"], d["k"], d["base"], d["ae"], d["lo"], d["esc_ptr"],
+                            d["esc_col"], d["esc_val"])
+
+
+def assert_records_equal(got: oracle.W12Record, want: oracle.W12Record, what=""):
+    assert got.n == want.n and got.k == want.k
+    for name in ("base", "ae", "lo", "esc_ptr", "esc_col", "esc_val"):
+        a, b = getattr(got, name), getattr(want, name)
+        assert a.shape == b.shape, f"{what}: {name} shape {a.shape} != {b.shape}"
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            raise AssertionError(f"{what}: {name} differs at {bad[:5].tolist()} "
+                                 f"({len(bad)} positions)")
+
+
+def check_gemm(y_gpu: np.ndarray, x_bits, w_bits, what="", rel=1e-3):
+    """|y - y64| <= rel * sum|x w| for finite oracle values; non-finite oracle values must be
+    matched in kind (NaN with NaN, +-Inf with the same Inf).  Returns the worst error / bound."""
+    y = np.asarray(y_gpu, dtype=np.float64)
+    y64 = oracle.gemm64(x_bits, w_bits)
+    bound = rel * oracle.abs_bound64(x_bits, w_bits)
+    fin = np.isfinite(y64)
+    nan = np.isnan(y64)
+    inf = ~fin & ~nan
+    assert np.all(np.isnan(y[nan])), f"{what}: NaN expected"
+    assert np.array_equal(y[inf], y64[inf]), f"{what}: Inf mismatch"
+    err = np.abs(y[fin] - y64[fin])
+    ok = err <= bound[fin]
+    if not np.all(ok):
+        idx = np.argwhere(fin)[~ok][:5]
+        raise AssertionError(f"{what}: {np.count_nonzero(~ok)} elements outside the bound, first "
+                             f"{idx.tolist()} y={y[tuple(idx.T)]} ref={y64[tuple(idx.T)]} "
+                             f"bound={bound[tuple(idx.T)]}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(bound[fin] > 0, err / bound[fin], 0.0)
+    return float(r.max()) if r.size else 0.0
