@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the W12 hot path on one MI355X.
+
+Metric: W12 GEMM effective HBM GB/s (algorithmic bytes / kernel time) at M=1 and M=32, and the
+speedup over the same-build BF16 kernel.  Workload: the fused MLP gate+up projection of a
+27B-class dense model, W bf16 [34816, 5120] (synthetic weights, see
+lossless_bit_weight_02_amd/synth.py), activations x bf16 [M, 5120].
+
+One step = one pass of the whole path over one batch of R weight matrices (R copies of the
+gate+up weight, >= 1.1 GB per format, so every launch streams from HBM and not from the 256 MB
+Infinity Cache):
+  encode x R (window choice + plane packing + escape CSR, one host sync each) -> decode x R ->
+  read probe over 2 GiB (measured ceiling; also evicts the dirty lines the encoder and decoder
+  left in the caches, so their write-back does not overlap the GEMMs) -> exact W12 GEMM M=1
+  (GEMV) x R -> exact W12 GEMM M=32 (MFMA) x R -> Q-pass GEMM on the 8-bit view M=16 x R ->
+  same-build BF16 GEMM M=1 x R and M=32 x R.
+Each op's R back-to-back launches are bracketed by one pair of HIP events on the stream they run
+on; the per-launch time is the elapsed time / R.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor peak
+MFMA_BF16_PEAK_TFS = 2500.0      # dense bf16
+K_HIDDEN = 5120
+N_GATE_UP = 34816
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w12_gemv_m1_gate_up_traffic.md")
+KERNEL_SOURCES = ["lossless_bit_weight_02_amd/csrc/gemv.hip", "lossless_bit_weight_02_amd/csrc/w12_device.hpp"]
+
+
+def w12_bytes(n, k, n_esc, m):
+    """Algorithmic bytes of one exact W12 GEMM: planes, base, esc_ptr, escapes, x and y."""
+    return n * k * 1.5 + n + 4 * (n + 1) + 6 * n_esc + 2 * m * k + 4 * m * n
+
+
+def q8_bytes(n, k, n_esc, m):
+    return n * k * 1.0 + n + 4 * (n + 1) + 6 * n_esc + 2 * m * k + 4 * m * n
+
+
+def bf16_bytes(n, k, m):
+    return n * k * 2.0 + 2 * m * k + 4 * m * n
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the M=1 W12 GEMV from the committed rocprofv3 --pmc summary, or
+    None if there is none or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_count():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w_bits, x_bits, gpu_out, rows):
+    """Time the oracle (as it stands) on the first `rows` rows of the workload, and check the
+    GPU outputs of the timed step on the same rows."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    ws = w_bits[:rows]
+    t0 = time.perf_counter()
+    rec = oracle.encode(ws)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    dec = oracle.decode(rec)
+    t_dec = time.perf_counter() - t0
+    assert np.array_equal(dec, ws)
+    t0 = time.perf_counter()
+    y1 = oracle.w12_gemm64(x_bits[:1], rec)
+    t_g1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    y32 = oracle.w12_gemm64(x_bits[:32], rec)
+    t_g32 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    yq = oracle.q8_gemm64(x_bits[:16], rec)
+    t_q = time.perf_counter() - t0
+    total = t_enc + t_dec + t_g1 + t_g32 + t_q
+
+    # parity of the timed GPU outputs on these rows (same bar as the tests)
+    worst = 0.0
+    for name, y, xb, wref in (("w12_m1", y1, x_bits[:1], ws), ("w12_m32", y32, x_bits[:32], ws),
+                              ("q8_m16", yq, x_bits[:16], oracle.q8_view_bits(rec))):
+        g = gpu_out[name][:, :rows].astype(np.float64)
+        bound = 1e-3 * oracle.abs_bound64(xb, wref)
+        err = np.abs(g - y)
+        if not np.all(err <= bound):
+            raise SystemExit(f"parity failure in {name}: GPU output outside the bound")
+        worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+    blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    gbs = w12_bytes(rows, ws.shape[1], rec.n_esc, 1) / t_g1 / 1e9
+    return {
+        "value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"first {rows} of {w_bits.shape[0]} rows of the gate+up matrix; oracle encode "
+                  f"{t_enc:.2f}s, decode {t_dec:.2f}s, exact GEMM M=1 {t_g1:.2f}s (value: W12 "
+                  f"bytes / this time), M=32 {t_g32:.2f}s, Q8 M=16 {t_q:.2f}s; numpy, BLAS threads "
+                  f"{blas} of {cpu_count()} host cores",
+        "seconds": round(total, 3),
+        "parity_worst_err_over_bound": round(worst, 5),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the M sweep (crossover)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 192 MiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--min-rot-bytes", type=float, default=1.1e9)
+    a = ap.parse_args()
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the W12 path here is a single-GPU kernel set "
+              "(multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lossless_bit_weight_02_amd import synth, w12
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    spec = synth.CONFIGS["gate_up"].weights[0][2]
+    tid = synth.CONFIGS["gate_up"].weights[0][0]
+    n, k = spec.n, spec.k
+    t0 = time.perf_counter()
+    w_bits = synth.gen_weight(spec, 0, tid)
+    x_bits = synth.gen_x(64, k, tensor_id=tid)
+    t_gen = time.perf_counter() - t0
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    w_dev = to_dev(w_bits)
+    rec0 = w12.encode(w_dev)
+    n_esc = rec0.n_esc
+    rec_bytes = rec0.nbytes()
+    rot = max(2, int(np.ceil(a.min_rot_bytes / rec_bytes)))
+    recs = [rec0] + [rec0.clone() for _ in range(rot - 1)]
+    wcopies = [w_dev] + [w_dev.clone() for _ in range(rot - 1)]
+    x1, x16, x32 = to_dev(x_bits[:1]), to_dev(x_bits[:16]), to_dev(x_bits[:32])
+    y1 = torch.empty((1, n), dtype=torch.float32, device=dev)
+    y16 = torch.empty((16, n), dtype=torch.float32, device=dev)
+    y32 = torch.empty((32, n), dtype=torch.float32, device=dev)
+    yb1 = torch.empty_like(y1)
+    yb32 = torch.empty_like(y32)
+    dec_out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+
+    # encode target: a preallocated record reused every step (escape arrays sized once)
+    enc = rec0.clone()
+    enc_struct = enc.c_struct()
+    import ctypes
+    n_esc_c = ctypes.c_uint64(0)
+
+    def do_encode(wd):
+        st = w12.lib().w12_encode(wd.data_ptr(), ctypes.byref(enc_struct), ctypes.byref(n_esc_c),
+                                  stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(w12.lib().w12_last_error())
+
+    probe_buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+
+    # (name, launches per step, fn(copy index))
+    ops = [
+        ("encode", rot, lambda r: do_encode(wcopies[r])),
+        ("decode", rot, lambda r: w12.decode_into(recs[r], dec_out)),
+        ("read_probe", 1, lambda r: w12.read_probe(probe_buf, sink)),
+        ("w12_m1", rot, lambda r: w12.gemm(x1, recs[r], path="gemv", out=y1)),
+        ("w12_m32", rot, lambda r: w12.gemm(x32, recs[r], path="mfma", out=y32)),
+        ("q8_m16", rot, lambda r: w12.q8_gemm(x16, recs[r], path="mfma", out=y16)),
+        ("bf16_m1", rot, lambda r: w12.bf16_gemm(x1, wcopies[r], path="gemv", out=yb1)),
+        ("bf16_m32", rot, lambda r: w12.bf16_gemm(x32, wcopies[r], path="mfma", out=yb32)),
+    ]
+
+    def step(evs=None):
+        for j, (_, reps, fn) in enumerate(ops):
+            if evs is not None:
+                evs[2 * j].record(stream)
+            for r in range(reps):
+                fn(r)
+            if evs is not None:
+                evs[2 * j + 1].record(stream)
+
+    for i in range(a.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(ops))] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(a.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    per_op = {name: [] for name, _, _ in ops}
+    for evs in events:
+        for j, (name, reps, _) in enumerate(ops):
+            per_op[name].append(evs[2 * j].elapsed_time(evs[2 * j + 1]) * 1e-3 / reps)
+    mean = {name: float(np.mean(v)) for name, v in per_op.items()}
+    med = {name: float(np.median(v)) for name, v in per_op.items()}
+
+    gpu_out = {"w12_m1": y1.cpu().numpy(), "w12_m32": y32.cpu().numpy(), "q8_m16": y16.cpu().numpy()}
+
+    b_w12_1 = w12_bytes(n, k, n_esc, 1)
+    b_w12_32 = w12_bytes(n, k, n_esc, 32)
+    gbs = {
+        "w12_m1": b_w12_1 / mean["w12_m1"] / 1e9,
+        "w12_m32": b_w12_32 / mean["w12_m32"] / 1e9,
+        "q8_m16": q8_bytes(n, k, n_esc, 16) / mean["q8_m16"] / 1e9,
+        "bf16_m1": bf16_bytes(n, k, 1) / mean["bf16_m1"] / 1e9,
+        "bf16_m32": bf16_bytes(n, k, 32) / mean["bf16_m32"] / 1e9,
+        "decode": (1.5 * n * k + n + 4 * (n + 1) + 6 * n_esc + 2 * n * k) / mean["decode"] / 1e9,
+        "encode": (2 * n * k + 1.5 * n * k + n + 4 * (n + 1) + 6 * n_esc) / mean["encode"] / 1e9,
+    }
+
+    probe_gbs = probe_buf.numel() / mean["read_probe"] / 1e9
+    del probe_buf
+
+    if a.calibrate_copy:
+        src = torch.empty(192 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    sweep = None
+    if not a.no_sweep:
+        sweep = {}
+        xs = to_dev(x_bits)
+        for m in (1, 4, 8, 16, 32, 64):
+            xm = xs[:m].contiguous()
+            ym = torch.empty((m, n), dtype=torch.float32, device=dev)
+            row = {}
+            for path in ("gemv", "mfma"):
+                for fmt in ("w12", "bf16"):
+                    def run(r, fmt=fmt, path=path):
+                        if fmt == "w12":
+                            w12.gemm(xm, recs[r], path=path, out=ym)
+                        else:
+                            w12.bf16_gemm(xm, wcopies[r], path=path, out=ym)
+                    run(0)
+                    reps = 2 * rot
+                    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    ea.record(stream)
+                    for r in range(reps):
+                        run(r % rot)
+                    eb.record(stream)
+                    torch.cuda.synchronize()
+                    t = ea.elapsed_time(eb) * 1e-3 / reps
+                    byt = w12_bytes(n, k, n_esc, m) if fmt == "w12" else bf16_bytes(n, k, m)
+                    row[f"{fmt}_{path}_us"] = round(t * 1e6, 2)
+                    row[f"{fmt}_{path}_gbs"] = round(byt / t / 1e9, 1)
+            row["best_w12_path"] = "gemv" if row["w12_gemv_us"] <= row["w12_mfma_us"] else "mfma"
+            sweep[str(m)] = row
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(w_bits, x_bits, gpu_out, min(a.cpu_rows, n))
+
+    value = gbs["w12_m1"]
+    traffic = measured_traffic()
+    out = {
+        "metric": "W12 GEMM effective HBM GB/s (and % of peak) at M=1 and M=32; speedup vs BF16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mlp_gate_up_fused W bf16 [34816,5120] (27B-class projection), "
+                               "x bf16 [M,5120]; value at M=1, also M=32",
+                   "n": n, "k": k, "m_values": [1, 32], "rotation_copies": rot,
+                   "escapes": n_esc, "bits_per_weight": round(8.0 * rec_bytes / (n * k), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 1),
+                     "kernel": "k_gemv<W12, M=1>", "bytes_per_launch": round(b_w12_1, 1),
+                     "avg_launch_us": round(mean["w12_m1"] * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "m32": {"gbs": round(gbs["w12_m32"], 2), "frac_hbm": round(gbs["w12_m32"] / HBM_PEAK_GBS, 4),
+                "tflops": round(2 * 32 * n * k / mean["w12_m32"] / 1e12, 2),
+                "frac_mfma_bf16": round(2 * 32 * n * k / mean["w12_m32"] / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+        "speedup_vs_bf16": {"m1": round(mean["bf16_m1"] / mean["w12_m1"], 4),
+                            "m32": round(mean["bf16_m32"] / mean["w12_m32"], 4)},
+        "ops_us_mean": {kk: round(v * 1e6, 3) for kk, v in mean.items()},
+        "ops_us_median": {kk: round(v * 1e6, 3) for kk, v in med.items()},
+        "ops_gbs": {kk: round(v, 1) for kk, v in gbs.items()},
+        "read_probe_gbs": round(probe_gbs, 1),
+        "w12_m1_frac_of_probe": round(value / probe_gbs, 4),
+        "sweep": sweep,
+        "setup_s": {"generate": round(t_gen, 2)},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -228,24 +228,29 @@ __global__ __launch_bounds__(kBlock) void k_escape_scatter(const uint32_t* __res
 }
 
 // ---------------------------------------------------------------------------------------------
-// Read probe: every thread streams 128-bit words, folds them with XOR, one word per workgroup.
+// Read probe: every wave streams contiguous 1 KiB lines (one 128-bit word per lane), four lines
+// in flight, and folds them with XOR; one word per workgroup goes to the sink.
 // ---------------------------------------------------------------------------------------------
+constexpr int kProbeLines = 4;
+
 __global__ __launch_bounds__(kBlock) void k_read_probe(const u32x4* __restrict__ buf, uint64_t words,
                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t wave = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint64_t nwaves = (uint64_t)gridDim.x * 4;
   uint32_t acc = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-  for (; i + 3 * stride < words; i += 4 * stride) {
-    const u32x4 a = load_nt(buf + i), b = load_nt(buf + i + stride);
-    const u32x4 c = load_nt(buf + i + 2 * stride), d = load_nt(buf + i + 3 * stride);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-  }
-  for (; i < words; i += stride) {
-    const u32x4 a = load_nt(buf + i);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  for (uint64_t t = wave * 64 * kProbeLines; t < words; t += nwaves * 64 * kProbeLines) {
+    u32x4 v[kProbeLines];
+#pragma unroll
+    for (int u = 0; u < kProbeLines; ++u) {
+      const uint64_t i = t + (uint64_t)u * 64 + lane;
+      v[u] = i < words ? load_nt(buf + i) : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeLines; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off);
-  if ((threadIdx.x & 63) == 0) atomicXor(&sink[blockIdx.x & 4095], acc);
+  if (lane == 0) atomicXor(&sink[blockIdx.x & 4095], acc);
 }
 
 // ---------------------------------------------------------------------------------------------

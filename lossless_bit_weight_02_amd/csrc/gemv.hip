@@ -39,9 +39,10 @@ struct GemvArgs {
 };
 
 constexpr int kStep = 1024;  // k per wave per step: 64 lanes x 16
-constexpr int kUnroll = 4;   // steps whose loads are issued together
 
-template <int FMT, int M>
+// R rows per wave task (their loads interleave, so a wave keeps 2*U*R loads in flight), U steps
+// of 1024 k issued together.
+template <int FMT, int M, int R, int U>
 __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   extern __shared__ u32x4 xs[];  // [M][kn / 8] in 16-byte words
   const int tid = threadIdx.x, lane = tid & 63;
@@ -57,114 +58,136 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   const uint32_t e112 = exp112_pair();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t tasks = (a.n + R - 1) / R;
 
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.n; row += nwaves) {
-    float acc[M];
+  for (int64_t task = (int64_t)blockIdx.x * 4 + wave; task < tasks; task += nwaves) {
+    const int64_t row0 = task * R;
+    float acc[R][M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-    const uint8_t* aer = nullptr;
-    const uint8_t* lor = nullptr;
-    const uint16_t* wr = nullptr;
-    if constexpr (FMT == kFmtBF16) {
-      wr = a.w + row * a.k + a.k0;
-    } else {
-      aer = a.ae + row * a.k + a.k0;
-      if constexpr (FMT == kFmtW12) lor = a.lo + row * (a.k >> 1) + (a.k0 >> 1);
-    }
-
-    for (int kb = lane * 16; kb < kn; kb += kStep * kUnroll) {
-      u32x4 A[kUnroll], A2[kUnroll];
-      u32x2 L[kUnroll];
+    // rows past the end of W (last task only) read the last row; their results are dropped
+    const uint8_t* aer[R];
+    const uint8_t* lor[R];
+    const uint16_t* wr[R];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kk = kb + u * kStep;
-        if (kk < kn) {
-          if constexpr (FMT == kFmtBF16) {
-            A[u] = load_nt(reinterpret_cast<const u32x4*>(wr + kk));
-            A2[u] = load_nt(reinterpret_cast<const u32x4*>(wr + kk + 8));
-          } else {
-            A[u] = load_nt(reinterpret_cast<const u32x4*>(aer + kk));
-            if constexpr (FMT == kFmtW12) L[u] = load_nt(reinterpret_cast<const u32x2*>(lor + (kk >> 1)));
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kk = kb + u * kStep;
-        if (kk < kn) {
-          uint32_t p[8];
-          if constexpr (FMT == kFmtBF16) {
-            p[0] = A[u].x; p[1] = A[u].y; p[2] = A[u].z; p[3] = A[u].w;
-            p[4] = A2[u].x; p[5] = A2[u].y; p[6] = A2[u].z; p[7] = A2[u].w;
-          } else if constexpr (FMT == kFmtW12) {
-            window_group8(A[u].x, A[u].y, L[u].x, e112, p);
-            window_group8(A[u].z, A[u].w, L[u].y, e112, p + 4);
-          } else {
-            window_group8_q(A[u].x, A[u].y, e112, p);
-            window_group8_q(A[u].z, A[u].w, e112, p + 4);
-          }
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const u32x4 x0 = xs[m * kn8 + (kk >> 3)];
-            const u32x4 x1 = xs[m * kn8 + (kk >> 3) + 1];
-            float s = acc[m];
-            s = dot2_bf16(p[0], x0.x, s);
-            s = dot2_bf16(p[1], x0.y, s);
-            s = dot2_bf16(p[2], x0.z, s);
-            s = dot2_bf16(p[3], x0.w, s);
-            s = dot2_bf16(p[4], x1.x, s);
-            s = dot2_bf16(p[5], x1.y, s);
-            s = dot2_bf16(p[6], x1.z, s);
-            s = dot2_bf16(p[7], x1.w, s);
-            acc[m] = s;
-          }
-        }
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
+      aer[r] = nullptr; lor[r] = nullptr; wr[r] = nullptr;
+      if constexpr (FMT == kFmtBF16) {
+        wr[r] = a.w + row * a.k + a.k0;
+      } else {
+        aer[r] = a.ae + row * a.k + a.k0;
+        if constexpr (FMT == kFmtW12) lor[r] = a.lo + row * (a.k >> 1) + (a.k0 >> 1);
       }
     }
 
-    if constexpr (FMT != kFmtBF16) {
-      // Escapes of this row inside the slice: remove the placeholder x * 2^-15 from the dense
-      // sum P and collect the exact part Q = sum x * v separately, so that y = 2^(base-112) P + Q
-      // rounds only once per reduction (a one-hot x then returns every weight exactly).
-      const uint32_t e0 = a.esc_ptr[row], e1 = a.esc_ptr[row + 1];
-      const bool has_esc = e1 > e0;
-      float q[M];
+    for (int kb = lane * 16; kb < kn; kb += kStep * U) {
+      u32x4 A[R][U], A2[R][U];
+      u32x2 L[R][U];
 #pragma unroll
-      for (int m = 0; m < M; ++m) q[m] = 0.0f;
-      if (has_esc) {
-        for (uint32_t e = e0 + lane; e < e1; e += 64) {
-          const int64_t c = (int64_t)a.esc_col[e] - a.k0;
-          if (c >= 0 && c < kn) {
-            const float v = bf16_to_float(a.esc_val[e]);
+      for (int u = 0; u < U; ++u) {
+        const int kk = kb + u * kStep;
+        if (kk < kn) {
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const float xv = bf16_to_float(xs16[m * kn + c]);
-              acc[m] = fmaf(-xv, kPlaceholder, acc[m]);
-              q[m] = fmaf(xv, v, q[m]);
+          for (int r = 0; r < R; ++r) {
+            if constexpr (FMT == kFmtBF16) {
+              A[r][u] = load_nt(reinterpret_cast<const u32x4*>(wr[r] + kk));
+              A2[r][u] = load_nt(reinterpret_cast<const u32x4*>(wr[r] + kk + 8));
+            } else {
+              A[r][u] = load_nt(reinterpret_cast<const u32x4*>(aer[r] + kk));
+              if constexpr (FMT == kFmtW12) L[r][u] = load_nt(reinterpret_cast<const u32x2*>(lor[r] + (kk >> 1)));
             }
           }
         }
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = wave_sum_to_lane63(acc[m]);
-      if (has_esc) {
+      for (int u = 0; u < U; ++u) {
+        const int kk = kb + u * kStep;
+        if (kk < kn) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) q[m] = wave_sum_to_lane63(q[m]);
+          for (int r = 0; r < R; ++r) {
+            uint32_t p[8];
+            if constexpr (FMT == kFmtBF16) {
+              p[0] = A[r][u].x; p[1] = A[r][u].y; p[2] = A[r][u].z; p[3] = A[r][u].w;
+              p[4] = A2[r][u].x; p[5] = A2[r][u].y; p[6] = A2[r][u].z; p[7] = A2[r][u].w;
+            } else if constexpr (FMT == kFmtW12) {
+              window_group8(A[r][u].x, A[r][u].y, L[r][u].x, e112, p);
+              window_group8(A[r][u].z, A[r][u].w, L[r][u].y, e112, p + 4);
+            } else {
+              window_group8_q(A[r][u].x, A[r][u].y, e112, p);
+              window_group8_q(A[r][u].z, A[r][u].w, e112, p + 4);
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              const u32x4 x0 = xs[m * kn8 + (kk >> 3)];
+              const u32x4 x1 = xs[m * kn8 + (kk >> 3) + 1];
+              float s = acc[r][m];
+              s = dot2_bf16(p[0], x0.x, s);
+              s = dot2_bf16(p[1], x0.y, s);
+              s = dot2_bf16(p[2], x0.z, s);
+              s = dot2_bf16(p[3], x0.w, s);
+              s = dot2_bf16(p[4], x1.x, s);
+              s = dot2_bf16(p[5], x1.y, s);
+              s = dot2_bf16(p[6], x1.z, s);
+              s = dot2_bf16(p[7], x1.w, s);
+              acc[r][m] = s;
+            }
+          }
+        }
       }
-      const float sc = window_scale(a.base[row]);
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = fmaf(sc, acc[m], q[m]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = wave_sum_to_lane63(acc[m]);
     }
 
-    if (lane == 63) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float* yp = a.y + m * a.ldy + row;
-        *yp = a.accumulate ? *yp + acc[m] : acc[m];
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      if (row >= a.n) break;
+      float* acr = acc[r];
+      if constexpr (FMT != kFmtBF16) {
+        // Escapes of this row inside the slice: remove the placeholder x * 2^-15 from the dense
+        // sum P and collect the exact part Q = sum x * v separately, so that
+        // y = 2^(base-112) P + Q rounds only once per reduction (a one-hot x then returns every
+        // weight exactly).
+        const uint32_t e0 = a.esc_ptr[row], e1 = a.esc_ptr[row + 1];
+        const bool has_esc = e1 > e0;
+        float q[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) q[m] = 0.0f;
+        if (has_esc) {
+          for (uint32_t e = e0 + lane; e < e1; e += 64) {
+            const int64_t c = (int64_t)a.esc_col[e] - a.k0;
+            if (c >= 0 && c < kn) {
+              const float v = bf16_to_float(a.esc_val[e]);
+#pragma unroll
+              for (int m = 0; m < M; ++m) {
+                const float xv = bf16_to_float(xs16[m * kn + c]);
+                acr[m] = fmaf(-xv, kPlaceholder, acr[m]);
+                q[m] = fmaf(xv, v, q[m]);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) acr[m] = wave_sum_to_lane63(acr[m]);
+        if (has_esc) {
+#pragma unroll
+          for (int m = 0; m < M; ++m) q[m] = wave_sum_to_lane63(q[m]);
+        }
+        const float sc = window_scale(a.base[row]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) acr[m] = fmaf(sc, acr[m], q[m]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m) acr[m] = wave_sum_to_lane63(acr[m]);
+      }
+      if (lane == 63) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float* yp = a.y + m * a.ldy + row;
+          *yp = a.accumulate ? *yp + acr[m] : acr[m];
+        }
       }
     }
   }
@@ -175,24 +198,50 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 // ---------------------------------------------------------------------------------------------
 typedef void (*GemvKernel)(GemvArgs);
 
+// Steps of 1024 k issued together: all of a row when it has at most 6 steps.
+static int unroll_for(int64_t kn) {
+  const int64_t steps = (kn + kStep - 1) / kStep;
+  return steps <= 2 ? 2 : steps <= 4 ? 4 : steps == 5 ? 5 : 6;
+}
+
+// Rows per wave task: two for the W12 and Q8 streams while the x reads stay cheap (m <= 4); the
+// dense bf16 stream already moves 32 B per lane per step and runs best with one.
 template <int FMT>
-static GemvKernel pick(int m) {
-  switch (m) {
-    case 1: return k_gemv<FMT, 1>;
-    case 2: return k_gemv<FMT, 2>;
-    case 3: return k_gemv<FMT, 3>;
-    case 4: return k_gemv<FMT, 4>;
-    case 5: return k_gemv<FMT, 5>;
-    case 6: return k_gemv<FMT, 6>;
-    case 7: return k_gemv<FMT, 7>;
-    default: return k_gemv<FMT, 8>;
+constexpr int rows_for(int m) { return FMT != kFmtBF16 && m <= 4 ? 2 : 1; }
+
+template <int FMT, int M>
+static GemvKernel pick_u(int u) {
+  constexpr int R = rows_for<FMT>(M);
+  switch (u) {
+    case 2: return k_gemv<FMT, M, R, 2>;
+    case 4: return k_gemv<FMT, M, R, 4>;
+    case 5: return k_gemv<FMT, M, R, 5>;
+    default: return k_gemv<FMT, M, R, 6>;
   }
 }
 
-static GemvKernel pick_kernel(Fmt f, int m) {
-  if (f == kFmtW12) return pick<kFmtW12>(m);
-  if (f == kFmtQ8) return pick<kFmtQ8>(m);
-  return pick<kFmtBF16>(m);
+template <int FMT>
+static GemvKernel pick(int m, int u) {
+  switch (m) {
+    case 1: return pick_u<FMT, 1>(u);
+    case 2: return pick_u<FMT, 2>(u);
+    case 3: return pick_u<FMT, 3>(u);
+    case 4: return pick_u<FMT, 4>(u);
+    case 5: return pick_u<FMT, 5>(u);
+    case 6: return pick_u<FMT, 6>(u);
+    case 7: return pick_u<FMT, 7>(u);
+    default: return pick_u<FMT, 8>(u);
+  }
+}
+
+static GemvKernel pick_kernel(Fmt f, int m, int u) {
+  if (f == kFmtW12) return pick<kFmtW12>(m, u);
+  if (f == kFmtQ8) return pick<kFmtQ8>(m, u);
+  return pick<kFmtBF16>(m, u);
+}
+
+static int rows_per_task(Fmt f, int m) {
+  return f == kFmtW12 ? rows_for<kFmtW12>(m) : f == kFmtQ8 ? rows_for<kFmtQ8>(m) : rows_for<kFmtBF16>(m);
 }
 
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
@@ -202,21 +251,22 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   if (err != hipSuccess) return err;
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int mb = (int)((m - m0) < 8 ? (m - m0) : 8);
-    GemvKernel kern = pick_kernel(f, mb);
     // k-slices whose x copy fits the LDS budget (one slice for every shape with 2*m*k <= 64 KiB)
     const int64_t lds_budget = di.max_lds < 65536 ? di.max_lds : 65536;
     int64_t slice = (lds_budget / (2 * mb)) & ~(int64_t)(kStep - 1);
-    if (slice <= 0) slice = 16;
+    if (slice <= 0) slice = kStep;
     if (slice > k) slice = k;
     for (int64_t k0 = 0; k0 < k; k0 += slice) {
       const int kn = (int)((k - k0) < slice ? (k - k0) : slice);
+      GemvKernel kern = pick_kernel(f, mb, unroll_for(kn));
       const size_t lds = (size_t)2 * mb * kn;
       int occ = 0;
       err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
                                                          kBlock, lds);
       if (err != hipSuccess) return err;
       if (occ < 1) occ = 1;
-      int64_t blocks = (n + 3) / 4;
+      const int64_t tasks = (n + rows_per_task(f, mb) - 1) / rows_per_task(f, mb);
+      int64_t blocks = (tasks + 3) / 4;
       const int64_t cap = (int64_t)di.cus * occ;
       if (blocks > cap) blocks = cap;
       GemvArgs a;

@@ -178,12 +178,18 @@ def encode(w: torch.Tensor, esc_guess: int | None = None) -> W12Weight:
     return W12Weight(n, k, base, ae, lo, esc_ptr, esc_col[:ne], esc_val[:ne])
 
 
-def decode(wt: W12Weight) -> torch.Tensor:
-    """W12Weight -> bfloat16 W [n, k] (bit-exact)."""
-    out = torch.empty((wt.n, wt.k), dtype=torch.bfloat16, device=wt.device)
+def decode_into(wt: W12Weight, out: torch.Tensor) -> torch.Tensor:
+    """Decode into a preallocated contiguous bfloat16 [n, k] tensor."""
+    if out.numel() != wt.n * wt.k or not out.is_contiguous() or out.element_size() != 2:
+        raise ValueError("out must be a contiguous 16-bit tensor with n*k elements")
     s = wt.c_struct()
     _check(lib().w12_decode(ctypes.byref(s), out.data_ptr(), _stream_handle(wt.device)))
     return out
+
+
+def decode(wt: W12Weight) -> torch.Tensor:
+    """W12Weight -> bfloat16 W [n, k] (bit-exact)."""
+    return decode_into(wt, torch.empty((wt.n, wt.k), dtype=torch.bfloat16, device=wt.device))
 
 
 def _gemm_out(x, n):
