@@ -173,7 +173,8 @@ def main():
     rec_bytes = rec0.nbytes()
     rot = max(2, int(np.ceil(a.min_rot_bytes / rec_bytes)))
     recs = [rec0] + [rec0.clone() for _ in range(rot - 1)]
-    wcopies = [w_dev] + [w_dev.clone() for _ in range(rot - 1)]
+    wcopies = [w_dev] + [w_dev.clone() for _ in range(rot - 1)]      # row-major (encode input)
+    btiles = [w12.bf16_tiles(wc) for wc in wcopies]                   # baseline layout
     x1, x16, x32 = to_dev(x_bits[:1]), to_dev(x_bits[:16]), to_dev(x_bits[:32])
     y1 = torch.empty((1, n), dtype=torch.float32, device=dev)
     y16 = torch.empty((16, n), dtype=torch.float32, device=dev)
@@ -205,8 +206,8 @@ def main():
         ("w12_m1", rot, lambda r: w12.gemm(x1, recs[r], path="gemv", out=y1)),
         ("w12_m32", rot, lambda r: w12.gemm(x32, recs[r], path="mfma", out=y32)),
         ("q8_m16", rot, lambda r: w12.q8_gemm(x16, recs[r], path="mfma", out=y16)),
-        ("bf16_m1", rot, lambda r: w12.bf16_gemm(x1, wcopies[r], path="gemv", out=yb1)),
-        ("bf16_m32", rot, lambda r: w12.bf16_gemm(x32, wcopies[r], path="mfma", out=yb32)),
+        ("bf16_m1", rot, lambda r: w12.bf16_gemm(x1, btiles[r], path="gemv", out=yb1)),
+        ("bf16_m32", rot, lambda r: w12.bf16_gemm(x32, btiles[r], path="mfma", out=yb32)),
     ]
 
     def step(evs=None):
@@ -273,7 +274,7 @@ def main():
                         if fmt == "w12":
                             w12.gemm(xm, recs[r], path=path, out=ym)
                         else:
-                            w12.bf16_gemm(xm, wcopies[r], path=path, out=ym)
+                            w12.bf16_gemm(xm, btiles[r], path=path, out=ym)
                     run(0)
                     reps = 2 * rot
                     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -9,18 +9,25 @@
  * go to an exact escape list.  A and E together are the 8-bit view that a low-precision
  * "Q pass" reads without touching B (same page, Fig. 5(a) and Fig. 7).
  *
- * Byte layout of a record (the pages fix only the plane contents; this layout is ours):
+ * Logical content of a record (the pages fix only the plane contents; this layout is ours):
  *   base[n]      u8   lowest biased exponent of row n's window, 1..239 (window = base..base+15)
- *   ae[n][k]     u8   s<<7 | E<<3 | m[6:4],  E = e - base       (the 8-bit view, row-major)
- *   lo[n][k/2]   u8   B plane.  For weights k = 8g+i (i = 0..7) the nibble m[3:0] is in byte
+ *   AE[n][k]     u8   s<<7 | E<<3 | m[6:4],  E = e - base       (the 8-bit view)
+ *   B[n][k/2]    u8   B plane.  For weights k = 8g+i (i = 0..7) the nibble m[3:0] is in byte
  *                     4g + (i % 4) of the row: low nibble for i < 4, high nibble for i >= 4
  *   esc_ptr[n+1] u32  row CSR offsets into the escape arrays, esc_ptr[0] = 0
  *   esc_col[]    u32  column k of each escape, strictly ascending within a row
  *   esc_val[]    u16  exact bfloat16 bits of each escape
+ * Storage order of the AE and B planes on the device (`ae`, `lo` below): tiles of 16 rows x 128
+ * columns in row-tile-major order, rows padded with zero bytes to npad = 16 * ceil(n / 16).
+ * Inside a tile (2048 bytes of AE, 1024 bytes of B), the AE byte of (row r, column c) sits at
+ * 1024*((c % 32) / 16) + 16*(r + 16*(c / 32)) + c % 16, and the 16 B-plane bytes of row r for
+ * columns 32g..32g+31 (row bytes 16g..16g+15 of the tile's 64) sit at 16*(r + 16*g).  Every
+ * wave-wide 128-bit load of a kernel then reads 1 KiB of contiguous memory, already in the lane
+ * order of the 16x16x32 matrix-core operand.
  * Window rule: the window holds as many of the row's weights as possible; ties go to the
  * smallest base; a row with no normal weight gets base 1.  Zeros, subnormals, Inf and NaN
  * (exponent field 0 or 255) are never inside a window, so they are always escapes.  An
- * escaped slot holds ae = 0 and a zero nibble.  Decoding reproduces every input bit (NaN
+ * escaped slot holds AE = 0 and a zero nibble.  Decoding reproduces every input bit (NaN
  * payloads and -0 included).
  *
  * Conventions for every call:
@@ -33,7 +40,7 @@
  *     nothing has been enqueued unless stated, and w12_last_error() returns a message
  *     (thread-local, valid until the next call on the same thread).  Faults inside kernels
  *     surface at the caller's next synchronisation, as usual in HIP.
- *   - The GPU kernels need k % 32 == 0 (W12_ERR_SHAPE otherwise).
+ *   - k must be a multiple of 128 (W12_ERR_SHAPE otherwise); n is any positive count.
  */
 #ifndef W12_H
 #define W12_H
@@ -49,7 +56,7 @@ extern "C" {
 /* status codes */
 #define W12_OK            0
 #define W12_ERR_ARG      (-1)  /* null pointer, n, k or m <= 0, unknown flag */
-#define W12_ERR_SHAPE    (-2)  /* k % 32 != 0 */
+#define W12_ERR_SHAPE    (-2)  /* k % 128 != 0 */
 #define W12_ERR_ALIGN    (-3)  /* a device pointer is not 16-byte aligned */
 #define W12_ERR_CAPACITY (-4)  /* esc_cap smaller than the escape total (w12_encode) */
 #define W12_ERR_RANGE    (-5)  /* escape total >= 2^32 - 1, or a size overflows */
@@ -65,8 +72,8 @@ typedef struct w12_weight {
     int64_t   n;        /* output channels (rows of W)  */
     int64_t   k;        /* input features (columns of W) */
     uint8_t  *base;     /* [n]                           */
-    uint8_t  *ae;       /* [n * k]                       */
-    uint8_t  *lo;       /* [n * k / 2]                   */
+    uint8_t  *ae;       /* [npad * k]      tiled storage */
+    uint8_t  *lo;       /* [npad * k / 2]  tiled storage */
     uint32_t *esc_ptr;  /* [n + 1]                       */
     uint32_t *esc_col;  /* [esc_cap]                     */
     uint16_t *esc_val;  /* [esc_cap]                     */
@@ -87,7 +94,7 @@ typedef struct w12_weight {
 int w12_encode(const uint16_t *w, w12_weight *out, uint64_t *n_esc, void *stream);
 
 /*
- * w12_decode -- W12 record -> bfloat16 bits W [n, k] (device).  Bit-exact inverse of
+ * w12_decode -- W12 record -> bfloat16 bits W [n, k] (device, row-major).  Bit-exact inverse of
  * w12_encode (the format is lossless: figure-captions page, Fig. 5(a) "exact escape list";
  * summary page, "Key Contributions" 3).  Reads 1.5 bytes per weight plus metadata, writes 2.
  */
@@ -114,11 +121,19 @@ int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, ui
                 void *stream);
 
 /*
- * w12_bf16_gemm -- same-build dense baseline: y = x * W^T with W as plain bfloat16 [n, k]
- * (device), same kernel structure and flags as w12_gemm, 2 bytes per weight.
+ * w12_bf16_gemm -- same-build dense baseline: y = x * W^T with W bfloat16 in the same tiled
+ * storage order as the W12 planes (npad * k values, from w12_bf16_to_tiles), same kernel
+ * structure and flags as w12_gemm, 2 bytes per weight.
  */
-int w12_bf16_gemm(const uint16_t *x, int64_t m, const uint16_t *w, int64_t n, int64_t k,
+int w12_bf16_gemm(const uint16_t *x, int64_t m, const uint16_t *w_tiles, int64_t n, int64_t k,
                   float *y, uint32_t flags, void *stream);
+
+/*
+ * w12_bf16_to_tiles -- dense bfloat16 W [n, k] (device, row-major) -> the tiled storage order of
+ * the baseline (out: npad * k values; padding rows zero).  Inside a tile (16 rows x 128 columns,
+ * 4096 bytes) the 8 values of row r at columns 32g + 8q .. +7 sit at byte 1024*q + 16*(r + 16g).
+ */
+int w12_bf16_to_tiles(const uint16_t *w, int64_t n, int64_t k, uint16_t *out, void *stream);
 
 /*
  * w12_read_probe -- bandwidth probe: streams `bytes` bytes of `buf` (device, 16-byte

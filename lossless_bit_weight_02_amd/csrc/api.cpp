@@ -39,7 +39,7 @@ int check_nk(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0) return fail(W12_ERR_ARG, "n and k must be positive (n=%lld, k=%lld)",
                                     (long long)n, (long long)k);
   if (n >= kMaxDim || k >= kMaxDim) return fail(W12_ERR_RANGE, "n or k too large");
-  if (k % 32 != 0) return fail(W12_ERR_SHAPE, "k must be a multiple of 32 (k=%lld)", (long long)k);
+  if (k % 128 != 0) return fail(W12_ERR_SHAPE, "k must be a multiple of 128 (k=%lld)", (long long)k);
   return W12_OK;
 }
 
@@ -177,6 +177,16 @@ int w12_bf16_gemm(const uint16_t* x, int64_t m, const uint16_t* w, int64_t n, in
   w12::Planes p;
   p.w = w;
   return run_gemm(w12::kFmtBF16, x, m, p, n, k, y, flags, stream);
+}
+
+int w12_bf16_to_tiles(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, void* stream) {
+  if (!w || !out) return fail(W12_ERR_ARG, "w or out is NULL");
+  int rc = check_nk(n, k);
+  if (rc) return rc;
+  if (!aligned16(w) || !aligned16(out)) return fail(W12_ERR_ALIGN, "w and out must be 16-byte aligned");
+  hipError_t e = w12::launch_bf16_tile(w, n, k, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bf16 tiling launch");
+  return ok();
 }
 
 int w12_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {

@@ -116,11 +116,27 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(uint32_t* __restrict__ es
 }
 
 // ---------------------------------------------------------------------------------------------
-// Encoder step 3: planes + escapes.  One workgroup per row; thread t of a pass owns the aligned
-// group of 8 weights g = pass*256 + t, so escapes come out in ascending k after a workgroup
-// exclusive scan of the per-thread escape counts.
+// Encoder step 3: planes + escapes.  One workgroup per row (rows of the last row tile past n are
+// padding and get zero planes); thread t of a pass owns the aligned group of 8 weights
+// g = pass*256 + t, so escapes come out in ascending k after a workgroup exclusive scan of the
+// per-thread escape counts.  The group's 8 AE bytes and 4 B bytes land at their tiled positions
+// (see w12_device.hpp).
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w, int64_t n, int64_t k,
+__device__ __forceinline__ int64_t ae_offset(int64_t row, int64_t col, int64_t ktiles) {
+  const int64_t tile = (row >> 4) * ktiles + (col >> 7);
+  const int64_t c = col & 127;
+  return tile * kTileAE + 1024 * ((c & 31) >> 4) + 16 * ((row & 15) + 16 * (c >> 5)) + (c & 15);
+}
+
+__device__ __forceinline__ int64_t lo_offset(int64_t row, int64_t col, int64_t ktiles) {
+  // byte holding the B nibbles of the aligned group of 8 starting at col (col % 8 == 0)
+  const int64_t tile = (row >> 4) * ktiles + (col >> 7);
+  const int64_t c = col & 127;
+  return tile * kTileLO + 16 * ((row & 15) + 16 * (c >> 5)) + ((c & 31) >> 1);
+}
+
+__global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w, int64_t n,
+                                                 int64_t npad, int64_t k,
                                                  const uint8_t* __restrict__ base,
                                                  const uint32_t* __restrict__ esc_ptr,
                                                  uint8_t* __restrict__ ae, uint8_t* __restrict__ lo,
@@ -129,7 +145,15 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
   __shared__ uint32_t wave_cnt[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t groups = k >> 3;
-  for (int64_t row = blockIdx.x; row < n; row += gridDim.x) {
+  const int64_t ktiles = k / kTileCols;
+  for (int64_t row = blockIdx.x; row < npad; row += gridDim.x) {
+    if (row >= n) {  // padding row of the last tile: zero planes, no escapes
+      for (int64_t g = tid; g < groups; g += kBlock) {
+        *reinterpret_cast<u32x2*>(ae + ae_offset(row, 8 * g, ktiles)) = (u32x2){0u, 0u};
+        *reinterpret_cast<uint32_t*>(lo + lo_offset(row, 8 * g, ktiles)) = 0u;
+      }
+      continue;  // uniform over the workgroup
+    }
     const uint32_t b = base[row];
     const uint64_t out0 = esc_ptr[row];
     uint64_t running = 0;
@@ -166,8 +190,8 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
         pass_total += wave_cnt[i];
       }
       if (act) {
-        *reinterpret_cast<u32x2*>(ae + row * k + 8 * g) = (u32x2){a0, a1};
-        *reinterpret_cast<uint32_t*>(lo + row * (k >> 1) + 4 * g) = nib;
+        *reinterpret_cast<u32x2*>(ae + ae_offset(row, 8 * g, ktiles)) = (u32x2){a0, a1};
+        *reinterpret_cast<uint32_t*>(lo + lo_offset(row, 8 * g, ktiles)) = nib;
         if (escmask) {
           uint64_t idx = out0 + running + before + incl - c;
           const uint64_t row_end = esc_ptr[row + 1];  // never write past the row's CSR range
@@ -188,27 +212,54 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decoder: one thread per aligned group of 8 weights.  The group's w' pairs (exponent 112 + E)
-// get (base - 112) added to both exponent fields at once: (base - 112) * 0x00800080 mod 2^32.
-// Neither half can carry or borrow into the other because base + E stays within 1..254.
+// Decoder: one thread per aligned group of 8 weights of a real row.  The group's w' pairs
+// (exponent 112 + E) get (base - 112) added to both exponent fields at once:
+// (base - 112) * 0x00800080 mod 2^32.  Neither half can carry or borrow into the other because
+// base + E stays within 1..254.  Reads the tiled planes, writes row-major bf16.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_decode(const uint8_t* __restrict__ base,
                                                    const uint8_t* __restrict__ ae,
                                                    const uint8_t* __restrict__ lo, int64_t n,
                                                    int64_t k, uint16_t* __restrict__ out) {
-  const int64_t groups_per_row = k >> 3;
-  const int64_t total = n * groups_per_row;
+  // One workgroup per tile; thread u reads AE bytes 8u..8u+7 of the tile (coalesced) =
+  // row r = l % 16, columns 32g + 16h + 8s .. +7 with u = 128h + 2l + s, l = r + 16g.
+  const int64_t ktiles = k / kTileCols;
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows * ktiles;
   const uint32_t e112 = exp112_pair();
+  const int u = threadIdx.x, h = u >> 7, l = (u & 127) >> 1, sh = u & 1;
+  const int r = l & 15, g = l >> 4;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t row = (t / ktiles) * kTileRows + r;
+    if (row >= n) continue;
+    const int64_t col = (t % ktiles) * kTileCols + 32 * g + 16 * h + 8 * sh;
+    const u32x2 a = load_nt(reinterpret_cast<const u32x2*>(ae + t * kTileAE) + u);
+    const uint32_t lw = *reinterpret_cast<const uint32_t*>(lo + t * kTileLO + 16 * l + 8 * h + 4 * sh);
+    const uint32_t shift = ((uint32_t)base[row] - 112u) * 0x00800080u;
+    uint32_t p[4];
+    window_group8(a.x, a.y, lw, e112, p);
+    const u32x4 res = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
+    *reinterpret_cast<u32x4*>(out + row * k + col) = res;
+  }
+}
+
+// Dense bf16 W [n][k] (row-major) -> the tiled storage order of the baseline (npad rows; padding
+// rows zero).  One thread per aligned group of 8 values.
+__global__ __launch_bounds__(kBlock) void k_bf16_tile(const uint16_t* __restrict__ w, int64_t n,
+                                                      int64_t npad, int64_t k,
+                                                      uint16_t* __restrict__ out) {
+  const int64_t groups_per_row = k >> 3;
+  const int64_t total = npad * groups_per_row;
+  const int64_t ktiles = k / kTileCols;
   for (int64_t g = (int64_t)blockIdx.x * kBlock + threadIdx.x; g < total;
        g += (int64_t)gridDim.x * kBlock) {
     const int64_t row = g / groups_per_row;
-    const u32x2 a = load_nt(reinterpret_cast<const u32x2*>(ae) + g);
-    const uint32_t l = load_nt(reinterpret_cast<const uint32_t*>(lo) + g);
-    const uint32_t shift = ((uint32_t)base[row] - 112u) * 0x00800080u;
-    uint32_t p[4];
-    window_group8(a.x, a.y, l, e112, p);
-    const u32x4 r = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
-    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(out) + g);
+    const int64_t col = 8 * (g - row * groups_per_row);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < n) v = *reinterpret_cast<const u32x4*>(w + row * k + col);
+    const int64_t tile = (row >> 4) * ktiles + (col >> 7);
+    const int64_t c = col & 127;
+    const int64_t byte = tile * kTileBF + 1024 * ((c & 31) >> 3) + 16 * ((row & 15) + 16 * (c >> 5));
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(out) + byte) = v;
   }
 }
 
@@ -274,8 +325,21 @@ hipError_t launch_scan(uint32_t* esc_ptr, int64_t n, hipStream_t s) {
 hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* base,
                        const uint32_t* esc_ptr, uint8_t* ae, uint8_t* lo, uint32_t* esc_col,
                        uint16_t* esc_val, hipStream_t s) {
-  hipLaunchKernelGGL(k_pack, dim3(grid_rows(n)), dim3(kBlock), 0, s, w, n, k, base, esc_ptr, ae, lo,
-                     esc_col, esc_val);
+  const int64_t npad = padded_rows(n);
+  hipLaunchKernelGGL(k_pack, dim3(grid_rows(npad)), dim3(kBlock), 0, s, w, n, npad, k, base, esc_ptr,
+                     ae, lo, esc_col, esc_val);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t s) {
+  DevInfo di;
+  hipError_t err = dev_info(&di);
+  if (err != hipSuccess) return err;
+  const int64_t npad = padded_rows(n);
+  int64_t blocks = (npad * (k >> 3) + kBlock - 1) / kBlock;
+  const int64_t cap = (int64_t)di.cus * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(k_bf16_tile, dim3((unsigned)blocks), dim3(kBlock), 0, s, w, n, npad, k, out);
   return hipGetLastError();
 }
 
@@ -283,11 +347,10 @@ hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, h
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
-  const int64_t groups = n * (k >> 3);
-  int64_t blocks = (groups + kBlock - 1) / kBlock;
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows * (k / kTileCols);
   const int64_t cap = (int64_t)di.cus * 8;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(k_decode, dim3((unsigned)blocks), dim3(kBlock), 0, s, p.base, p.ae, p.lo, n, k, out);
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)(tiles < cap ? tiles : cap)), dim3(kBlock), 0, s, p.base,
+                     p.ae, p.lo, n, k, out);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int64_t sblocks = (n + 3) / 4;

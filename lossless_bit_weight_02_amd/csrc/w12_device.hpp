@@ -16,6 +16,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 waves per workgroup for every kernel here
 
+// Storage order of the planes: tiles of 16 rows x 128 columns, row-tile-major (rows padded with
+// zero bytes to a multiple of 16).  Inside a tile, lane l = r + 16*g of a wave (row r, column
+// group g = columns 32g..32g+31) owns:
+//   AE bytes of columns 32g + 16h .. +16 at byte 1024*h + 16*l          (h = 0, 1)
+//   B bytes of columns 32g .. +32 (16 bytes, four R1 groups of 8) at 16*l
+//   dense bf16 (baseline) columns 32g + 8q .. +8 at byte 1024*q + 16*l   (q = 0..3)
+// so each of these wave-wide 128-bit loads reads 1 KiB of contiguous memory, and the lane's
+// data is exactly what the 16x16x32 MFMA operand layout wants for row r.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 128;
+constexpr int kTileAE = 2048;   // bytes of AE per tile
+constexpr int kTileLO = 1024;   // bytes of B per tile
+constexpr int kTileBF = 4096;   // bytes of dense bf16 per tile
+
 // Selectors for v_perm_b32 (bytes 0-3 come from the second source, 4-7 from the first,
 // 0x0C yields a zero byte).  Each builds a pair of 16-bit halves, one per weight, whose high
 // byte is the weight's AE byte and whose low byte carries its B nibble in bits 7..4.

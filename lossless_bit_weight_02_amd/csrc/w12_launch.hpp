@@ -16,6 +16,9 @@ struct DevInfo {
 // Properties of the current device (cached per device id).
 hipError_t dev_info(DevInfo* out);
 
+// Rows of the padded (tiled) plane storage.
+inline int64_t padded_rows(int64_t n) { return (n + 15) / 16 * 16; }
+
 struct Planes {
   const uint8_t* base = nullptr;
   const uint8_t* ae = nullptr;
@@ -23,7 +26,7 @@ struct Planes {
   const uint32_t* esc_ptr = nullptr;
   const uint32_t* esc_col = nullptr;
   const uint16_t* esc_val = nullptr;
-  const uint16_t* w = nullptr;  // kFmtBF16 only: the dense bfloat16 weight
+  const uint16_t* w = nullptr;  // kFmtBF16 only: the dense bfloat16 weight, tiled storage order
 };
 
 // encoder: window choice per row (writes base[n] and the escape count of row i to esc_ptr[i+1])
@@ -37,6 +40,8 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
                        uint16_t* esc_val, hipStream_t s);
 // decoder: planes -> bfloat16 bits, then every escape written over its slot
 hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
+// dense bf16 [n][k] -> tiled storage order (baseline layout)
+hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
 // bandwidth probe
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 

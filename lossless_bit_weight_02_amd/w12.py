@@ -57,9 +57,16 @@ EXPORTS = {
     "w12_bf16_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_bf16_to_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
     "w12_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_void_p]),
 }
+
+
+def padded_rows(n: int) -> int:
+    """Rows of the tiled plane storage (16-row tiles)."""
+    return 16 * ((int(n) + 15) // 16)
 
 
 def lib():
@@ -101,7 +108,8 @@ def _bits16(t: torch.Tensor) -> torch.Tensor:
 
 
 class W12Weight:
-    """A W12 record held as torch device tensors (layout of include/w12.h)."""
+    """A W12 record held as torch device tensors (layout of include/w12.h; ``ae`` and ``lo`` are
+    in the tiled storage order, padded_rows(n) rows)."""
 
     def __init__(self, n, k, base, ae, lo, esc_ptr, esc_col, esc_val):
         self.n, self.k = int(n), int(k)
@@ -134,13 +142,13 @@ class W12Weight:
                                             self.esc_col, self.esc_val)))
 
     def to_numpy(self) -> dict:
-        """Host copies of every array (uint8/uint32/uint16 numpy arrays)."""
+        """Host copies of every array as stored (uint8/uint32/uint16 numpy arrays; ``ae_s`` and
+        ``lo_s`` flat, in the tiled storage order)."""
         def host(t, dt):
             return t.cpu().numpy().view(dt)
         import numpy as np
         return dict(n=self.n, k=self.k, base=host(self.base, np.uint8),
-                    ae=host(self.ae, np.uint8).reshape(self.n, self.k),
-                    lo=host(self.lo, np.uint8).reshape(self.n, self.k // 2),
+                    ae_s=host(self.ae, np.uint8), lo_s=host(self.lo, np.uint8),
                     esc_ptr=host(self.esc_ptr, np.uint32), esc_col=host(self.esc_col, np.uint32),
                     esc_val=host(self.esc_val, np.uint16))
 
@@ -155,8 +163,9 @@ def encode(w: torch.Tensor, esc_guess: int | None = None) -> W12Weight:
     dev = w.device
     u8, i32, i16 = torch.uint8, torch.int32, torch.int16
     base = torch.empty(n, dtype=u8, device=dev)
-    ae = torch.empty(n * k, dtype=u8, device=dev)
-    lo = torch.empty(n * k // 2, dtype=u8, device=dev)
+    npad = padded_rows(n)
+    ae = torch.empty(npad * k, dtype=u8, device=dev)
+    lo = torch.empty(npad * k // 2, dtype=u8, device=dev)
     esc_ptr = torch.empty(n + 1, dtype=i32, device=dev)
     cap = max(1024, (n * k) // 256) if esc_guess is None else max(1, int(esc_guess))
     esc_col = torch.empty(cap, dtype=i32, device=dev)
@@ -220,12 +229,30 @@ def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.
     return out
 
 
-def bf16_gemm(x: torch.Tensor, w: torch.Tensor, path: str | None = None, out: torch.Tensor | None = None):
-    """Same-build dense baseline: y = x W^T with W plain bfloat16."""
+class Bf16Tiles:
+    """Dense bfloat16 W in the tiled storage order of the baseline kernels."""
+
+    def __init__(self, n, k, data):
+        self.n, self.k, self.data = int(n), int(k), data
+
+    def nbytes(self) -> int:
+        return self.data.numel() * 2
+
+
+def bf16_tiles(w: torch.Tensor) -> Bf16Tiles:
+    """bfloat16 W [n, k] (row-major, on the GPU) -> the baseline's tiled storage."""
     w = _bits16(w).contiguous()
+    n, k = w.shape
+    out = torch.empty(padded_rows(n) * k, dtype=torch.bfloat16, device=w.device)
+    _check(lib().w12_bf16_to_tiles(w.data_ptr(), n, k, out.data_ptr(), _stream_handle(w.device)))
+    return Bf16Tiles(n, k, out)
+
+
+def bf16_gemm(x: torch.Tensor, wt: Bf16Tiles, path: str | None = None, out: torch.Tensor | None = None):
+    """Same-build dense baseline: y = x W^T with W plain bfloat16 (tiled storage)."""
     if out is None:
-        x, out = _gemm_out(x, w.shape[0])
-    _check(lib().w12_bf16_gemm(x.data_ptr(), x.shape[0], w.data_ptr(), w.shape[0], w.shape[1],
+        x, out = _gemm_out(x, wt.n)
+    _check(lib().w12_bf16_gemm(x.data_ptr(), x.shape[0], wt.data.data_ptr(), wt.n, wt.k,
                                out.data_ptr(), _PATHS[path], _stream_handle(x.device)))
     return out
 

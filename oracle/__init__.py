@@ -15,5 +15,6 @@ from .w12 import (  # noqa: F401
     W12Record, bf16_fields, exponent_histogram, window_coverage, choose_window,
     encode, decode, q8_view_bits, validate, ValidationError, bf16_to_f64,
     gemm64, w12_gemm64, q8_gemm64, abs_bound64, top1, record_nbytes,
-    bits_per_weight, lo_row_bytes, lo_position,
+    bits_per_weight, lo_row_bytes, lo_position, to_storage, from_storage,
+    bf16_to_storage, padded_rows, TILE_ROWS, TILE_COLS,
 )

@@ -31,6 +31,13 @@ layout.  The readings used here (numbered as in the design notes):
 * R8  the Q pass weight is the 8-bit view with B taken as 0 (for an
       in-window weight that is bits & 0xFFF0); escapes stay exact.
 * R11 argmax ties go to the lowest index.
+* R15 storage order of the planes on the device: 16-row x 128-column tiles
+      (rows padded with zero bytes to a multiple of 16, k a multiple of 128),
+      tiles in row-tile-major order; inside a tile the AE byte of (row r,
+      column c) sits at 1024*h + 16*(r + 16*g) + j with g = c // 32,
+      h = (c % 32) // 16, j = c % 16, and the B-plane bytes of row r for
+      columns [32g, 32g+32) sit at 16*(r + 16*g) .. +16.  This is only a
+      permutation of the logical arrays above (see ``to_storage``).
 
 Parity status: every function below is pinned by the CPU tests against
 values fixed independently of this file (exhaustive round trip over all 65536
@@ -299,6 +306,59 @@ def top1(y) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Size accounting (summary page, Main Findings: 12.01-12.02 bits per weight)
 # ----------------------------------------------------------------------------
+# ----------------------------------------------------------------------------
+# Device storage order of the planes (R15)
+# ----------------------------------------------------------------------------
+TILE_ROWS = 16
+TILE_COLS = 128
+
+
+def padded_rows(n: int) -> int:
+    return TILE_ROWS * ((n + TILE_ROWS - 1) // TILE_ROWS)
+
+
+def to_storage(rec: W12Record):
+    """(ae_s, lo_s): the AE and B planes as flat uint8 arrays in the tiled storage order."""
+    n, k = rec.n, rec.k
+    if k % TILE_COLS:
+        raise ValueError("the tiled storage order needs k % 128 == 0")
+    npad = padded_rows(n)
+    ae = np.zeros((npad, k), dtype=np.uint8)
+    ae[:n] = rec.ae
+    lo = np.zeros((npad, k // 2), dtype=np.uint8)
+    lo[:n] = rec.lo
+    tr, tk = npad // TILE_ROWS, k // TILE_COLS
+    # ae[tile_r, r, tile_k, g, h, j] -> ae_s[tile_r, tile_k, h, g, r, j]
+    a6 = ae.reshape(tr, TILE_ROWS, tk, 4, 2, 16)
+    ae_s = a6.transpose(0, 2, 4, 3, 1, 5).reshape(-1)
+    # lo[tile_r, r, tile_k, g, b] -> lo_s[tile_r, tile_k, g, r, b]
+    l5 = lo.reshape(tr, TILE_ROWS, tk, 4, 16)
+    lo_s = l5.transpose(0, 2, 3, 1, 4).reshape(-1)
+    return np.ascontiguousarray(ae_s), np.ascontiguousarray(lo_s)
+
+
+def from_storage(ae_s, lo_s, n: int, k: int):
+    """Inverse of ``to_storage``: row-major (ae [n, k], lo [n, k/2]); padding rows dropped."""
+    npad = padded_rows(n)
+    tr, tk = npad // TILE_ROWS, k // TILE_COLS
+    ae = np.asarray(ae_s, dtype=np.uint8).reshape(tr, tk, 2, 4, TILE_ROWS, 16).transpose(0, 4, 1, 3, 2, 5)
+    lo = np.asarray(lo_s, dtype=np.uint8).reshape(tr, tk, 4, TILE_ROWS, 16).transpose(0, 3, 1, 2, 4)
+    return ae.reshape(npad, k)[:n].copy(), lo.reshape(npad, k // 2)[:n].copy()
+
+
+def bf16_to_storage(w_bits) -> np.ndarray:
+    """Dense bf16 W in the same tile order (the baseline's layout): inside a tile, the 8 values of
+    row r at columns 32g + 8q .. +8 sit at element offset 512*q + 8*(r + 16*g)."""
+    w = np.atleast_2d(np.asarray(w_bits, dtype=np.uint16))
+    n, k = w.shape
+    npad = padded_rows(n)
+    wp = np.zeros((npad, k), dtype=np.uint16)
+    wp[:n] = w
+    tr, tk = npad // TILE_ROWS, k // TILE_COLS
+    # w[tile_r, r, tile_k, g, q, e] -> s[tile_r, tile_k, q, g, r, e]
+    return np.ascontiguousarray(wp.reshape(tr, TILE_ROWS, tk, 4, 4, 8).transpose(0, 2, 4, 3, 1, 5).reshape(-1))
+
+
 def record_nbytes(rec: W12Record) -> int:
     return int(rec.base.nbytes + rec.ae.nbytes + rec.lo.nbytes + rec.esc_ptr.nbytes
                + rec.esc_col.nbytes + rec.esc_val.nbytes)

@@ -23,16 +23,31 @@ def to_host_bits(t) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def record_numpy(rec) -> oracle.W12Record:
-    d = rec.to_numpy()
-    return oracle.W12Record(d["n"], d["k"], d["base"], d["ae"], d["lo"], d["esc_ptr"],
-                            d["esc_col"], d["esc_val"])
+def record_numpy(rec) -> dict:
+    """The GPU record's arrays as stored (planes in the tiled storage order)."""
+    return rec.to_numpy()
 
 
-def assert_records_equal(got: oracle.W12Record, want: oracle.W12Record, what=""):
-    assert got.n == want.n and got.k == want.k
-    for name in ("base", "ae", "lo", "esc_ptr", "esc_col", "esc_val"):
-        a, b = getattr(got, name), getattr(want, name)
+def oracle_storage(rec: oracle.W12Record) -> dict:
+    """The oracle's record in the same storage form."""
+    ae_s, lo_s = oracle.to_storage(rec)
+    return dict(n=rec.n, k=rec.k, base=rec.base, ae_s=ae_s, lo_s=lo_s, esc_ptr=rec.esc_ptr,
+                esc_col=rec.esc_col, esc_val=rec.esc_val)
+
+
+def logical_record(d: dict) -> oracle.W12Record:
+    """A stored record back in the oracle's row-major form."""
+    ae, lo = oracle.from_storage(d["ae_s"], d["lo_s"], d["n"], d["k"])
+    return oracle.W12Record(d["n"], d["k"], d["base"], ae, lo, d["esc_ptr"], d["esc_col"],
+                            d["esc_val"])
+
+
+def assert_records_equal(got: dict, want, what=""):
+    if isinstance(want, oracle.W12Record):
+        want = oracle_storage(want)
+    assert got["n"] == want["n"] and got["k"] == want["k"]
+    for name in ("base", "ae_s", "lo_s", "esc_ptr", "esc_col", "esc_val"):
+        a, b = got[name], want[name]
         assert a.shape == b.shape, f"{what}: {name} shape {a.shape} != {b.shape}"
         if not np.array_equal(a, b):
             bad = np.argwhere(a != b)

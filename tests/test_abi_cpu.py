@@ -46,7 +46,7 @@ def test_abi_version_and_status_codes_match_header():
         assert m and int(m.group(1)) == getattr(w12, f"W12_{name}"), name
 
 
-def _rec(n=64, k=64, **over):
+def _rec(n=64, k=128, **over):
     s = w12._W12Weight(n, k, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 10)
     for key, v in over.items():
         setattr(s, key, v)
@@ -58,8 +58,8 @@ def test_argument_errors_are_host_side():
     n_esc = ctypes.c_uint64(0)
     assert L.w12_encode(None, None, None, None) == w12.W12_ERR_ARG
     assert b"NULL" in L.w12_last_error()
-    # k not a multiple of 32
-    assert L.w12_encode(0x1000, ctypes.byref(_rec(k=48)), ctypes.byref(n_esc), None) == w12.W12_ERR_SHAPE
+    # k not a multiple of 128
+    assert L.w12_encode(0x1000, ctypes.byref(_rec(k=96)), ctypes.byref(n_esc), None) == w12.W12_ERR_SHAPE
     # non-positive sizes
     assert L.w12_decode(ctypes.byref(_rec(n=0)), 0x1000, None) == w12.W12_ERR_ARG
     assert L.w12_gemm(0x1000, 0, ctypes.byref(_rec()), 0x1000, 0, None) == w12.W12_ERR_ARG
@@ -73,8 +73,10 @@ def test_argument_errors_are_host_side():
     # escape arrays missing while esc_cap > 0
     assert L.w12_decode(ctypes.byref(_rec(esc_col=None)), 0x1000, None) == w12.W12_ERR_ARG
     # dense baseline
-    assert L.w12_bf16_gemm(0x1000, 1, None, 8, 64, 0x1000, 0, None) == w12.W12_ERR_ARG
-    assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, 40, 0x1000, 0, None) == w12.W12_ERR_SHAPE
+    assert L.w12_bf16_gemm(0x1000, 1, None, 8, 128, 0x1000, 0, None) == w12.W12_ERR_ARG
+    assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, 64, 0x1000, 0, None) == w12.W12_ERR_SHAPE
+    assert L.w12_bf16_to_tiles(None, 8, 128, 0x1000, None) == w12.W12_ERR_ARG
+    assert L.w12_bf16_to_tiles(0x1000, 8, 200, 0x1000, None) == w12.W12_ERR_SHAPE
     assert L.w12_read_probe(0x1000, 20, 0x1000, None) == w12.W12_ERR_SHAPE
     # huge sizes
     assert L.w12_decode(ctypes.byref(_rec(n=1 << 40)), 0x1000, None) == w12.W12_ERR_RANGE

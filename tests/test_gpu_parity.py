@@ -64,7 +64,7 @@ def test_codec_all_65536_patterns(layout):
 
 
 def test_codec_edge_rows():
-    k = 96
+    k = 128
     rows = [np.zeros(k, np.uint16),                                   # all zero -> base 1, all escape
             np.full(k, 0x8000, np.uint16),                            # all -0
             np.full(k, 0x7FC0, np.uint16),                            # all NaN
@@ -78,7 +78,7 @@ def test_codec_edge_rows():
 
 def test_codec_ragged_rows_and_min_k():
     rng = np.random.default_rng(4)
-    for n, k in ((1, 32), (3, 32), (37, 64), (129, 160), (255, 1056)):
+    for n, k in ((1, 128), (3, 128), (17, 256), (37, 384), (129, 640), (255, 1152)):
         w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
         w[rng.random((n, k)) < 0.01] = 0
         _encode_check(w, f"random {n}x{k}")
@@ -92,9 +92,10 @@ def test_encode_capacity_protocol():
     w, _, _ = synth.config_weight("tiny")
     dev_w = to_dev(w)
     n, k = w.shape
+    npad = w12.padded_rows(n)
     base = torch.empty(n, dtype=torch.uint8, device="cuda")
-    ae = torch.empty(n * k, dtype=torch.uint8, device="cuda")
-    lo = torch.empty(n * k // 2, dtype=torch.uint8, device="cuda")
+    ae = torch.empty(npad * k, dtype=torch.uint8, device="cuda")
+    lo = torch.empty(npad * k // 2, dtype=torch.uint8, device="cuda")
     ptr = torch.empty(n + 1, dtype=torch.int32, device="cuda")
     col = torch.empty(4, dtype=torch.int32, device="cuda")
     val = torch.empty(4, dtype=torch.int16, device="cuda")
@@ -124,7 +125,7 @@ def test_encode_deterministic():
 
 def test_encode_errors():
     w12 = _w12()
-    bad = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    bad = torch.zeros((4, 192), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(w12.W12Error) as ei:
         w12.encode(bad)
     assert ei.value.status == w12.W12_ERR_SHAPE
@@ -141,7 +142,7 @@ def _gemm_case(w_bits, x_bits, what, paths=("gemv", "mfma"), rec=None, rows=None
     ref = oracle.encode(w_bits if rows is None else w_bits)
     q8w = oracle.q8_view_bits(ref)
     x = to_dev(x_bits)
-    dw = to_dev(w_bits)
+    dw = w12.bf16_tiles(to_dev(w_bits))
     worst = {}
     for path in paths:
         say(f"gemm {what} m={x_bits.shape[0]} path={path}")
@@ -169,8 +170,9 @@ def test_gemm_attn_m1():
     _gemm_case(w, x, "attn 5120x5120")
 
 
-@pytest.mark.parametrize("n,k,m", [(1, 32, 1), (37, 64, 3), (129, 160, 16), (300, 1056, 8),
-                                   (300, 1056, 40), (77, 4128, 1), (64, 9216, 8)])
+@pytest.mark.parametrize("n,k,m", [(1, 128, 1), (37, 256, 3), (129, 384, 16), (300, 1152, 8),
+                                   (300, 1152, 40), (77, 4224, 1), (64, 9216, 8), (50, 640, 2),
+                                   (33, 128, 64), (16, 3968, 5), (1000, 2176, 33), (8, 128, 100)])
 def test_gemm_ragged(n, k, m):
     rng = np.random.default_rng(n * 7 + k + m)
     w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
@@ -201,7 +203,7 @@ def test_gemm_special_values():
     """NaN / Inf weights propagate; zero, subnormal and -0 weights are exact escapes; an
     all-escape row returns only the placeholder residue allowed by the bound's absolute floor."""
     w12 = _w12()
-    k = 64
+    k = 128
     rng = np.random.default_rng(9)
     w = synth.f32_to_bf16_bits((rng.standard_normal((8, k)) * 0.05).astype(np.float32))
     w[0, 5] = 0x7F80          # +Inf
@@ -211,7 +213,7 @@ def test_gemm_special_values():
     w[4, 3] = 0x8000          # -0
     w[5, :] = 0x3F80          # constant
     w[6, 10] = 0x7F00         # 2^127 (escape, finite)
-    w[7, :] = (np.arange(k) % 40 + 100) << 7  # wide row: many escapes
+    w[7, :] = ((np.arange(k) % 40 + 100) << 7).astype(np.uint16)  # wide row: many escapes
     rec = w12.encode(to_dev(w))
     ref = oracle.encode(w)
     assert_records_equal(record_numpy(rec), ref, "special")

@@ -189,3 +189,54 @@ def test_validate_rejects(corruption):
         r.base[:] = 250
     with pytest.raises(oracle.ValidationError):
         oracle.validate(r)
+
+
+def _rand_record(rng, n, k):
+    ae = rng.integers(0, 256, (n, k), dtype=np.uint8)
+    lo = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    z = np.zeros(n + 1, np.uint32)
+    return oracle.W12Record(n, k, np.ones(n, np.uint8), ae, lo, z, z[:0], np.zeros(0, np.uint16))
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (37, 256), (5, 384)])
+def test_storage_order_literal(n, k):
+    """The tiled storage order against a literal per-byte placement (R15)."""
+    rng = np.random.default_rng(n + k)
+    rec = _rand_record(rng, n, k)
+    ae_s, lo_s = oracle.to_storage(rec)
+    npad = 16 * ((n + 15) // 16)
+    kt = k // 128
+    assert ae_s.shape == (npad * k,) and lo_s.shape == (npad * k // 2,)
+    want_ae = np.zeros(npad * k, np.uint8)
+    want_lo = np.zeros(npad * k // 2, np.uint8)
+    for row in range(n):
+        for col in range(k):
+            tile = (row // 16) * kt + col // 128
+            r, c = row % 16, col % 128
+            off = tile * 2048 + 1024 * ((c % 32) // 16) + 16 * (r + 16 * (c // 32)) + c % 16
+            want_ae[off] = rec.ae[row, col]
+        for byte in range(k // 2):
+            tile = (row // 16) * kt + byte // 64
+            r, b = row % 16, byte % 64
+            off = tile * 1024 + 16 * (r + 16 * (b // 16)) + b % 16
+            want_lo[off] = rec.lo[row, byte]
+    assert np.array_equal(ae_s, want_ae)
+    assert np.array_equal(lo_s, want_lo)
+    ae2, lo2 = oracle.from_storage(ae_s, lo_s, n, k)
+    assert np.array_equal(ae2, rec.ae) and np.array_equal(lo2, rec.lo)
+
+
+def test_bf16_storage_order_literal():
+    rng = np.random.default_rng(3)
+    n, k = 21, 256
+    w = rng.integers(0, 65536, (n, k)).astype(np.uint16)
+    s = oracle.bf16_to_storage(w)
+    npad, kt = 32, k // 128
+    want = np.zeros(npad * k, np.uint16)
+    for row in range(n):
+        for col in range(k):
+            tile = (row // 16) * kt + col // 128
+            r, c = row % 16, col % 128
+            off = tile * 2048 + 512 * ((c % 32) // 8) + 8 * (r + 16 * (c // 32)) + c % 8
+            want[off] = w[row, col]
+    assert np.array_equal(s, want)
