@@ -40,7 +40,8 @@
  *     nothing has been enqueued unless stated, and w12_last_error() returns a message
  *     (thread-local, valid until the next call on the same thread).  Faults inside kernels
  *     surface at the caller's next synchronisation, as usual in HIP.
- *   - k must be a multiple of 128 (W12_ERR_SHAPE otherwise); n is any positive count.
+ *   - k must be a multiple of 128 (W12_ERR_SHAPE otherwise) and at most 2^24, n below 2^31
+ *     (W12_ERR_RANGE otherwise).
  */
 #ifndef W12_H
 #define W12_H
@@ -59,7 +60,7 @@ extern "C" {
 #define W12_ERR_SHAPE    (-2)  /* k % 128 != 0 */
 #define W12_ERR_ALIGN    (-3)  /* a device pointer is not 16-byte aligned */
 #define W12_ERR_CAPACITY (-4)  /* esc_cap smaller than the escape total (w12_encode) */
-#define W12_ERR_RANGE    (-5)  /* escape total >= 2^32 - 1, or a size overflows */
+#define W12_ERR_RANGE    (-5)  /* escape total >= 2^32 - 1, k > 2^24, n or m >= 2^31 */
 #define W12_ERR_HIP      (-6)  /* HIP runtime or launch error; message from hipGetErrorString */
 
 /* flags for the GEMM calls: which kernel family runs */

@@ -33,12 +33,13 @@ int hip_fail(hipError_t e, const char* where) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-constexpr int64_t kMaxDim = int64_t(1) << 31;  // n, k, m each below 2^31; n*k below 2^62
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // n and m below 2^31
+constexpr int64_t kMaxK = int64_t(1) << 24;    // k at most 2^24: 32-bit buffer offsets in kernels
 
 int check_nk(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0) return fail(W12_ERR_ARG, "n and k must be positive (n=%lld, k=%lld)",
                                     (long long)n, (long long)k);
-  if (n >= kMaxDim || k >= kMaxDim) return fail(W12_ERR_RANGE, "n or k too large");
+  if (n >= kMaxDim || k > kMaxK) return fail(W12_ERR_RANGE, "n or k too large (n < 2^31, k <= 2^24)");
   if (k % 128 != 0) return fail(W12_ERR_SHAPE, "k must be a multiple of 128 (k=%lld)", (long long)k);
   return W12_OK;
 }

@@ -10,25 +10,46 @@
 // lane l rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.  A = 16 weight rows, B = 16 activation
 // rows, so the result is y^T for a 16 x 16 tile.
 //
-// The tiled plane storage (w12_device.hpp) already holds each 16-row x 128-column block in this
-// lane order: lane l = r + 16g loads row r, columns 32g..32g+31 with wave-wide 1 KiB reads and
-// decodes them straight into four A operands (MFMA step t takes columns 32g + 8t .. +7 from
-// group g; the B operand is built with the same column mapping).  Each wave owns one tile and
-// keeps the next D blocks of it in flight.  The four waves of a workgroup share x: 256-column
-// chunks of the m rows of x are staged in LDS (double buffered, the next chunk held in
-// registers), and every wave reads its B operands from there.
+// Work split.  One workgroup of kWaves waves per CU (the x chunks fill most of the CU's LDS).
+// A wave owns one 16-row tile at a time and streams all of its 128-column blocks; tiles are dealt
+// round-robin over the workgroups first, so every CU gets the same number of tiles to within one
+// (the weight stream is the bottleneck, and a CU with one more workgroup than the rest would set
+// the kernel's time).  The tiled plane storage (w12_device.hpp) holds each 16-row x 128-column
+// block in operand order: lane l = r + 16g loads row r, columns 32g..32g+31 with wave-wide 1 KiB
+// reads and decodes them straight into four A operands.
 //
-// Epilogue per (row n, column m): y = 2^(base-112) * (acc - 2^-15 * sum_esc x) + sum_esc x*v,
-// the escape lists of rows n walked by the lanes that own (n, m); the tile's escapes are copied
-// to LDS at the start of the tile so the epilogue only waits for its x loads.
+// Software pipeline.  Every load is a buffer load whose offset is pushed past the buffer's range
+// when there is nothing to load (the hardware then returns zeros and fetches nothing), so no load
+// sits behind a branch and every ring slot is a compile-time register set.  Vector-memory loads
+// complete in issue order, so a wait for one load is a wait for all older ones; the kernel
+// therefore issues its loads in one fixed pattern per step -- one x fragment, then the refill of
+// the A block D steps ahead -- and consumes each load exactly D - 1 (x) or D (A) steps later, and
+// the prologue issues the same pattern for D virtual steps.  No wait then ever covers a block
+// that is not due yet.
+//
+// x: chunks of S k-blocks (128 S columns) of the m rows live in LDS in fragment order (each B
+// operand is one contiguous 1 KiB read), double buffered.  While chunk c is consumed, the 4 NT
+// pieces per step of chunk c+1 stream in through a D-deep register ring; the piece jobs rotate
+// over the waves.  A piece is 1 KiB of row-major x (2 rows x 256 columns: a coalesced read);
+// its lanes scatter into the fragment layout, whose 16-byte slots are XOR-swizzled inside each
+// 128-byte row (slot = lane ^ (t | (g & 1) << 2) for k-group t and column group g) so that
+// both these writes and the operand reads are free of bank conflicts.  One barrier per chunk.
+//
+// Escapes (exact weights outside a row's window): the lanes of column group g own output rows
+// 4g..4g+3 of the tile.  The tile's escape list (up to kEscCap entries) is copied to LDS at the
+// start of the tile; at the end of every chunk each lane walks its rows' column-sorted runs up to
+// the chunk's last column, reading x from the chunk still in LDS, and accumulates
+//   y = 2^(base-112) * (acc - 2^-15 * sum_esc x) + sum_esc x * v,
+// which takes the placeholder value 2^-15 of an escaped slot (AE = 0, B = 0) back out of acc
+// (subtracted from the accumulator itself at the end of the chunk).
+// Escapes past the LDS copy of a crowded tile are read from memory after the loop.
 #include "w12_device.hpp"
 #include "w12_launch.hpp"
 
 namespace w12 {
 
 struct MfmaArgs {
-  const uint16_t* x;   // x[m][ldx]
-  int64_t ldx;
+  const uint16_t* x;   // x[m][k] (this launch's rows)
   int m;               // activation rows in this launch (<= 16 * NT)
   const uint8_t* base;
   const uint8_t* ae;   // tiled storage
@@ -40,30 +61,40 @@ struct MfmaArgs {
   float* y;            // y[m][ldy]
   int64_t ldy;
   int64_t n, k;
+  int rounds;          // tiles per wave (the last ones may be empty)
 };
 
-constexpr int kChunk = 256;           // columns of x staged per LDS buffer
-constexpr int kXPitch = kChunk + 8;   // padded LDS row (bfloat16 elements)
-constexpr int kEscCap = 256;          // escapes of one tile staged in LDS (more: read from memory)
-constexpr int kEscBatch = 4;          // escapes per epilogue step
+constexpr int kWaves = 12;                  // waves per workgroup, one workgroup per CU
+constexpr uint32_t kOOB = 0x80000000u;      // buffer offset past every range used here
+constexpr int kAuxNT = 2;                   // cache policy bits: non-temporal (weights stream once)
+constexpr int kEscCap = 128;                // escapes of one tile copied to LDS
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Raw buffer over `bytes` bytes at `p` (stride 0, 32-bit data format word of the gfx9 family).
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 template <int FMT>
 struct ABlock {
   u32x4 v[FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2];
 };
 
+// Block kb of the wave's tile; offsets past the tile's range read zeros.
 template <int FMT>
-__device__ __forceinline__ void load_ablock(const MfmaArgs& a, int64_t tile_block, int lane, ABlock<FMT>& r) {
+__device__ __forceinline__ void load_ablock(Rsrc r0, Rsrc r1, uint32_t kb, uint32_t lane16,
+                                            ABlock<FMT>& b) {
   if constexpr (FMT == kFmtBF16) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.w) + tile_block * (kTileBF / 16) + lane;
+    const uint32_t off = kb * kTileBF + lane16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.v[q] = load_nt(src + 64 * q);
+    for (int q = 0; q < 4; ++q) b.v[q] = __builtin_amdgcn_raw_buffer_load_b128(r0, off + 1024 * q, 0, kAuxNT);
   } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.ae) + tile_block * (kTileAE / 16) + lane;
-    r.v[0] = load_nt(src);
-    r.v[1] = load_nt(src + 64);
+    const uint32_t off = kb * kTileAE + lane16;
+    b.v[0] = __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, kAuxNT);
+    b.v[1] = __builtin_amdgcn_raw_buffer_load_b128(r0, off + 1024, 0, kAuxNT);
     if constexpr (FMT == kFmtW12)
-      r.v[2] = load_nt(reinterpret_cast<const u32x4*>(a.lo) + tile_block * (kTileLO / 16) + lane);
+      b.v[2] = __builtin_amdgcn_raw_buffer_load_b128(r1, kb * kTileLO + lane16, 0, kAuxNT);
   }
 }
 
@@ -87,182 +118,283 @@ __device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112
   }
 }
 
-// Registers are capped so that three workgroups (12 waves) fit on a CU for up to 32 activation
-// rows: the 544 tiles-of-4 of a 34816-row weight are then all resident at once, no second round.
-template <int FMT, int NT, int D>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 3 : 2, 8)))
+// Workgroup barrier that orders LDS only (vector-memory loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Compile-time shape of one instantiation.  Decoding formats keep a 3-deep ring at two activation
+// tiles (the decode needs its own registers); the others 4 (up to 32 rows), 3 and 2.
+template <int FMT, int NT>
+struct Shape {
+  static constexpr int D = NT == 1 ? 4 : NT == 2 ? (FMT == kFmtBF16 ? 4 : 3) : NT == 3 ? 3 : 2;
+  static constexpr int S = D == 4 ? 8 : D == 3 ? 6 : 4;   // k-blocks per x chunk
+  static constexpr int FS = 4 * NT;                   // 1 KiB x pieces per k-block
+  static constexpr int F = FS * S;                    // 1 KiB x pieces per chunk
+  static constexpr int XL = (FS + kWaves - 1) / kWaves;  // pieces a wave loads per step
+  static_assert(S % D == 0 && S % 2 == 0, "a chunk must hold whole rings and 256-column blocks");
+};
+
+// Twelve waves (three per SIMD) on the CU: at most 168 VGPRs.
+template <int FMT, int NT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_mfma(MfmaArgs a) {
-  constexpr int NX = 16 * NT * kChunk / 8 / kBlock;   // 16-byte words of x per thread per chunk
-  static_assert(NX >= 1, "x chunk too small for the workgroup");
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][16 * NT * kXPitch];
-  __shared__ uint32_t s_ecol[4][kEscCap];       // per wave: escapes of its tile (column, value)
-  __shared__ uint16_t s_eval[4][kEscCap];
+  using SH = Shape<FMT, NT>;
+  constexpr int D = SH::D, S = SH::S, FS = SH::FS, F = SH::F, XL = SH::XL;
+  constexpr bool kEsc = FMT != kFmtBF16;
+  __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
+  __shared__ __attribute__((aligned(16))) u32x4 s_scratch[64];   // stores of waves with no piece
+  __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];   // per wave: tile escapes
+  __shared__ uint16_t s_eval[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];
+
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const uint32_t lane16 = 16u * lane;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t ktiles = a.k / kTileCols;
-  const int KB = (int)ktiles;
-  const int nch = (int)((a.k + kChunk - 1) / kChunk);
+  const uint32_t KB = (uint32_t)(a.k / kTileCols);
+  const uint32_t KBp = (KB + S - 1) / S * S;
   const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
-  const int64_t passes = (tiles + 3) / 4;
   const uint32_t e112 = exp112_pair();
+  const uint32_t kx = (uint32_t)a.k;
+  const Rsrc rx = make_rsrc(a.x, (uint32_t)a.m * kx * 2u);
 
-  for (int64_t pass = blockIdx.x; pass < passes; pass += gridDim.x) {
-    int64_t tile = pass * 4 + w;
+  // Piece I of chunk c (I < F): lanes 0..31 and 32..63 read rows 2q and 2q+1, columns
+  // 256 hb + 8 (lane % 32) .. +7 of the chunk, where q = I % (8 NT), hb = I / (8 NT).  Pieces
+  // are numbered per tile, P = c F + I.
+  const uint32_t prow = lane >> 5, pcol = 8u * (lane & 31);
+  const uint32_t lpart = 2u * (prow * kx + pcol);
+  // The address is computed unconditionally and hidden from the optimizer, so that the
+  // out-of-range select stays a select instead of a branch around the address arithmetic.
+  const auto piece_load = [&](uint32_t P, bool have) {
+    const uint32_t c = P / F, I = P % F, q = I % (8 * NT), hb = I / (8 * NT);
+    const uint32_t col0 = 128u * S * c + 256u * hb;
+    uint32_t off = 2u * (2u * q * kx + col0) + lpart;
+    asm volatile("" : "+v"(off));
+    const bool ok = have && col0 + pcol < kx && (int)(2 * q + prow) < a.m;
+    return __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off : kOOB, 0, 0);
+  };
+  // LDS slot of this lane's 16 bytes of piece I: fragment f = (k-block * 4 + t) * NT + cc holds
+  // x[16 cc + r][.. + 32 g + 8 t .. +7] for operand lane r + 16 g, at slot (r + 16 g) ^ swz(t, g),
+  // swz = t | (g & 1) << 2.  With a = 2q % 16 even, (a + row bit + 16 g) ^ swz splits into a
+  // uniform part, a lane part and (a % 8) ^ (row bit ^ swz).
+  const uint32_t pt = (pcol >> 3) & 3u, pg = (pcol >> 5) & 3u;
+  const uint32_t lslot = ((pcol >> 7) * 4u + pt) * NT * 64u + 16u * pg;
+  const uint32_t lkey = prow ^ (pt | ((pg & 1u) << 2));
+  const auto piece_slot = [&](uint32_t I) {
+    const uint32_t q = I % (8 * NT), hb = I / (8 * NT), aa = (2 * q) & 15u;
+    return (2 * hb * 4 * NT + (q >> 3)) * 64u + (aa & 8u) + lslot + ((aa & 7u) ^ lkey);
+  };
+  // Streamed pieces (P >= F) are dealt to the waves round-robin: wave w loads the pieces
+  // P = w (mod kWaves), each in the step whose range [F + (u + D - 1) FS, F + (u + D) FS) holds it,
+  // and stores it D - 1 steps later (into chunk P / F, which is then the next chunk).
+  const uint32_t first_piece = F + (uint32_t)((w - F % kWaves + kWaves) % kWaves);
+  // Branch-free: a wave without a piece this step loads nothing (offset past the range) and
+  // stores to s_scratch, which is never read; its ring entry has bit 31 set.
+  const auto x_stream_load = [&](int u, uint32_t& nxt, uint32_t (&pr)[XL], u32x4 (&dst)[XL]) {
+    const uint32_t hi = (uint32_t)(F + (u + D) * FS);
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const bool have = nxt < hi;
+      pr[i] = have ? nxt : (nxt | 0x80000000u);
+      dst[i] = piece_load(nxt, have);
+      nxt = have ? nxt + kWaves : nxt;
+    }
+  };
+  const auto x_stream_store = [&](const uint32_t (&pr)[XL], const u32x4 (&src)[XL]) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const uint32_t P = pr[i] & 0x7FFFFFFFu;
+      uint32_t at = ((P / F) & 1u) * (F * 64) + piece_slot(P % F);
+      asm volatile("" : "+v"(at));
+      u32x4* dst = (pr[i] >> 31) ? &s_scratch[lane] : &s_x[0][0] + at;
+      *dst = src[i];
+    }
+  };
+  const uint32_t bswz = lane ^ (((uint32_t)g & 1u) << 2);   // operand slot of k-group t: bswz ^ t
+
+  for (int round = 0; round < a.rounds; ++round) {
+    const int64_t tile = ((int64_t)round * kWaves + w) * gridDim.x + blockIdx.x;
     const bool valid = tile < tiles;
-    tile = valid ? tile : tiles - 1;             // every wave stays in the barriers below
-    const int64_t tb0 = tile * ktiles;
+    const int64_t row0 = (valid ? tile : 0) * kTileRows;
 
-    floatx4 acc[NT];
+    lds_barrier();                                 // the previous tile no longer reads LDS
+
+    // ---- escape list of the tile (oldest loads: waited for before the loop) ----
+    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0;
+    uint32_t ecol[kEscCap / 64], evalv[kEscCap / 64];
+    if constexpr (kEsc) {
+      const int64_t rg = row0 + 4 * g;
+      const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
 #pragma unroll
-    for (int c = 0; c < NT; ++c) acc[c] = (floatx4){0.f, 0.f, 0.f, 0.f};
-
-    ABlock<FMT> buf[D];
+      for (int r = 0; r < 5; ++r) st[r] = ptr_at(rg + r);
+      const Rsrc rb = make_rsrc(a.base, (uint32_t)a.n);
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < KB) load_ablock<FMT>(a, tb0 + d, lane, buf[d]);
-
-    // The escapes of this lane's four rows 4g..4g+3 form one contiguous CSR range; the whole
-    // tile's escapes are copied into LDS now, while the A blocks stream, so the epilogue only
-    // waits for its x loads.
-    uint32_t my_e0 = 0, my_b1 = 0, my_b2 = 0, my_b3 = 0, my_e1 = 0, t_e0 = 0, t_e1 = 0;
-    if constexpr (FMT != kFmtBF16) {
-      const int64_t row0 = tile * kTileRows;
-      auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
-      t_e0 = ptr_at(row0);
-      t_e1 = ptr_at(row0 + kTileRows);
-      my_e0 = ptr_at(row0 + 4 * g);
-      my_b1 = ptr_at(row0 + 4 * g + 1);
-      my_b2 = ptr_at(row0 + 4 * g + 2);
-      my_b3 = ptr_at(row0 + 4 * g + 3);
-      my_e1 = ptr_at(row0 + 4 * g + 4);
-      if (t_e1 - t_e0 <= (uint32_t)kEscCap) {
-        for (uint32_t e = t_e0 + lane; e < t_e1; e += 64) {
-          s_ecol[w][e - t_e0] = a.esc_col[e];
-          s_eval[w][e - t_e0] = a.esc_val[e];
-        }
+      for (int r = 0; r < 4; ++r)
+        bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
+      t_e0 = __builtin_amdgcn_readfirstlane(a.esc_ptr[row0]);
+      const uint32_t t_e1 = __builtin_amdgcn_readfirstlane(valid ? ptr_at(row0 + kTileRows) : t_e0);
+      const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCap ? t_e1 - t_e0 : (uint32_t)kEscCap;
+      const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
+      const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
+#pragma unroll
+      for (int i = 0; i < kEscCap / 64; ++i) {
+        ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
+        evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
+      }
+      if (!valid) {
+#pragma unroll
+        for (int r = 0; r < 5; ++r) st[r] = t_e0;
       }
     }
 
-    u32x4 rx[NX];
-    auto load_x = [&](int c) {
+    // ---- chunk 0 of x ----
+    constexpr int XF = (F + kWaves - 1) / kWaves;
+    u32x4 x0[XF];
 #pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        const int e = tid + i * kBlock, mr = e / (kChunk / 8), c8 = e % (kChunk / 8);
-        const int64_t col = (int64_t)c * kChunk + 8 * c8;
-        rx[i] = (mr < a.m && col < a.k) ? *reinterpret_cast<const u32x4*>(a.x + mr * a.ldx + col)
-                                        : (u32x4){0u, 0u, 0u, 0u};
-      }
-    };
-    auto store_x = [&](int b) {
-#pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        const int e = tid + i * kBlock, mr = e / (kChunk / 8), c8 = e % (kChunk / 8);
-        *reinterpret_cast<u32x4*>(&s_x[b][mr * kXPitch + 8 * c8]) = rx[i];
-      }
-    };
+    for (int i = 0; i < XF; ++i) x0[i] = piece_load((uint32_t)(w + kWaves * i), w + kWaves * i < F);
 
-    __syncthreads();                             // the previous pass no longer reads s_x
-    load_x(0);
-    store_x(0);
-    if (nch > 1) load_x(1);
-    __syncthreads();
+    // ---- D virtual steps -D .. -1: the same load pattern as a loop step ----
+    Rsrc ra, rl;
+    if constexpr (FMT == kFmtBF16) {
+      ra = make_rsrc(a.w + row0 * a.k, valid ? KB * (uint32_t)kTileBF : 0u);
+      rl = ra;
+    } else {
+      ra = make_rsrc(a.ae + row0 * a.k, valid ? KB * (uint32_t)kTileAE : 0u);
+      rl = make_rsrc(a.lo + row0 * a.k / 2, valid ? KB * (uint32_t)kTileLO : 0u);
+    }
+    ABlock<FMT> buf[D];
+    u32x4 xr[D][XL];
+    uint32_t pr[D][XL];
+    uint32_t nxt = first_piece;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      x_stream_load(d - D, nxt, pr[d], xr[d]);     // step d - D uses ring slot d
+      load_ablock<FMT>(ra, rl, (uint32_t)d, lane16, buf[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
-    int kb = 0;
-    for (int c = 0; c < nch; ++c) {
-      const int b = c & 1;
 #pragma unroll
-      for (int qb = 0; qb < kChunk / kTileCols; ++qb) {
-        if (kb < KB) {
-          const int slot = kb % D;
-          uint32_t p[16];
+    for (int i = 0; i < XF; ++i)
+      if (w + kWaves * i < F) s_x[0][piece_slot((uint32_t)(w + kWaves * i))] = x0[i];
+    if constexpr (kEsc) {
 #pragma unroll
-          for (int s = 0; s < D; ++s) {
-            if (s == slot) {
-              ablock_pairs<FMT>(buf[s], e112, p);
-              if (kb + D < KB) load_ablock<FMT>(a, tb0 + kb + D, lane, buf[s]);
-            }
-          }
+      for (int i = 0; i < kEscCap / 64; ++i) {
+        s_ecol[w][lane + 64 * i] = ecol[i];
+        s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
+      }
+    }
+    lds_barrier();
+
+    // per row r: cursor (absolute escape index) and the column under it (~0: none in LDS)
+    const uint32_t lds_end = t_e0 + kEscCap;
+    const auto run_end = [&](int r) { return st[r + 1] < lds_end ? st[r + 1] : lds_end; };
+    uint32_t cur[4], ncol[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
+    for (int r = 0; r < 4; ++r) {
+      cur[r] = st[r];
+      ncol[r] = 0xFFFFFFFFu;
+      if constexpr (kEsc) ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
+    }
+
+    floatx4 acc[NT];
+    float qv[NT][4];
 #pragma unroll
-            for (int cc = 0; cc < NT; ++cc) {
-              const u32x4 bv = *reinterpret_cast<const u32x4*>(
-                  &s_x[b][(16 * cc + r16) * kXPitch + kTileCols * qb + 32 * g + 8 * t]);
-              acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                               __builtin_bit_cast(bf16x8, bv), acc[cc],
-                                                               0, 0, 0);
-            }
+    for (int cc = 0; cc < NT; ++cc) {
+      acc[cc] = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qv[cc][r] = 0.f;
+    }
+
+    for (uint32_t c = 0; c * S < KBp; ++c) {       // chunk c: k-blocks S c .. S c + S - 1
+      const uint32_t b = c & 1u;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int slot = s % D;
+        const uint32_t kb = S * c + s;
+        uint32_t p[16];
+        ablock_pairs<FMT>(buf[slot], e112, p);
+        __builtin_amdgcn_sched_barrier(0);
+        // x ring: the fragments loaded at step kb - D + 1 go to LDS, then this step's fragments
+        x_stream_store(pr[(s + 1) % D], xr[(s + 1) % D]);
+        x_stream_load((int)kb, nxt, pr[slot], xr[slot]);
+        // A ring: refill this slot with block kb + D (dense blocks are their own A operands and
+        // are refilled after the MFMAs below)
+        if constexpr (FMT != kFmtBF16) load_ablock<FMT>(ra, rl, kb + D, lane16, buf[slot]);
+
+        const u32x4* xb = &s_x[b][s * FS * 64];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
+#pragma unroll
+          for (int cc = 0; cc < NT; ++cc) {
+            const u32x4 bv = xb[(t * NT + cc) * 64 + (bswz ^ (uint32_t)t)];
+            acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, bv), acc[cc],
+                                                             0, 0, 0);
           }
         }
-        ++kb;
+        if constexpr (FMT == kFmtBF16) load_ablock<FMT>(ra, rl, kb + D, lane16, buf[slot]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (c + 1 < nch) {
-        __syncthreads();
-        store_x(b ^ 1);
-        if (c + 2 < nch) load_x(c + 2);
-        __syncthreads();
+
+      if constexpr (kEsc) {
+        // escapes of rows 4g..4g+3 with a column in this chunk, x from LDS buffer b
+        const uint32_t lim = 128u * S * (c + 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          while (ncol[r] < lim) {
+            const uint32_t e = cur[r] - t_e0;
+            const uint32_t col = ncol[r] - 128u * S * c;
+            const float v = bf16_to_float(s_eval[w][e]);
+            const uint32_t tt = (col >> 3) & 3u, gg = (col >> 5) & 3u;
+            const uint32_t f0 = ((col >> 7) * 4u + tt) * NT;
+            const uint32_t ln = (r16 + 16u * gg) ^ (tt | ((gg & 1u) << 2));
+#pragma unroll
+            for (int cc = 0; cc < NT; ++cc) {
+              const float xv = bf16_to_float(
+                  reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
+              acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+              qv[cc][r] = fmaf(xv, v, qv[cc][r]);
+            }
+            cur[r] += 1;
+            ncol[r] = cur[r] < run_end(r) ? s_ecol[w][e + 1] : 0xFFFFFFFFu;
+          }
+        }
       }
+      lds_barrier();
     }
 
     if (!valid) continue;
-    float q[NT][4];
+    if constexpr (kEsc) {
+      // escapes beyond the LDS copy of a crowded tile
 #pragma unroll
-    for (int cc = 0; cc < NT; ++cc)
+      for (int r = 0; r < 4; ++r) {
+        for (uint32_t e = cur[r]; e < st[r + 1]; ++e) {
+          const uint32_t col = a.esc_col[e];
+          const float v = bf16_to_float(a.esc_val[e]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) q[cc][r] = 0.0f;
-    if constexpr (FMT != kFmtBF16) {
-      // Escapes of rows 4g..4g+3, kEscBatch at a time (their x loads are issued together).  The
-      // placeholder x * 2^-15 comes off the accumulator, the exact x * v goes to q.
-      const bool in_lds = t_e1 - t_e0 <= (uint32_t)kEscCap;
-      for (uint32_t e = my_e0; e < my_e1; e += kEscBatch) {
-        uint32_t col[kEscBatch];
-        float val[kEscBatch];
-        int rr[kEscBatch];
-#pragma unroll
-        for (int j = 0; j < kEscBatch; ++j) {
-          const uint32_t ej = e + j;
-          const bool ok = ej < my_e1;
-          if (in_lds) {
-            col[j] = ok ? s_ecol[w][ej - t_e0] : 0u;
-            val[j] = ok ? bf16_to_float(s_eval[w][ej - t_e0]) : 0.0f;
-          } else {
-            col[j] = ok ? a.esc_col[ej] : 0u;
-            val[j] = ok ? bf16_to_float(a.esc_val[ej]) : 0.0f;
-          }
-          rr[j] = ok ? (int)(ej >= my_b1) + (int)(ej >= my_b2) + (int)(ej >= my_b3) : -1;
-        }
-#pragma unroll
-        for (int cc = 0; cc < NT; ++cc) {
-          const int mcol = 16 * cc + r16;
-          float xv[kEscBatch];
-#pragma unroll
-          for (int j = 0; j < kEscBatch; ++j)
-            xv[j] = (rr[j] >= 0 && mcol < a.m) ? bf16_to_float(a.x[mcol * a.ldx + col[j]]) : 0.0f;
-#pragma unroll
-          for (int j = 0; j < kEscBatch; ++j) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (rr[j] == r) {
-                acc[cc][r] = fmaf(-xv[j], kPlaceholder, acc[cc][r]);
-                q[cc][r] = fmaf(xv[j], val[j], q[cc][r]);
-              }
-            }
+          for (int cc = 0; cc < NT; ++cc) {
+            const int mrow = 16 * cc + r16;
+            const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
+            acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+            qv[cc][r] = fmaf(xv, v, qv[cc][r]);
           }
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t nrow = tile * kTileRows + 4 * g + r;
+      const int64_t nrow = row0 + 4 * g + r;
       if (nrow >= a.n) continue;
-      float sc = 1.0f;
-      if constexpr (FMT != kFmtBF16) sc = window_scale(a.base[nrow]);
+      const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
 #pragma unroll
       for (int cc = 0; cc < NT; ++cc) {
         const int mcol = 16 * cc + r16;
         if (mcol >= a.m) continue;
-        const float v = FMT != kFmtBF16 ? fmaf(sc, acc[cc][r], q[cc][r]) : acc[cc][r];
+        const float v = kEsc ? fmaf(sc, acc[cc][r], qv[cc][r])
+                             : acc[cc][r];
         a.y[mcol * a.ldy + nrow] = v;
       }
     }
@@ -274,16 +406,13 @@ void k_mfma(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 typedef void (*MfmaKernel)(MfmaArgs);
 
-// Blocks of A in flight per wave: fewer when more activation tiles (or the 4-word dense bf16
-// blocks of the baseline) need registers.
 template <int FMT>
 static MfmaKernel pick(int nt) {
-  constexpr int D2 = 3;
   switch (nt) {
-    case 1: return k_mfma<FMT, 1, 4>;
-    case 2: return k_mfma<FMT, 2, D2>;
-    case 3: return k_mfma<FMT, 3, 3>;
-    default: return k_mfma<FMT, 4, 3>;
+    case 1: return k_mfma<FMT, 1>;
+    case 2: return k_mfma<FMT, 2>;
+    case 3: return k_mfma<FMT, 3>;
+    default: return k_mfma<FMT, 4>;
   }
 }
 
@@ -299,20 +428,13 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t grid = tiles < di.cus ? tiles : di.cus;
+  const int64_t rounds = (tiles + grid * kWaves - 1) / (grid * kWaves);
   for (int64_t m0 = 0; m0 < m; m0 += 64) {
     const int mb = (int)((m - m0) < 64 ? (m - m0) : 64);
     const int nt = (mb + 15) / 16;
-    MfmaKernel kern = pick_kernel(f, nt);
-    int occ = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern), kBlock, 0);
-    if (err != hipSuccess) return err;
-    if (occ < 1) occ = 1;
-    int64_t blocks = (tiles + 3) / 4;
-    const int64_t cap = (int64_t)di.cus * occ;
-    if (blocks > cap) blocks = cap;
     MfmaArgs a;
     a.x = x + m0 * k;
-    a.ldx = k;
     a.m = mb;
     a.base = p.base; a.ae = p.ae; a.lo = p.lo;
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
@@ -320,7 +442,8 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     a.y = y + m0 * n;
     a.ldy = n;
     a.n = n; a.k = k;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    a.rounds = (int)rounds;
+    hipLaunchKernelGGL(pick_kernel(f, nt), dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
