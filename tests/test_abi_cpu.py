@@ -78,5 +78,7 @@ def test_argument_errors_are_host_side():
     assert L.w12_bf16_to_tiles(None, 8, 128, 0x1000, None) == w12.W12_ERR_ARG
     assert L.w12_bf16_to_tiles(0x1000, 8, 200, 0x1000, None) == w12.W12_ERR_SHAPE
     assert L.w12_read_probe(0x1000, 20, 0x1000, None) == w12.W12_ERR_SHAPE
-    # huge sizes
+    # huge sizes: n >= 2^31, k > 2^24 (kernels use 32-bit buffer offsets)
     assert L.w12_decode(ctypes.byref(_rec(n=1 << 40)), 0x1000, None) == w12.W12_ERR_RANGE
+    assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec(k=(1 << 24) + 128)), 0x1000, 0, None) == w12.W12_ERR_RANGE
+    assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, (1 << 24) + 128, 0x1000, 0, None) == w12.W12_ERR_RANGE
