@@ -6,11 +6,23 @@
 // bandwidth-bound matrix-vector stream, not a dense contraction.
 //
 // Work split: persistent workgroups of 4 waves.  A workgroup copies its k-slice of x into LDS
-// once.  A wave owns one 16-row tile of the tiled plane storage (see w12_device.hpp) and, with
-// KS > 1, only every KS-th 128-column block of it (the KS waves of a tile are in the same
+// once.  A wave owns one 16-row tile of the tiled plane storage (see w12_device.hpp) at a time
+// and, with KS > 1, only every KS-th 128-column block of it (the KS waves of a tile are in the same
 // workgroup and add their partial sums through LDS in a fixed order).  Lane l = r + 16g works on
 // row r, columns 32g..32g+31 of each block: its AE (2 x 128-bit) and B (1 x 128-bit) loads are
-// wave-wide 1 KiB contiguous reads.  The next D blocks are always in flight.
+// wave-wide 1 KiB contiguous reads.
+//
+// Escapes: the part-0 wave of a tile patches them from x in LDS.  Their metadata is fetched one
+// tile ahead so the patch never waits on memory: the row bounds of the wave's next tile at the
+// start of a tile, that tile's first kEscPre escapes per row at its end (rows with more read the
+// rest from memory).
+//
+// Pipeline: D blocks in flight per wave, through buffer loads whose offset is pushed past the
+// range when there is nothing to load (w12_device.hpp), so the ring slots are static registers and
+// each step waits only for the block it consumes.  The ring runs on across the wave's tiles: the
+// last D refills of a tile already fetch the first blocks of the wave's next tile, so a tile's
+// epilogue (escape patch, cross-wave sum, store) does not drain the stream.  Padding steps (when a
+// wave has fewer blocks than the ring period) read zeros and skip their arithmetic.
 //
 // Window trick: a decoded pair is w' = w / 2^(base - 112), with the exponent field 112 + E
 // (see w12_device.hpp), so the row's dot product sum_k x w' is scaled once by 2^(base - 112)
@@ -45,19 +57,41 @@ struct BlockRegs {
   u32x4 v[FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2];
 };
 
+// Buffers over one tile's blocks of the planes (or the dense baseline); an absent tile reads zeros.
 template <int FMT>
-__device__ __forceinline__ void load_block(const GemvArgs& a, int64_t tile_block, int lane,
+struct TileRsrc {
+  Rsrc r0, r1;
+};
+
+template <int FMT>
+__device__ __forceinline__ TileRsrc<FMT> tile_rsrc(const GemvArgs& a, int64_t tile, bool valid,
+                                                   uint32_t ktiles) {
+  TileRsrc<FMT> t;
+  const int64_t t0 = valid ? tile : 0;
+  if constexpr (FMT == kFmtBF16) {
+    t.r0 = make_rsrc(a.w + t0 * ktiles * (kTileBF / 2), valid ? ktiles * (uint32_t)kTileBF : 0u);
+    t.r1 = t.r0;
+  } else {
+    t.r0 = make_rsrc(a.ae + t0 * ktiles * kTileAE, valid ? ktiles * (uint32_t)kTileAE : 0u);
+    t.r1 = make_rsrc(a.lo + t0 * ktiles * kTileLO, valid ? ktiles * (uint32_t)kTileLO : 0u);
+  }
+  return t;
+}
+
+// Block `kb` of the tile (kb = ~0: nothing) into the lane's registers.
+template <int FMT>
+__device__ __forceinline__ void load_block(const TileRsrc<FMT>& t, uint32_t kb, uint32_t lane16,
                                            BlockRegs<FMT>& r) {
   if constexpr (FMT == kFmtBF16) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.w) + tile_block * (kTileBF / 16) + lane;
+    const uint32_t off = kb == ~0u ? kOOB : kb * kTileBF + lane16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r.v[q] = load_nt(src + 64 * q);
+    for (int q = 0; q < 4; ++q) r.v[q] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off + 1024 * q, 0, kAuxNT);
   } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.ae) + tile_block * (kTileAE / 16) + lane;
-    r.v[0] = load_nt(src);
-    r.v[1] = load_nt(src + 64);
+    const uint32_t off = kb == ~0u ? kOOB : kb * kTileAE + lane16;
+    r.v[0] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off, 0, kAuxNT);
+    r.v[1] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off + 1024, 0, kAuxNT);
     if constexpr (FMT == kFmtW12)
-      r.v[2] = load_nt(reinterpret_cast<const u32x4*>(a.lo) + tile_block * (kTileLO / 16) + lane);
+      r.v[2] = __builtin_amdgcn_raw_buffer_load_b128(t.r1, kb == ~0u ? kOOB : kb * kTileLO + lane16, 0, kAuxNT);
   }
 }
 
@@ -89,55 +123,111 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+constexpr int kEscPre = 4;   // escapes per lane fetched ahead (16 per row)
+
 template <int FMT, int M, int D, int KS>
 __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   extern __shared__ u32x4 xs[];                 // [M][kn / 8] in 16-byte words
   __shared__ float red[4][M][64];                // partial sums of the KS waves of a tile
   constexpr int TPB = 4 / KS;                    // tiles per workgroup pass
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const uint32_t lane16 = 16u * lane;
   const int kn = a.kn, kn8 = kn >> 3;
 
-  for (int i = tid; i < M * kn8; i += kBlock) {
-    const int m = i / kn8, j = i - m * kn8;
-    xs[i] = *reinterpret_cast<const u32x4*>(a.x + m * a.ldx + a.k0 + 8 * j);
-  }
-  __syncthreads();
   const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(xs);
 
   const uint32_t e112 = exp112_pair();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int part = w % KS, tsub = w / KS;
-  const int64_t ktiles = a.k / kTileCols;
+  const uint32_t ktiles = (uint32_t)(a.k / kTileCols);
   const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
   const int64_t passes = (tiles + TPB - 1) / TPB;
-  const int64_t kb0 = a.k0 / kTileCols;
+  const uint32_t kb0 = (uint32_t)(a.k0 / kTileCols);
   const int nblk = kn / kTileCols;
   const int mine = (nblk - part + KS - 1) / KS;  // blocks of this slice owned by this wave
+  const int JP = ((nblk + KS - 1) / KS + D - 1) / D * D;   // ring steps per tile, all waves
+  // block of step j (0 <= j < JP) of this wave, ~0 for a padding step
+  const auto blk = [&](int j) { return j < mine ? kb0 + (uint32_t)(part + j * KS) : ~0u; };
 
-  for (int64_t pass = blockIdx.x; pass < passes; pass += gridDim.x) {
-    int64_t tile = pass * TPB + tsub;
+  int64_t pass = blockIdx.x;
+  const auto tile_of = [&](int64_t ps) { return ps * TPB + tsub; };
+  TileRsrc<FMT> cur = tile_rsrc<FMT>(a, tile_of(pass), pass < passes && tile_of(pass) < tiles, ktiles);
+  int64_t npass = pass + gridDim.x;
+  TileRsrc<FMT> nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
+
+  // escape metadata of a tile for this lane's row (part-0 waves only; others load nothing):
+  // bounds [e0, e1) of the row, the tile's first escape te0, and entries e0 + g + 4 i
+  constexpr bool kEsc = FMT != kFmtBF16;
+  uint32_t ce0 = 0, ce1 = 0, ecol[kEscPre], evalv[kEscPre];   // current tile
+  uint32_t ne0 = 0, ne1 = 0, nte0 = 0;                         // next tile (bounds only)
+  uint32_t cbase = 0, nbase = 0;                               // window bottom of the row
+  const auto esc_bounds = [&](int64_t ps, uint32_t& e0, uint32_t& e1, uint32_t& te0, uint32_t& bs) {
+    const int64_t t = tile_of(ps);
+    const bool use = kEsc && part == 0 && ps < passes && t < tiles;
+    const int64_t r = use ? t * kTileRows + r16 : 0;
+    e0 = use ? a.esc_ptr[r < a.n ? r : a.n] : 0u;
+    e1 = use ? a.esc_ptr[r + 1 < a.n ? r + 1 : a.n] : 0u;
+    bs = use ? a.base[r < a.n ? r : a.n - 1] : 0u;
+    te0 = use ? a.esc_ptr[t * kTileRows] : 0u;   // made uniform only when used, a tile later:
+  };                                              // a uniform copy now would wait for the ring
+  const auto esc_entries = [&](uint32_t e0, uint32_t e1, uint32_t te0v) {
+    const uint32_t te0 = __builtin_amdgcn_readfirstlane(te0v);
+    const Rsrc rc = make_rsrc(a.esc_col + te0, 0x7FFFFFF0u), rv = make_rsrc(a.esc_val + te0, 0x7FFFFFF0u);
+#pragma unroll
+    for (int i = 0; i < kEscPre; ++i) {
+      const uint32_t e = e0 + g + 4 * i;
+      ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, e < e1 ? 4u * (e - te0) : kOOB, 0, 0);
+      evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, e < e1 ? 2u * (e - te0) : kOOB, 0, 0);
+    }
+  };
+  // Start the weight stream first; the x copy and the first escape bounds load behind it.
+  BlockRegs<FMT> buf[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_block<FMT>(cur, blk(d), lane16, buf[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  uint32_t te0 = 0;
+  if constexpr (kEsc) esc_bounds(pass, ce0, ce1, te0, cbase);
+  for (int i = tid; i < M * kn8; i += kBlock) {
+    const int m = i / kn8, j = i - m * kn8;
+    xs[i] = *reinterpret_cast<const u32x4*>(a.x + m * a.ldx + a.k0 + 8 * j);
+  }
+  lds_barrier();
+  if constexpr (kEsc) esc_entries(ce0, ce1, te0);
+
+  for (; pass < passes; pass += gridDim.x) {
+    const int64_t tile = tile_of(pass);
     const bool valid = tile < tiles;
-    tile = valid ? tile : tiles - 1;             // every wave stays in the barriers below
-    const int64_t tile_block0 = tile * ktiles + kb0;
+    if constexpr (kEsc) esc_bounds(pass + gridDim.x, ne0, ne1, nte0, nbase);
 
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-    BlockRegs<FMT> buf[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < mine) load_block<FMT>(a, tile_block0 + part + d * KS, lane, buf[d]);
-
-    for (int j0 = 0; j0 < mine; j0 += D) {
+    // do-while: at least one body runs, so its first wait also covers the older escape loads
+    // and the epilogue needs no wait of its own
+    int j0 = 0;
+    do {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int j = j0 + d;
+        uint32_t p[16];
+        block_pairs<FMT>(buf[d], e112, p);
+        if constexpr (FMT != kFmtBF16) pin16(p);
+        __builtin_amdgcn_sched_barrier(0);
+        // refill: step j + D of this tile, or of the wave's next tile (dense blocks are their own
+        // operands: refilled after the arithmetic below)
+        const auto refill = [&]() {
+          const bool here = j + D < JP;
+          TileRsrc<FMT> t;
+          t.r0 = here ? cur.r0 : nxt.r0;
+          t.r1 = here ? cur.r1 : nxt.r1;
+          load_block<FMT>(t, blk(here ? j + D : j + D - JP), lane16, buf[d]);
+        };
+        if constexpr (FMT != kFmtBF16) refill();
         if (j < mine) {
           const int kb = part + j * KS;          // block within the slice
-          uint32_t p[16];
-          block_pairs<FMT>(buf[d], e112, p);
-          if (j + D < mine) load_block<FMT>(a, tile_block0 + part + (j + D) * KS, lane, buf[d]);
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             const u32x4* xr = xs + m * kn8 + (kTileCols * kb + 32 * g) / 8;
@@ -154,31 +244,38 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
             acc[m] = s;
           }
         }
+        if constexpr (FMT == kFmtBF16) refill();
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+      j0 += D;
+    } while (j0 < JP);
+    cur = nxt;
+    npass += gridDim.x;
+    nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
 
     const int64_t row = tile * kTileRows + r16;
     float q[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) q[m] = 0.0f;
-    if constexpr (FMT != kFmtBF16) {
+    if constexpr (kEsc) {
       // Escapes of this lane's row inside the slice (part-0 wave; the 4 column-group lanes of the
       // row share the list): remove the placeholder from P, collect Q = sum x * v.
-      if (part == 0 && valid && row < a.n) {
-        const uint32_t e0 = a.esc_ptr[row], e1 = a.esc_ptr[row + 1];
-        for (uint32_t e = e0 + g; e < e1; e += 4) {
-          const int64_t c = (int64_t)a.esc_col[e] - a.k0;
-          if (c >= 0 && c < kn) {
-            const float v = bf16_to_float(a.esc_val[e]);
+      const auto patch = [&](uint32_t col, uint32_t vbits) {
+        const int64_t c = (int64_t)col - a.k0;
+        if (c >= 0 && c < kn) {
+          const float v = bf16_to_float(vbits);
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const float xv = bf16_to_float(xs16[m * kn + c]);
-              acc[m] = fmaf(-xv, kPlaceholder, acc[m]);
-              q[m] = fmaf(xv, v, q[m]);
-            }
+          for (int m = 0; m < M; ++m) {
+            const float xv = bf16_to_float(xs16[m * kn + c]);
+            acc[m] = fmaf(-xv, kPlaceholder, acc[m]);
+            q[m] = fmaf(xv, v, q[m]);
           }
         }
-      }
+      };
+#pragma unroll
+      for (int i = 0; i < kEscPre; ++i)
+        if (ce0 + g + 4 * i < ce1) patch(ecol[i], evalv[i]);
+      for (uint32_t e = ce0 + g + 4 * kEscPre; e < ce1; e += 4) patch(a.esc_col[e], a.esc_val[e]);
 #pragma unroll
       for (int m = 0; m < M; ++m) q[m] = group_sum(q[m]);
     }
@@ -188,25 +285,35 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     if constexpr (KS > 1) {
 #pragma unroll
       for (int m = 0; m < M; ++m) red[w][m][lane] = acc[m];
-      __syncthreads();
+      lds_barrier();
       if (part == 0) {
 #pragma unroll
         for (int pp = 1; pp < KS; ++pp)
 #pragma unroll
           for (int m = 0; m < M; ++m) acc[m] += red[w + pp][m][lane];
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     if (part == 0 && valid && g == 0 && row < a.n) {
       float sc = 1.0f;
-      if constexpr (FMT != kFmtBF16) sc = window_scale(a.base[row]);
+      if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float v = FMT != kFmtBF16 ? fmaf(sc, acc[m], q[m]) : acc[m];
         float* yp = a.y + m * a.ldy + row;
-        *yp = a.accumulate ? *yp + v : v;
+        // later k-slices add to y; the read stays in its branch (a hoisted read would make every
+        // tile wait for the whole stream in flight)
+        if (a.accumulate) *yp = *reinterpret_cast<volatile float*>(yp) + v;
+        else *yp = v;
       }
+    }
+    if constexpr (kEsc) {
+      // the next tile's entries and window bottoms (its bounds arrived during this tile)
+      ce0 = ne0;
+      ce1 = ne1;
+      cbase = nbase;
+      esc_entries(ne0, ne1, nte0);
     }
   }
 }
@@ -221,7 +328,7 @@ typedef void (*GemvKernel)(GemvArgs);
 // 5-8 keep one wave per tile.
 template <int FMT, int M>
 static GemvKernel pick_m() {
-  if constexpr (M <= 2) return k_gemv<FMT, M, 2, 4>;
+  if constexpr (M <= 2) return k_gemv<FMT, M, 3, 4>;
   else if constexpr (M <= 4) return k_gemv<FMT, M, 4, 2>;
   else return k_gemv<FMT, M, 4, 1>;
 }

@@ -65,16 +65,7 @@ struct MfmaArgs {
 };
 
 constexpr int kWaves = 12;                  // waves per workgroup, one workgroup per CU
-constexpr uint32_t kOOB = 0x80000000u;      // buffer offset past every range used here
-constexpr int kAuxNT = 2;                   // cache policy bits: non-temporal (weights stream once)
 constexpr int kEscCap = 128;                // escapes of one tile copied to LDS
-
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-
-// Raw buffer over `bytes` bytes at `p` (stride 0, 32-bit data format word of the gfx9 family).
-__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 
 template <int FMT>
 struct ABlock {
@@ -116,13 +107,6 @@ __device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112
     window_group8_q(r.v[1].x, r.v[1].y, e112, p + 8);
     window_group8_q(r.v[1].z, r.v[1].w, e112, p + 12);
   }
-}
-
-// Workgroup barrier that orders LDS only (vector-memory loads in flight are not waited for).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Compile-time shape of one instantiation.  Decoding formats keep a 3-deep ring at two activation
@@ -315,6 +299,7 @@ void k_mfma(MfmaArgs a) {
         const uint32_t kb = S * c + s;
         uint32_t p[16];
         ablock_pairs<FMT>(buf[slot], e112, p);
+        if constexpr (FMT != kFmtBF16) pin16(p);
         __builtin_amdgcn_sched_barrier(0);
         // x ring: the fragments loaded at step kb - D + 1 go to LDS, then this step's fragments
         x_stream_store(pr[(s + 1) % D], xr[(s + 1) % D]);

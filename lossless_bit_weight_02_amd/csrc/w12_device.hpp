@@ -128,4 +128,34 @@ __device__ __forceinline__ T load_nt(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// ---- buffer loads (raw buffer resources) ----
+// An offset at or past a buffer's num_records reads zeros and fetches nothing, so a kernel can
+// issue every load of a software pipeline unconditionally (no load behind a branch, static ring
+// registers) and switch a load off by its offset alone.
+constexpr uint32_t kOOB = 0x80000000u;      // offset past every range used here
+constexpr int kAuxNT = 2;                   // cache policy bits: non-temporal (weights stream once)
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Raw buffer over `bytes` bytes at `p` (stride 0, 32-bit data format word of the gfx9 family).
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Forces the 16 decoded words to exist here: a decode is pure arithmetic, which the optimizer
+// would otherwise sink to its first use -- past the refill of the ring slot it reads, which then
+// needs other registers and a copy back (after a wait) at the end of every loop body.
+__device__ __forceinline__ void pin16(uint32_t p[16]) {
+  asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]),
+               "+v"(p[6]), "+v"(p[7]), "+v"(p[8]), "+v"(p[9]), "+v"(p[10]), "+v"(p[11]),
+               "+v"(p[12]), "+v"(p[13]), "+v"(p[14]), "+v"(p[15]));
+}
+
+// Workgroup barrier that orders LDS only (vector-memory loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace w12
