@@ -58,12 +58,17 @@ def assert_records_equal(got: dict, want, what=""):
 def check_gemm(y_gpu: np.ndarray, x_bits, w_bits, what="", rel=1e-3):
     """|y - y64| <= rel * sum|x w| for finite oracle values; non-finite oracle values must be
     matched in kind (NaN with NaN, +-Inf with the same Inf).  Returns the worst error / bound."""
+    return check_y(y_gpu, oracle.gemm64(x_bits, w_bits), oracle.abs_bound64(x_bits, w_bits), what, rel)
+
+
+def check_y(y_gpu: np.ndarray, y64: np.ndarray, absum: np.ndarray, what="", rel=1e-3):
+    """check_gemm against a precomputed oracle product y64 and sum |x w| (same shapes)."""
     y = np.asarray(y_gpu, dtype=np.float64)
-    y64 = oracle.gemm64(x_bits, w_bits)
-    bound = rel * oracle.abs_bound64(x_bits, w_bits)
+    bound = rel * absum
     fin = np.isfinite(y64)
     nan = np.isnan(y64)
     inf = ~fin & ~nan
+    assert y.shape == y64.shape, f"{what}: shape {y.shape} != {y64.shape}"
     assert np.all(np.isnan(y[nan])), f"{what}: NaN expected"
     assert np.array_equal(y[inf], y64[inf]), f"{what}: Inf mismatch"
     err = np.abs(y[fin] - y64[fin])
@@ -76,3 +81,20 @@ def check_gemm(y_gpu: np.ndarray, x_bits, w_bits, what="", rel=1e-3):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(bound[fin] > 0, err / bound[fin], 0.0)
     return float(r.max()) if r.size else 0.0
+
+
+def check_top1(y_gpu: np.ndarray, y64: np.ndarray, absum: np.ndarray, what="", rel=1e-3):
+    """Top-1 over the last axis: the GPU's argmax must be a maximum of y64 within the error bound
+    (a tie within the bound may resolve either way).  Returns the number of exact agreements."""
+    g = np.argmax(np.asarray(y_gpu, dtype=np.float64), axis=-1)
+    o = oracle.top1(y64)
+    agree = 0
+    for m in range(y64.shape[0]):
+        a, b = int(g[m]), int(o[m])
+        if a == b:
+            agree += 1
+            continue
+        slack = rel * (absum[m, a] + absum[m, b])
+        assert y64[m, a] >= y64[m, b] - slack, (f"{what}: row {m}: GPU argmax {a} "
+                                                f"(y64 {y64[m, a]}) vs oracle {b} (y64 {y64[m, b]})")
+    return agree

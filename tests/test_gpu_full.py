@@ -1,0 +1,123 @@
+"""GPU parity at the full workload sizes, in the launch configurations bench.py times.
+
+gate+up [34816, 5120] (every M of its config, both kernel families), the LM-head-shaped Q pass
+[152064, 5120] at M=16 with top-1, and three layers (0, 31, 63) of the 64-layer 27B-class stack.
+The oracle runs over row chunks in spawned worker processes (tests/oracle_pool.py), so every
+output element and every stored byte is compared, not a sample.
+"""
+import numpy as np
+import pytest
+
+from lossless_bit_weight_02_amd import synth
+from tests import oracle_pool
+from tests.gpu_util import (assert_records_equal, check_top1, check_y, record_numpy, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_bit_weight_02_amd import w12
+    w12.lib()  # fails loudly if the library is missing
+
+
+@pytest.fixture(scope="module")
+def pool():
+    ex = oracle_pool.make_pool()
+    yield ex
+    ex.shutdown()
+
+
+def _w12():
+    from lossless_bit_weight_02_amd import w12
+    return w12
+
+
+def _codec(w, what, pool):
+    """GPU encode byte-identical to the oracle's record, GPU decode bit-exact; returns the record."""
+    w12 = _w12()
+    dw = to_dev(w)
+    say(f"{what}: encode {w.shape}")
+    rec = w12.encode(dw)
+    say(f"{what}: oracle encode (row chunks)")
+    ref = oracle_pool.encode(w, pool)
+    assert_records_equal(record_numpy(rec), ref, what)
+    say(f"{what}: decode")
+    back = w12.decode(rec)
+    assert torch.equal(back.view(torch.int16), dw.view(torch.int16)), f"{what}: decode not bit-exact"
+    del back
+    return rec, dw
+
+
+def test_gate_up_full(pool):
+    """Config gate+up: codec, exact GEMM at M = 1, 4, 8, 16, 32, 64 on both kernel families, the
+    Q pass at M=16 and the dense baseline at M=1 and 32 -- every output element."""
+    w12 = _w12()
+    w, spec, tid = synth.config_weight("gate_up")
+    rec, dw = _codec(w, "gate_up", pool)
+    x = synth.gen_x(64, spec.k, tensor_id=tid)
+    say("gate_up: oracle GEMM M=64 (all rows)")
+    y64, absum = oracle_pool.gemm(x, w, pool)
+    for m in (1, 4, 8, 16, 32, 64):
+        for path in ("gemv", "mfma"):
+            say(f"gate_up: gemm m={m} path={path}")
+            y = w12.gemm(to_dev(x[:m]), rec, path=path).cpu().numpy()
+            check_y(y, y64[:m], absum[:m], f"gate_up w12 m={m} {path}")
+    say("gate_up: oracle Q-pass GEMM M=16")
+    yq64, qabs = oracle_pool.gemm(x[:16], w, pool, view="q8")
+    for path in ("gemv", "mfma"):
+        say(f"gate_up: q8_gemm m=16 path={path}")
+        yq = w12.q8_gemm(to_dev(x[:16]), rec, path=path).cpu().numpy()
+        check_y(yq, yq64, qabs, f"gate_up q8 m=16 {path}")
+    bt = w12.bf16_tiles(dw)
+    for m, path in ((1, "gemv"), (32, "mfma")):
+        say(f"gate_up: bf16_gemm m={m} path={path}")
+        yb = w12.bf16_gemm(to_dev(x[:m]), bt, path=path).cpu().numpy()
+        check_y(yb, y64[:m], absum[:m], f"gate_up bf16 m={m} {path}")
+
+
+def test_lm_head_q_pass_top1(pool):
+    """Config LM head [152064, 5120], M=16: Q pass and exact pass on every output, and the top-1
+    token of each row within the error bound (a near-tie may resolve either way)."""
+    w12 = _w12()
+    w, spec, tid = synth.config_weight("lm_head")
+    rec, dw = _codec(w, "lm_head", pool)
+    del dw
+    x = synth.gen_x(16, spec.k, tensor_id=tid)
+    xd = to_dev(x)
+    say("lm_head: q8_gemm m=16")
+    yq = w12.q8_gemm(xd, rec).cpu().numpy()
+    say("lm_head: oracle Q-pass GEMM (all rows)")
+    yq64, qabs = oracle_pool.gemm(x, w, pool, view="q8")
+    check_y(yq, yq64, qabs, "lm_head q8")
+    agree_q = check_top1(yq, yq64, qabs, "lm_head q8 top-1")
+    say("lm_head: gemm m=16")
+    y = w12.gemm(xd, rec).cpu().numpy()
+    say("lm_head: oracle exact GEMM (all rows)")
+    y64, absum = oracle_pool.gemm(x, w, pool)
+    check_y(y, y64, absum, "lm_head exact")
+    agree = check_top1(y, y64, absum, "lm_head exact top-1")
+    say(f"lm_head: top-1 exact agreement q8 {agree_q}/16, exact {agree}/16")
+
+
+@pytest.mark.parametrize("layer", [0, 31, 63])
+def test_stack_layer(pool, layer):
+    """Config 27B stack, layers 0, 31 and 63 (all seven projections): codec and the exact GEMM at
+    M = 1 and 32 in the bench's launch configuration (GEMV at 1, MFMA at 32)."""
+    w12 = _w12()
+    cfg = synth.CONFIGS["stack"]
+    for p in range(len(synth.STACK_PROJ)):
+        tid, label, spec = cfg.weights[layer * len(synth.STACK_PROJ) + p]
+        w = synth.gen_weight(spec, 0, tid)
+        rec, dw = _codec(w, label, pool)
+        del dw
+        x = synth.gen_x(32, spec.k, tensor_id=tid)
+        y64, absum = oracle_pool.gemm(x, w, pool)
+        for m in (1, 32):
+            say(f"{label}: gemm m={m}")
+            y = w12.gemm(to_dev(x[:m]), rec).cpu().numpy()
+            check_y(y, y64[:m], absum[:m], f"{label} w12 m={m}")
