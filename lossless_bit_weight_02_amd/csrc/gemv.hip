@@ -180,7 +180,20 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, e < e1 ? 2u * (e - te0) : kOOB, 0, 0);
     }
   };
-  // Start the weight stream first; the x copy and the first escape bounds load behind it.
+  // x first (loads complete in issue order: x queued behind the weight stream would hold the
+  // workgroup's first barrier until the first blocks arrived), then the weight stream, then the
+  // first escape bounds.  The first kXF words per thread cover x of every shape with
+  // 2 m kn <= 16 KiB; the rest (long rows) is copied after.
+  constexpr int kXF = 4;
+  const Rsrc r_x = make_rsrc(a.x, (uint32_t)(M * a.ldx * 2));
+  u32x4 xv[kXF];
+#pragma unroll
+  for (int q = 0; q < kXF; ++q) {
+    const int i = tid + q * kBlock, m = i / kn8, j = i - m * kn8;
+    xv[q] = __builtin_amdgcn_raw_buffer_load_b128(
+        r_x, i < M * kn8 ? (uint32_t)(2 * (m * a.ldx + a.k0 + 8 * j)) : kOOB, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   BlockRegs<FMT> buf[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -189,7 +202,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   }
   uint32_t te0 = 0;
   if constexpr (kEsc) esc_bounds(pass, ce0, ce1, te0, cbase);
-  for (int i = tid; i < M * kn8; i += kBlock) {
+#pragma unroll
+  for (int q = 0; q < kXF; ++q) {
+    const int i = tid + q * kBlock;
+    if (i < M * kn8) xs[i] = xv[q];
+  }
+  for (int i = tid + kXF * kBlock; i < M * kn8; i += kBlock) {
     const int m = i / kn8, j = i - m * kn8;
     xs[i] = *reinterpret_cast<const u32x4*>(a.x + m * a.ldx + a.k0 + 8 * j);
   }

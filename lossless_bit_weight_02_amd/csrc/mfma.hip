@@ -40,8 +40,10 @@
 // start of the tile; at the end of every chunk each lane walks its rows' column-sorted runs up to
 // the chunk's last column, reading x from the chunk still in LDS, and accumulates
 //   y = 2^(base-112) * (acc - 2^-15 * sum_esc x) + sum_esc x * v,
-// which takes the placeholder value 2^-15 of an escaped slot (AE = 0, B = 0) back out of acc
-// (subtracted from the accumulator itself at the end of the chunk).
+// which takes the placeholder value 2^-15 of an escaped slot (AE = 0, B = 0) back out of acc.
+// Up to two activation tiles the x sums of the escaped slots are kept apart from the
+// matrix-core accumulators: a vector write into an accumulator between MFMAs that feed it
+// stalls the chain.
 // Escapes past the LDS copy of a crowded tile are read from memory after the loop.
 #include "w12_device.hpp"
 #include "w12_launch.hpp"
@@ -128,6 +130,9 @@ void k_mfma(MfmaArgs a) {
   using SH = Shape<FMT, NT>;
   constexpr int D = SH::D, S = SH::S, FS = SH::FS, F = SH::F, XL = SH::XL;
   constexpr bool kEsc = FMT != kFmtBF16;
+  // x sums of escaped slots in registers of their own (up to two activation tiles; beyond that
+  // the registers are not there and the placeholders come out of the accumulators directly)
+  constexpr bool kSepSx = NT <= 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
   __shared__ __attribute__((aligned(16))) u32x4 s_scratch[64];   // stores of waves with no piece
   __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];   // per wave: tile escapes
@@ -283,12 +288,12 @@ void k_mfma(MfmaArgs a) {
     }
 
     floatx4 acc[NT];
-    float qv[NT][4];
+    float qv[NT][4], sx[NT][4];
 #pragma unroll
     for (int cc = 0; cc < NT; ++cc) {
       acc[cc] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qv[cc][r] = 0.f;
+      for (int r = 0; r < 4; ++r) qv[cc][r] = sx[cc][r] = 0.f;
     }
 
     for (uint32_t c = 0; c * S < KBp; ++c) {       // chunk c: k-blocks S c .. S c + S - 1
@@ -340,7 +345,8 @@ void k_mfma(MfmaArgs a) {
             for (int cc = 0; cc < NT; ++cc) {
               const float xv = bf16_to_float(
                   reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
-              acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+              if constexpr (kSepSx) sx[cc][r] += xv;
+              else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -363,7 +369,8 @@ void k_mfma(MfmaArgs a) {
           for (int cc = 0; cc < NT; ++cc) {
             const int mrow = 16 * cc + r16;
             const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
-            acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+            if constexpr (kSepSx) sx[cc][r] += xv;
+            else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
             qv[cc][r] = fmaf(xv, v, qv[cc][r]);
           }
         }
@@ -378,7 +385,7 @@ void k_mfma(MfmaArgs a) {
       for (int cc = 0; cc < NT; ++cc) {
         const int mcol = 16 * cc + r16;
         if (mcol >= a.m) continue;
-        const float v = kEsc ? fmaf(sc, acc[cc][r], qv[cc][r])
+        const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
                              : acc[cc][r];
         a.y[mcol * a.ldy + nrow] = v;
       }
