@@ -64,7 +64,7 @@ extern "C" {
 #define W12_ERR_HIP      (-6)  /* HIP runtime or launch error; message from hipGetErrorString */
 
 /* flags for the GEMM calls: which kernel family runs */
-#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 8, bf16 MFMA for m >= 9 */
+#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 4, bf16 MFMA for m >= 5 */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 

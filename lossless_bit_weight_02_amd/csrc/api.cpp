@@ -79,7 +79,8 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   if (flags > W12_PATH_MFMA) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned4(y)) return fail(W12_ERR_ALIGN, "y must be 4-byte aligned");
-  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && m <= 8);
+  // GEMV up to 4 rows: from 5 rows on the matrix-core kernel is faster on the 27B-class shapes
+  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && m <= 4);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, y, s) : w12::launch_mfma(f, x, m, p, n, k, y, s);
   if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");

@@ -11,60 +11,74 @@ namespace w12 {
 
 // ---------------------------------------------------------------------------------------------
 // Encoder step 1: per-row window choice.
-// One workgroup per row.  Each wave keeps its own 256-bin exponent histogram in LDS (exponent
-// fields 0 and 255 are not counted: zeros, subnormals, Inf and NaN never sit in a window).
-// Coverage of window b is the sum of bins b..b+15 for b = 1..239; the row's base is the b of
-// largest coverage, the smallest such b on ties, found with a max over the key
-// (coverage << 32 | ~b).  A row with nothing counted gets base 1.
+// One workgroup per group of 16 rows (a row of tiles): wave w owns rows 4w..4w+3, and lane q of
+// row r (16 lanes per row) reads columns 8q..8q+7 of every 128-column block, so a wave reads
+// four 256-byte row segments per block; kEncU blocks are loaded together.  Each row keeps a
+// 256-bin exponent histogram in LDS (exponent fields 0 and 255 are not counted: zeros,
+// subnormals, Inf and NaN never sit in a window).  Coverage of window b is the sum of bins
+// b..b+15 for b = 1..239; the row's base is the b of largest coverage, the smallest such b on
+// ties, found with a max over the key (coverage << 32 | ~b).  A row with nothing counted gets
+// base 1.  A row's lanes are all in one wave, so no workgroup barrier is needed.
 // ---------------------------------------------------------------------------------------------
+constexpr int kEncU = 4;   // 128-column blocks per loop pass of the encoder kernels
+
 __global__ __launch_bounds__(kBlock) void k_analyze(const uint16_t* __restrict__ w, int64_t n,
                                                     int64_t k, uint8_t* __restrict__ base,
                                                     uint32_t* __restrict__ esc_ptr) {
-  __shared__ uint32_t hist[4][256];
-  __shared__ uint64_t wave_best[4];
-  const int tid = threadIdx.x, wid = tid >> 6;
-  for (int64_t row = blockIdx.x; row < n; row += gridDim.x) {
-    for (int i = tid; i < 4 * 256; i += kBlock) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    const uint16_t* r = w + row * k;
-    for (int64_t kk = 8 * (int64_t)tid; kk < k; kk += 8 * kBlock) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(r + kk);
+  __shared__ uint32_t hist[16][256];
+  const int tid = threadIdx.x, r = tid >> 4, q = tid & 15;
+  const int64_t groups = (n + kTileRows - 1) / kTileRows;
+  const int64_t ktiles = k / kTileCols;
+  uint32_t* const hr = hist[r];
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t row = grp * kTileRows + r;
+    const bool real = row < n;
+    for (int i = q; i < 256; i += 16) hr[i] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    const uint16_t* src = w + (real ? row : 0) * k + 8 * q;
+    for (int64_t j0 = 0; j0 < ktiles; j0 += kEncU) {
+      u32x4 v[kEncU];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t h = (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        const uint32_t e = (h >> 7) & 0xFFu;
-        if (e != 0u && e != 255u) atomicAdd(&hist[wid][e], 1u);
+      for (int i = 0; i < kEncU; ++i) {
+        const bool ok = real && j0 + i < ktiles;
+        v[i] = ok ? load_nt(reinterpret_cast<const u32x4*>(src + (j0 + i) * kTileCols))
+                  : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < kEncU; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t e = (v[i][jj >> 1] >> (16 * (jj & 1) + 7)) & 0xFFu;
+          if (e != 0u && e != 255u) atomicAdd(&hr[e], 1u);
+        }
       }
     }
-    __syncthreads();
-    const uint32_t total = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
-    __syncthreads();
-    hist[0][tid] = total;
-    __syncthreads();
-    uint64_t key = 0;
-    const uint32_t b = (uint32_t)tid + 1u;
-    if (b <= 239u) {
-      uint32_t cov = 0;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");
+    // windows b = 16q .. 16q + 15 from a running sum over bins 16q .. 16q + 30
+    uint32_t run = 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) cov += hist[0][b + j];
-      key = ((uint64_t)cov << 32) | (uint64_t)(0xFFFFFFFFu - b);
+    for (int j = 0; j < 15; ++j) run += hr[16 * q + j];
+    uint64_t key = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int b = 16 * q + j;
+      run += b + 15 < 256 ? hr[b + 15] : 0u;   // run = bins b .. b + 15
+      if (b >= 1 && b <= 239) {
+        const uint64_t kb = ((uint64_t)run << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)b);
+        key = kb > key ? kb : key;
+      }
+      run -= hr[b];
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = 1; off < 16; off <<= 1) {   // max over the row's 16 lanes
       const uint64_t o = __shfl_xor(key, off);
       key = o > key ? o : key;
     }
-    if ((tid & 63) == 0) wave_best[wid] = key;
-    __syncthreads();
-    if (tid == 0) {
-      uint64_t best = wave_best[0];
-      for (int i = 1; i < 4; ++i) best = wave_best[i] > best ? wave_best[i] : best;
-      const uint32_t bb = 0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull);
-      const uint64_t cov = best >> 32;
-      base[row] = (uint8_t)bb;
-      esc_ptr[row + 1] = (uint32_t)((uint64_t)k - cov);
+    if (q == 0 && real) {
+      base[row] = (uint8_t)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+      esc_ptr[row + 1] = (uint32_t)((uint64_t)k - (key >> 32));
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup", "local");   // reads done before re-zeroing
   }
 }
 
@@ -116,25 +130,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(uint32_t* __restrict__ es
 }
 
 // ---------------------------------------------------------------------------------------------
-// Encoder step 3: planes + escapes.  One workgroup per row (rows of the last row tile past n are
-// padding and get zero planes); thread t of a pass owns the aligned group of 8 weights
-// g = pass*256 + t, so escapes come out in ascending k after a workgroup exclusive scan of the
-// per-thread escape counts.  The group's 8 AE bytes and 4 B bytes land at their tiled positions
-// (see w12_device.hpp).
+// Encoder step 3: planes + escapes.
+// One workgroup per group of 16 rows (npad / 16 groups; rows past n are padding and get zero
+// planes).  Lane q of row r packs columns 8q..8q+7 of every 128-column block: its 8 AE bytes
+// go to 1024 h + 16 (r + 16 g) + 8 (q % 2) and its 4 B-plane bytes to 16 (r + 16 g) + 4 (q % 4)
+// of the tile (g = q / 4, h = (q / 2) % 2; see w12_device.hpp), so each tile's 2 KiB of AE and
+// 1 KiB of B are written whole by one workgroup.  The row's escapes come out in ascending
+// column order: within a block by an exclusive scan over the row's 16 lanes, across blocks by a
+// running count those lanes keep.  A row's lanes are all in one wave: no workgroup barrier.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ int64_t ae_offset(int64_t row, int64_t col, int64_t ktiles) {
-  const int64_t tile = (row >> 4) * ktiles + (col >> 7);
-  const int64_t c = col & 127;
-  return tile * kTileAE + 1024 * ((c & 31) >> 4) + 16 * ((row & 15) + 16 * (c >> 5)) + (c & 15);
-}
-
-__device__ __forceinline__ int64_t lo_offset(int64_t row, int64_t col, int64_t ktiles) {
-  // byte holding the B nibbles of the aligned group of 8 starting at col (col % 8 == 0)
-  const int64_t tile = (row >> 4) * ktiles + (col >> 7);
-  const int64_t c = col & 127;
-  return tile * kTileLO + 16 * ((row & 15) + 16 * (c >> 5)) + ((c & 31) >> 1);
-}
-
 __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w, int64_t n,
                                                  int64_t npad, int64_t k,
                                                  const uint8_t* __restrict__ base,
@@ -142,71 +146,71 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
                                                  uint8_t* __restrict__ ae, uint8_t* __restrict__ lo,
                                                  uint32_t* __restrict__ esc_col,
                                                  uint16_t* __restrict__ esc_val) {
-  __shared__ uint32_t wave_cnt[4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int64_t groups = k >> 3;
+  const int tid = threadIdx.x, r = tid >> 4, q = tid & 15;
+  const int g = q >> 2, h = (q >> 1) & 1;
+  const uint32_t ae_off = 1024u * h + 16u * (r + 16 * g) + 8u * (q & 1);
+  const uint32_t lo_off = 16u * (r + 16 * g) + 4u * (q & 3);
+  const int64_t groups = npad / kTileRows;
   const int64_t ktiles = k / kTileCols;
-  for (int64_t row = blockIdx.x; row < npad; row += gridDim.x) {
-    if (row >= n) {  // padding row of the last tile: zero planes, no escapes
-      for (int64_t g = tid; g < groups; g += kBlock) {
-        *reinterpret_cast<u32x2*>(ae + ae_offset(row, 8 * g, ktiles)) = (u32x2){0u, 0u};
-        *reinterpret_cast<uint32_t*>(lo + lo_offset(row, 8 * g, ktiles)) = 0u;
-      }
-      continue;  // uniform over the workgroup
-    }
-    const uint32_t b = base[row];
-    const uint64_t out0 = esc_ptr[row];
+  for (int64_t grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+    const int64_t row = grp * kTileRows + r;
+    const bool real = row < n;
+    const uint32_t b = real ? base[row] : 0u;
+    const uint64_t out0 = real ? esc_ptr[row] : 0u;
+    const uint64_t row_end = real ? esc_ptr[row + 1] : 0u;   // never write past the row's CSR range
     uint64_t running = 0;
-    for (int64_t g0 = 0; g0 < groups; g0 += kBlock) {
-      const int64_t g = g0 + tid;
-      const bool act = g < groups;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (act) v = *reinterpret_cast<const u32x4*>(w + row * k + 8 * g);
-      uint32_t a0 = 0, a1 = 0, nib = 0, escmask = 0;
+    const uint16_t* src = w + (real ? row : 0) * k + 8 * q;
+    for (int64_t j0 = 0; j0 < ktiles; j0 += kEncU) {
+      u32x4 v[kEncU];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t h = (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        const uint32_t s = h >> 15, e = (h >> 7) & 0xFFu, m = h & 0x7Fu;
-        const bool inside = e >= b && e <= b + 15u;
-        const uint32_t code = inside ? (s << 7) | ((e - b) << 3) | (m >> 4) : 0u;
-        const uint32_t nb = inside ? (m & 0xFu) : 0u;
-        if (j < 4) a0 |= code << (8 * j);
-        else a1 |= code << (8 * (j - 4));
-        nib |= nb << (8 * (j & 3) + 4 * (j >> 2));
-        if (act && !inside) escmask |= 1u << j;
+      for (int i = 0; i < kEncU; ++i) {
+        const bool ok = real && j0 + i < ktiles;
+        v[i] = ok ? load_nt(reinterpret_cast<const u32x4*>(src + (j0 + i) * kTileCols))
+                  : (u32x4){0u, 0u, 0u, 0u};
       }
-      const uint32_t c = __builtin_popcount(escmask);
-      uint32_t incl = c;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (lane == 63) wave_cnt[wid] = incl;
-      __syncthreads();
-      uint32_t before = 0, pass_total = 0;
-      for (int i = 0; i < 4; ++i) {
-        if (i < wid) before += wave_cnt[i];
-        pass_total += wave_cnt[i];
-      }
-      if (act) {
-        *reinterpret_cast<u32x2*>(ae + ae_offset(row, 8 * g, ktiles)) = (u32x2){a0, a1};
-        *reinterpret_cast<uint32_t*>(lo + lo_offset(row, 8 * g, ktiles)) = nib;
+      for (int i = 0; i < kEncU; ++i) {
+        const int64_t j = j0 + i;
+        if (j >= ktiles) break;   // uniform
+        uint32_t a0 = 0, a1 = 0, nib = 0, escmask = 0;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t hw = (v[i][jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu;
+          const uint32_t sg = hw >> 15, e = (hw >> 7) & 0xFFu, m = hw & 0x7Fu;
+          const bool inside = e >= b && e <= b + 15u;
+          const uint32_t code = inside ? (sg << 7) | ((e - b) << 3) | (m >> 4) : 0u;
+          const uint32_t nb = inside ? (m & 0xFu) : 0u;
+          if (jj < 4) a0 |= code << (8 * jj);
+          else a1 |= code << (8 * (jj - 4));
+          nib |= nb << (8 * (jj & 3) + 4 * (jj >> 2));
+          if (real && !inside) escmask |= 1u << jj;
+        }
+        const int64_t tile = grp * ktiles + j;
+        __builtin_nontemporal_store((u32x2){a0, a1}, reinterpret_cast<u32x2*>(ae + tile * kTileAE + ae_off));
+        __builtin_nontemporal_store(nib, reinterpret_cast<uint32_t*>(lo + tile * kTileLO + lo_off));
+        // escapes of this block: exclusive scan of the counts over the row's lanes q = 0..15
+        const uint32_t c = __builtin_popcount(escmask);
+        uint32_t incl = c;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const uint32_t o = __shfl_up(incl, off, 16);
+          if (q >= off) incl += o;
+        }
+        const uint32_t block_total = __shfl(incl, 15, 16);
         if (escmask) {
-          uint64_t idx = out0 + running + before + incl - c;
-          const uint64_t row_end = esc_ptr[row + 1];  // never write past the row's CSR range
+          uint64_t idx = out0 + running + incl - c;
+          const int64_t col0 = j * kTileCols + 8 * q;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (((escmask >> j) & 1u) && idx < row_end) {
-              esc_col[idx] = (uint32_t)(8 * g + j);
-              esc_val[idx] = (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+          for (int jj = 0; jj < 8; ++jj) {
+            if (((escmask >> jj) & 1u) && idx < row_end) {
+              esc_col[idx] = (uint32_t)(col0 + jj);
+              esc_val[idx] = (uint16_t)((v[i][jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu);
               ++idx;
             }
           }
         }
+        running += block_total;
       }
-      running += pass_total;
-      __syncthreads();
     }
   }
 }
@@ -217,28 +221,51 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
 // (base - 112) * 0x00800080 mod 2^32.  Neither half can carry or borrow into the other because
 // base + E stays within 1..254.  Reads the tiled planes, writes row-major bf16.
 // ---------------------------------------------------------------------------------------------
+constexpr int kDecU = 4;   // tiles per workgroup pass of the decoder (loads issued together)
+
 __global__ __launch_bounds__(kBlock) void k_decode(const uint8_t* __restrict__ base,
                                                    const uint8_t* __restrict__ ae,
                                                    const uint8_t* __restrict__ lo, int64_t n,
                                                    int64_t k, uint16_t* __restrict__ out) {
-  // One workgroup per tile; thread u reads AE bytes 8u..8u+7 of the tile (coalesced) =
-  // row r = l % 16, columns 32g + 16h + 8s .. +7 with u = 128h + 2l + s, l = r + 16g.
+  // Thread u handles row r = u / 16 of a tile, columns 8 c8 .. 8 c8 + 7 (c8 = u % 16), so a
+  // wave writes four 256-byte row segments.  Those 8 AE bytes sit at 1024 h + 16 (r + 16 g) +
+  // 8 (c8 % 2) with g = c8 / 4, h = (c8 / 2) % 2, their B nibbles in the 4 bytes at
+  // 16 (r + 16 g) + 4 (c8 % 4) of the tile's B plane.  A workgroup takes kDecU tiles per pass
+  // and issues all their loads before decoding, so enough bytes are in flight per CU.
   const int64_t ktiles = k / kTileCols;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows * ktiles;
   const uint32_t e112 = exp112_pair();
-  const int u = threadIdx.x, h = u >> 7, l = (u & 127) >> 1, sh = u & 1;
-  const int r = l & 15, g = l >> 4;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row = (t / ktiles) * kTileRows + r;
-    if (row >= n) continue;
-    const int64_t col = (t % ktiles) * kTileCols + 32 * g + 16 * h + 8 * sh;
-    const u32x2 a = load_nt(reinterpret_cast<const u32x2*>(ae + t * kTileAE) + u);
-    const uint32_t lw = *reinterpret_cast<const uint32_t*>(lo + t * kTileLO + 16 * l + 8 * h + 4 * sh);
-    const uint32_t shift = ((uint32_t)base[row] - 112u) * 0x00800080u;
-    uint32_t p[4];
-    window_group8(a.x, a.y, lw, e112, p);
-    const u32x4 res = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
-    *reinterpret_cast<u32x4*>(out + row * k + col) = res;
+  const int u = threadIdx.x, r = u >> 4, c8 = u & 15;
+  const int g = c8 >> 2, h = (c8 >> 1) & 1;
+  const uint32_t ae_off = 1024u * h + 16u * (r + 16 * g) + 8u * (c8 & 1);
+  const uint32_t lo_off = 16u * (r + 16 * g) + 4u * (c8 & 3);
+  const int64_t step = (int64_t)gridDim.x * kDecU;
+  for (int64_t t0 = blockIdx.x; t0 < tiles; t0 += step) {
+    u32x2 a[kDecU];
+    uint32_t lw[kDecU], bs[kDecU];
+#pragma unroll
+    for (int i = 0; i < kDecU; ++i) {
+      const int64_t t = t0 + (int64_t)i * gridDim.x;
+      const bool ok = t < tiles;
+      const int64_t tt = ok ? t : 0;
+      const int64_t row = (tt / ktiles) * kTileRows + r;
+      a[i] = load_nt(reinterpret_cast<const u32x2*>(ae + tt * kTileAE + ae_off));
+      lw[i] = load_nt(reinterpret_cast<const uint32_t*>(lo + tt * kTileLO + lo_off));
+      bs[i] = base[row < n ? row : n - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kDecU; ++i) {
+      const int64_t t = t0 + (int64_t)i * gridDim.x;
+      const int64_t row = (t / ktiles) * kTileRows + r;
+      if (t >= tiles || row >= n) continue;
+      const int64_t col = (t % ktiles) * kTileCols + 8 * c8;
+      const uint32_t shift = (bs[i] - 112u) * 0x00800080u;
+      uint32_t p[4];
+      window_group8(a[i].x, a[i].y, lw[i], e112, p);
+      const u32x4 res = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
+      // streaming store: the decoded matrix is not read back by this kernel
+      __builtin_nontemporal_store(res, reinterpret_cast<u32x4*>(out + row * k + col));
+    }
   }
 }
 
@@ -307,13 +334,15 @@ __global__ __launch_bounds__(kBlock) void k_read_probe(const u32x4* __restrict__
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
-static int grid_rows(int64_t n) {
-  return (int)(n < 1048576 ? n : 1048576);
+// Workgroups for a loop over groups of 16 rows (each loop takes the groups blockIdx + i grid).
+static int grid_groups(int64_t groups) {
+  return (int)(groups < 1048576 ? groups : 1048576);
 }
 
 hipError_t launch_analyze(const uint16_t* w, int64_t n, int64_t k, uint8_t* base, uint32_t* esc_ptr,
                           hipStream_t s) {
-  hipLaunchKernelGGL(k_analyze, dim3(grid_rows(n)), dim3(kBlock), 0, s, w, n, k, base, esc_ptr);
+  hipLaunchKernelGGL(k_analyze, dim3(grid_groups((n + kTileRows - 1) / kTileRows)), dim3(kBlock), 0, s,
+                     w, n, k, base, esc_ptr);
   return hipGetLastError();
 }
 
@@ -326,7 +355,7 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
                        const uint32_t* esc_ptr, uint8_t* ae, uint8_t* lo, uint32_t* esc_col,
                        uint16_t* esc_val, hipStream_t s) {
   const int64_t npad = padded_rows(n);
-  hipLaunchKernelGGL(k_pack, dim3(grid_rows(npad)), dim3(kBlock), 0, s, w, n, npad, k, base, esc_ptr,
+  hipLaunchKernelGGL(k_pack, dim3(grid_groups(npad / kTileRows)), dim3(kBlock), 0, s, w, n, npad, k, base, esc_ptr,
                      ae, lo, esc_col, esc_val);
   return hipGetLastError();
 }
@@ -349,7 +378,8 @@ hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, h
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows * (k / kTileCols);
   const int64_t cap = (int64_t)di.cus * 8;
-  hipLaunchKernelGGL(k_decode, dim3((unsigned)(tiles < cap ? tiles : cap)), dim3(kBlock), 0, s, p.base,
+  const int64_t want = (tiles + kDecU - 1) / kDecU;
+  hipLaunchKernelGGL(k_decode, dim3((unsigned)(want < cap ? want : cap)), dim3(kBlock), 0, s, p.base,
                      p.ae, p.lo, n, k, out);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
