@@ -25,7 +25,9 @@ constexpr int kEncU = 4;   // 128-column blocks per loop pass of the encoder ker
 __global__ __launch_bounds__(kBlock) void k_analyze(const uint16_t* __restrict__ w, int64_t n,
                                                     int64_t k, uint8_t* __restrict__ base,
                                                     uint32_t* __restrict__ esc_ptr) {
-  __shared__ uint32_t hist[16][256];
+  // rows 264 words apart: the four rows of a wave start 8 banks apart, so the bins they hit
+  // (a few neighbouring exponents) do not share LDS banks across rows
+  __shared__ uint32_t hist[16][264];
   const int tid = threadIdx.x, r = tid >> 4, q = tid & 15;
   const int64_t groups = (n + kTileRows - 1) / kTileRows;
   const int64_t ktiles = k / kTileCols;
@@ -84,23 +86,31 @@ __global__ __launch_bounds__(kBlock) void k_analyze(const uint16_t* __restrict__
 
 // ---------------------------------------------------------------------------------------------
 // Encoder step 2: esc_ptr[1..n] (row escape counts) -> inclusive prefix sums, esc_ptr[0] = 0.
-// One workgroup of 1024 threads walks the array in chunks; sums are kept in 64 bits and any
-// offset that does not fit 32 bits is stored as 0xFFFFFFFF (the host reports W12_ERR_RANGE).
+// One workgroup of 1024 threads walks the array in chunks of 20480.  A chunk goes through LDS:
+// coalesced loads in, each thread scans a run of 20 consecutive counts, coalesced stores out.
+// Sums are kept in 64 bits and any offset that does not fit 32 bits is stored as 0xFFFFFFFF (the
+// host reports W12_ERR_RANGE).
 // ---------------------------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
-constexpr int kScanPer = 4;
+constexpr int kScanPer = 20;   // counts per thread and chunk
 
 __global__ __launch_bounds__(kScanThreads) void k_scan(uint32_t* __restrict__ esc_ptr, int64_t n) {
+  __shared__ uint32_t buf[kScanThreads * kScanPer];
   __shared__ uint64_t wave_tot[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint64_t carry = 0;
   for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kScanThreads * kScanPer) {
-    uint64_t v[kScanPer];
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t i = c0 + (int64_t)j * kScanThreads + tid;
+      buf[j * kScanThreads + tid] = i < n ? esc_ptr[1 + i] : 0u;
+    }
+    __syncthreads();
+    uint32_t v[kScanPer];
     uint64_t s = 0;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int64_t i = c0 + (int64_t)tid * kScanPer + j;
-      v[j] = i < n ? esc_ptr[1 + i] : 0u;
+      v[j] = buf[tid * kScanPer + j];
       s += v[j];
     }
     uint64_t incl = s;
@@ -119,9 +129,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(uint32_t* __restrict__ es
     uint64_t run = before + incl - s;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int64_t i = c0 + (int64_t)tid * kScanPer + j;
       run += v[j];
-      if (i < n) esc_ptr[1 + i] = run >= 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)run;
+      buf[tid * kScanPer + j] = run >= 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t i = c0 + (int64_t)j * kScanThreads + tid;
+      if (i < n) esc_ptr[1 + i] = buf[j * kScanThreads + tid];
     }
     carry += chunk;
     __syncthreads();
