@@ -1,16 +1,14 @@
-// Skinny GEMM for 9..64 activation rows on the matrix cores: y[m][n] = sum_k x[m][k] W[n][k].
+// Skinny GEMM for up to 32 activation rows (one or two 16-row activation tiles) on the matrix
+// cores: y[m][n] = sum_k x[m][k] W[n][k].  Three and four tiles run the register-staged variant
+// in mfma_wide.hip.
 //
 // From about 16 rows the product is a dense contraction again (SpecPilot, arXiv 2611.02501,
 // summary page, "Main Findings": the W12 GEMM is measured at 1 and at 32 rows), so the decoded
 // weights feed v_mfma_f32_16x16x32_bf16 as its A operand -- the register operand of the pages'
 // design (figure-captions page, Fig. 5(b), there for wgmma).
 //
-// Operand layout of v_mfma_f32_16x16x32_bf16 (wave64): lane l supplies row (l % 16) of A and
-// column (l % 16) of B, each as 8 bfloat16 of the k-group (l / 16); the 16x16 fp32 result gives
-// lane l rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.  A = 16 weight rows, B = 16 activation
-// rows, so the result is y^T for a 16 x 16 tile.
-//
-// Work split.  One workgroup of kWaves waves per CU (the x chunks fill most of the CU's LDS).
+// Work split.  One workgroup of kWaves waves per CU (twelve waves of up to 168 VGPRs fill the
+// CU's register file).
 // A wave owns one 16-row tile at a time and streams all of its 128-column blocks; tiles are dealt
 // round-robin over the workgroups first, so every CU gets the same number of tiles to within one
 // (the weight stream is the bottleneck, and a CU with one more workgroup than the rest would set
@@ -28,12 +26,11 @@
 // that is not due yet.
 //
 // x: chunks of S k-blocks (128 S columns) of the m rows live in LDS in fragment order (each B
-// operand is one contiguous 1 KiB read), double buffered.  While chunk c is consumed, the 4 NT
-// pieces per step of chunk c+1 stream in through a D-deep register ring; the piece jobs rotate
-// over the waves.  A piece is 1 KiB of row-major x (2 rows x 256 columns: a coalesced read);
-// its lanes scatter into the fragment layout, whose 16-byte slots are XOR-swizzled inside each
-// 128-byte row (slot = lane ^ (t | (g & 1) << 2) for k-group t and column group g) so that
-// both these writes and the operand reads are free of bank conflicts.  One barrier per chunk.
+// operand is one contiguous 1 KiB read, lane l at byte 16 l), double buffered.  The fragments of
+// chunk c+1 are loaded straight from memory into LDS (global-to-LDS loads: lane l of a fragment
+// reads its 16 bytes of row-major x and the hardware writes them at byte 16 l) at the first step
+// of chunk c, dealt round-robin over the waves; no register holds x on its way.  Rows past m and
+// columns past k read zeros (buffer loads out of range).  One barrier per chunk.
 //
 // Escapes (exact weights outside a row's window): the lanes of column group g own output rows
 // 4g..4g+3 of the tile.  The tile's escape list (up to kEscCap entries) is copied to LDS at the
@@ -41,100 +38,52 @@
 // the chunk's last column, reading x from the chunk still in LDS, and accumulates
 //   y = 2^(base-112) * (acc - 2^-15 * sum_esc x) + sum_esc x * v,
 // which takes the placeholder value 2^-15 of an escaped slot (AE = 0, B = 0) back out of acc.
-// Up to two activation tiles the x sums of the escaped slots are kept apart from the
-// matrix-core accumulators: a vector write into an accumulator between MFMAs that feed it
-// stalls the chain.
+// The x sums of the escaped slots are kept apart from the matrix-core accumulators: a vector
+// write into an accumulator between MFMAs that feed it stalls the chain.
 // Escapes past the LDS copy of a crowded tile are read from memory after the loop.
-#include "w12_device.hpp"
-#include "w12_launch.hpp"
+#include "mfma_common.hpp"
 
 namespace w12 {
 
-struct MfmaArgs {
-  const uint16_t* x;   // x[m][k] (this launch's rows)
-  int m;               // activation rows in this launch (<= 16 * NT)
-  const uint8_t* base;
-  const uint8_t* ae;   // tiled storage
-  const uint8_t* lo;
-  const uint32_t* esc_ptr;
-  const uint32_t* esc_col;
-  const uint16_t* esc_val;
-  const uint16_t* w;   // dense bfloat16 W (baseline), tiled storage
-  float* y;            // y[m][ldy]
-  int64_t ldy;
-  int64_t n, k;
-  int rounds;          // tiles per wave (the last ones may be empty)
-};
-
-constexpr int kWaves = 12;                  // waves per workgroup, one workgroup per CU
-constexpr int kEscCap = 128;                // escapes of one tile copied to LDS
-
-template <int FMT>
-struct ABlock {
-  u32x4 v[FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2];
-};
-
-// Block kb of the wave's tile; offsets past the tile's range read zeros.
-template <int FMT>
-__device__ __forceinline__ void load_ablock(Rsrc r0, Rsrc r1, uint32_t kb, uint32_t lane16,
-                                            ABlock<FMT>& b) {
-  if constexpr (FMT == kFmtBF16) {
-    const uint32_t off = kb * kTileBF + lane16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b.v[q] = __builtin_amdgcn_raw_buffer_load_b128(r0, off + 1024 * q, 0, kAuxNT);
-  } else {
-    const uint32_t off = kb * kTileAE + lane16;
-    b.v[0] = __builtin_amdgcn_raw_buffer_load_b128(r0, off, 0, kAuxNT);
-    b.v[1] = __builtin_amdgcn_raw_buffer_load_b128(r0, off + 1024, 0, kAuxNT);
-    if constexpr (FMT == kFmtW12)
-      b.v[2] = __builtin_amdgcn_raw_buffer_load_b128(r1, kb * kTileLO + lane16, 0, kAuxNT);
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112, uint32_t p[16]) {
-  if constexpr (FMT == kFmtBF16) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      p[4 * q] = r.v[q].x; p[4 * q + 1] = r.v[q].y; p[4 * q + 2] = r.v[q].z; p[4 * q + 3] = r.v[q].w;
-    }
-  } else if constexpr (FMT == kFmtW12) {
-    window_group8(r.v[0].x, r.v[0].y, r.v[2].x, e112, p);
-    window_group8(r.v[0].z, r.v[0].w, r.v[2].y, e112, p + 4);
-    window_group8(r.v[1].x, r.v[1].y, r.v[2].z, e112, p + 8);
-    window_group8(r.v[1].z, r.v[1].w, r.v[2].w, e112, p + 12);
-  } else {
-    window_group8_q(r.v[0].x, r.v[0].y, e112, p);
-    window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
-    window_group8_q(r.v[1].x, r.v[1].y, e112, p + 8);
-    window_group8_q(r.v[1].z, r.v[1].w, e112, p + 12);
-  }
-}
-
-// Compile-time shape of one instantiation.  Decoding formats keep a 3-deep ring at two activation
-// tiles (the decode needs its own registers); the others 4 (up to 32 rows), 3 and 2.
+// Compile-time shape of one instantiation: D weight blocks in flight per wave (as many as the
+// 168 VGPRs allow), chunks of S k-blocks of x (a multiple of D).  Four k-blocks per chunk
+// measured faster than eight at one tile.
 template <int FMT, int NT>
 struct Shape {
-  static constexpr int D = NT == 1 ? 4 : NT == 2 ? (FMT == kFmtBF16 ? 4 : 3) : NT == 3 ? 3 : 2;
-  static constexpr int S = D == 4 ? 8 : D == 3 ? 6 : 4;   // k-blocks per x chunk
-  static constexpr int FS = 4 * NT;                   // 1 KiB x pieces per k-block
-  static constexpr int F = FS * S;                    // 1 KiB x pieces per chunk
-  static constexpr int XL = (FS + kWaves - 1) / kWaves;  // pieces a wave loads per step
-  static_assert(S % D == 0 && S % 2 == 0, "a chunk must hold whole rings and 256-column blocks");
+  static_assert(NT == 1 || NT == 2, "three and four tiles run k_mfma_wide");
+  static constexpr int D = 4;
+  static constexpr int S = 4;                         // k-blocks per x chunk
+  static constexpr int FS = 4 * NT;                   // 1 KiB x fragments per k-block
+  static constexpr int F = FS * S;                    // 1 KiB x fragments per chunk
+  static constexpr int FW = (F + kWaves - 1) / kWaves;   // fragments a wave loads per chunk
+  static constexpr int FPS = (FW + S - 1) / S;         // fragment loads per step
+  static constexpr int LS = (FW + FPS - 1) / FPS - 1;   // last step with a fragment load
+  static_assert(S % D == 0 && S % 2 == 0, "a chunk must hold whole rings and 256-column pieces");
 };
+
+// Global-to-LDS loads are not covered by the compiler's wait counts for the LDS reads that
+// follow a barrier: before a barrier that publishes a chunk, a wave waits until at most N
+// vector-memory operations (those it issued after its fragment loads) are outstanding; they
+// complete in issue order.
+template <int N>
+__device__ __forceinline__ void vm_wait_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 
 // Twelve waves (three per SIMD) on the CU: at most 168 VGPRs.
 template <int FMT, int NT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_mfma(MfmaArgs a) {
   using SH = Shape<FMT, NT>;
-  constexpr int D = SH::D, S = SH::S, FS = SH::FS, F = SH::F, XL = SH::XL;
+  constexpr int D = SH::D, S = SH::S, F = SH::F, FW = SH::FW, FPS = SH::FPS, LS = SH::LS;
   constexpr bool kEsc = FMT != kFmtBF16;
   // x sums of escaped slots in registers of their own (up to two activation tiles; beyond that
   // the registers are not there and the placeholders come out of the accumulators directly)
-  constexpr bool kSepSx = NT <= 2;
+  constexpr bool kSepSx = true;    // escape x sums kept apart from the accumulators
+  constexpr int kLoadsPerStep = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
-  __shared__ __attribute__((aligned(16))) u32x4 s_scratch[64];   // stores of waves with no piece
+  __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * kWaves > F) ? 64 : 1];   // target of unused fragment loads
   __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];   // per wave: tile escapes
   __shared__ uint16_t s_eval[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];
 
@@ -148,59 +97,46 @@ void k_mfma(MfmaArgs a) {
   const uint32_t kx = (uint32_t)a.k;
   const Rsrc rx = make_rsrc(a.x, (uint32_t)a.m * kx * 2u);
 
-  // Piece I of chunk c (I < F): lanes 0..31 and 32..63 read rows 2q and 2q+1, columns
-  // 256 hb + 8 (lane % 32) .. +7 of the chunk, where q = I % (8 NT), hb = I / (8 NT).  Pieces
-  // are numbered per tile, P = c F + I.
-  const uint32_t prow = lane >> 5, pcol = 8u * (lane & 31);
-  const uint32_t lpart = 2u * (prow * kx + pcol);
-  // The address is computed unconditionally and hidden from the optimizer, so that the
-  // out-of-range select stays a select instead of a branch around the address arithmetic.
-  const auto piece_load = [&](uint32_t P, bool have) {
-    const uint32_t c = P / F, I = P % F, q = I % (8 * NT), hb = I / (8 * NT);
-    const uint32_t col0 = 128u * S * c + 256u * hb;
-    uint32_t off = 2u * (2u * q * kx + col0) + lpart;
-    asm volatile("" : "+v"(off));
-    const bool ok = have && col0 + pcol < kx && (int)(2 * q + prow) < a.m;
-    return __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off : kOOB, 0, 0);
+  // LDS layout of a chunk: for each 256-column half hb of the chunk and each of the 16 NT rows
+  // m, a 512-byte row segment at (hb * 16 NT + m) * 512, whose 16-byte column slots c16 are
+  // rotated by the row: slot (c16 + m) % 32.  A global-to-LDS load moves one coalesced 1 KiB piece
+  // of row-major x (rows 2q and 2q + 1, 256 columns; piece P = hb * 8 NT + q lands at P * 1 KiB):
+  // lane j writes LDS slot j, so it reads the column slot ((j % 32) - row) % 32 of its row.  The
+  // operand reads (16 consecutive rows, one slot each) and the escape reads then hit distinct
+  // banks in every group of 8 lanes.
+  // Wave w loads pieces w, w + 12, ... of a chunk (piece w + 12 i at step i / FPS of the chunk
+  // before).  Every wave issues FW loads at every chunk (a fixed pattern, so the compiler's wait
+  // counts stay exact): a load past the last piece reads nothing and writes zeros to s_dummy,
+  // and rows past m and columns past k read zeros.
+  const uint32_t prow = (uint32_t)lane >> 5, pslot = (uint32_t)lane & 31u;
+  const auto x_fetch_one = [&](uint32_t c, uint32_t buf, int i) {
+    const uint32_t P = (uint32_t)(w + kWaves * i);
+    const bool real = FW * kWaves <= F || P < (uint32_t)F;
+    const uint32_t q = P % (8u * NT), hb = P / (8u * NT);
+    const uint32_t row = 2u * q + prow;
+    const uint32_t c16 = (pslot - row) & 31u;
+    const uint32_t col = 128u * S * c + 256u * hb + 8u * c16;
+    const bool ok = real && (int)row < a.m && col < kx;
+    u32x4* dst = real ? &s_x[buf][P * 64u] : &s_dummy[0];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)dst, 16,
+                                             ok ? 2u * (row * kx + col) : kOOB, 0, 0, 0);
   };
-  // LDS slot of this lane's 16 bytes of piece I: fragment f = (k-block * 4 + t) * NT + cc holds
-  // x[16 cc + r][.. + 32 g + 8 t .. +7] for operand lane r + 16 g, at slot (r + 16 g) ^ swz(t, g),
-  // swz = t | (g & 1) << 2.  With a = 2q % 16 even, (a + row bit + 16 g) ^ swz splits into a
-  // uniform part, a lane part and (a % 8) ^ (row bit ^ swz).
-  const uint32_t pt = (pcol >> 3) & 3u, pg = (pcol >> 5) & 3u;
-  const uint32_t lslot = ((pcol >> 7) * 4u + pt) * NT * 64u + 16u * pg;
-  const uint32_t lkey = prow ^ (pt | ((pg & 1u) << 2));
-  const auto piece_slot = [&](uint32_t I) {
-    const uint32_t q = I % (8 * NT), hb = I / (8 * NT), aa = (2 * q) & 15u;
-    return (2 * hb * 4 * NT + (q >> 3)) * 64u + (aa & 8u) + lslot + ((aa & 7u) ^ lkey);
+  // LDS index (16-byte units) of row m, 16-byte column slot c16 of half hb of a chunk buffer
+  const auto x_slot = [](uint32_t hb, uint32_t m, uint32_t c16) {
+    return (hb * 16u * NT + m) * 32u + ((c16 + m) & 31u);
   };
-  // Streamed pieces (P >= F) are dealt to the waves round-robin: wave w loads the pieces
-  // P = w (mod kWaves), each in the step whose range [F + (u + D - 1) FS, F + (u + D) FS) holds it,
-  // and stores it D - 1 steps later (into chunk P / F, which is then the next chunk).
-  const uint32_t first_piece = F + (uint32_t)((w - F % kWaves + kWaves) % kWaves);
-  // Branch-free: a wave without a piece this step loads nothing (offset past the range) and
-  // stores to s_scratch, which is never read; its ring entry has bit 31 set.
-  const auto x_stream_load = [&](int u, uint32_t& nxt, uint32_t (&pr)[XL], u32x4 (&dst)[XL]) {
-    const uint32_t hi = (uint32_t)(F + (u + D) * FS);
+  // Operand reads: lane l = r + 16 g of step t reads row 16 cc + r, slot 16 (s % 2) + 4 g + t of
+  // half s / 2.  With (v + 16) % 32 = v ^ 16 and 4 g + r + t < 32 that is
+  //   s / 2 * 512 NT + 512 cc + 32 r + ((4 g + r + t) ^ 16 ((s + cc) % 2)),
+  // a lane part from xo[(s + cc) % 2][t] plus a constant the read instruction carries.
+  uint32_t xo[2][4];
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const bool have = nxt < hi;
-      pr[i] = have ? nxt : (nxt | 0x80000000u);
-      dst[i] = piece_load(nxt, have);
-      nxt = have ? nxt + kWaves : nxt;
-    }
-  };
-  const auto x_stream_store = [&](const uint32_t (&pr)[XL], const u32x4 (&src)[XL]) {
+  for (int par = 0; par < 2; ++par)
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const uint32_t P = pr[i] & 0x7FFFFFFFu;
-      uint32_t at = ((P / F) & 1u) * (F * 64) + piece_slot(P % F);
-      asm volatile("" : "+v"(at));
-      u32x4* dst = (pr[i] >> 31) ? &s_scratch[lane] : &s_x[0][0] + at;
-      *dst = src[i];
+    for (int t = 0; t < 4; ++t) {
+      xo[par][t] = 32u * (uint32_t)r16 + ((4u * (uint32_t)g + (uint32_t)r16 + (uint32_t)t) ^ (16u * par));
+      asm volatile("" : "+v"(xo[par][t]));
     }
-  };
-  const uint32_t bswz = lane ^ (((uint32_t)g & 1u) << 2);   // operand slot of k-group t: bswz ^ t
 
   for (int round = 0; round < a.rounds; ++round) {
     const int64_t tile = ((int64_t)round * kWaves + w) * gridDim.x + blockIdx.x;
@@ -237,11 +173,10 @@ void k_mfma(MfmaArgs a) {
       }
     }
 
-    // ---- chunk 0 of x ----
-    constexpr int XF = (F + kWaves - 1) / kWaves;
-    u32x4 x0[XF];
+    // ---- chunk 0 of x, straight into LDS buffer 0 ----
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < XF; ++i) x0[i] = piece_load((uint32_t)(w + kWaves * i), w + kWaves * i < F);
+    for (int i = 0; i < FW; ++i) x_fetch_one(0u, 0u, i);
 
     // ---- D virtual steps -D .. -1: the same load pattern as a loop step ----
     Rsrc ra, rl;
@@ -253,20 +188,13 @@ void k_mfma(MfmaArgs a) {
       rl = make_rsrc(a.lo + row0 * a.k / 2, valid ? KB * (uint32_t)kTileLO : 0u);
     }
     ABlock<FMT> buf[D];
-    u32x4 xr[D][XL];
-    uint32_t pr[D][XL];
-    uint32_t nxt = first_piece;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      x_stream_load(d - D, nxt, pr[d], xr[d]);     // step d - D uses ring slot d
       load_ablock<FMT>(ra, rl, (uint32_t)d, lane16, buf[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-#pragma unroll
-    for (int i = 0; i < XF; ++i)
-      if (w + kWaves * i < F) s_x[0][piece_slot((uint32_t)(w + kWaves * i))] = x0[i];
     if constexpr (kEsc) {
 #pragma unroll
       for (int i = 0; i < kEscCap / 64; ++i) {
@@ -274,6 +202,7 @@ void k_mfma(MfmaArgs a) {
         s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
       }
     }
+    vm_wait_le<D * kLoadsPerStep>();   // chunk 0 is in LDS
     lds_barrier();
 
     // per row r: cursor (absolute escape index) and the column under it (~0: none in LDS)
@@ -306,20 +235,21 @@ void k_mfma(MfmaArgs a) {
         ablock_pairs<FMT>(buf[slot], e112, p);
         if constexpr (FMT != kFmtBF16) pin16(p);
         __builtin_amdgcn_sched_barrier(0);
-        // x ring: the fragments loaded at step kb - D + 1 go to LDS, then this step's fragments
-        x_stream_store(pr[(s + 1) % D], xr[(s + 1) % D]);
-        x_stream_load((int)kb, nxt, pr[slot], xr[slot]);
+        // x: the wave's fragments FPS s .. FPS s + FPS - 1 of the next chunk at step s of a chunk
+        // (spread over the steps, so the weight stream never queues behind a burst of them)
+#pragma unroll
+        for (int i = FPS * s; i < FPS * (s + 1) && i < FW; ++i) x_fetch_one(c + 1, b ^ 1u, i);
         // A ring: refill this slot with block kb + D (dense blocks are their own A operands and
         // are refilled after the MFMAs below)
         if constexpr (FMT != kFmtBF16) load_ablock<FMT>(ra, rl, kb + D, lane16, buf[slot]);
 
-        const u32x4* xb = &s_x[b][s * FS * 64];
+        const u32x4* xb = &s_x[b][0];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
 #pragma unroll
           for (int cc = 0; cc < NT; ++cc) {
-            const u32x4 bv = xb[(t * NT + cc) * 64 + (bswz ^ (uint32_t)t)];
+            const u32x4 bv = xb[(s >> 1) * 512 * NT + 512 * cc + xo[(s + cc) & 1][t]];
             acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                              __builtin_bit_cast(bf16x8, bv), acc[cc],
                                                              0, 0, 0);
@@ -338,13 +268,10 @@ void k_mfma(MfmaArgs a) {
             const uint32_t e = cur[r] - t_e0;
             const uint32_t col = ncol[r] - 128u * S * c;
             const float v = bf16_to_float(s_eval[w][e]);
-            const uint32_t tt = (col >> 3) & 3u, gg = (col >> 5) & 3u;
-            const uint32_t f0 = ((col >> 7) * 4u + tt) * NT;
-            const uint32_t ln = (r16 + 16u * gg) ^ (tt | ((gg & 1u) << 2));
 #pragma unroll
             for (int cc = 0; cc < NT; ++cc) {
-              const float xv = bf16_to_float(
-                  reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
+              const uint32_t at = x_slot(col >> 8, 16u * cc + (uint32_t)r16, (col >> 3) & 31u);
+              const float xv = bf16_to_float(reinterpret_cast<const uint16_t*>(&s_x[b][at])[col & 7u]);
               if constexpr (kSepSx) sx[cc][r] += xv;
               else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
@@ -354,6 +281,9 @@ void k_mfma(MfmaArgs a) {
           }
         }
       }
+      // the next chunk is in LDS: the wave's last fragment load went out at step LS, before that
+      // step's refill
+      vm_wait_le<(S - LS) * kLoadsPerStep>();
       lds_barrier();
     }
 
@@ -396,16 +326,10 @@ void k_mfma(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------------------
-typedef void (*MfmaKernel)(MfmaArgs);
-
 template <int FMT>
 static MfmaKernel pick(int nt) {
-  switch (nt) {
-    case 1: return k_mfma<FMT, 1>;
-    case 2: return k_mfma<FMT, 2>;
-    case 3: return k_mfma<FMT, 3>;
-    default: return k_mfma<FMT, 4>;
-  }
+  if (nt >= 3) return mfma_wide_kernel(static_cast<Fmt>(FMT), nt);
+  return nt == 1 ? k_mfma<FMT, 1> : k_mfma<FMT, 2>;
 }
 
 static MfmaKernel pick_kernel(Fmt f, int nt) {
