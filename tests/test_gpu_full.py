@@ -54,7 +54,7 @@ def _codec(w, what, pool):
 
 
 def test_gate_up_full(pool):
-    """Config gate+up: codec, exact GEMM at M = 1, 4, 8, 16, 32, 64 on both kernel families, the
+    """Config gate+up: codec, exact GEMM at M = 1, 2, 4, 8, 16, 32, 64 on both kernel families, the
     Q pass at M=16 and the dense baseline at M=1 and 32 -- every output element."""
     w12 = _w12()
     w, spec, tid = synth.config_weight("gate_up")
@@ -62,7 +62,7 @@ def test_gate_up_full(pool):
     x = synth.gen_x(64, spec.k, tensor_id=tid)
     say("gate_up: oracle GEMM M=64 (all rows)")
     y64, absum = oracle_pool.gemm(x, w, pool)
-    for m in (1, 4, 8, 16, 32, 64):
+    for m in (1, 2, 4, 8, 16, 32, 64):
         for path in ("gemv", "mfma"):
             say(f"gate_up: gemm m={m} path={path}")
             y = w12.gemm(to_dev(x[:m]), rec, path=path).cpu().numpy()

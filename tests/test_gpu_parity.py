@@ -181,6 +181,21 @@ def test_gemm_ragged(n, k, m):
     _gemm_case(w, x, f"ragged {n}x{k}")
 
 
+@pytest.mark.parametrize("n,k,ms", [(17989, 384, (1,)), (33609, 128, (1, 2, 4))])
+def test_gemv_many_rounds(n, k, ms):
+    """More 16-row tiles than the persistent GEMV grid holds workgroups (1125 and 2101 tiles), so
+    workgroups take several tiles and the last round is partly idle; the last tile is ragged (5
+    and 9 rows)."""
+    rng = np.random.default_rng(n + k)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w12 = _w12()
+    rec = w12.encode(to_dev(w))
+    for m in ms:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        _gemm_case(w, x, f"many rounds {n}x{k}", paths=("gemv",), rec=rec)
+
+
 def test_gemm_one_hot_exact():
     """x = e_k must return column k of W exactly, escapes included, on both kernel families."""
     w12 = _w12()
