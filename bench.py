@@ -301,6 +301,29 @@ def main():
             row["best_w12_path"] = "gemv" if row["w12_gemv_us"] <= row["w12_mfma_us"] else "mfma"
             sweep[str(m)] = row
 
+    # Context, not a metric: the vendor library's dense bf16 GEMM on the same weights (torch.mm,
+    # which dispatches to hipBLASLt/rocBLAS), computed as y^T = W x^T with both operands
+    # contiguous; the pages compare W12 against the vendor library of their GPU.
+    vendor = None
+    if not a.no_sweep:
+        vendor = {}
+        for m in (1, 32):
+            xt = to_dev(x_bits[:m]).t().contiguous()
+            yt = torch.empty((n, m), dtype=torch.bfloat16, device=dev)
+            torch.mm(wcopies[0], xt, out=yt)
+            reps = 2 * rot
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            for r in range(reps):
+                torch.mm(wcopies[r % rot], xt, out=yt)
+            eb.record(stream)
+            torch.cuda.synchronize()
+            t = ea.elapsed_time(eb) * 1e-3 / reps
+            w12_t = mean["w12_m1"] if m == 1 else mean["w12_m32"]
+            vendor[f"m{m}_us"] = round(t * 1e6, 2)
+            vendor[f"m{m}_gbs"] = round(bf16_bytes(n, k, m) / t / 1e9, 1)
+            vendor[f"w12_speedup_m{m}"] = round(t / w12_t, 4)
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(w_bits, x_bits, gpu_out, min(a.cpu_rows, n))
@@ -341,6 +364,7 @@ def main():
         "read_probe_gbs": round(probe_gbs, 1),
         "w12_m1_frac_of_probe": round(value / probe_gbs, 4),
         "sweep": sweep,
+        "vendor_bf16_torch_mm": vendor,
         "setup_s": {"generate": round(t_gen, 2)},
         "kernel_source_sha256_16": kernel_source_hash(),
     }
