@@ -49,7 +49,6 @@ struct GemvArgs {
   int64_t k0;             // first column of this slice (multiple of 128)
   int kn;                 // slice length (multiple of 128)
   int accumulate;         // add to y instead of overwriting (second and later slices)
-  int cus;                // compute units of the device (work balance only)
 };
 
 // One 128-column block of the lane's row: the raw 128-bit words it loads.
@@ -150,33 +149,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   // block of step j (0 <= j < JP) of this wave, ~0 for a padding step
   const auto blk = [&](int j) { return j < mine ? kb0 + (uint32_t)(part + j * KS) : ~0u; };
 
-  // Work units: unit u (u = blockIdx.x + i G) is one pass over TPB tiles, all rows.  The time
-  // follows the bytes of the busiest CU, so when the last round leaves r2 = rem % cus passes over
-  // (rem = passes % G, the whole ones landing one per CU) and r2 <= cus / 2, those r2 passes run
-  // twice instead, once for rows 0..7 and once for rows 8..15 of their tiles, on 2 r2 workgroups
-  // of distinct CUs: every CU then streams the same bytes to half a tile.  The lanes of the other
-  // rows load and store nothing, and the halves write disjoint rows of y (no reduction).
-  const uint32_t G = gridDim.x, C = a.cus > 0 ? (uint32_t)a.cus : 1u;
-  const uint32_t rem = (uint32_t)(passes % G), r2 = rem % C;
-  const bool split = passes > (int64_t)G && r2 > 0 && 2 * r2 <= C && rem + r2 <= G;
-  const uint32_t whole = (uint32_t)passes - (split ? r2 : 0u);   // units that are whole passes
-  const uint32_t units = split ? whole + 2 * r2 : (uint32_t)passes;
-  const auto tile_of = [&](uint32_t u) {
-    return (int64_t)(u < whole || !split ? u : whole + (u - whole) % r2) * TPB + tsub;
-  };
-  const auto live = [&](uint32_t u) { return u < units && tile_of(u) < tiles; };
-  // this lane's row belongs to unit u (all rows, or the unit's half)
-  const auto lane_on = [&](uint32_t u) {
-    return u < whole || !split || (uint32_t)(r16 >> 3) == (u - whole) / r2;
-  };
-  const auto l16_of = [&](uint32_t u) { return lane_on(u) ? lane16 : kOOB; };
-
-  uint32_t pass = blockIdx.x;
-  TileRsrc<FMT> cur = tile_rsrc<FMT>(a, tile_of(pass), live(pass), ktiles);
-  uint32_t cur_l16 = l16_of(pass);
-  uint32_t npass = pass + G;
-  TileRsrc<FMT> nxt = tile_rsrc<FMT>(a, tile_of(npass), live(npass), ktiles);
-  uint32_t nxt_l16 = l16_of(npass);
+  int64_t pass = blockIdx.x;
+  const auto tile_of = [&](int64_t ps) { return ps * TPB + tsub; };
+  TileRsrc<FMT> cur = tile_rsrc<FMT>(a, tile_of(pass), pass < passes && tile_of(pass) < tiles, ktiles);
+  int64_t npass = pass + gridDim.x;
+  TileRsrc<FMT> nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
 
   // escape metadata of a tile for this lane's row (part-0 waves only; others load nothing):
   // bounds [e0, e1) of the row, the tile's first escape te0, and entries e0 + g + 4 i
@@ -184,15 +161,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   uint32_t ce0 = 0, ce1 = 0, ecol[kEscPre], evalv[kEscPre];   // current tile
   uint32_t ne0 = 0, ne1 = 0, nte0 = 0;                         // next tile (bounds only)
   uint32_t cbase = 0, nbase = 0;                               // window bottom of the row
-  const auto esc_bounds = [&](uint32_t ps, uint32_t& e0, uint32_t& e1, uint32_t& te0, uint32_t& bs) {
+  const auto esc_bounds = [&](int64_t ps, uint32_t& e0, uint32_t& e1, uint32_t& te0, uint32_t& bs) {
     const int64_t t = tile_of(ps);
-    const bool use_t = kEsc && part == 0 && live(ps), use = use_t && lane_on(ps);
+    const bool use = kEsc && part == 0 && ps < passes && t < tiles;
     const int64_t r = use ? t * kTileRows + r16 : 0;
     e0 = use ? a.esc_ptr[r < a.n ? r : a.n] : 0u;
     e1 = use ? a.esc_ptr[r + 1 < a.n ? r + 1 : a.n] : 0u;
     bs = use ? a.base[r < a.n ? r : a.n - 1] : 0u;
-    te0 = use_t ? a.esc_ptr[t * kTileRows] : 0u;   // made uniform only when used, a tile later:
-  };                                                // a uniform copy now would wait for the ring
+    te0 = use ? a.esc_ptr[t * kTileRows] : 0u;   // made uniform only when used, a tile later:
+  };                                              // a uniform copy now would wait for the ring
   const auto esc_entries = [&](uint32_t e0, uint32_t e1, uint32_t te0v) {
     const uint32_t te0 = __builtin_amdgcn_readfirstlane(te0v);
     const Rsrc rc = make_rsrc(a.esc_col + te0, 0x7FFFFFF0u), rv = make_rsrc(a.esc_val + te0, 0x7FFFFFF0u);
@@ -220,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   BlockRegs<FMT> buf[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    load_block<FMT>(cur, blk(d), cur_l16, buf[d]);
+    load_block<FMT>(cur, blk(d), lane16, buf[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
   uint32_t te0 = 0;
@@ -237,10 +214,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   lds_barrier();
   if constexpr (kEsc) esc_entries(ce0, ce1, te0);
 
-  for (; pass < units; pass += G) {
+  for (; pass < passes; pass += gridDim.x) {
     const int64_t tile = tile_of(pass);
-    const bool valid = tile < tiles, on = lane_on(pass);
-    if constexpr (kEsc) esc_bounds(pass + G, ne0, ne1, nte0, nbase);
+    const bool valid = tile < tiles;
+    if constexpr (kEsc) esc_bounds(pass + gridDim.x, ne0, ne1, nte0, nbase);
 
     float acc[M];
 #pragma unroll
@@ -264,7 +241,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
           TileRsrc<FMT> t;
           t.r0 = here ? cur.r0 : nxt.r0;
           t.r1 = here ? cur.r1 : nxt.r1;
-          load_block<FMT>(t, blk(here ? j + D : j + D - JP), here ? cur_l16 : nxt_l16, buf[d]);
+          load_block<FMT>(t, blk(here ? j + D : j + D - JP), lane16, buf[d]);
         };
         if constexpr (FMT != kFmtBF16) refill();
         if (j < mine) {
@@ -291,10 +268,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       j0 += D;
     } while (j0 < JP);
     cur = nxt;
-    cur_l16 = nxt_l16;
-    npass += G;
-    nxt = tile_rsrc<FMT>(a, tile_of(npass), live(npass), ktiles);
-    nxt_l16 = l16_of(npass);
+    npass += gridDim.x;
+    nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
 
     const int64_t row = tile * kTileRows + r16;
     float q[M];
@@ -338,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       lds_barrier();
     }
 
-    if (part == 0 && valid && on && g == 0 && row < a.n) {
+    if (part == 0 && valid && g == 0 && row < a.n) {
       float sc = 1.0f;
       if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
 #pragma unroll
@@ -436,7 +411,6 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
       a.ldy = n;
       a.n = n; a.k = k; a.k0 = k0; a.kn = kn;
       a.accumulate = k0 > 0;
-      a.cus = di.cus;
       hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, a);
       err = hipGetLastError();
       if (err != hipSuccess) return err;
