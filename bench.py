@@ -78,6 +78,195 @@ def measured_traffic():
     return float(m_val.group(1))
 
 
+def time_eager(fns, stream, reps):
+    """Mean seconds per pass over the launch list `fns`, launched one by one from Python (host
+    launch overhead included), timed with HIP events on `stream`."""
+    import torch
+    for f in fns:
+        f()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for _ in range(reps):
+        for f in fns:
+            f()
+    eb.record(stream)
+    torch.cuda.synchronize()
+    return ea.elapsed_time(eb) * 1e-3 / reps
+
+
+def capture_graph(fns, outs):
+    """Capture the launch list in one HIP graph and check its replays against the eager result:
+    every output is cleared, the graph replayed, and the output compared bit for bit, three
+    times, with eager work in between.  Returns the graph."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            if not torch.equal(o.view(torch.int32), w.view(torch.int32)):
+                raise SystemExit("graph replay differs from the eager launches")
+    return g
+
+
+def time_graph(g, stream, reps):
+    """Mean seconds per replay of a captured HIP graph (HIP events on `stream`)."""
+    import torch
+    g.replay()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record(stream)
+    for _ in range(reps):
+        g.replay()
+    eb.record(stream)
+    torch.cuda.synchronize()
+    return ea.elapsed_time(eb) * 1e-3 / reps
+
+
+def to_dev_bits(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def attn_bench(dev, stream, min_rot_bytes, reps):
+    """Attention projection W [5120, 5120] at M=1: W12 GEMV and the same-build BF16 GEMV over R
+    copies (>= min_rot_bytes per format, so every launch reads HBM), launched one by one and as
+    one captured HIP graph.  At ~5 us per launch the host's launch rate, not the kernel, sets the
+    eager time, so the graph figure is the kernel's.  Returns (results, parity samples)."""
+    import torch
+    from lossless_bit_weight_02_amd import synth, w12
+
+    w_bits, spec, tid = synth.config_weight("attn")
+    n, k = spec.n, spec.k
+    x_bits = synth.gen_x(1, k, tensor_id=tid)
+    w = to_dev_bits(w_bits, dev)
+    rec = w12.encode(w)
+    rot = max(2, int(np.ceil(min_rot_bytes / rec.nbytes())))
+    recs = [rec] + [rec.clone() for _ in range(rot - 1)]
+    tiles = [w12.bf16_tiles(w)]
+    tiles += [w12.Bf16Tiles(n, k, tiles[0].data.clone()) for _ in range(rot - 1)]
+    del w
+    x = to_dev_bits(x_bits, dev)
+    y = [torch.empty((1, n), dtype=torch.float32, device=dev) for _ in range(rot)]
+    yb = [torch.empty((1, n), dtype=torch.float32, device=dev) for _ in range(rot)]
+    w12_fns = [lambda r=r: w12.gemm(x, recs[r], path="gemv", out=y[r]) for r in range(rot)]
+    bf_fns = [lambda r=r: w12.bf16_gemm(x, tiles[r], path="gemv", out=yb[r]) for r in range(rot)]
+    out = {"n": n, "k": k, "m": 1, "rotation_copies": rot, "escapes": rec.n_esc}
+    b_w12, b_bf = w12_bytes(n, k, rec.n_esc, 1), bf16_bytes(n, k, 1)
+    for name, fns, outs, byt in (("w12", w12_fns, y, b_w12), ("bf16", bf_fns, yb, b_bf)):
+        t_e = time_eager(fns, stream, reps) / rot
+        g = capture_graph(fns, outs)
+        t_g = time_graph(g, stream, reps) / rot
+        out[f"{name}_us_graph"] = round(t_g * 1e6, 3)
+        out[f"{name}_gbs_graph"] = round(byt / t_g / 1e9, 1)
+        out[f"{name}_us_eager"] = round(t_e * 1e6, 3)
+        del g
+    out["w12_frac_hbm_graph"] = round(b_w12 / (out["w12_us_graph"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    out["speedup_vs_bf16_graph"] = round(out["bf16_us_graph"] / out["w12_us_graph"], 4)
+    samples = [("attn w12 m=1", x_bits, w_bits, y[0].cpu().numpy())]
+    return out, samples
+
+
+def stack_bench(dev, stream, layers, reps, sample_layer):
+    """The 27B-class dense stack: `layers` layers of {q, k, v, o, gate, up, down} (tensor id
+    8*layer + projection).  Every matrix is drawn on the GPU (synth.gen_weight_torch), encoded,
+    decoded and compared bit for bit with its source, and tiled for the BF16 baseline; then one
+    pass over all matrices at M=1 and at M=32 (automatic path) is timed launched one by one
+    (wall time, host gaps included) and as one captured HIP graph (~kernel-sum time).
+    Returns (results, parity samples of `sample_layer`: its first 128 rows per projection)."""
+    import torch
+    from lossless_bit_weight_02_amd import synth, w12
+
+    cfg = synth.CONFIGS["stack"]
+    n_proj = len(synth.STACK_PROJ)
+    entries = cfg.weights[:layers * n_proj]
+    recs, tiles, keep = [], [], {}
+    t0 = time.perf_counter()
+    t_enc = 0.0
+    n_esc = 0
+    weights = 0
+    for i, (tid, label, spec) in enumerate(entries):
+        w = synth.gen_weight_torch(spec, 0, tid, dev)
+        torch.cuda.synchronize()
+        te = time.perf_counter()
+        rec = w12.encode(w)
+        torch.cuda.synchronize()
+        t_enc += time.perf_counter() - te
+        back = w12.decode(rec)
+        if not torch.equal(back.view(torch.int16), w.view(torch.int16)):
+            raise SystemExit(f"stack {label}: decode(encode(W)) is not bit-exact")
+        del back
+        tiles.append(w12.bf16_tiles(w))
+        if i // n_proj == sample_layer:
+            keep[i] = w[:128].view(torch.int16).cpu().numpy().view(np.uint16)
+        del w
+        recs.append(rec)
+        n_esc += rec.n_esc
+        weights += spec.n * spec.k
+    t_build = time.perf_counter() - t0
+    xs = {}
+    for p, (nm, n, k) in enumerate(synth.STACK_PROJ):
+        if k not in xs:
+            xb = synth.gen_x(32, k, tensor_id=p)
+            xs[k] = (xb, to_dev_bits(xb, dev))
+    out = {"layers": layers, "matrices": len(entries), "weights": weights, "escapes": n_esc,
+           "escape_fraction": round(n_esc / weights, 7),
+           "bits_per_weight": round(8.0 * sum(r.nbytes() for r in recs) / weights, 4),
+           "lossless_all": True, "encode_s_total": round(t_enc, 3),
+           "build_s": round(t_build, 2)}
+    samples = []
+    for m in (1, 32):
+        ys = [torch.empty((m, spec.n), dtype=torch.float32, device=dev) for _, _, spec in entries]
+        yb = [torch.empty((m, spec.n), dtype=torch.float32, device=dev) for _, _, spec in entries]
+        xm = {k: v[1][:m] for k, v in xs.items()}
+        w12_fns = [lambda i=i: w12.gemm(xm[recs[i].k], recs[i], out=ys[i]) for i in range(len(recs))]
+        bf_fns = [lambda i=i: w12.bf16_gemm(xm[tiles[i].k], tiles[i], out=yb[i])
+                  for i in range(len(tiles))]
+        b_w12 = sum(w12_bytes(r.n, r.k, r.n_esc, m) for r in recs)
+        b_bf = sum(bf16_bytes(t.n, t.k, m) for t in tiles)
+        row = {"w12_bytes": b_w12, "bf16_bytes": b_bf}
+        for name, fns, outs, byt in (("w12", w12_fns, ys, b_w12), ("bf16", bf_fns, yb, b_bf)):
+            t_e = time_eager(fns, stream, reps)
+            g = capture_graph(fns, outs)
+            t_g = time_graph(g, stream, reps)
+            del g
+            row[f"{name}_ms_graph"] = round(t_g * 1e3, 4)
+            row[f"{name}_gbs_graph"] = round(byt / t_g / 1e9, 1)
+            row[f"{name}_ms_eager"] = round(t_e * 1e3, 4)
+            row[f"{name}_gbs_eager"] = round(byt / t_e / 1e9, 1)
+        row["w12_frac_hbm_graph"] = round(row["w12_gbs_graph"] / HBM_PEAK_GBS, 4)
+        row["speedup_vs_bf16_graph"] = round(row["bf16_ms_graph"] / row["w12_ms_graph"], 4)
+        # per projection: its `layers` launches as one graph (us per launch)
+        per = {}
+        for p, (nm, _, _) in enumerate(synth.STACK_PROJ):
+            idx = list(range(p, len(recs), n_proj))
+            for name, fns, outs in (("w12", w12_fns, ys), ("bf16", bf_fns, yb)):
+                g = capture_graph([fns[i] for i in idx], [outs[i] for i in idx])
+                t = time_graph(g, stream, reps) / len(idx)
+                del g
+                r0 = recs[idx[0]]
+                byt = (w12_bytes(r0.n, r0.k, r0.n_esc, m) if name == "w12" else
+                       bf16_bytes(r0.n, r0.k, m))
+                per[f"{nm}_{name}_us"] = round(t * 1e6, 2)
+                per[f"{nm}_{name}_gbs"] = round(byt / t / 1e9, 1)
+        row["per_projection"] = per
+        out[f"m{m}"] = row
+        for i, wrows in keep.items():
+            samples.append((f"stack {entries[i][1]} w12 m={m}", xs[recs[i].k][0][:m], wrows,
+                            ys[i][:, :128].cpu().numpy()))
+        del ys, yb
+    return out, samples
+
+
 def cpu_count():
     try:
         return len(os.sched_getaffinity(0))
@@ -85,9 +274,10 @@ def cpu_count():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(w_bits, x_bits, gpu_out, rows):
+def cpu_baseline(w_bits, x_bits, gpu_out, rows, samples=()):
     """Time the oracle (as it stands) on the first `rows` rows of the workload, and check the
-    GPU outputs of the timed step on the same rows."""
+    GPU outputs of the timed step on the same rows; then check each extra sample
+    (label, x bits [m, k], W bits [r, k], GPU y [m, r]) against the oracle's exact GEMM."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -120,6 +310,13 @@ def cpu_baseline(w_bits, x_bits, gpu_out, rows):
         if not np.all(err <= bound):
             raise SystemExit(f"parity failure in {name}: GPU output outside the bound")
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+    for label, xb, wb, gy in samples:
+        y = oracle.gemm64(xb, wb)
+        bound = 1e-3 * oracle.abs_bound64(xb, wb)
+        err = np.abs(gy.astype(np.float64) - y)
+        if not np.all(err <= bound):
+            raise SystemExit(f"parity failure in {label}: GPU output outside the bound")
+        worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
     blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     gbs = w12_bytes(rows, ws.shape[1], rec.n_esc, 1) / t_g1 / 1e9
     return {
@@ -130,6 +327,7 @@ def cpu_baseline(w_bits, x_bits, gpu_out, rows):
                   f"{blas} of {cpu_count()} host cores",
         "seconds": round(total, 3),
         "parity_worst_err_over_bound": round(worst, 5),
+        "parity_samples": len(samples),
     }
 
 
@@ -141,6 +339,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M sweep (crossover)")
+    ap.add_argument("--no-attn", action="store_true", help="skip the attention-projection section")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack section")
+    ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 192 MiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--min-rot-bytes", type=float, default=1.1e9)
@@ -324,9 +525,24 @@ def main():
             vendor[f"m{m}_gbs"] = round(bf16_bytes(n, k, m) / t / 1e9, 1)
             vendor[f"w12_speedup_m{m}"] = round(t / w12_t, 4)
 
+    # Context beside the step: the attention projection at M=1, and the whole 64-layer stack at
+    # M=1 and M=32 (both also run as captured HIP graphs); their outputs are parity-checked in
+    # the CPU-oracle leg.
+    samples = []
+    attn = None
+    if not a.no_attn:
+        attn, smp = attn_bench(dev, stream, a.min_rot_bytes, reps=20)
+        samples += smp
+    stack = None
+    if not a.no_stack:
+        stack, smp = stack_bench(dev, stream, a.stack_layers, reps=5,
+                                 sample_layer=min(31, a.stack_layers - 1))
+        samples += smp
+        torch.cuda.empty_cache()
+
     cpu = None
     if not a.no_cpu:
-        cpu = cpu_baseline(w_bits, x_bits, gpu_out, min(a.cpu_rows, n))
+        cpu = cpu_baseline(w_bits, x_bits, gpu_out, min(a.cpu_rows, n), samples)
 
     value = gbs["w12_m1"]
     traffic = measured_traffic()
@@ -365,6 +581,8 @@ def main():
         "w12_m1_frac_of_probe": round(value / probe_gbs, 4),
         "sweep": sweep,
         "vendor_bf16_torch_mm": vendor,
+        "attn_m1": attn,
+        "stack": stack,
         "setup_s": {"generate": round(t_gen, 2)},
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "w12.h"
 #include "w12_launch.hpp"
@@ -109,6 +110,39 @@ hipError_t dev_info(DevInfo* out) {
     cache[dev] = d;
   }
   *out = cache[dev];
+  return hipSuccess;
+}
+
+hipError_t workspace(hipStream_t s, float** out) {
+  struct Entry {
+    int device;
+    hipStream_t stream;
+    void* ptr;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& en : table)
+    if (en.device == dev && en.stream == s) {
+      *out = static_cast<float*>(en.ptr);
+      return hipSuccess;
+    }
+  // The first call on a stream may come while that stream is being captured into a graph (a
+  // graph is often captured on a stream of its own): the allocation is not a stream operation,
+  // so this thread's capture mode is relaxed around it.
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  e = hipThreadExchangeStreamCaptureMode(&mode);
+  if (e != hipSuccess) return e;
+  void* p = nullptr;
+  e = hipMalloc(&p, kWorkspaceBytes);
+  hipError_t e2 = hipThreadExchangeStreamCaptureMode(&mode);
+  if (e != hipSuccess) return e;
+  if (e2 != hipSuccess) return e2;
+  table.push_back(Entry{dev, s, p});
+  *out = static_cast<float*>(p);
   return hipSuccess;
 }
 

@@ -12,6 +12,10 @@
 // row r, columns 32g..32g+31 of each block: its AE (2 x 128-bit) and B (1 x 128-bit) loads are
 // wave-wide 1 KiB contiguous reads.
 //
+// Split k: a shape with few tiles for the chip (the k and v projections of a 27B-class layer
+// have 64) splits the slice into `splits` k ranges; workgroup b takes range b % splits and writes
+// partial sums to its own slice of a workspace, which a second kernel adds in range order.
+//
 // Escapes: the part-0 wave of a tile patches them from x in LDS.  Their metadata is fetched one
 // tile ahead so the patch never waits on memory: the row bounds of the wave's next tile at the
 // start of a tile, that tile's first kEscPre escapes per row at its end (rows with more read the
@@ -43,12 +47,15 @@ struct GemvArgs {
   const uint32_t* esc_col;
   const uint16_t* esc_val;
   const uint16_t* w;      // dense bfloat16 W (baseline), tiled storage
-  float* y;               // y[m][ldy]
+  float* y;               // y[m][ldy]; with splits > 1, range j writes y + j * ysplit
   int64_t ldy;
   int64_t n, k;           // rows of W, row length
-  int64_t k0;             // first column of this slice (multiple of 128)
-  int kn;                 // slice length (multiple of 128)
+  int64_t k0;             // first column of this launch's slice (multiple of 128)
+  int kn;                 // length of one k range of the slice (multiple of 128)
   int accumulate;         // add to y instead of overwriting (second and later slices)
+  int splits;             // k ranges of the slice: workgroup b takes range b % splits
+  int64_t kend;           // end of the slice (the last range may be shorter)
+  int64_t ysplit;         // floats between the partial outputs of consecutive ranges
 };
 
 // One 128-column block of the lane's row: the raw 128-bit words it loads.
@@ -132,7 +139,12 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   constexpr int TPB = 4 / KS;                    // tiles per workgroup pass
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
-  const int kn = a.kn, kn8 = kn >> 3;
+  // this workgroup's k range [k0, k0 + kn) and workgroup group
+  const int sp = (int)(blockIdx.x % (uint32_t)a.splits);
+  const int64_t grp = blockIdx.x / (uint32_t)a.splits, n_grp = gridDim.x / (uint32_t)a.splits;
+  const int64_t k0 = a.k0 + (int64_t)sp * a.kn;
+  const int kn = (int)(a.kend - k0 < a.kn ? a.kend - k0 : a.kn), kn8 = kn >> 3;
+  float* const yout = a.y + sp * a.ysplit;
 
   const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(xs);
 
@@ -142,17 +154,17 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   const uint32_t ktiles = (uint32_t)(a.k / kTileCols);
   const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
   const int64_t passes = (tiles + TPB - 1) / TPB;
-  const uint32_t kb0 = (uint32_t)(a.k0 / kTileCols);
+  const uint32_t kb0 = (uint32_t)(k0 / kTileCols);
   const int nblk = kn / kTileCols;
   const int mine = (nblk - part + KS - 1) / KS;  // blocks of this slice owned by this wave
   const int JP = ((nblk + KS - 1) / KS + D - 1) / D * D;   // ring steps per tile, all waves
   // block of step j (0 <= j < JP) of this wave, ~0 for a padding step
   const auto blk = [&](int j) { return j < mine ? kb0 + (uint32_t)(part + j * KS) : ~0u; };
 
-  int64_t pass = blockIdx.x;
+  int64_t pass = grp;
   const auto tile_of = [&](int64_t ps) { return ps * TPB + tsub; };
   TileRsrc<FMT> cur = tile_rsrc<FMT>(a, tile_of(pass), pass < passes && tile_of(pass) < tiles, ktiles);
-  int64_t npass = pass + gridDim.x;
+  int64_t npass = pass + n_grp;
   TileRsrc<FMT> nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
 
   // escape metadata of a tile for this lane's row (part-0 waves only; others load nothing):
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   for (int q = 0; q < kXF; ++q) {
     const int i = tid + q * kBlock, m = i / kn8, j = i - m * kn8;
     xv[q] = __builtin_amdgcn_raw_buffer_load_b128(
-        r_x, i < M * kn8 ? (uint32_t)(2 * (m * a.ldx + a.k0 + 8 * j)) : kOOB, 0, 0);
+        r_x, i < M * kn8 ? (uint32_t)(2 * (m * a.ldx + k0 + 8 * j)) : kOOB, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   BlockRegs<FMT> buf[D];
@@ -209,15 +221,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   }
   for (int i = tid + kXF * kBlock; i < M * kn8; i += kBlock) {
     const int m = i / kn8, j = i - m * kn8;
-    xs[i] = *reinterpret_cast<const u32x4*>(a.x + m * a.ldx + a.k0 + 8 * j);
+    xs[i] = *reinterpret_cast<const u32x4*>(a.x + m * a.ldx + k0 + 8 * j);
   }
   lds_barrier();
   if constexpr (kEsc) esc_entries(ce0, ce1, te0);
 
-  for (; pass < passes; pass += gridDim.x) {
+  for (; pass < passes; pass += n_grp) {
     const int64_t tile = tile_of(pass);
     const bool valid = tile < tiles;
-    if constexpr (kEsc) esc_bounds(pass + gridDim.x, ne0, ne1, nte0, nbase);
+    if constexpr (kEsc) esc_bounds(pass + n_grp, ne0, ne1, nte0, nbase);
 
     float acc[M];
 #pragma unroll
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       j0 += D;
     } while (j0 < JP);
     cur = nxt;
-    npass += gridDim.x;
+    npass += n_grp;
     nxt = tile_rsrc<FMT>(a, tile_of(npass), npass < passes && tile_of(npass) < tiles, ktiles);
 
     const int64_t row = tile * kTileRows + r16;
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       // Escapes of this lane's row inside the slice (part-0 wave; the 4 column-group lanes of the
       // row share the list): remove the placeholder from P, collect Q = sum x * v.
       const auto patch = [&](uint32_t col, uint32_t vbits) {
-        const int64_t c = (int64_t)col - a.k0;
+        const int64_t c = (int64_t)col - k0;
         if (c >= 0 && c < kn) {
           const float v = bf16_to_float(vbits);
 #pragma unroll
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float v = FMT != kFmtBF16 ? fmaf(sc, acc[m], q[m]) : acc[m];
-        float* yp = a.y + m * a.ldy + row;
+        float* yp = yout + m * a.ldy + row;
         // later k-slices add to y; the read stays in its branch (a hoisted read would make every
         // tile wait for the whole stream in flight)
         if (a.accumulate) *yp = *reinterpret_cast<volatile float*>(yp) + v;
@@ -378,40 +390,77 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t nkb = k / kTileCols;
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int mb = (int)((m - m0) < 8 ? (m - m0) : 8);
     GemvKernel kern = pick_kernel(f, mb);
     const int ks = ks_for(mb);
-    // k-slices whose x copy fits the LDS budget (every shape with 2*m*k <= 80 KiB uses one slice)
+    const int64_t tpb = 4 / ks;
+    const int64_t passes = (tiles + tpb - 1) / tpb;
+    // longest k range whose x copy fits the LDS budget (2*m*k <= 80 KiB: the whole row)
     const int64_t red_bytes = (int64_t)4 * mb * 64 * 4;
     int64_t budget = 81920;
     if (budget > di.max_lds - red_bytes) budget = di.max_lds - red_bytes;
     int64_t slice = (budget / (2 * mb)) / kTileCols * kTileCols;
     if (slice < kTileCols) slice = kTileCols;
     if (slice > k) slice = k;
+    int occ = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
+                                                       kBlock, (size_t)2 * mb * slice);
+    if (err != hipSuccess) return err;
+    if (occ < 1) occ = 1;
+    const int64_t slots = (int64_t)di.cus * occ;
+    // k ranges in one launch: when the shape has few tiles and long rows (more than 16 blocks per
+    // wave of a tile), as many as keep every workgroup slot busy, with at least two blocks per
+    // wave in each; at least as many as the LDS needs; their partial outputs must fit the
+    // workspace.  (On shorter rows the second kernel costs more than the ranges gain.)
+    int64_t ranges = nkb / ks > 16 ? slots / passes : 1;
+    if (ranges > nkb / (2 * ks)) ranges = nkb / (2 * ks);
+    const int64_t need = (k + slice - 1) / slice;
+    if (ranges < need) ranges = need;
+    int64_t rlen = (nkb + ranges - 1) / ranges * kTileCols;
+    if (rlen > slice) rlen = slice;
+    ranges = (k + rlen - 1) / rlen;
+    float* ws = nullptr;
+    if (ranges > 1 && (size_t)ranges * mb * n * sizeof(float) <= kWorkspaceBytes) {
+      err = workspace(s, &ws);
+      if (err != hipSuccess) return err;
+    }
+    GemvArgs a;
+    a.ldx = k;
+    a.base = p.base; a.ae = p.ae; a.lo = p.lo;
+    a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
+    a.w = p.w;
+    a.ldy = n;
+    a.n = n; a.k = k;
+    a.x = x + m0 * k;
+    if (ws) {
+      // one launch over all ranges into the workspace, then the ordered sum into y
+      int64_t groups = slots / ranges;
+      if (groups > passes) groups = passes;
+      if (groups < 1) groups = 1;
+      a.y = ws;
+      a.k0 = 0; a.kn = (int)rlen; a.kend = k;
+      a.accumulate = 0;
+      a.splits = (int)ranges;
+      a.ysplit = (int64_t)mb * n;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(groups * ranges)), dim3(kBlock), (size_t)2 * mb * rlen, s, a);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      err = launch_split_reduce(ws, (int)ranges, (int64_t)mb * n, y + m0 * n, s);
+      if (err != hipSuccess) return err;
+      continue;
+    }
+    // one range per launch: later slices add to y in slice order
+    int64_t groups = passes < slots ? passes : slots;
+    a.y = y + m0 * n;
+    a.splits = 1;
+    a.ysplit = 0;
     for (int64_t k0 = 0; k0 < k; k0 += slice) {
       const int kn = (int)((k - k0) < slice ? (k - k0) : slice);
-      const size_t lds = (size_t)2 * mb * kn;
-      int occ = 0;
-      err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
-                                                         kBlock, lds);
-      if (err != hipSuccess) return err;
-      if (occ < 1) occ = 1;
-      const int64_t tpb = 4 / ks;
-      int64_t blocks = (tiles + tpb - 1) / tpb;
-      const int64_t cap = (int64_t)di.cus * occ;
-      if (blocks > cap) blocks = cap;
-      GemvArgs a;
-      a.x = x + m0 * k;
-      a.ldx = k;
-      a.base = p.base; a.ae = p.ae; a.lo = p.lo;
-      a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
-      a.w = p.w;
-      a.y = y + m0 * n;
-      a.ldy = n;
-      a.n = n; a.k = k; a.k0 = k0; a.kn = kn;
+      a.k0 = k0; a.kn = kn; a.kend = k0 + kn;
       a.accumulate = k0 > 0;
-      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, a);
+      hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kBlock), (size_t)2 * mb * kn, s, a);
       err = hipGetLastError();
       if (err != hipSuccess) return err;
     }

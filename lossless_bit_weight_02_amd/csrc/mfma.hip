@@ -32,8 +32,14 @@
 // of chunk c, dealt round-robin over the waves; no register holds x on its way.  Rows past m and
 // columns past k read zeros (buffer loads out of range).  One barrier per chunk.
 //
+// Split k.  A shape with too few tiles to give every wave of the chip one (the k and v
+// projections of a 27B-class layer have 64, the down projection 320 tiles of 136 blocks) splits
+// each row into `splits` k ranges of whole x chunks: workgroup b takes range b % splits of the
+// tiles dealt to workgroup group b / splits, and writes its partial sums to its own slice of a
+// workspace; a second kernel adds the slices in range order (deterministic).
+//
 // Escapes (exact weights outside a row's window): the lanes of column group g own output rows
-// 4g..4g+3 of the tile.  The tile's escape list (up to kEscCap entries) is copied to LDS at the
+// 4g..4g+3 of the tile.  The tile's escape list (up to kEscCapM entries) is copied to LDS at the
 // start of the tile; at the end of every chunk each lane walks its rows' column-sorted runs up to
 // the chunk's last column, reading x from the chunk still in LDS, and accumulates
 //   y = 2^(base-112) * (acc - 2^-15 * sum_esc x) + sum_esc x * v,
@@ -48,11 +54,17 @@ namespace w12 {
 // Compile-time shape of one instantiation: D weight blocks in flight per wave (as many as the
 // 168 VGPRs allow), chunks of S k-blocks of x (a multiple of D).  Four k-blocks per chunk
 // measured faster than eight at one tile.
+constexpr int kChunkBlocks = 4;   // k-blocks per x chunk (both instantiations)
+// Escapes of one tile copied to LDS: a 16-row tile of a 17408-column row holds ~315 escapes at
+// the synthetic projections' escape rate (zeros dominate), ~20 at the pages' rate.
+constexpr int kEscCapM = 384;
+constexpr int kEscStage = 128;    // of which staged through registers with the first loads
+
 template <int FMT, int NT>
 struct Shape {
   static_assert(NT == 1 || NT == 2, "three and four tiles run k_mfma_wide");
   static constexpr int D = 4;
-  static constexpr int S = 4;                         // k-blocks per x chunk
+  static constexpr int S = kChunkBlocks;              // k-blocks per x chunk
   static constexpr int FS = 4 * NT;                   // 1 KiB x fragments per k-block
   static constexpr int F = FS * S;                    // 1 KiB x fragments per chunk
   static constexpr int FW = (F + kWaves - 1) / kWaves;   // fragments a wave loads per chunk
@@ -84,15 +96,24 @@ void k_mfma(MfmaArgs a) {
   constexpr int kLoadsPerStep = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
   __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * kWaves > F) ? 64 : 1];   // target of unused fragment loads
-  __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];   // per wave: tile escapes
-  __shared__ uint16_t s_eval[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];
+  __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCapM : 1];   // per wave: tile escapes
+  __shared__ uint16_t s_eval[kEsc ? kWaves : 1][kEsc ? kEscCapM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t KB = (uint32_t)(a.k / kTileCols);
-  const uint32_t KBp = (KB + S - 1) / S * S;
+  const uint32_t n_chunks = (KB + S - 1) / S;
   const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
+  // this workgroup's k range: chunks [c0, c1), blocks [kb0, kb0 + nkb), columns [col0, col1)
+  const int sp = (int)(blockIdx.x % (uint32_t)a.splits);
+  const int64_t grp = blockIdx.x / (uint32_t)a.splits, n_grp = gridDim.x / (uint32_t)a.splits;
+  const uint32_t c0 = (uint32_t)sp * (uint32_t)a.cps;
+  const uint32_t c1 = c0 + (uint32_t)a.cps < n_chunks ? c0 + (uint32_t)a.cps : n_chunks;
+  const uint32_t kb0 = c0 * S;
+  const uint32_t nkb = (c1 * S < KB ? c1 * S : KB) - kb0;
+  const uint32_t col0 = 128u * kb0, col1 = 128u * (kb0 + nkb);
+  float* const yout = a.y + sp * a.ysplit;
   const uint32_t e112 = exp112_pair();
   const uint32_t kx = (uint32_t)a.k;
   const Rsrc rx = make_rsrc(a.x, (uint32_t)a.m * kx * 2u);
@@ -139,15 +160,15 @@ void k_mfma(MfmaArgs a) {
     }
 
   for (int round = 0; round < a.rounds; ++round) {
-    const int64_t tile = ((int64_t)round * kWaves + w) * gridDim.x + blockIdx.x;
+    const int64_t tile = ((int64_t)round * kWaves + w) * n_grp + grp;
     const bool valid = tile < tiles;
     const int64_t row0 = (valid ? tile : 0) * kTileRows;
 
     lds_barrier();                                 // the previous tile no longer reads LDS
 
     // ---- escape list of the tile (oldest loads: waited for before the loop) ----
-    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0;
-    uint32_t ecol[kEscCap / 64], evalv[kEscCap / 64];
+    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0, t_cnt = 0;
+    uint32_t ecol[kEscStage / 64], evalv[kEscStage / 64];
     if constexpr (kEsc) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
@@ -159,11 +180,12 @@ void k_mfma(MfmaArgs a) {
         bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
       t_e0 = __builtin_amdgcn_readfirstlane(a.esc_ptr[row0]);
       const uint32_t t_e1 = __builtin_amdgcn_readfirstlane(valid ? ptr_at(row0 + kTileRows) : t_e0);
-      const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCap ? t_e1 - t_e0 : (uint32_t)kEscCap;
+      const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCapM ? t_e1 - t_e0 : (uint32_t)kEscCapM;
+      t_cnt = cnt;
       const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
       const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
 #pragma unroll
-      for (int i = 0; i < kEscCap / 64; ++i) {
+      for (int i = 0; i < kEscStage / 64; ++i) {
         ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
         evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
       }
@@ -173,19 +195,20 @@ void k_mfma(MfmaArgs a) {
       }
     }
 
-    // ---- chunk 0 of x, straight into LDS buffer 0 ----
+    // ---- the range's first chunk of x, straight into LDS buffer 0 ----
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < FW; ++i) x_fetch_one(0u, 0u, i);
+    for (int i = 0; i < FW; ++i) x_fetch_one(c0, 0u, i);
 
     // ---- D virtual steps -D .. -1: the same load pattern as a loop step ----
+    // (buffers over the range's blocks only: the ring's refills past the range read zeros)
     Rsrc ra, rl;
     if constexpr (FMT == kFmtBF16) {
-      ra = make_rsrc(a.w + row0 * a.k, valid ? KB * (uint32_t)kTileBF : 0u);
+      ra = make_rsrc(a.w + row0 * a.k + (int64_t)kb0 * (kTileBF / 2), valid ? nkb * (uint32_t)kTileBF : 0u);
       rl = ra;
     } else {
-      ra = make_rsrc(a.ae + row0 * a.k, valid ? KB * (uint32_t)kTileAE : 0u);
-      rl = make_rsrc(a.lo + row0 * a.k / 2, valid ? KB * (uint32_t)kTileLO : 0u);
+      ra = make_rsrc(a.ae + row0 * a.k + (int64_t)kb0 * kTileAE, valid ? nkb * (uint32_t)kTileAE : 0u);
+      rl = make_rsrc(a.lo + row0 * a.k / 2 + (int64_t)kb0 * kTileLO, valid ? nkb * (uint32_t)kTileLO : 0u);
     }
     ABlock<FMT> buf[D];
     __builtin_amdgcn_sched_barrier(0);
@@ -197,23 +220,41 @@ void k_mfma(MfmaArgs a) {
 
     if constexpr (kEsc) {
 #pragma unroll
-      for (int i = 0; i < kEscCap / 64; ++i) {
+      for (int i = 0; i < kEscStage / 64; ++i) {
         s_ecol[w][lane + 64 * i] = ecol[i];
         s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
+      }
+      // a crowded tile: the rest of the LDS copy (these loads were issued after the ring's, so
+      // their wait also covers the ring)
+      for (uint32_t i = kEscStage + (uint32_t)lane; i < t_cnt; i += 64) {
+        s_ecol[w][i] = a.esc_col[t_e0 + i];
+        s_eval[w][i] = a.esc_val[t_e0 + i];
       }
     }
     vm_wait_le<D * kLoadsPerStep>();   // chunk 0 is in LDS
     lds_barrier();
 
     // per row r: cursor (absolute escape index) and the column under it (~0: none in LDS)
-    const uint32_t lds_end = t_e0 + kEscCap;
+    const uint32_t lds_end = t_e0 + kEscCapM;
     const auto run_end = [&](int r) { return st[r + 1] < lds_end ? st[r + 1] : lds_end; };
+    // (escapes left of the range are skipped; a crowded row whose LDS copy ends before the range
+    // starts finds the rest in memory after the loop)
     uint32_t cur[4], ncol[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       cur[r] = st[r];
       ncol[r] = 0xFFFFFFFFu;
-      if constexpr (kEsc) ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
+      if constexpr (kEsc) {
+        // first escape of the row at or right of col0 (the run is sorted by column)
+        uint32_t lo = cur[r], hi = run_end(r);
+        while (lo < hi) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (s_ecol[w][mid - t_e0] < col0) lo = mid + 1;
+          else hi = mid;
+        }
+        cur[r] = lo;
+        ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
+      }
     }
 
     floatx4 acc[NT];
@@ -225,12 +266,12 @@ void k_mfma(MfmaArgs a) {
       for (int r = 0; r < 4; ++r) qv[cc][r] = sx[cc][r] = 0.f;
     }
 
-    for (uint32_t c = 0; c * S < KBp; ++c) {       // chunk c: k-blocks S c .. S c + S - 1
-      const uint32_t b = c & 1u;
+    for (uint32_t c = c0; c < c1; ++c) {           // chunk c: k-blocks S c .. S c + S - 1
+      const uint32_t b = (c - c0) & 1u;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int slot = s % D;
-        const uint32_t kb = S * c + s;
+        const uint32_t kb = S * (c - c0) + s;      // block within the range
         uint32_t p[16];
         ablock_pairs<FMT>(buf[slot], e112, p);
         if constexpr (FMT != kFmtBF16) pin16(p);
@@ -289,20 +330,39 @@ void k_mfma(MfmaArgs a) {
 
     if (!valid) continue;
     if constexpr (kEsc) {
-      // escapes beyond the LDS copy of a crowded tile
+      // escapes beyond the LDS copy of a crowded tile, four at a time (their loads issued
+      // together, then the x values they select)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        for (uint32_t e = cur[r]; e < st[r + 1]; ++e) {
-          const uint32_t col = a.esc_col[e];
-          const float v = bf16_to_float(a.esc_val[e]);
+        for (uint32_t e = cur[r]; e < st[r + 1]; e += 4) {
+          uint32_t col[4], vb[4];
 #pragma unroll
-          for (int cc = 0; cc < NT; ++cc) {
-            const int mrow = 16 * cc + r16;
-            const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
-            if constexpr (kSepSx) sx[cc][r] += xv;
-            else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
-            qv[cc][r] = fmaf(xv, v, qv[cc][r]);
+          for (int i = 0; i < 4; ++i) {
+            const bool in = e + i < st[r + 1];
+            col[i] = in ? a.esc_col[e + i] : 0xFFFFFFFFu;
+            vb[i] = in ? a.esc_val[e + i] : 0u;
           }
+          float xv[4][NT];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int cc = 0; cc < NT; ++cc) {
+              const int mrow = 16 * cc + r16;
+              const bool use = col[i] >= col0 && col[i] < col1 && mrow < a.m;
+              xv[i][cc] = use ? bf16_to_float(a.x[(int64_t)mrow * a.k + col[i]]) : 0.0f;
+            }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (col[i] < col0 || col[i] >= col1) continue;
+            const float v = bf16_to_float(vb[i]);
+#pragma unroll
+            for (int cc = 0; cc < NT; ++cc) {
+              if constexpr (kSepSx) sx[cc][r] += xv[i][cc];
+              else acc[cc][r] = fmaf(-xv[i][cc], kPlaceholder, acc[cc][r]);
+              qv[cc][r] = fmaf(xv[i][cc], v, qv[cc][r]);
+            }
+          }
+          if (col[3] >= col1) break;
         }
       }
     }
@@ -317,7 +377,7 @@ void k_mfma(MfmaArgs a) {
         if (mcol >= a.m) continue;
         const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
                              : acc[cc][r];
-        a.y[mcol * a.ldy + nrow] = v;
+        yout[mcol * a.ldy + nrow] = v;
       }
     }
   }
@@ -344,24 +404,51 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t grid = tiles < di.cus ? tiles : di.cus;
-  const int64_t rounds = (tiles + grid * kWaves - 1) / (grid * kWaves);
+  const int64_t chunks = (k / kTileCols + kChunkBlocks - 1) / kChunkBlocks;
   for (int64_t m0 = 0; m0 < m; m0 += 64) {
     const int mb = (int)((m - m0) < 64 ? (m - m0) : 64);
     const int nt = (mb + 15) / 16;
+    // k ranges (up to two activation tiles): as many as give every wave of the chip a tile when
+    // the shape has few tiles, with at least two x chunks (eight blocks) in each; their partial
+    // outputs must fit the workspace
+    int64_t ranges = 1;
+    if (nt <= 2) {
+      ranges = (int64_t)di.cus * kWaves / tiles;
+      if (ranges > chunks / 2) ranges = chunks / 2;
+      if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes)
+        ranges = (int64_t)(kWorkspaceBytes / ((size_t)mb * n * sizeof(float)));
+      if (ranges < 1) ranges = 1;
+    }
+    const int64_t cps = (chunks + ranges - 1) / ranges;
+    ranges = (chunks + cps - 1) / cps;
+    float* ws = nullptr;
+    if (ranges > 1) {
+      err = workspace(s, &ws);
+      if (err != hipSuccess) return err;
+    }
+    int64_t groups = di.cus / ranges;
+    if (groups > tiles) groups = tiles;
+    if (groups < 1) groups = 1;
     MfmaArgs a;
     a.x = x + m0 * k;
     a.m = mb;
     a.base = p.base; a.ae = p.ae; a.lo = p.lo;
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
     a.w = p.w;
-    a.y = y + m0 * n;
+    a.y = ws ? ws : y + m0 * n;
     a.ldy = n;
     a.n = n; a.k = k;
-    a.rounds = (int)rounds;
-    hipLaunchKernelGGL(pick_kernel(f, nt), dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a);
+    a.rounds = (int)((tiles + groups * kWaves - 1) / (groups * kWaves));
+    a.splits = (int)ranges;
+    a.cps = (int)cps;
+    a.ysplit = (int64_t)mb * n;
+    hipLaunchKernelGGL(pick_kernel(f, nt), dim3((unsigned)(groups * ranges)), dim3(64 * kWaves), 0, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (ws) {
+      err = launch_split_reduce(ws, (int)ranges, (int64_t)mb * n, y + m0 * n, s);
+      if (err != hipSuccess) return err;
+    }
   }
   return hipSuccess;
 }

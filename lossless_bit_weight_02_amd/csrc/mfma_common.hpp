@@ -24,10 +24,13 @@ struct MfmaArgs {
   const uint32_t* esc_col;
   const uint16_t* esc_val;
   const uint16_t* w;   // dense bfloat16 W (baseline), tiled storage
-  float* y;            // y[m][ldy]
+  float* y;            // y[m][ldy]; with splits > 1, split j writes y + j * ysplit
   int64_t ldy;
   int64_t n, k;
   int rounds;          // tiles per wave (the last ones may be empty)
+  int splits;          // k ranges (workgroup b takes range b % splits); 1: the whole row
+  int cps;             // x chunks per k range (the last range may be shorter)
+  int64_t ysplit;      // floats between the partial outputs of consecutive k ranges
 };
 
 constexpr int kWaves = 12;                  // waves per workgroup, one workgroup per CU

@@ -16,6 +16,14 @@ struct DevInfo {
 // Properties of the current device (cached per device id).
 hipError_t dev_info(DevInfo* out);
 
+// Device workspace for the partial sums of split-k GEMMs: kWorkspaceBytes per (device, stream),
+// allocated on the first call that needs it on that stream and kept until the process ends.
+constexpr size_t kWorkspaceBytes = size_t(64) << 20;
+hipError_t workspace(hipStream_t s, float** out);
+
+// y[i] = sum over j = 0 .. splits-1 (in that order) of part[j * cnt + i], i < cnt
+hipError_t launch_split_reduce(const float* part, int splits, int64_t cnt, float* y, hipStream_t s);
+
 // Rows of the padded (tiled) plane storage.
 inline int64_t padded_rows(int64_t n) { return (n + 15) / 16 * 16; }
 

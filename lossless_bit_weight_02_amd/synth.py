@@ -33,6 +33,7 @@ import numpy as np
 
 CHUNK = 4096
 X_STREAM = 0x5EED_0001
+DEVICE_STREAM = 0x5EED_0002
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -165,3 +166,40 @@ def config_weight(name: str, seed: int = 0, index: int = 0, rows=None):
     cfg = CONFIGS[name]
     tid, label, spec = cfg.weights[index]
     return gen_weight(spec, seed, tid, rows), spec, tid
+
+
+def device_seed(seed: int, tensor_id: int) -> int:
+    """63-bit seed of tensor ``tensor_id`` for torch's generator (from numpy's SeedSequence)."""
+    st = np.random.SeedSequence([seed, tensor_id, DEVICE_STREAM]).generate_state(1, np.uint64)[0]
+    return int(st) & ((1 << 63) - 1)
+
+
+def gen_weight_torch(spec: WeightSpec, seed: int = 0, tensor_id: int = 0, device="cpu"):
+    """W [n, k] as a torch bfloat16 tensor, drawn on ``device`` with torch's own generator.
+
+    Same distribution and steps as ``gen_weight`` (per-row scale, z ~ N(0,1) float32, outliers
+    multiplied by 2**out_pow, zeros last, round to nearest even), but a different random stream:
+    torch's generator seeded with ``device_seed(seed, tensor_id)``.  It serves workloads too large
+    to draw on the host in reasonable time (the 64-layer stack holds 2.18e10 weights).
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(seed, tensor_id))
+    n, k = spec.n, spec.k
+    if spec.scale == "lognormal":
+        s = spec.median * torch.exp(spec.sigma * torch.randn(n, generator=g, device=device,
+                                                             dtype=torch.float64))
+    elif spec.scale == "loguniform":
+        lo, hi = np.log10(spec.s_lo), np.log10(spec.s_hi)
+        s = 10.0 ** (lo + (hi - lo) * torch.rand(n, generator=g, device=device, dtype=torch.float64))
+    else:
+        raise ValueError(spec.scale)
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    w *= s.to(torch.float32)[:, None]
+    u = torch.rand((n, k), generator=g, device=device, dtype=torch.float32)
+    w[u < spec.p_out] *= float(2.0 ** spec.out_pow)
+    torch.rand((n, k), generator=g, device=device, dtype=torch.float32, out=u)
+    w[u < spec.p_zero] = 0.0
+    del u
+    return w.to(torch.bfloat16)

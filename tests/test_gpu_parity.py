@@ -254,3 +254,45 @@ def test_gemm_deterministic():
         a = w12.gemm(x, rec, path=path).cpu().numpy()
         b = w12.gemm(x, rec, path=path).cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k,ms,p_zero", [(64, 5120, (1, 3, 8, 16, 32), 0.01),
+                                           (320, 17408, (1, 32), 0.001),
+                                           (48, 5120, (1, 16, 32), 0.05),
+                                           (200, 6144, (2, 20), 0.01)])
+def test_gemm_split_k(n, k, ms, p_zero):
+    """Shapes with few tiles and long rows run as several k ranges whose partial sums are added by
+    a second kernel (k and v projections: 4 tiles of 40 blocks; down projection: 20 tiles of 136
+    blocks; 5% zeros put ~4000 escapes in a tile, past the matrix-core kernel's LDS copy, so
+    ranges also read escapes from memory)."""
+    rng = np.random.default_rng(n + k + len(ms))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < p_zero] = 0
+    w12 = _w12()
+    rec = _encode_check(w, f"split {n}x{k}")
+    for m in ms:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        _gemm_case(w, x, f"split {n}x{k}", rec=rec)
+
+
+def test_gemm_split_k_one_hot_exact():
+    """x = e_c on a split shape returns column c of W exactly for columns at the edges of the k
+    ranges and for escaped columns, on both kernel families."""
+    w12 = _w12()
+    n, k = 64, 5120
+    rng = np.random.default_rng(3)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[:, 1024] = 0
+    w[5, 2047] = 0x4500                       # outlier far above the row's window
+    rec = w12.encode(to_dev(w))
+    cols = [0, 127, 128, 1023, 1024, 1025, 2047, 2048, 3071, 3072, 4095, 4096, 5119]
+    for path, group in (("gemv", 8), ("mfma", len(cols))):
+        for i in range(0, len(cols), group):
+            cs = cols[i:i + group]
+            x = np.zeros((len(cs), k), np.uint16)
+            for j, c in enumerate(cs):
+                x[j, c] = 0x3F80
+            say(f"split one-hot path={path} cols={cs}")
+            y = w12.gemm(to_dev(x), rec, path=path).cpu().numpy().astype(np.float64)
+            assert np.array_equal(y, oracle.bf16_to_f64(w[:, cs]).T), (path, cs)
