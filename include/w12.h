@@ -33,7 +33,18 @@
  * Conventions for every call:
  *   - Pointers named as device memory must be device memory of the current HIP device,
  *     16-byte aligned; the caller owns every buffer and keeps it alive until the stream work
- *     is finished.  The library allocates nothing on the device and keeps no per-call state.
+ *     is finished.  The only device memory the library allocates is the GEMM workspace below;
+ *     it keeps no other per-call state.
+ *   - GEMM workspace: a GEMM call whose shape has too few 16-row tiles to occupy the device
+ *     (for example W [1024, 5120], or [5120, 17408] at up to 32 rows of x) splits each row into
+ *     k ranges whose partial sums go to a 64 MiB device buffer, then adds them in range order.
+ *     The buffer belongs to the (device, stream) pair, is allocated with hipMalloc on the first
+ *     such call on that stream (also while the stream is being captured into a graph: the
+ *     allocation is made under the relaxed capture mode) and is kept until the process ends.
+ *     Calls on one stream are ordered by the stream; a captured graph uses the buffer of the
+ *     stream it was captured on, so replaying it concurrently with other GEMM calls on that
+ *     stream races.  Whether a shape splits depends only on the shape and the device, so
+ *     repeated calls give bit-identical results.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work and return
  *     without synchronising, except w12_encode (see there).
  *   - Arguments are checked on the host before anything is launched; on a non-zero status
