@@ -413,7 +413,8 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     // k ranges in one launch: when the shape has few tiles and long rows (more than 16 blocks per
     // wave of a tile), as many as keep every workgroup slot busy, with at least two blocks per
     // wave in each; at least as many as the LDS needs; their partial outputs must fit the
-    // workspace.  (On shorter rows the second kernel costs more than the ranges gain.)
+    // workspace.  (On shorter rows -- the k and v projections included -- the second kernel
+    // costs more than the ranges gain.)
     int64_t ranges = nkb / ks > 16 ? slots / passes : 1;
     if (ranges > nkb / (2 * ks)) ranges = nkb / (2 * ks);
     const int64_t need = (k + slice - 1) / slice;

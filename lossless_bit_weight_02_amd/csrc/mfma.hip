@@ -7,8 +7,9 @@
 // weights feed v_mfma_f32_16x16x32_bf16 as its A operand -- the register operand of the pages'
 // design (figure-captions page, Fig. 5(b), there for wgmma).
 //
-// Work split.  One workgroup of kWaves waves per CU (twelve waves of up to 168 VGPRs fill the
-// CU's register file).
+// Work split.  One workgroup of W waves per CU: W = 12 (three waves of up to 168 VGPRs per SIMD,
+// 4 blocks in flight each), or for the dense baseline on shapes whose tiles fit one round of
+// 8 waves per CU, W = 8 (two waves of up to 256 VGPRs per SIMD, 8 blocks in flight each).
 // A wave owns one 16-row tile at a time and streams all of its 128-column blocks; tiles are dealt
 // round-robin over the workgroups first, so every CU gets the same number of tiles to within one
 // (the weight stream is the bottleneck, and a CU with one more workgroup than the rest would set
@@ -54,20 +55,21 @@ namespace w12 {
 // Compile-time shape of one instantiation: D weight blocks in flight per wave (as many as the
 // 168 VGPRs allow), chunks of S k-blocks of x (a multiple of D).  Four k-blocks per chunk
 // measured faster than eight at one tile.
-constexpr int kChunkBlocks = 4;   // k-blocks per x chunk (both instantiations)
+constexpr int kChunkBlocks = 4;   // k-blocks per x chunk with 12 waves (8 with 8 waves)
 // Escapes of one tile copied to LDS: a 16-row tile of a 17408-column row holds ~315 escapes at
 // the synthetic projections' escape rate (zeros dominate), ~20 at the pages' rate.
 constexpr int kEscCapM = 384;
 constexpr int kEscStage = 128;    // of which staged through registers with the first loads
 
-template <int FMT, int NT>
+template <int FMT, int NT, int W>
 struct Shape {
   static_assert(NT == 1 || NT == 2, "three and four tiles run k_mfma_wide");
-  static constexpr int D = 4;
-  static constexpr int S = kChunkBlocks;              // k-blocks per x chunk
+  static_assert(W == 12 || W == 8, "12 or 8 waves per workgroup");
+  static constexpr int D = W == 12 ? 4 : 8;           // blocks in flight per wave
+  static constexpr int S = W == 12 ? kChunkBlocks : 8;   // k-blocks per x chunk
   static constexpr int FS = 4 * NT;                   // 1 KiB x fragments per k-block
   static constexpr int F = FS * S;                    // 1 KiB x fragments per chunk
-  static constexpr int FW = (F + kWaves - 1) / kWaves;   // fragments a wave loads per chunk
+  static constexpr int FW = (F + W - 1) / W;          // fragments a wave loads per chunk
   static constexpr int FPS = (FW + S - 1) / S;         // fragment loads per step
   static constexpr int LS = (FW + FPS - 1) / FPS - 1;   // last step with a fragment load
   static_assert(S % D == 0 && S % 2 == 0, "a chunk must hold whole rings and 256-column pieces");
@@ -83,11 +85,11 @@ __device__ __forceinline__ void vm_wait_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// Twelve waves (three per SIMD) on the CU: at most 168 VGPRs.
-template <int FMT, int NT>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// W waves (W / 4 per SIMD) on the CU: at most 168 VGPRs with 12, 256 with 8.
+template <int FMT, int NT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void k_mfma(MfmaArgs a) {
-  using SH = Shape<FMT, NT>;
+  using SH = Shape<FMT, NT, W>;
   constexpr int D = SH::D, S = SH::S, F = SH::F, FW = SH::FW, FPS = SH::FPS, LS = SH::LS;
   constexpr bool kEsc = FMT != kFmtBF16;
   // x sums of escaped slots in registers of their own (up to two activation tiles; beyond that
@@ -95,9 +97,9 @@ void k_mfma(MfmaArgs a) {
   constexpr bool kSepSx = true;    // escape x sums kept apart from the accumulators
   constexpr int kLoadsPerStep = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
-  __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * kWaves > F) ? 64 : 1];   // target of unused fragment loads
-  __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCapM : 1];   // per wave: tile escapes
-  __shared__ uint16_t s_eval[kEsc ? kWaves : 1][kEsc ? kEscCapM : 1];
+  __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * W > F) ? 64 : 1];   // target of unused fragment loads
+  __shared__ uint32_t s_ecol[kEsc ? W : 1][kEsc ? kEscCapM : 1];   // per wave: tile escapes
+  __shared__ uint16_t s_eval[kEsc ? W : 1][kEsc ? kEscCapM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
@@ -131,8 +133,8 @@ void k_mfma(MfmaArgs a) {
   // and rows past m and columns past k read zeros.
   const uint32_t prow = (uint32_t)lane >> 5, pslot = (uint32_t)lane & 31u;
   const auto x_fetch_one = [&](uint32_t c, uint32_t buf, int i) {
-    const uint32_t P = (uint32_t)(w + kWaves * i);
-    const bool real = FW * kWaves <= F || P < (uint32_t)F;
+    const uint32_t P = (uint32_t)(w + W * i);
+    const bool real = FW * W <= F || P < (uint32_t)F;
     const uint32_t q = P % (8u * NT), hb = P / (8u * NT);
     const uint32_t row = 2u * q + prow;
     const uint32_t c16 = (pslot - row) & 31u;
@@ -160,15 +162,14 @@ void k_mfma(MfmaArgs a) {
     }
 
   for (int round = 0; round < a.rounds; ++round) {
-    const int64_t tile = ((int64_t)round * kWaves + w) * n_grp + grp;
+    const int64_t tile = ((int64_t)round * W + w) * n_grp + grp;
     const bool valid = tile < tiles;
     const int64_t row0 = (valid ? tile : 0) * kTileRows;
 
     lds_barrier();                                 // the previous tile no longer reads LDS
 
-    // ---- escape list of the tile (oldest loads: waited for before the loop) ----
+    // ---- row bounds and window bottoms of the tile's escapes (oldest loads) ----
     uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0, t_cnt = 0;
-    uint32_t ecol[kEscStage / 64], evalv[kEscStage / 64];
     if constexpr (kEsc) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
@@ -178,21 +179,6 @@ void k_mfma(MfmaArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
-      t_e0 = __builtin_amdgcn_readfirstlane(a.esc_ptr[row0]);
-      const uint32_t t_e1 = __builtin_amdgcn_readfirstlane(valid ? ptr_at(row0 + kTileRows) : t_e0);
-      const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCapM ? t_e1 - t_e0 : (uint32_t)kEscCapM;
-      t_cnt = cnt;
-      const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
-      const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
-#pragma unroll
-      for (int i = 0; i < kEscStage / 64; ++i) {
-        ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
-        evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
-      }
-      if (!valid) {
-#pragma unroll
-        for (int r = 0; r < 5; ++r) st[r] = t_e0;
-      }
     }
 
     // ---- the range's first chunk of x, straight into LDS buffer 0 ----
@@ -218,17 +204,36 @@ void k_mfma(MfmaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // ---- the tile's escape list into LDS (its loads go out after the ring's, so the ring is
+    // not held behind the wait for the row bounds; waiting for them waits for the ring, which
+    // the first step needs anyway) ----
     if constexpr (kEsc) {
+      // escape range of the tile: row0's start (lane 0, g = 0) and row0 + 16's (lane 48, g = 3)
+      t_e0 = __builtin_amdgcn_readfirstlane(st[0]);
+      const uint32_t t_e1 = valid ? (uint32_t)__builtin_amdgcn_readlane((int)st[4], 48) : t_e0;
+      const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCapM ? t_e1 - t_e0 : (uint32_t)kEscCapM;
+      t_cnt = cnt;
+      const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
+      const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
+      uint32_t ecol[kEscStage / 64], evalv[kEscStage / 64];
+#pragma unroll
+      for (int i = 0; i < kEscStage / 64; ++i) {
+        ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
+        evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < kEscStage / 64; ++i) {
         s_ecol[w][lane + 64 * i] = ecol[i];
         s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
       }
-      // a crowded tile: the rest of the LDS copy (these loads were issued after the ring's, so
-      // their wait also covers the ring)
+      // a crowded tile: the rest of the LDS copy
       for (uint32_t i = kEscStage + (uint32_t)lane; i < t_cnt; i += 64) {
         s_ecol[w][i] = a.esc_col[t_e0 + i];
         s_eval[w][i] = a.esc_val[t_e0 + i];
+      }
+      if (!valid) {
+#pragma unroll
+        for (int r = 0; r < 5; ++r) st[r] = t_e0;
       }
     }
     vm_wait_le<D * kLoadsPerStep>();   // chunk 0 is in LDS
@@ -386,16 +391,21 @@ void k_mfma(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int W>
 static MfmaKernel pick(int nt) {
   if (nt >= 3) return mfma_wide_kernel(static_cast<Fmt>(FMT), nt);
-  return nt == 1 ? k_mfma<FMT, 1> : k_mfma<FMT, 2>;
+  return nt == 1 ? k_mfma<FMT, 1, W> : k_mfma<FMT, 2, W>;
 }
 
-static MfmaKernel pick_kernel(Fmt f, int nt) {
-  if (f == kFmtW12) return pick<kFmtW12>(nt);
-  if (f == kFmtQ8) return pick<kFmtQ8>(nt);
-  return pick<kFmtBF16>(nt);
+static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
+  if (waves == 8) {
+    if (f == kFmtW12) return pick<kFmtW12, 8>(nt);
+    if (f == kFmtQ8) return pick<kFmtQ8, 8>(nt);
+    return pick<kFmtBF16, 8>(nt);
+  }
+  if (f == kFmtW12) return pick<kFmtW12, 12>(nt);
+  if (f == kFmtQ8) return pick<kFmtQ8, 12>(nt);
+  return pick<kFmtBF16, 12>(nt);
 }
 
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
@@ -404,21 +414,33 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t chunks = (k / kTileCols + kChunkBlocks - 1) / kChunkBlocks;
+  const int64_t kb = k / kTileCols;
   for (int64_t m0 = 0; m0 < m; m0 += 64) {
     const int mb = (int)((m - m0) < 64 ? (m - m0) : 64);
     const int nt = (mb + 15) / 16;
-    // k ranges (up to two activation tiles): as many as give every wave of the chip a tile when
-    // the shape has few tiles, with at least two x chunks (eight blocks) in each; their partial
-    // outputs must fit the workspace
+    // Up to two activation tiles: the dense baseline runs 8 waves per CU with 8 blocks in flight
+    // when every tile fits one round of them (measured faster there), the W12 and Q8 kernels
+    // always 12 waves with 4 (their decode needs three waves per SIMD to hide: 8 waves measured
+    // 49 us against 39 us on W [17408, 5120] at 32 rows).  k ranges: as many as give every wave
+    // a tile when the shape has few tiles (and at least 3), with at least 8 blocks in each;
+    // their partial outputs must fit the workspace.
+    int waves = kWaves;
+    int64_t chunk_blocks = kChunkBlocks;
     int64_t ranges = 1;
     if (nt <= 2) {
-      ranges = (int64_t)di.cus * kWaves / tiles;
-      if (ranges > chunks / 2) ranges = chunks / 2;
+      if (f == kFmtBF16 && tiles <= (int64_t)di.cus * 8) {
+        waves = 8;
+        chunk_blocks = 8;
+      }
+      const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
+      ranges = (int64_t)di.cus * waves / tiles;
+      const int64_t cap = chunks * chunk_blocks / 8;
+      if (ranges > cap) ranges = cap;
       if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes)
         ranges = (int64_t)(kWorkspaceBytes / ((size_t)mb * n * sizeof(float)));
-      if (ranges < 1) ranges = 1;
+      if (ranges < 3) ranges = 1;
     }
+    const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
     const int64_t cps = (chunks + ranges - 1) / ranges;
     ranges = (chunks + cps - 1) / cps;
     float* ws = nullptr;
@@ -438,11 +460,12 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     a.y = ws ? ws : y + m0 * n;
     a.ldy = n;
     a.n = n; a.k = k;
-    a.rounds = (int)((tiles + groups * kWaves - 1) / (groups * kWaves));
+    a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
     a.splits = (int)ranges;
     a.cps = (int)cps;
     a.ysplit = (int64_t)mb * n;
-    hipLaunchKernelGGL(pick_kernel(f, nt), dim3((unsigned)(groups * ranges)), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL(pick_kernel(f, nt, waves), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
+                       s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ws) {
