@@ -193,9 +193,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     }
   };
   // x first (loads complete in issue order: x queued behind the weight stream would hold the
-  // workgroup's first barrier until the first blocks arrived), then the weight stream, then the
-  // first escape bounds.  The first kXF words per thread cover x of every shape with
-  // 2 m kn <= 16 KiB; the rest (long rows) is copied after.
+  // workgroup's first barrier until the first blocks arrived), then the first tile's escape
+  // bounds (so the escape entries, whose addresses need them, can go out right after the
+  // barrier without waiting for the weight stream), then the weight stream.  The first kXF words
+  // per thread cover x of every shape with 2 m kn <= 16 KiB; the rest (long rows) is copied
+  // after.
   constexpr int kXF = 4;
   const Rsrc r_x = make_rsrc(a.x, (uint32_t)(M * a.ldx * 2));
   u32x4 xv[kXF];
@@ -205,6 +207,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     xv[q] = __builtin_amdgcn_raw_buffer_load_b128(
         r_x, i < M * kn8 ? (uint32_t)(2 * (m * a.ldx + k0 + 8 * j)) : kOOB, 0, 0);
   }
+  uint32_t te0 = 0;
+  if constexpr (kEsc) esc_bounds(pass, ce0, ce1, te0, cbase);
   __builtin_amdgcn_sched_barrier(0);
   BlockRegs<FMT> buf[D];
 #pragma unroll
@@ -212,8 +216,6 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     load_block<FMT>(cur, blk(d), lane16, buf[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  uint32_t te0 = 0;
-  if constexpr (kEsc) esc_bounds(pass, ce0, ce1, te0, cbase);
 #pragma unroll
   for (int q = 0; q < kXF; ++q) {
     const int i = tid + q * kBlock;

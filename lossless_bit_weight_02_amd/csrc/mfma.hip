@@ -249,17 +249,33 @@ void k_mfma(MfmaArgs a) {
     for (int r = 0; r < 4; ++r) {
       cur[r] = st[r];
       ncol[r] = 0xFFFFFFFFu;
-      if constexpr (kEsc) {
-        // first escape of the row at or right of col0 (the run is sorted by column)
-        uint32_t lo = cur[r], hi = run_end(r);
-        while (lo < hi) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (s_ecol[w][mid - t_e0] < col0) lo = mid + 1;
-          else hi = mid;
+    }
+    if constexpr (kEsc) {
+      // first escape at or right of col0 of each row (runs are sorted by column): the four
+      // binary searches in lockstep, branch-free, so each halving issues its four LDS reads
+      // together (a run in LDS has at most kEscCapM < 2^9 entries); none for the first range
+      uint32_t hi[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hi[r] = run_end(r);
+#pragma unroll
+      for (int it = 0; it < (col0 > 0 ? 9 : 0); ++it) {
+        uint32_t v[4], mid[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mid[r] = (cur[r] + hi[r]) >> 1;
+          const uint32_t at = mid[r] - t_e0;
+          v[r] = s_ecol[w][at < (uint32_t)kEscCapM ? at : 0u];
         }
-        cur[r] = lo;
-        ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool open = cur[r] < hi[r];
+          const bool right = v[r] < col0;
+          cur[r] = open && right ? mid[r] + 1 : cur[r];
+          hi[r] = open && !right ? mid[r] : hi[r];
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
     }
 
     floatx4 acc[NT];
