@@ -264,6 +264,46 @@ def stack_bench(dev, stream, layers, reps, sample_layer):
             samples.append((f"stack {entries[i][1]} w12 m={m}", xs[recs[i].k][0][:m], wrows,
                             ys[i][:, :128].cpu().numpy()))
         del ys, yb
+
+    # The same layers as an inference engine lays them out: q, k, v stacked into one qkv matrix and
+    # gate, up into one gate_up matrix (they read the same activations), 4 launches per layer.
+    # The stacked W12 records come from w12_concat_rows (no re-encoding); the stacked dense tiles
+    # are the parts' tiles back to back (the tiled order is row-tile-major).
+    assert n_proj == 7
+    frecs, ftiles = [], []
+    for l in range(layers):
+        r = recs[l * 7:(l + 1) * 7]
+        t = tiles[l * 7:(l + 1) * 7]
+        for grp in ((0, 1, 2), (3,), (4, 5), (6,)):
+            if len(grp) == 1:
+                frecs.append(r[grp[0]])
+                ftiles.append(t[grp[0]])
+            else:
+                frecs.append(w12.concat_rows([r[g] for g in grp]))
+                ftiles.append(w12.Bf16Tiles(sum(t[g].n for g in grp), t[grp[0]].k,
+                                            torch.cat([t[g].data for g in grp])))
+    fused = {"layout": "per layer: qkv [8192,5120], o [5120,6144], gate_up [34816,5120], down [5120,17408]"}
+    for m in (1, 32):
+        ys = [torch.empty((m, r.n), dtype=torch.float32, device=dev) for r in frecs]
+        yb = [torch.empty((m, t.n), dtype=torch.float32, device=dev) for t in ftiles]
+        xm = {k: v[1][:m] for k, v in xs.items()}
+        w12_fns = [lambda i=i: w12.gemm(xm[frecs[i].k], frecs[i], out=ys[i]) for i in range(len(frecs))]
+        bf_fns = [lambda i=i: w12.bf16_gemm(xm[ftiles[i].k], ftiles[i], out=yb[i]) for i in range(len(ftiles))]
+        b_w12 = sum(w12_bytes(r.n, r.k, r.n_esc, m) for r in frecs)
+        b_bf = sum(bf16_bytes(t.n, t.k, m) for t in ftiles)
+        row = {}
+        for name, fns, outs, byt in (("w12", w12_fns, ys, b_w12), ("bf16", bf_fns, yb, b_bf)):
+            g = capture_graph(fns, outs)
+            t_g = time_graph(g, stream, reps)
+            del g
+            row[f"{name}_ms_graph"] = round(t_g * 1e3, 4)
+            row[f"{name}_gbs_graph"] = round(byt / t_g / 1e9, 1)
+        row["w12_frac_hbm_graph"] = round(row["w12_gbs_graph"] / HBM_PEAK_GBS, 4)
+        row["speedup_vs_bf16_graph"] = round(row["bf16_ms_graph"] / row["w12_ms_graph"], 4)
+        fused[f"m{m}"] = row
+        del ys, yb
+    out["fused_layout"] = fused
+    del frecs, ftiles
     return out, samples
 
 

@@ -133,6 +133,23 @@ int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, ui
                 void *stream);
 
 /*
+ * w12_concat_rows -- the record of W = [W_0; W_1; ...; W_{count-1}] (the parts' rows stacked in
+ * order) built on the device from the parts' records, without decoding or re-encoding.  Windows
+ * and escape lists are per output row (figure-captions page, Fig. 5(a)), so the stacked record is
+ * the parts' window bottoms, planes and escapes side by side, with the escape offsets rebased; it
+ * is byte-identical to w12_encode of the stacked matrix.  Used to run projections that read the
+ * same activations (q, k and v; gate and up) as one GEMM.
+ * parts: host array of `count` (1..64) records; every part has the same k, and every part but
+ * the last has n % 16 == 0 (whole 16-row tiles of the storage order).  out: a record whose n is
+ * the sum of the parts' n and whose arrays are sized for it (ae npad*k, lo npad*k/2, base n,
+ * esc_ptr n+1, esc_col/esc_val esc_cap entries).  Synchronises `stream` once to read the parts'
+ * escape totals into *n_esc (host); if out->esc_cap is smaller, returns W12_ERR_CAPACITY before
+ * writing anything.  The parts must not overlap `out`.
+ */
+int w12_concat_rows(const w12_weight *parts, int count, w12_weight *out, uint64_t *n_esc,
+                    void *stream);
+
+/*
  * w12_bf16_gemm -- same-build dense baseline: y = x * W^T with W bfloat16 in the same tiled
  * storage order as the W12 planes (npad * k values, from w12_bf16_to_tiles), same kernel
  * structure and flags as w12_gemm, 2 bytes per weight.

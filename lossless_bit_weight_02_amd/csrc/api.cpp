@@ -204,6 +204,66 @@ int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, ui
   return run_gemm(w12::kFmtQ8, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream);
 }
 
+int w12_concat_rows(const w12_weight* parts, int count, w12_weight* out, uint64_t* n_esc, void* stream) {
+  if (!parts || !out || !n_esc) return fail(W12_ERR_ARG, "parts, out or n_esc is NULL");
+  if (count < 1 || count > 64) return fail(W12_ERR_ARG, "count must be 1..64 (count=%d)", count);
+  int rc = check_record(out, true);
+  if (rc) return rc;
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    rc = check_record(&parts[i], true);
+    if (rc) return rc;
+    if (parts[i].k != out->k) return fail(W12_ERR_SHAPE, "part %d has k=%lld, out has k=%lld", i,
+                                          (long long)parts[i].k, (long long)out->k);
+    if (i + 1 < count && parts[i].n % 16 != 0)
+      return fail(W12_ERR_SHAPE, "part %d has n=%lld, not a multiple of 16 (only the last part may be)", i,
+                  (long long)parts[i].n);
+    rows += parts[i].n;
+  }
+  if (rows != out->n) return fail(W12_ERR_ARG, "out->n=%lld but the parts hold %lld rows",
+                                  (long long)out->n, (long long)rows);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t tot[64];
+  for (int i = 0; i < count; ++i) {
+    hipError_t e = hipMemcpyAsync(&tot[i], parts[i].esc_ptr + parts[i].n, sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "escape total copy");
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "concat synchronisation");
+  uint64_t total = 0;
+  for (int i = 0; i < count; ++i) total += tot[i];
+  *n_esc = total;
+  if (total >= 0xFFFFFFFFull) return fail(W12_ERR_RANGE, "escape total does not fit the 32-bit CSR");
+  if (out->esc_cap < total)
+    return fail(W12_ERR_CAPACITY, "esc_cap %llu < escape total %llu", (unsigned long long)out->esc_cap,
+                (unsigned long long)total);
+  const int64_t k = out->k;
+  int64_t r0 = 0;
+  uint64_t e0 = 0;
+  for (int i = 0; i < count; ++i) {
+    const w12_weight& p = parts[i];
+    const int64_t np = w12::padded_rows(p.n);
+    const struct { void* dst; const void* src; size_t bytes; } cp[] = {
+        {out->base + r0, p.base, (size_t)p.n},
+        {out->ae + r0 * k, p.ae, (size_t)(np * k)},
+        {out->lo + r0 * k / 2, p.lo, (size_t)(np * k / 2)},
+        {out->esc_col + e0, p.esc_col, (size_t)tot[i] * 4},
+        {out->esc_val + e0, p.esc_val, (size_t)tot[i] * 2},
+    };
+    for (const auto& c : cp) {
+      if (c.bytes == 0) continue;
+      e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "concat copy");
+    }
+    e = w12::launch_rebase(p.esc_ptr, p.n + 1, (uint32_t)e0, out->esc_ptr + r0, s);
+    if (e != hipSuccess) return hip_fail(e, "escape offset launch");
+    r0 += p.n;
+    e0 += tot[i];
+  }
+  return ok();
+}
+
 int w12_bf16_gemm(const uint16_t* x, int64_t m, const uint16_t* w, int64_t n, int64_t k, float* y,
                   uint32_t flags, void* stream) {
   if (!w) return fail(W12_ERR_ARG, "w is NULL");

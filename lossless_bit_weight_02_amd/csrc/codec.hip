@@ -375,6 +375,22 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
   return hipGetLastError();
 }
 
+// Escape offsets of one part of a row-stacked record: its CSR shifted by the escapes of the parts
+// before it.
+__global__ __launch_bounds__(kBlock) void k_rebase(const uint32_t* __restrict__ src, int64_t cnt,
+                                                   uint32_t add, uint32_t* __restrict__ dst) {
+  const int64_t step = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < cnt; i += step) dst[i] = src[i] + add;
+}
+
+hipError_t launch_rebase(const uint32_t* src, int64_t cnt, uint32_t add, uint32_t* dst, hipStream_t s) {
+  int64_t blocks = (cnt + kBlock - 1) / kBlock;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_rebase, dim3((unsigned)blocks), dim3(kBlock), 0, s, src, cnt, add, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t s) {
   DevInfo di;
   hipError_t err = dev_info(&di);

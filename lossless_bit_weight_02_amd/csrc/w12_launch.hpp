@@ -48,6 +48,8 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
                        uint16_t* esc_val, hipStream_t s);
 // decoder: planes -> bfloat16 bits, then every escape written over its slot
 hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
+// dst[i] = src[i] + add, i < cnt (escape offsets of a part placed after earlier parts)
+hipError_t launch_rebase(const uint32_t* src, int64_t cnt, uint32_t add, uint32_t* dst, hipStream_t s);
 // dense bf16 [n][k] -> tiled storage order (baseline layout)
 hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
 // bandwidth probe

@@ -54,6 +54,9 @@ EXPORTS = {
                                 ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_q8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                    ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_concat_rows": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_int,
+                                       ctypes.POINTER(_W12Weight), ctypes.POINTER(ctypes.c_uint64),
+                                       ctypes.c_void_p]),
     "w12_bf16_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_uint32, ctypes.c_void_p]),
@@ -185,6 +188,31 @@ def encode(w: torch.Tensor, esc_guess: int | None = None) -> W12Weight:
     _check(st)
     ne = n_esc.value
     return W12Weight(n, k, base, ae, lo, esc_ptr, esc_col[:ne], esc_val[:ne])
+
+
+def concat_rows(parts) -> W12Weight:
+    """Record of the row-stacked matrix [W_0; W_1; ...] from the parts' records (same k; every part
+    but the last with n % 16 == 0), built on the device without re-encoding."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no parts")
+    dev = parts[0].device
+    k = parts[0].k
+    n = sum(p.n for p in parts)
+    ne = sum(p.n_esc for p in parts)
+    npad = padded_rows(n)
+    u8 = torch.uint8
+    out = W12Weight(n, k, torch.empty(n, dtype=u8, device=dev), torch.empty(npad * k, dtype=u8, device=dev),
+                    torch.empty(npad * k // 2, dtype=u8, device=dev),
+                    torch.empty(n + 1, dtype=torch.int32, device=dev),
+                    torch.empty(max(1, ne), dtype=torch.int32, device=dev)[:ne],
+                    torch.empty(max(1, ne), dtype=torch.int16, device=dev)[:ne])
+    arr = (_W12Weight * len(parts))(*[p.c_struct() for p in parts])
+    s = out.c_struct()
+    s.esc_cap = ne
+    n_esc = ctypes.c_uint64(0)
+    _check(lib().w12_concat_rows(arr, len(parts), ctypes.byref(s), ctypes.byref(n_esc), _stream_handle(dev)))
+    return out
 
 
 def decode_into(wt: W12Weight, out: torch.Tensor) -> torch.Tensor:

@@ -82,3 +82,28 @@ def test_argument_errors_are_host_side():
     assert L.w12_decode(ctypes.byref(_rec(n=1 << 40)), 0x1000, None) == w12.W12_ERR_RANGE
     assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec(k=(1 << 24) + 128)), 0x1000, 0, None) == w12.W12_ERR_RANGE
     assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, (1 << 24) + 128, 0x1000, 0, None) == w12.W12_ERR_RANGE
+
+
+def test_concat_rows_argument_errors_are_host_side():
+    """w12_concat_rows rejects bad part lists before any device access (fake device pointers)."""
+    L = _lib()
+    n_esc = ctypes.c_uint64(0)
+
+    def parts(*ns, k=128):
+        return (w12._W12Weight * len(ns))(*[_rec(n=n, k=k) for n in ns])
+
+    assert L.w12_concat_rows(None, 1, ctypes.byref(_rec()), ctypes.byref(n_esc), None) == w12.W12_ERR_ARG
+    assert L.w12_concat_rows(parts(16), 0, ctypes.byref(_rec(n=16)), ctypes.byref(n_esc), None) == w12.W12_ERR_ARG
+    assert L.w12_concat_rows(parts(16), 65, ctypes.byref(_rec(n=16)), ctypes.byref(n_esc), None) == w12.W12_ERR_ARG
+    # a part other than the last is not whole 16-row tiles
+    assert L.w12_concat_rows(parts(20, 16), 2, ctypes.byref(_rec(n=36)), ctypes.byref(n_esc),
+                             None) == w12.W12_ERR_SHAPE
+    assert b"multiple of 16" in L.w12_last_error()
+    # parts disagree on k
+    mixed = (w12._W12Weight * 2)(_rec(n=16, k=128), _rec(n=16, k=256))
+    assert L.w12_concat_rows(mixed, 2, ctypes.byref(_rec(n=32)), ctypes.byref(n_esc), None) == w12.W12_ERR_SHAPE
+    # out->n is not the parts' total
+    assert L.w12_concat_rows(parts(16, 5), 2, ctypes.byref(_rec(n=20)), ctypes.byref(n_esc), None) == w12.W12_ERR_ARG
+    # misaligned part plane
+    bad = (w12._W12Weight * 2)(_rec(n=16), _rec(n=16, ae=0x2004))
+    assert L.w12_concat_rows(bad, 2, ctypes.byref(_rec(n=32)), ctypes.byref(n_esc), None) == w12.W12_ERR_ALIGN

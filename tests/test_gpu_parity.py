@@ -296,3 +296,26 @@ def test_gemm_split_k_one_hot_exact():
             say(f"split one-hot path={path} cols={cs}")
             y = w12.gemm(to_dev(x), rec, path=path).cpu().numpy().astype(np.float64)
             assert np.array_equal(y, oracle.bf16_to_f64(w[:, cs]).T), (path, cs)
+
+
+@pytest.mark.parametrize("ns,k", [((48, 16, 37), 256), ((16,), 128), ((64, 32, 32, 128), 640)])
+def test_concat_rows_equals_encode_of_stacked(ns, k):
+    """The record built from the parts' records equals, byte for byte, the encoder's record of the
+    stacked matrix; the fused GEMM then matches the oracle."""
+    w12 = _w12()
+    rng = np.random.default_rng(sum(ns) + k)
+    parts = []
+    for n in ns:
+        w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02 * rng.uniform(0.1, 3)).astype(np.float32))
+        w[rng.random((n, k)) < 0.02] = 0
+        parts.append(w)
+    stacked = np.concatenate(parts, axis=0)
+    recs = [w12.encode(to_dev(w)) for w in parts]
+    say(f"concat {ns} k={k}")
+    fused = w12.concat_rows(recs)
+    assert fused.n_esc == sum(r.n_esc for r in recs)
+    assert_records_equal(record_numpy(fused), oracle.encode(stacked), f"concat {ns}")
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, k)).astype(np.float32))
+    for path in ("gemv", "mfma"):
+        y = w12.gemm(to_dev(x), fused, path=path).cpu().numpy()
+        check_gemm(y, x, stacked, f"concat gemm {path}")
