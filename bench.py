@@ -176,6 +176,57 @@ def attn_bench(dev, stream, min_rot_bytes, reps):
     return out, samples
 
 
+def lm_head_bench(dev, stream, reps):
+    """LM-head-like W [152064, 5120] at M=16: the Q pass on the 8-bit view and the exact pass, as
+    full outputs and as top-1 per row (no logits written), and the same-build BF16 kernel; each
+    timed as a captured HIP graph of back-to-back launches (the 1.17 GB record streams from HBM
+    on every launch).  Reports the Q pass's top-1 agreement with the exact pass on these inputs.
+    Weights drawn on the GPU (synth.gen_weight_torch)."""
+    import torch
+    from lossless_bit_weight_02_amd import synth, w12
+
+    tid, _, spec = synth.CONFIGS["lm_head"].weights[0]
+    n, k, m = spec.n, spec.k, 16
+    w = synth.gen_weight_torch(spec, 0, tid, dev)
+    rec = w12.encode(w)
+    tiles = w12.bf16_tiles(w)
+    keep = w[:128].view(torch.int16).cpu().numpy().view(np.uint16)
+    del w
+    x_bits = synth.gen_x(m, k, tensor_id=tid)
+    x = to_dev_bits(x_bits, dev)
+    yq = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ye = torch.empty_like(yq)
+    yb = torch.empty_like(yq)
+    tq = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
+    te = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
+    cases = (("q8_m16", lambda: w12.q8_gemm(x, rec, out=yq), [yq], q8_bytes(n, k, rec.n_esc, m)),
+             ("w12_m16", lambda: w12.gemm(x, rec, out=ye), [ye], w12_bytes(n, k, rec.n_esc, m)),
+             ("q8_top1_m16", lambda: w12.q8_top1(x, rec, out=tq), list(tq),
+              q8_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
+             ("w12_top1_m16", lambda: w12.gemm_top1(x, rec, out=te), list(te),
+              w12_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
+             ("bf16_m16", lambda: w12.bf16_gemm(x, tiles, out=yb), [yb], bf16_bytes(n, k, m)))
+    out = {"n": n, "k": k, "m": m, "escapes": rec.n_esc, "launches_per_graph": 8}
+    for name, fn, outs, byt in cases:
+        g = capture_graph([fn] * 8, outs)
+        t = time_graph(g, stream, reps) / 8
+        del g
+        out[f"{name}_us"] = round(t * 1e6, 2)
+        out[f"{name}_gbs"] = round(byt / t / 1e9, 1)
+    out["q8_frac_hbm"] = round(out["q8_m16_gbs"] / HBM_PEAK_GBS, 4)
+    out["w12_frac_hbm"] = round(out["w12_m16_gbs"] / HBM_PEAK_GBS, 4)
+    out["q8_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["q8_m16_us"], 4)
+    out["w12_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["w12_m16_us"], 4)
+    iq, ie = tq[0].cpu().numpy(), te[0].cpu().numpy()
+    out["top1_agreement_q8_vs_exact"] = f"{int((iq == ie).sum())}/{m}"
+    # the top-1 entry points against the argmax of the full outputs of the same kernels
+    out["top1_matches_full_outputs"] = bool(
+        np.array_equal(iq, yq.argmax(dim=1).cpu().numpy()) and np.array_equal(ie, ye.argmax(dim=1).cpu().numpy()))
+    samples = [("lm_head q8 m=16 (rows 0..127)", x_bits, keep, yq[:, :128].cpu().numpy(), "q8"),
+               ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy())]
+    return out, samples
+
+
 def stack_bench(dev, stream, layers, reps, sample_layer):
     """The 27B-class dense stack: `layers` layers of {q, k, v, o, gate, up, down} (tensor id
     8*layer + projection).  Every matrix is drawn on the GPU (synth.gen_weight_torch), encoded,
@@ -350,7 +401,9 @@ def cpu_baseline(w_bits, x_bits, gpu_out, rows, samples=()):
         if not np.all(err <= bound):
             raise SystemExit(f"parity failure in {name}: GPU output outside the bound")
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
-    for label, xb, wb, gy in samples:
+    for label, xb, wb, gy, *view in samples:
+        if view and view[0] == "q8":
+            wb = oracle.q8_view_bits(oracle.encode(wb))
         y = oracle.gemm64(xb, wb)
         bound = 1e-3 * oracle.abs_bound64(xb, wb)
         err = np.abs(gy.astype(np.float64) - y)
@@ -381,6 +434,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the M sweep (crossover)")
     ap.add_argument("--no-attn", action="store_true", help="skip the attention-projection section")
     ap.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack section")
+    ap.add_argument("--no-lm-head", action="store_true", help="skip the LM-head Q-pass section")
     ap.add_argument("--stack-layers", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 192 MiB device copy (counter calibration under rocprofv3)")
@@ -573,6 +627,11 @@ def main():
     if not a.no_attn:
         attn, smp = attn_bench(dev, stream, a.min_rot_bytes, reps=20)
         samples += smp
+    lm_head = None
+    if not a.no_lm_head:
+        lm_head, smp = lm_head_bench(dev, stream, reps=10)
+        samples += smp
+        torch.cuda.empty_cache()
     stack = None
     if not a.no_stack:
         stack, smp = stack_bench(dev, stream, a.stack_layers, reps=5,
@@ -622,6 +681,7 @@ def main():
         "sweep": sweep,
         "vendor_bf16_torch_mm": vendor,
         "attn_m1": attn,
+        "lm_head_q_pass": lm_head,
         "stack": stack,
         "setup_s": {"generate": round(t_gen, 2)},
         "kernel_source_sha256_16": kernel_source_hash(),

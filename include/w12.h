@@ -133,6 +133,23 @@ int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, ui
                 void *stream);
 
 /*
+ * w12_q8_top1 / w12_gemm_top1 -- the top-1 output of each row of x, for the Q pass (8-bit view,
+ * as w12_q8_gemm) or the exact pass (as w12_gemm), without writing the [m, n] outputs: the
+ * two-level verification compares only the argmax chain of the cheap pass with the exact one
+ * (figure-captions page, Fig. 7; summary page, Main Findings: 98.7% top-1 agreement).
+ * idx[j] (int32, device) = the n at which y[j][n] is largest, ties to the smallest n; val[j]
+ * (float, device) = that y[j][n], computed exactly as the matrix-core path of w12_q8_gemm /
+ * w12_gemm computes it for a shape too large to split (a NaN output counts as the largest).
+ * Runs the matrix-core kernel in passes of up to 32 rows of x (each pass reads the weights once)
+ * plus one small kernel per pass; uses the GEMM workspace (see the conventions above).
+ * Same record checks as w12_q8_gemm / w12_gemm; idx and val 4-byte aligned.
+ */
+int w12_q8_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *idx, float *val,
+                void *stream);
+int w12_gemm_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *idx, float *val,
+                  void *stream);
+
+/*
  * w12_concat_rows -- the record of W = [W_0; W_1; ...; W_{count-1}] (the parts' rows stacked in
  * order) built on the device from the parts' records, without decoding or re-encoding.  Windows
  * and escape lists are per output row (figure-captions page, Fig. 5(a)), so the stacked record is

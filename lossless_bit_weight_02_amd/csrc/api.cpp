@@ -204,6 +204,33 @@ int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, ui
   return run_gemm(w12::kFmtQ8, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream);
 }
 
+namespace {
+int run_top1(w12::Fmt f, const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val,
+             void* stream) {
+  if (!x || !idx || !val) return fail(W12_ERR_ARG, "x, idx or val is NULL");
+  if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
+  if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
+  if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned4(idx) || !aligned4(val)) return fail(W12_ERR_ALIGN, "idx and val must be 4-byte aligned");
+  hipError_t e = w12::launch_mfma_top1(f, x, m, planes_of(wt), wt->n, wt->k, idx, val,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "top-1 launch");
+  return ok();
+}
+}  // namespace
+
+int w12_gemm_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val, void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  return run_top1(w12::kFmtW12, x, m, wt, idx, val, stream);
+}
+
+int w12_q8_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val, void* stream) {
+  int rc = check_record(wt, false);
+  if (rc) return rc;
+  return run_top1(w12::kFmtQ8, x, m, wt, idx, val, stream);
+}
+
 int w12_concat_rows(const w12_weight* parts, int count, w12_weight* out, uint64_t* n_esc, void* stream) {
   if (!parts || !out || !n_esc) return fail(W12_ERR_ARG, "parts, out or n_esc is NULL");
   if (count < 1 || count > 64) return fail(W12_ERR_ARG, "count must be 1..64 (count=%d)", count);

@@ -450,7 +450,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
       hipLaunchKernelGGL(kern, dim3((unsigned)(groups * ranges)), dim3(kBlock), (size_t)2 * mb * rlen, s, a);
       err = hipGetLastError();
       if (err != hipSuccess) return err;
-      err = launch_split_reduce(ws, (int)ranges, (int64_t)mb * n, y + m0 * n, s);
+      err = launch_split_reduce(ws, (int)ranges, mb, n, y + m0 * n, n, s);
       if (err != hipSuccess) return err;
       continue;
     }

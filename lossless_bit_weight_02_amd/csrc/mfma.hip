@@ -86,7 +86,8 @@ __device__ __forceinline__ void vm_wait_le() {
 }
 
 // W waves (W / 4 per SIMD) on the CU: at most 168 VGPRs with 12, 256 with 8.
-template <int FMT, int NT, int W>
+// TOP1: the top-1 mode of MfmaArgs (no y; per-workgroup best keys).
+template <int FMT, int NT, int W, bool TOP1>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void k_mfma(MfmaArgs a) {
   using SH = Shape<FMT, NT, W>;
@@ -160,6 +161,10 @@ void k_mfma(MfmaArgs a) {
       xo[par][t] = 32u * (uint32_t)r16 + ((4u * (uint32_t)g + (uint32_t)r16 + (uint32_t)t) ^ (16u * par));
       asm volatile("" : "+v"(xo[par][t]));
     }
+
+  __shared__ unsigned long long s_best[TOP1 ? 32 : 1];   // top-1 mode: best key per x row
+  if constexpr (TOP1)
+    if (tid < 32) s_best[tid] = 0ull;              // published by the first barrier below
 
   for (int round = 0; round < a.rounds; ++round) {
     const int64_t tile = ((int64_t)round * W + w) * n_grp + grp;
@@ -387,20 +392,80 @@ void k_mfma(MfmaArgs a) {
         }
       }
     }
+    uint64_t best[NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t nrow = row0 + 4 * g + r;
-      if (nrow >= a.n) continue;
-      const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+    for (int cc = 0; cc < NT; ++cc) best[cc] = 0;
+    if constexpr (!TOP1) {
+      // lane (g, r16) holds rows 4 g .. 4 g + 3 of x row 16 cc + r16: written to the wave's part of
+      // the idle x buffer as [x row][20 floats] (4 of padding), read back so that lane l holds
+      // rows 4 (l % 4) .. +3 of x row 16 j + l / 4, and stored as one 16-byte vector (or four
+      // floats when y is not 16-byte aligned).  Every wave is past the last chunk's barrier, and
+      // the next tile's loads into this buffer wait for the barrier at its start.
+      float* res = reinterpret_cast<float*>(&s_x[0][0]) + w * (16 * NT * 20);
 #pragma unroll
       for (int cc = 0; cc < NT; ++cc) {
-        const int mcol = 16 * cc + r16;
-        if (mcol >= a.m) continue;
-        const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
-                             : acc[cc][r];
-        yout[mcol * a.ldy + nrow] = v;
+        float v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r]) : acc[cc][r];
+        }
+        *reinterpret_cast<floatx4*>(&res[(16 * cc + r16) * 20 + 4 * g]) = (floatx4){v4[0], v4[1], v4[2], v4[3]};
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int q = lane & 3;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int mcol = 16 * j + (lane >> 2);
+        const floatx4 o = *reinterpret_cast<const floatx4*>(&res[mcol * 20 + 4 * q]);
+        const int64_t nrow = row0 + 4 * q;
+        if (mcol < a.m) {
+          float* yp = &yout[mcol * a.ldy + nrow];
+          if (a.yvec) {
+            if (nrow < a.n) *reinterpret_cast<floatx4*>(yp) = o;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (nrow + i < a.n) yp[i] = o[i];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t nrow = row0 + 4 * g + r;
+        if (nrow >= a.n) continue;
+        const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+#pragma unroll
+        for (int cc = 0; cc < NT; ++cc) {
+          const int mcol = 16 * cc + r16;
+          if (mcol >= a.m) continue;
+          const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
+                               : acc[cc][r];
+          const uint64_t key = top1_key(v, nrow);
+          best[cc] = key > best[cc] ? key : best[cc];
+        }
       }
     }
+    if constexpr (TOP1) {
+      // the tile's best row per x row: over the four row groups g (lanes r16 + 16 g), then over
+      // the workgroup's waves through LDS
+#pragma unroll
+      for (int cc = 0; cc < NT; ++cc) {
+#pragma unroll
+        for (int sh = 16; sh <= 32; sh *= 2) {
+          const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best[cc], sh, 64);
+          const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best[cc] >> 32), sh, 64);
+          const uint64_t o = ((uint64_t)hi << 32) | lo;
+          best[cc] = o > best[cc] ? o : best[cc];
+        }
+        if (g == 0 && 16 * cc + r16 < a.m) atomicMax(&s_best[16 * cc + r16], (unsigned long long)best[cc]);
+      }
+    }
+  }
+  if constexpr (TOP1) {
+    lds_barrier();
+    if (tid < 32) a.top1[(int64_t)blockIdx.x * 32 + tid] = s_best[tid];
   }
 }
 
@@ -410,7 +475,13 @@ void k_mfma(MfmaArgs a) {
 template <int FMT, int W>
 static MfmaKernel pick(int nt) {
   if (nt >= 3) return mfma_wide_kernel(static_cast<Fmt>(FMT), nt);
-  return nt == 1 ? k_mfma<FMT, 1, W> : k_mfma<FMT, 2, W>;
+  return nt == 1 ? k_mfma<FMT, 1, W, false> : k_mfma<FMT, 2, W, false>;
+}
+
+// top-1 mode: the exact pass or the Q pass, one or two activation tiles, 12 waves
+static MfmaKernel pick_top1(Fmt f, int nt) {
+  if (f == kFmtW12) return nt == 1 ? k_mfma<kFmtW12, 1, kWaves, true> : k_mfma<kFmtW12, 2, kWaves, true>;
+  return nt == 1 ? k_mfma<kFmtQ8, 1, kWaves, true> : k_mfma<kFmtQ8, 2, kWaves, true>;
 }
 
 static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
@@ -424,70 +495,169 @@ static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
   return pick<kFmtBF16, 12>(nt);
 }
 
+// One launch (plus the split-k sum) for mb <= 64 rows of x over the n rows of `p`, output rows
+// y[j * ldy + 0 .. n).
+// Partial sums of a split go to the workspace from byte ws_off on.
+static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb, const Planes& p,
+                            int64_t n, int64_t k, float* y, int64_t ldy, hipStream_t s,
+                            size_t ws_off = 0) {
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t kb = k / kTileCols;
+  const int nt = (mb + 15) / 16;
+  // Up to two activation tiles: the dense baseline runs 8 waves per CU with 8 blocks in flight
+  // when every tile fits one round of them (measured faster there), the W12 and Q8 kernels
+  // always 12 waves with 4 (their decode needs three waves per SIMD to hide: 8 waves measured
+  // 49 us against 39 us on W [17408, 5120] at 32 rows).  k ranges: as many as give every wave
+  // a tile when the shape has few tiles (and at least 3), with at least 8 blocks in each;
+  // their partial outputs must fit the workspace.
+  int waves = kWaves;
+  int64_t chunk_blocks = kChunkBlocks;
+  int64_t ranges = 1;
+  if (nt <= 2) {
+    if (f == kFmtBF16 && tiles <= (int64_t)di.cus * 8) {
+      waves = 8;
+      chunk_blocks = 8;
+    }
+    const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
+    ranges = (int64_t)di.cus * waves / tiles;
+    const int64_t cap = chunks * chunk_blocks / 8;
+    if (ranges > cap) ranges = cap;
+    if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes - ws_off)
+      ranges = (int64_t)((kWorkspaceBytes - ws_off) / ((size_t)mb * n * sizeof(float)));
+    if (ranges < 3) ranges = 1;
+  }
+  const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
+  const int64_t cps = (chunks + ranges - 1) / ranges;
+  ranges = (chunks + cps - 1) / cps;
+  float* ws = nullptr;
+  if (ranges > 1) {
+    hipError_t err = workspace(s, &ws);
+    if (err != hipSuccess) return err;
+    ws += ws_off / sizeof(float);
+  }
+  int64_t groups = di.cus / ranges;
+  if (groups > tiles) groups = tiles;
+  if (groups < 1) groups = 1;
+  MfmaArgs a;
+  a.x = x;
+  a.m = mb;
+  a.base = p.base; a.ae = p.ae; a.lo = p.lo;
+  a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
+  a.w = p.w;
+  a.y = ws ? ws : y;
+  a.ldy = ws ? n : ldy;                        // partial slices are [mb][n], contiguous
+  a.n = n; a.k = k;
+  a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
+  a.splits = (int)ranges;
+  a.cps = (int)cps;
+  a.ysplit = (int64_t)mb * n;
+  a.top1 = nullptr;
+  a.yvec = (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
+  hipLaunchKernelGGL(pick_kernel(f, nt, waves), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
+                     s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ws) return launch_split_reduce(ws, (int)ranges, mb, n, y, ldy, s);
+  return hipSuccess;
+}
+
+// First row of the tail launch (0: none) -- see launch_mfma.
+static int64_t tail_split_row(const DevInfo& di, int mb, int64_t tiles) {
+  const int64_t per_round = (int64_t)di.cus * kWaves;
+  const int64_t full = tiles / per_round, tail = tiles - full * per_round;
+  return mb <= 32 && full >= 1 && tail > 0 && 2 * tail <= per_round ? full * per_round * kTileRows : 0;
+}
+
+// The record's rows r0 .. n as a record of their own (r0 a multiple of 16; escape offsets stay
+// absolute indices into the escape arrays).
+static Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
+  Planes t = p;
+  if (t.base) t.base += r0;
+  if (t.ae) t.ae += r0 * k;
+  if (t.lo) t.lo += r0 * k / 2;
+  if (t.esc_ptr) t.esc_ptr += r0;
+  if (t.w) t.w += r0 * k;
+  return t;
+}
+
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        float* y, hipStream_t s) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t kb = k / kTileCols;
   for (int64_t m0 = 0; m0 < m; m0 += 64) {
     const int mb = (int)((m - m0) < 64 ? (m - m0) : 64);
-    const int nt = (mb + 15) / 16;
-    // Up to two activation tiles: the dense baseline runs 8 waves per CU with 8 blocks in flight
-    // when every tile fits one round of them (measured faster there), the W12 and Q8 kernels
-    // always 12 waves with 4 (their decode needs three waves per SIMD to hide: 8 waves measured
-    // 49 us against 39 us on W [17408, 5120] at 32 rows).  k ranges: as many as give every wave
-    // a tile when the shape has few tiles (and at least 3), with at least 8 blocks in each;
-    // their partial outputs must fit the workspace.
-    int waves = kWaves;
-    int64_t chunk_blocks = kChunkBlocks;
-    int64_t ranges = 1;
-    if (nt <= 2) {
-      if (f == kFmtBF16 && tiles <= (int64_t)di.cus * 8) {
-        waves = 8;
-        chunk_blocks = 8;
-      }
-      const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
-      ranges = (int64_t)di.cus * waves / tiles;
-      const int64_t cap = chunks * chunk_blocks / 8;
-      if (ranges > cap) ranges = cap;
-      if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes)
-        ranges = (int64_t)(kWorkspaceBytes / ((size_t)mb * n * sizeof(float)));
-      if (ranges < 3) ranges = 1;
-    }
-    const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
-    const int64_t cps = (chunks + ranges - 1) / ranges;
-    ranges = (chunks + cps - 1) / cps;
-    float* ws = nullptr;
-    if (ranges > 1) {
-      err = workspace(s, &ws);
+    // A shape with more tiles than the chip's waves runs in rounds of one tile per wave; when the
+    // last round would keep at most half of the waves busy (the LM head: 9504 tiles = 3 rounds
+    // of 3072 and 288), the full rounds run as one launch and the remaining tiles as a second,
+    // split-k launch over the same record's last rows, so they take a fraction of a round.
+    const int64_t r0 = tail_split_row(di, mb, tiles);
+    if (r0 > 0) {
+      err = mfma_pass(f, di, x + m0 * k, mb, p, r0, k, y + m0 * n, n, s);
       if (err != hipSuccess) return err;
+      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, y + m0 * n + r0, n, s);
+    } else {
+      err = mfma_pass(f, di, x + m0 * k, mb, p, n, k, y + m0 * n, n, s);
     }
-    int64_t groups = di.cus / ranges;
-    if (groups > tiles) groups = tiles;
-    if (groups < 1) groups = 1;
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n,
+                            int64_t k, int32_t* idx, float* val, hipStream_t s) {
+  DevInfo di;
+  hipError_t err = dev_info(&di);
+  if (err != hipSuccess) return err;
+  // workspace: per-workgroup keys [groups + 1][32] at 0 (at most 257 x 32 x 8 bytes); the tail's
+  // outputs [32][n - r0] (at most 32 x 1536 tiles x 16 rows x 4 bytes) from 128 KiB; the tail's
+  // split partial sums from 4 MiB
+  float* ws = nullptr;
+  err = workspace(s, &ws);
+  if (err != hipSuccess) return err;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws);
+  float* ytail = ws + (size_t(128) << 10) / sizeof(float);
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t kb = k / kTileCols;
+  for (int64_t m0 = 0; m0 < m; m0 += 32) {
+    const int mb = (int)((m - m0) < 32 ? (m - m0) : 32);
+    const int nt = (mb + 15) / 16;
+    // the same launches as the full outputs: the full rounds in top-1 mode, the tail rows (if
+    // any) through the split path into the workspace and then scanned for their best key
+    const int64_t r0 = tail_split_row(di, mb, tiles);
+    const int64_t nh = r0 > 0 ? r0 : n;
+    const int64_t th = (nh + kTileRows - 1) / kTileRows;
+    const int64_t groups = th < di.cus ? th : di.cus;
     MfmaArgs a;
     a.x = x + m0 * k;
     a.m = mb;
     a.base = p.base; a.ae = p.ae; a.lo = p.lo;
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
     a.w = p.w;
-    a.y = ws ? ws : y + m0 * n;
-    a.ldy = n;
-    a.n = n; a.k = k;
-    a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
-    a.splits = (int)ranges;
-    a.cps = (int)cps;
-    a.ysplit = (int64_t)mb * n;
-    hipLaunchKernelGGL(pick_kernel(f, nt, waves), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
-                       s, a);
+    a.y = nullptr;
+    a.ldy = nh;
+    a.n = nh; a.k = k;
+    a.rounds = (int)((th + groups * kWaves - 1) / (groups * kWaves));
+    a.splits = 1;
+    a.cps = (int)((kb + kChunkBlocks - 1) / kChunkBlocks);
+    a.ysplit = 0;
+    a.top1 = keys;
+    a.yvec = 0;
+    hipLaunchKernelGGL(pick_top1(f, nt), dim3((unsigned)groups), dim3(64 * kWaves), 0, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (ws) {
-      err = launch_split_reduce(ws, (int)ranges, (int64_t)mb * n, y + m0 * n, s);
+    int g_all = (int)groups;
+    if (r0 > 0) {
+      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, ytail, n - r0, s,
+                      size_t(4) << 20);
       if (err != hipSuccess) return err;
+      err = launch_top1_rows(ytail, mb, n - r0, r0, keys + (int64_t)groups * 32, s);
+      if (err != hipSuccess) return err;
+      g_all += 1;
     }
+    err = launch_top1_final(keys, g_all, mb, idx + m0, val + m0, s);
+    if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }

@@ -31,7 +31,22 @@ struct MfmaArgs {
   int splits;          // k ranges (workgroup b takes range b % splits); 1: the whole row
   int cps;             // x chunks per k range (the last range may be shorter)
   int64_t ysplit;      // floats between the partial outputs of consecutive k ranges
+  // top-1 mode (non-null; one k range only): no y is written; for each x row j < m the largest
+  // output of the workgroup's tiles goes to top1[blockIdx.x * 32 + j] as an ordered key
+  // (top1_key below), and a second kernel picks the largest key over the workgroups
+  uint64_t* top1;
+  // y (or the range's workspace slice) is 16-byte aligned and ldy % 4 == 0: the epilogue stores
+  // 16-byte vectors of 4 consecutive outputs (transposed through LDS)
+  int yvec;
 };
+
+// Ordered key of output v of row n: larger v gives a larger key, and for equal v the smaller n.
+// (A NaN output compares above +Inf.)
+__device__ __forceinline__ uint64_t top1_key(float v, int64_t n) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+}
 
 constexpr int kWaves = 12;                  // waves per workgroup, one workgroup per CU
 constexpr int kEscCap = 128;                // escapes of one tile copied to LDS

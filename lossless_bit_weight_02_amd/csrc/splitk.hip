@@ -12,7 +12,9 @@ namespace w12 {
 // the loads of up to 16 slices at once -- buffer loads, which return 0 past the last slice
 // instead of needing a branch -- and then adds them in order.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits,
-                                                      int64_t cnt, float* __restrict__ y) {
+                                                      int64_t rows, int64_t cols,
+                                                      float* __restrict__ y, int64_t ldy) {
+  const int64_t cnt = rows * cols;
   const Rsrc rp = make_rsrc(part, (uint32_t)((int64_t)splits * cnt * 4));
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += step) {
@@ -27,14 +29,80 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
       for (int j = 0; j < 16; ++j)
         if (j0 + j < splits) s = (j0 + j == 0) ? v[j] : s + v[j];
     }
-    y[i] = s;
+    const int64_t r = i / cols;
+    y[r * ldy + (i - r * cols)] = s;
   }
 }
 
-hipError_t launch_split_reduce(const float* part, int splits, int64_t cnt, float* y, hipStream_t s) {
-  int64_t blocks = (cnt + 255) / 256;
+// Top-1 over the workgroups' keys (see MfmaArgs::top1): row j's winner is the largest of
+// part[g * 32 + j], g < groups; its row index and value are decoded from the key.
+__global__ __launch_bounds__(64) void k_top1_final(const uint64_t* __restrict__ part, int groups,
+                                                   int32_t* __restrict__ idx, float* __restrict__ val) {
+  const int j = blockIdx.x, t = threadIdx.x;
+  uint64_t b = 0;
+  for (int g = t; g < groups; g += 64) {
+    const uint64_t v = part[(int64_t)g * 32 + j];
+    b = v > b ? v : b;
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh /= 2) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)b, sh, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(b >> 32), sh, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    b = o > b ? o : b;
+  }
+  if (t == 0) {
+    const uint32_t ord = (uint32_t)(b >> 32);
+    const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+    idx[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)b);
+    val[j] = __builtin_bit_cast(float, u);
+  }
+}
+
+// Best key of each row j < m of y [m][cols] (row index = row0 + column), into keys[j].
+__global__ __launch_bounds__(256) void k_top1_rows(const float* __restrict__ y, int64_t cols, int64_t row0,
+                                                   uint64_t* __restrict__ keys) {
+  __shared__ uint64_t s_b[4];
+  const int j = blockIdx.x, t = threadIdx.x;
+  uint64_t b = 0;
+  for (int64_t c = t; c < cols; c += 256) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, y[(int64_t)j * cols + c]);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint64_t key = ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(row0 + c));
+    b = key > b ? key : b;
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh /= 2) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)b, sh, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(b >> 32), sh, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    b = o > b ? o : b;
+  }
+  if ((t & 63) == 0) s_b[t >> 6] = b;
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 1; i < 4; ++i) b = s_b[i] > b ? s_b[i] : b;
+    b = s_b[0] > b ? s_b[0] : b;
+    keys[j] = b;
+  }
+}
+
+hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s) {
+  hipLaunchKernelGGL(k_top1_rows, dim3((unsigned)m), dim3(256), 0, s, y, cols, row0, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_top1_final(const uint64_t* part, int groups, int m, int32_t* idx, float* val,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_top1_final, dim3((unsigned)m), dim3(64), 0, s, part, groups, idx, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, float* y,
+                               int64_t ldy, hipStream_t s) {
+  int64_t blocks = (rows * cols + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, cnt, y);
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, rows, cols, y, ldy);
   return hipGetLastError();
 }
 

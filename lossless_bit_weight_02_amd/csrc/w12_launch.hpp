@@ -21,8 +21,16 @@ hipError_t dev_info(DevInfo* out);
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
 hipError_t workspace(hipStream_t s, float** out);
 
-// y[i] = sum over j = 0 .. splits-1 (in that order) of part[j * cnt + i], i < cnt
-hipError_t launch_split_reduce(const float* part, int splits, int64_t cnt, float* y, hipStream_t s);
+// y[r * ldy + c] = sum over j = 0 .. splits-1 (in that order) of part[j * rows * cols + r * cols + c],
+// r < rows, c < cols
+hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, float* y,
+                               int64_t ldy, hipStream_t s);
+
+// best key of each row of y [m][cols] (row index row0 + column), into keys[0 .. m)
+hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s);
+// top-1 per x row from the per-workgroup keys of the matrix-core kernel's top-1 mode
+hipError_t launch_top1_final(const uint64_t* part, int groups, int m, int32_t* idx, float* val,
+                             hipStream_t s);
 
 // Rows of the padded (tiled) plane storage.
 inline int64_t padded_rows(int64_t n) { return (n + 15) / 16 * 16; }
@@ -61,5 +69,8 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
 // MFMA family (bf16 v_mfma_f32_16x16x32), any m (blocks of <= 64 rows of x)
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        float* y, hipStream_t s);
+// top-1 over the n outputs of each x row (no y written), passes of <= 32 rows of x
+hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n,
+                            int64_t k, int32_t* idx, float* val, hipStream_t s);
 
 }  // namespace w12

@@ -54,6 +54,10 @@ EXPORTS = {
                                 ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_q8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                    ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_q8_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "w12_gemm_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "w12_concat_rows": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_int,
                                        ctypes.POINTER(_W12Weight), ctypes.POINTER(ctypes.c_uint64),
                                        ctypes.c_void_p]),
@@ -255,6 +259,33 @@ def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.
     _check(lib().w12_q8_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
                              _PATHS[path], _stream_handle(x.device)))
     return out
+
+
+def _top1(fn, x, wt, lo, out):
+    x = _bits16(x)
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D CUDA tensor")
+    x = x.contiguous()
+    m = x.shape[0]
+    if out is None:
+        out = (torch.empty(m, dtype=torch.int32, device=x.device),
+               torch.empty(m, dtype=torch.float32, device=x.device))
+    s = wt.c_struct()
+    if not lo:
+        s.lo = None
+    _check(fn(x.data_ptr(), m, ctypes.byref(s), out[0].data_ptr(), out[1].data_ptr(),
+              _stream_handle(x.device)))
+    return out
+
+
+def q8_top1(x: torch.Tensor, wt: W12Weight, out=None):
+    """Top-1 of the Q pass per row of x: (index int32 [m], value float32 [m]), no logits written."""
+    return _top1(lib().w12_q8_top1, x, wt, False, out)
+
+
+def gemm_top1(x: torch.Tensor, wt: W12Weight, out=None):
+    """Top-1 of the exact pass per row of x: (index int32 [m], value float32 [m])."""
+    return _top1(lib().w12_gemm_top1, x, wt, True, out)
 
 
 class Bf16Tiles:

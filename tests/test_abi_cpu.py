@@ -107,3 +107,13 @@ def test_concat_rows_argument_errors_are_host_side():
     # misaligned part plane
     bad = (w12._W12Weight * 2)(_rec(n=16), _rec(n=16, ae=0x2004))
     assert L.w12_concat_rows(bad, 2, ctypes.byref(_rec(n=32)), ctypes.byref(n_esc), None) == w12.W12_ERR_ALIGN
+
+
+def test_top1_argument_errors_are_host_side():
+    L = _lib()
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec()), None, 0x1000, None) == w12.W12_ERR_ARG
+    assert L.w12_gemm_top1(0x1000, 0, ctypes.byref(_rec()), 0x1000, 0x1000, None) == w12.W12_ERR_ARG
+    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec()), 0x1002, 0x1000, None) == w12.W12_ERR_ALIGN
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec(k=100)), 0x1000, 0x1000, None) == w12.W12_ERR_SHAPE
+    # the Q pass does not need the B plane, the exact pass does
+    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec(lo=None)), 0x1000, 0x1000, None) == w12.W12_ERR_ARG

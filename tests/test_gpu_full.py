@@ -102,6 +102,15 @@ def test_lm_head_q_pass_top1(pool):
     check_y(y, y64, absum, "lm_head exact")
     agree = check_top1(y, y64, absum, "lm_head exact top-1")
     say(f"lm_head: top-1 exact agreement q8 {agree_q}/16, exact {agree}/16")
+    # the top-1 entry points run the same matrix-core kernel as the full outputs above (a shape
+    # this large does not split), so they must pick exactly those outputs' argmax (ties to the
+    # lowest index) and report exactly that value
+    for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y)):
+        say(f"lm_head: {name} top-1 entry point")
+        idx, val = (t.cpu().numpy() for t in fn(xd, rec))
+        want = np.argmax(yy, axis=1)
+        assert np.array_equal(idx, want), name
+        assert np.array_equal(val.view(np.uint32), yy[np.arange(16), want].view(np.uint32)), name
 
 
 @pytest.mark.parametrize("layer", [0, 31, 63])

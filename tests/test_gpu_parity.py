@@ -319,3 +319,57 @@ def test_concat_rows_equals_encode_of_stacked(ns, k):
     for path in ("gemv", "mfma"):
         y = w12.gemm(to_dev(x), fused, path=path).cpu().numpy()
         check_gemm(y, x, stacked, f"concat gemm {path}")
+
+
+@pytest.mark.parametrize("n,k,ms", [(300, 1152, (1, 5, 16)), (4099, 640, (17, 40)), (64, 5120, (16,))])
+def test_top1_within_bound(n, k, ms):
+    """w12_q8_top1 / w12_gemm_top1 pick, per row of x, an output that is a maximum of the exact
+    product within the error bound, and report its value within the bound (ragged last tile,
+    passes of 32 rows for m = 40)."""
+    w12 = _w12()
+    rng = np.random.default_rng(n + k)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    rec = w12.encode(to_dev(w))
+    q8w = oracle.q8_view_bits(oracle.encode(w))
+    for m in ms:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        for fn, ref_w, what in ((w12.q8_top1, q8w, "q8"), (w12.gemm_top1, w, "exact")):
+            say(f"top1 {what} n={n} k={k} m={m}")
+            idx, val = (t.cpu().numpy() for t in fn(to_dev(x), rec))
+            y64 = oracle.gemm64(x, ref_w)
+            bound = 1e-3 * oracle.abs_bound64(x, ref_w)
+            rows = np.arange(m)
+            assert np.all((idx >= 0) & (idx < n))
+            # the chosen output is within the bound of the true maximum, and its value is right
+            assert np.all(y64[rows, idx] + bound[rows, idx] >= y64.max(axis=1) - bound.max(axis=1)), what
+            assert np.all(np.abs(val - y64[rows, idx]) <= bound[rows, idx]), what
+
+
+def test_top1_ties_go_to_the_lowest_row():
+    """Planted exact ties: with x = e_c every output is one weight, exactly; rows 3, 10 and 200 hold
+    the column's largest value (row 100 a larger one in column 300, which the Q pass may or may
+    not see, depending on its window), so the top-1 is the lowest row holding the maximum of the
+    pass's own weights (oracle views), on both passes."""
+    w12 = _w12()
+    n, k = 256, 512
+    rng = np.random.default_rng(5)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    cols = [0, 77, 300, 511]
+    for c in cols:
+        w[:, c] = synth.f32_to_bf16_bits(np.full(n, 0.01, np.float32))
+        w[[3, 10, 200], c] = 0x3F80                                      # 1.0, three times
+    w[100, 300] = 0x3F8F                                                 # 1.1171875
+    rec = w12.encode(to_dev(w))
+    x = np.zeros((len(cols), k), np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3F80
+    q8w = oracle.q8_view_bits(oracle.encode(w))
+    for fn, ref in ((w12.q8_top1, q8w), (w12.gemm_top1, w)):
+        vals = oracle.bf16_to_f64(ref[:, cols]).T                         # [len(cols), n], exact
+        want_idx = np.argmax(vals, axis=1)                                # first maximum
+        assert want_idx[0] == 3 and want_idx[1] == 3 and want_idx[3] == 3
+        idx, val = (t.cpu().numpy() for t in fn(to_dev(x), rec))
+        assert np.array_equal(idx, want_idx), fn.__name__
+        assert np.array_equal(val.astype(np.float64), vals[np.arange(len(cols)), want_idx]), fn.__name__
+    assert w12.gemm_top1(to_dev(x), rec)[0].cpu().numpy()[2] == 100
