@@ -373,3 +373,49 @@ def test_top1_ties_go_to_the_lowest_row():
         assert np.array_equal(idx, want_idx), fn.__name__
         assert np.array_equal(val.astype(np.float64), vals[np.arange(len(cols)), want_idx]), fn.__name__
     assert w12.gemm_top1(to_dev(x), rec)[0].cpu().numpy()[2] == 100
+
+
+def test_graph_capture_replays_match_eager():
+    """Split-k GEMMs (workspace), both kernel families, the Q pass and the top-1 entry points
+    captured in one HIP graph on a fresh stream (its workspace is allocated inside the capture):
+    every replay, with eager work and cleared outputs in between, equals the eager launches bit
+    for bit."""
+    w12 = _w12()
+    rng = np.random.default_rng(11)
+    n, k = 320, 17408                                   # splits at 1 and at 16 rows
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.001] = 0
+    rec = w12.encode(to_dev(w))
+    x1 = to_dev(synth.f32_to_bf16_bits(rng.standard_normal((1, k)).astype(np.float32)))
+    x16 = to_dev(synth.f32_to_bf16_bits(rng.standard_normal((16, k)).astype(np.float32)))
+    outs = [torch.empty((1, n), dtype=torch.float32, device="cuda"),
+            torch.empty((16, n), dtype=torch.float32, device="cuda"),
+            torch.empty((16, n), dtype=torch.float32, device="cuda")]
+    t1 = (torch.empty(16, dtype=torch.int32, device="cuda"), torch.empty(16, dtype=torch.float32, device="cuda"))
+
+    def run():
+        w12.gemm(x1, rec, path="gemv", out=outs[0])
+        w12.gemm(x16, rec, path="mfma", out=outs[1])
+        w12.q8_gemm(x16, rec, out=outs[2])
+        w12.q8_top1(x16, rec, out=t1)
+
+    run()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs] + [t.clone() for t in t1]
+    check_gemm(outs[0].cpu().numpy(), to_host_bits(x1), w, "graph eager gemv")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs + list(t1):
+            o.zero_()
+        torch.mm(torch.ones(64, 64, device="cuda"), torch.ones(64, 64, device="cuda"))   # eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outs + list(t1)
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, i)
