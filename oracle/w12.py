@@ -30,6 +30,9 @@ layout.  The readings used here (numbered as in the design notes):
       (raw bits), ascending k within each row.
 * R8  the Q pass weight is the 8-bit view with B taken as 0 (for an
       in-window weight that is bits & 0xFFF0); escapes stay exact.
+* R8m the midpoint variant of the Q pass (a next step the scope table lists):
+      the dropped nibble is read as 8, the middle of its 16 possible values,
+      so an in-window weight becomes bits & 0xFFF0 | 0x8; escapes stay exact.
 * R11 argmax ties go to the lowest index.
 * R15 storage order of the planes on the device: 16-row x 128-column tiles
       (rows padded with zero bytes to a multiple of 16, k a multiple of 128),
@@ -215,9 +218,10 @@ def decode(rec: W12Record) -> np.ndarray:
     return _assemble(rec, _unpack_lo(rec.lo, rec.k))
 
 
-def q8_view_bits(rec: W12Record) -> np.ndarray:
-    """Weights the Q pass sees: the 8-bit view with B = 0, escapes exact (R8)."""
-    return _assemble(rec, np.zeros((rec.n, rec.k), dtype=np.int64))
+def q8_view_bits(rec: W12Record, midpoint: bool = False) -> np.ndarray:
+    """Weights the Q pass sees: the 8-bit view with B = 0 (R8), or with B = 8 (midpoint, R8m);
+    escapes exact."""
+    return _assemble(rec, np.full((rec.n, rec.k), 8 if midpoint else 0, dtype=np.int64))
 
 
 def validate(rec: W12Record) -> None:
@@ -293,9 +297,10 @@ def w12_gemm64(x_bits, rec: W12Record) -> np.ndarray:
     return gemm64(x_bits, _by_rows(rec, decode))
 
 
-def q8_gemm64(x_bits, rec: W12Record) -> np.ndarray:
-    """The Q pass: x times the 8-bit-view weights (B = 0, escapes exact), float64."""
-    return gemm64(x_bits, _by_rows(rec, q8_view_bits))
+def q8_gemm64(x_bits, rec: W12Record, midpoint: bool = False) -> np.ndarray:
+    """The Q pass: x times the 8-bit-view weights (B = 0, or 8 with ``midpoint``; escapes exact),
+    float64."""
+    return gemm64(x_bits, _by_rows(rec, lambda r: q8_view_bits(r, midpoint)))
 
 
 def top1(y) -> np.ndarray:

@@ -5,6 +5,8 @@
 * the Q-pass view equals an arithmetic truncation of the mantissa to 3 bits;
 * the error bound accepts an fp32 computation and rejects a perturbed one.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -76,6 +78,34 @@ def test_q8_view_is_arithmetic_truncation():
     # and the Q GEMM is the float64 product with those weights
     x = synth.gen_x(2, rec.k)
     assert np.array_equal(oracle.q8_gemm64(x, rec), oracle.gemm64(x, q))
+
+
+def test_q8_midpoint_view_is_truncation_plus_half_a_step():
+    """Midpoint Q-pass weight (reading R8m): an in-window weight becomes its 3-bit-mantissa
+    truncation moved away from zero by half of the dropped range (8/128 of the weight's binade),
+    i.e. the centre of the 16 values its 8-bit view stands for; escaped weights stay exact; the
+    midpoint error is at most half the truncation's worst case."""
+    w, _, _ = synth.config_weight("tiny", rows=(0, 16))
+    rec = oracle.encode(w)
+    q = oracle.q8_view_bits(rec, midpoint=True)
+    esc = set()
+    for r in range(rec.n):
+        for i in range(int(rec.esc_ptr[r]), int(rec.esc_ptr[r + 1])):
+            esc.add((r, int(rec.esc_col[i])))
+    for r in range(rec.n):
+        for c in range(0, rec.k, 3):
+            u, v = int(w[r, c]), int(q[r, c])
+            if (r, c) in esc:
+                assert v == u
+                continue
+            t = bf.truncate_mantissa_3(u)
+            step = Fraction(2) ** (bf.bf16_exponent(u) - 127) * Fraction(8, 128)
+            want = t + step if u < 0x8000 else t - step
+            assert bf.bf16_fraction(v) == want
+            exact = bf.bf16_fraction(u)
+            assert abs(bf.bf16_fraction(v) - exact) <= step          # half of the 16/128 range
+    x = synth.gen_x(2, rec.k)
+    assert np.array_equal(oracle.q8_gemm64(x, rec, midpoint=True), oracle.gemm64(x, q))
 
 
 def test_top1_ties_lowest():

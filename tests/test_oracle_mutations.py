@@ -96,7 +96,8 @@ def test_mutant_q8_midpoint(monkeypatch):
     def midpoint(rec, nib):
         return orig(rec, nib + 8)
 
-    monkeypatch.setattr(ow, "q8_view_bits", lambda rec: midpoint(rec, np.zeros((rec.n, rec.k), np.int64)))
+    monkeypatch.setattr(ow, "q8_view_bits",
+                        lambda rec, mid=False: midpoint(rec, np.zeros((rec.n, rec.k), np.int64)))
     monkeypatch.setattr(oracle, "q8_view_bits", ow.q8_view_bits)
     assert _fails(tg.test_q8_view_is_arithmetic_truncation)
 
@@ -113,3 +114,18 @@ def test_mutant_placeholder_not_cleared(monkeypatch):
 
     _patch(monkeypatch, "encode", leaky)
     assert _fails(tf.test_config_roundtrip_tiny)
+
+
+def test_mutant_q8_midpoint_wrong_direction(monkeypatch):
+    """A midpoint view that moves toward zero (B = 8 subtracted instead of added) is caught."""
+    orig = ow._assemble
+
+    def view(rec, mid=False):
+        if not mid:
+            return orig(rec, np.zeros((rec.n, rec.k), np.int64))
+        u = orig(rec, np.zeros((rec.n, rec.k), np.int64)).astype(np.int64)
+        return np.where((u & 0x7F) >= 8, u - 8, u).astype(np.uint16)
+
+    monkeypatch.setattr(ow, "q8_view_bits", view)
+    monkeypatch.setattr(oracle, "q8_view_bits", ow.q8_view_bits)
+    assert _fails(tg.test_q8_midpoint_view_is_truncation_plus_half_a_step)
