@@ -197,9 +197,12 @@ def lm_head_bench(dev, stream, reps):
     yq = torch.empty((m, n), dtype=torch.float32, device=dev)
     ye = torch.empty_like(yq)
     yb = torch.empty_like(yq)
+    ym = torch.empty_like(yq)
     tq = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     te = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     cases = (("q8_m16", lambda: w12.q8_gemm(x, rec, out=yq), [yq], q8_bytes(n, k, rec.n_esc, m)),
+             ("q8_midpoint_m16", lambda: w12.q8_gemm(x, rec, out=ym, midpoint=True), [ym],
+              q8_bytes(n, k, rec.n_esc, m)),
              ("w12_m16", lambda: w12.gemm(x, rec, out=ye), [ye], w12_bytes(n, k, rec.n_esc, m)),
              ("q8_top1_m16", lambda: w12.q8_top1(x, rec, out=tq), list(tq),
               q8_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
@@ -219,11 +222,17 @@ def lm_head_bench(dev, stream, reps):
     out["w12_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["w12_m16_us"], 4)
     iq, ie = tq[0].cpu().numpy(), te[0].cpu().numpy()
     out["top1_agreement_q8_vs_exact"] = f"{int((iq == ie).sum())}/{m}"
+    im = ym.argmax(dim=1).cpu().numpy()
+    out["top1_agreement_q8_midpoint_vs_exact"] = f"{int((im == ie).sum())}/{m}"
+    scale = float(ye.abs().mean())
+    out["q8_mean_abs_err_rel"] = round(float((yq - ye).abs().mean()) / scale, 6)
+    out["q8_midpoint_mean_abs_err_rel"] = round(float((ym - ye).abs().mean()) / scale, 6)
     # the top-1 entry points against the argmax of the full outputs of the same kernels
     out["top1_matches_full_outputs"] = bool(
         np.array_equal(iq, yq.argmax(dim=1).cpu().numpy()) and np.array_equal(ie, ye.argmax(dim=1).cpu().numpy()))
     samples = [("lm_head q8 m=16 (rows 0..127)", x_bits, keep, yq[:, :128].cpu().numpy(), "q8"),
-               ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy())]
+               ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy()),
+               ("lm_head q8 midpoint m=16 (rows 0..127)", x_bits, keep, ym[:, :128].cpu().numpy(), "q8m")]
     return out, samples
 
 
@@ -402,8 +411,8 @@ def cpu_baseline(w_bits, x_bits, gpu_out, rows, samples=()):
             raise SystemExit(f"parity failure in {name}: GPU output outside the bound")
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
     for label, xb, wb, gy, *view in samples:
-        if view and view[0] == "q8":
-            wb = oracle.q8_view_bits(oracle.encode(wb))
+        if view and view[0] in ("q8", "q8m"):
+            wb = oracle.q8_view_bits(oracle.encode(wb), midpoint=view[0] == "q8m")
         y = oracle.gemm64(xb, wb)
         bound = 1e-3 * oracle.abs_bound64(xb, wb)
         err = np.abs(gy.astype(np.float64) - y)

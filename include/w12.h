@@ -78,6 +78,9 @@ extern "C" {
 #define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 4, bf16 MFMA for m >= 5 */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
+/* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16
+ * values the 8-bit view stands for) instead of 0; escapes stay exact */
+#define W12_Q8_MIDPOINT 0x10u
 
 /* A W12 tensor: a non-owning view.  Every pointer is device memory owned by the caller. */
 typedef struct w12_weight {
@@ -127,7 +130,8 @@ int w12_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint3
  * the same product with every in-window weight taken from the 8-bit view alone (A + E, the
  * B nibble read as 0, i.e. the bfloat16 bits & 0xFFF0) and escapes exact.  Reads base, ae
  * and the escape arrays only; wt->lo may be NULL.  Same shapes and error bound as
- * w12_gemm, against that truncated weight.
+ * w12_gemm, against that truncated weight.  With W12_Q8_MIDPOINT in flags the in-window weight
+ * is bits & 0xFFF0 | 0x8 instead (same bytes read, half the worst-case weight error).
  */
 int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint32_t flags,
                 void *stream);

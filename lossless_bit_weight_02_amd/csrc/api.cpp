@@ -77,6 +77,10 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   if (!x || !y) return fail(W12_ERR_ARG, "x or y is NULL");
   if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
+  if (f == w12::kFmtQ8 && (flags & W12_Q8_MIDPOINT)) {
+    f = w12::kFmtQ8M;
+    flags &= ~W12_Q8_MIDPOINT;
+  }
   if (flags > W12_PATH_MFMA) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned4(y)) return fail(W12_ERR_ALIGN, "y must be 4-byte aligned");

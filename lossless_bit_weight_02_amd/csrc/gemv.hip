@@ -120,6 +120,7 @@ __device__ __forceinline__ void block_pairs(const BlockRegs<FMT>& r, uint32_t e1
     window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
     window_group8_q(r.v[1].x, r.v[1].y, e112, p + 8);
     window_group8_q(r.v[1].z, r.v[1].w, e112, p + 12);
+    if constexpr (FMT == kFmtQ8M) midpoint16(p);
   }
 }
 
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             const float xv = bf16_to_float(xs16[m * kn + c]);
-            acc[m] = fmaf(-xv, kPlaceholder, acc[m]);
+            acc[m] = fmaf(-xv, placeholder_of<FMT>(), acc[m]);
             q[m] = fmaf(xv, v, q[m]);
           }
         }
@@ -383,6 +384,7 @@ static GemvKernel pick(int m) {
 static GemvKernel pick_kernel(Fmt f, int m) {
   if (f == kFmtW12) return pick<kFmtW12>(m);
   if (f == kFmtQ8) return pick<kFmtQ8>(m);
+  if (f == kFmtQ8M) return pick<kFmtQ8M>(m);
   return pick<kFmtBF16>(m);
 }
 

@@ -340,7 +340,7 @@ void k_mfma(MfmaArgs a) {
               const uint32_t at = x_slot(col >> 8, 16u * cc + (uint32_t)r16, (col >> 3) & 31u);
               const float xv = bf16_to_float(reinterpret_cast<const uint16_t*>(&s_x[b][at])[col & 7u]);
               if constexpr (kSepSx) sx[cc][r] += xv;
-              else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+              else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -384,7 +384,7 @@ void k_mfma(MfmaArgs a) {
 #pragma unroll
             for (int cc = 0; cc < NT; ++cc) {
               if constexpr (kSepSx) sx[cc][r] += xv[i][cc];
-              else acc[cc][r] = fmaf(-xv[i][cc], kPlaceholder, acc[cc][r]);
+              else acc[cc][r] = fmaf(-xv[i][cc], placeholder_of<FMT>(), acc[cc][r]);
               qv[cc][r] = fmaf(xv[i][cc], v, qv[cc][r]);
             }
           }
@@ -408,7 +408,7 @@ void k_mfma(MfmaArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
-          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r]) : acc[cc][r];
+          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r]) : acc[cc][r];
         }
         *reinterpret_cast<floatx4*>(&res[(16 * cc + r16) * 20 + 4 * g]) = (floatx4){v4[0], v4[1], v4[2], v4[3]};
       }
@@ -440,7 +440,7 @@ void k_mfma(MfmaArgs a) {
         for (int cc = 0; cc < NT; ++cc) {
           const int mcol = 16 * cc + r16;
           if (mcol >= a.m) continue;
-          const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
+          const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
                                : acc[cc][r];
           const uint64_t key = top1_key(v, nrow);
           best[cc] = key > best[cc] ? key : best[cc];
@@ -478,20 +478,19 @@ static MfmaKernel pick(int nt) {
   return nt == 1 ? k_mfma<FMT, 1, W, false> : k_mfma<FMT, 2, W, false>;
 }
 
-// top-1 mode: the exact pass or the Q pass, one or two activation tiles, 12 waves
+// top-1 mode: the exact pass or the Q pass (truncated or midpoint), one or two activation tiles,
+// 12 waves
 static MfmaKernel pick_top1(Fmt f, int nt) {
   if (f == kFmtW12) return nt == 1 ? k_mfma<kFmtW12, 1, kWaves, true> : k_mfma<kFmtW12, 2, kWaves, true>;
+  if (f == kFmtQ8M) return nt == 1 ? k_mfma<kFmtQ8M, 1, kWaves, true> : k_mfma<kFmtQ8M, 2, kWaves, true>;
   return nt == 1 ? k_mfma<kFmtQ8, 1, kWaves, true> : k_mfma<kFmtQ8, 2, kWaves, true>;
 }
 
 static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
-  if (waves == 8) {
-    if (f == kFmtW12) return pick<kFmtW12, 8>(nt);
-    if (f == kFmtQ8) return pick<kFmtQ8, 8>(nt);
-    return pick<kFmtBF16, 8>(nt);
-  }
+  if (waves == 8) return pick<kFmtBF16, 8>(nt);   // only the dense baseline runs 8 waves
   if (f == kFmtW12) return pick<kFmtW12, 12>(nt);
   if (f == kFmtQ8) return pick<kFmtQ8, 12>(nt);
+  if (f == kFmtQ8M) return pick<kFmtQ8M, 12>(nt);
   return pick<kFmtBF16, 12>(nt);
 }
 

@@ -90,6 +90,7 @@ __device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112
     window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
     window_group8_q(r.v[1].x, r.v[1].y, e112, p + 8);
     window_group8_q(r.v[1].z, r.v[1].w, e112, p + 12);
+    if constexpr (FMT == kFmtQ8M) midpoint16(p);
   }
 }
 

@@ -280,7 +280,7 @@ void k_mfma_wide(MfmaArgs a) {
               const float xv = bf16_to_float(
                   reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
               if constexpr (kSepSx) sx[cc][r] += xv;
-              else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+              else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -304,7 +304,7 @@ void k_mfma_wide(MfmaArgs a) {
             const int mrow = 16 * cc + r16;
             const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
             if constexpr (kSepSx) sx[cc][r] += xv;
-            else acc[cc][r] = fmaf(-xv, kPlaceholder, acc[cc][r]);
+            else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
             qv[cc][r] = fmaf(xv, v, qv[cc][r]);
           }
         }
@@ -319,7 +319,7 @@ void k_mfma_wide(MfmaArgs a) {
       for (int cc = 0; cc < NT; ++cc) {
         const int mcol = 16 * cc + r16;
         if (mcol >= a.m) continue;
-        const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], kPlaceholder, acc[cc][r]), qv[cc][r])
+        const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
                              : acc[cc][r];
         a.y[mcol * a.ldy + nrow] = v;
       }
@@ -333,6 +333,7 @@ void k_mfma_wide(MfmaArgs a) {
 MfmaKernel mfma_wide_kernel(Fmt f, int nt) {
   if (f == kFmtW12) return nt == 3 ? k_mfma_wide<kFmtW12, 3> : k_mfma_wide<kFmtW12, 4>;
   if (f == kFmtQ8) return nt == 3 ? k_mfma_wide<kFmtQ8, 3> : k_mfma_wide<kFmtQ8, 4>;
+  if (f == kFmtQ8M) return nt == 3 ? k_mfma_wide<kFmtQ8M, 3> : k_mfma_wide<kFmtQ8M, 4>;
   return nt == 3 ? k_mfma_wide<kFmtBF16, 3> : k_mfma_wide<kFmtBF16, 4>;
 }
 

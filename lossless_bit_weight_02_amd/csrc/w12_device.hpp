@@ -89,6 +89,17 @@ __device__ __forceinline__ float window_scale(uint32_t base) {
 
 // w' of an escaped slot (AE = 0, B = 0): exponent 112, mantissa 0 -> 2^-15.
 constexpr float kPlaceholder = 3.0517578125e-05f;
+// The same slot in the midpoint Q pass (format 3 of the launch interface: B read as 8):
+// 2^-15 * (1 + 8/128).
+constexpr float kPlaceholderMid = 3.24249267578125e-05f;
+template <int FMT>
+constexpr float placeholder_of() { return FMT == 3 ? kPlaceholderMid : kPlaceholder; }
+
+// Midpoint Q pass: the B nibble of both bfloat16 halves of each decoded pair set to 8.
+__device__ __forceinline__ void midpoint16(uint32_t p[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] |= 0x00080008u;
+}
 
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -6,7 +6,8 @@
 
 namespace w12 {
 
-enum Fmt : int { kFmtW12 = 0, kFmtQ8 = 1, kFmtBF16 = 2 };
+// kFmtQ8M: the Q pass with the dropped B nibble read as 8 (the midpoint of its 16 values)
+enum Fmt : int { kFmtW12 = 0, kFmtQ8 = 1, kFmtBF16 = 2, kFmtQ8M = 3 };
 
 struct DevInfo {
   int device = -1;

@@ -24,6 +24,7 @@ W12_ERR_RANGE = -5
 W12_ERR_HIP = -6
 
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+Q8_MIDPOINT = 0x10
 _PATHS = {None: PATH_AUTO, "auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
 
 
@@ -250,14 +251,17 @@ def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Ten
     return out
 
 
-def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None):
-    """Q pass: y = x W_q^T with W_q the 8-bit view (B plane taken as 0), escapes exact."""
+def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None,
+            midpoint: bool = False):
+    """Q pass: y = x W_q^T with W_q the 8-bit view (B plane taken as 0, or as 8 with
+    ``midpoint``), escapes exact."""
     if out is None:
         x, out = _gemm_out(x, wt.n)
     s = wt.c_struct()
     s.lo = None
+    flags = _PATHS[path] | (Q8_MIDPOINT if midpoint else 0)
     _check(lib().w12_q8_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
-                             _PATHS[path], _stream_handle(x.device)))
+                             flags, _stream_handle(x.device)))
     return out
 
 

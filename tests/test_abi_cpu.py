@@ -117,3 +117,14 @@ def test_top1_argument_errors_are_host_side():
     assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec(k=100)), 0x1000, 0x1000, None) == w12.W12_ERR_SHAPE
     # the Q pass does not need the B plane, the exact pass does
     assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec(lo=None)), 0x1000, 0x1000, None) == w12.W12_ERR_ARG
+
+
+def test_midpoint_flag_only_on_the_q_pass():
+    L = _lib()
+    # the exact pass has no midpoint variant: the flag is an unknown flag there (host-side)
+    assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1000, w12.Q8_MIDPOINT, None) == w12.W12_ERR_ARG
+    assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, 128, 0x1000, w12.Q8_MIDPOINT, None) == w12.W12_ERR_ARG
+    # on the Q pass it combines with a path; other bits stay unknown
+    assert L.w12_q8_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1000, w12.Q8_MIDPOINT | 0x4, None) == w12.W12_ERR_ARG
+    text = open(HEADER).read()
+    assert int(re.search(r"#define W12_Q8_MIDPOINT (0x[0-9a-fA-F]+)u", text).group(1), 16) == w12.Q8_MIDPOINT

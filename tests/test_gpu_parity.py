@@ -419,3 +419,30 @@ def test_graph_capture_replays_match_eager():
         got = outs + list(t1)
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, i)
+
+
+@pytest.mark.parametrize("n,k,ms", [(256, 512, (1, 4, 16, 33)), (64, 5120, (1, 16, 32)), (4099, 640, (2, 17)),
+                                    (300, 1152, (8,))])
+def test_q8_midpoint_gemm(n, k, ms):
+    """w12_q8_gemm with W12_Q8_MIDPOINT against the oracle's midpoint view (in-window weights
+    bits & 0xFFF0 | 0x8, escapes exact), both kernel families, split-k and ragged shapes; and
+    one-hot exactness (every output is exactly one midpoint weight)."""
+    w12 = _w12()
+    rng = np.random.default_rng(n * 3 + k)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    rec = w12.encode(to_dev(w))
+    qm = oracle.q8_view_bits(oracle.encode(w), midpoint=True)
+    for m in ms:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+        for path in ("gemv", "mfma"):
+            say(f"q8 midpoint n={n} k={k} m={m} path={path}")
+            y = w12.q8_gemm(to_dev(x), rec, path=path, midpoint=True).cpu().numpy()
+            check_gemm(y, x, qm, f"q8 midpoint {path}")
+    cols = [0, k // 2 + 3, k - 1]
+    x = np.zeros((len(cols), k), np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3F80
+    for path in ("gemv", "mfma"):
+        y = w12.q8_gemm(to_dev(x), rec, path=path, midpoint=True).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, oracle.bf16_to_f64(qm[:, cols]).T), path
