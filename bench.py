@@ -19,6 +19,14 @@ Each op's back-to-back launches are bracketed by one pair of HIP events on the s
 on; the per-launch time is the elapsed time / launches (the M=1 groups launch every copy twice,
 so the gap around an event pair weighs less).
 
+Beside the step (context, outside `value` and `ms_per_step`): an M sweep on gate+up (GEMV and MFMA
+families, W12 and BF16) and the vendor library's bf16 GEMM; the attention projection [5120, 5120]
+at M=1; the LM-head-like [152064, 5120] Q pass at M=16 (truncated and midpoint views, exact pass,
+top-1 entry points, BF16, top-1 agreement); and the 64-layer 27B-class stack at M=1 and M=32,
+per projection and in the qkv / gate_up layout.  These are timed as captured HIP graphs whose
+replays are checked bit for bit against eager launches; their outputs are sampled into the CPU
+oracle leg.
+
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 """
 from __future__ import annotations
