@@ -208,11 +208,14 @@ def lm_head_bench(dev, stream, reps):
     ym = torch.empty_like(yq)
     tq = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     te = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
+    tm = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     cases = (("q8_m16", lambda: w12.q8_gemm(x, rec, out=yq), [yq], q8_bytes(n, k, rec.n_esc, m)),
              ("q8_midpoint_m16", lambda: w12.q8_gemm(x, rec, out=ym, midpoint=True), [ym],
               q8_bytes(n, k, rec.n_esc, m)),
              ("w12_m16", lambda: w12.gemm(x, rec, out=ye), [ye], w12_bytes(n, k, rec.n_esc, m)),
              ("q8_top1_m16", lambda: w12.q8_top1(x, rec, out=tq), list(tq),
+              q8_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
+             ("q8_midpoint_top1_m16", lambda: w12.q8_top1(x, rec, out=tm, midpoint=True), list(tm),
               q8_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
              ("w12_top1_m16", lambda: w12.gemm_top1(x, rec, out=te), list(te),
               w12_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
@@ -237,7 +240,8 @@ def lm_head_bench(dev, stream, reps):
     out["q8_midpoint_mean_abs_err_rel"] = round(float((ym - ye).abs().mean()) / scale, 6)
     # the top-1 entry points against the argmax of the full outputs of the same kernels
     out["top1_matches_full_outputs"] = bool(
-        np.array_equal(iq, yq.argmax(dim=1).cpu().numpy()) and np.array_equal(ie, ye.argmax(dim=1).cpu().numpy()))
+        np.array_equal(iq, yq.argmax(dim=1).cpu().numpy()) and np.array_equal(ie, ye.argmax(dim=1).cpu().numpy())
+        and np.array_equal(tm[0].cpu().numpy(), im))
     samples = [("lm_head q8 m=16 (rows 0..127)", x_bits, keep, yq[:, :128].cpu().numpy(), "q8"),
                ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy()),
                ("lm_head q8 midpoint m=16 (rows 0..127)", x_bits, keep, ym[:, :128].cpu().numpy(), "q8m")]

@@ -146,12 +146,14 @@ int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, ui
  * w12_gemm computes it for a shape too large to split (a NaN output counts as the largest).
  * Runs the matrix-core kernel in passes of up to 32 rows of x (each pass reads the weights once)
  * plus one small kernel per pass; uses the GEMM workspace (see the conventions above).
- * Same record checks as w12_q8_gemm / w12_gemm; idx and val 4-byte aligned.
+ * Same record checks as w12_q8_gemm / w12_gemm; idx and val 4-byte aligned.  flags: 0, or for
+ * w12_q8_top1 W12_Q8_MIDPOINT (the midpoint view, as in w12_q8_gemm); anything else is
+ * W12_ERR_ARG.
  */
 int w12_q8_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *idx, float *val,
-                void *stream);
+                uint32_t flags, void *stream);
 int w12_gemm_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *idx, float *val,
-                  void *stream);
+                  uint32_t flags, void *stream);
 
 /*
  * w12_concat_rows -- the record of W = [W_0; W_1; ...; W_{count-1}] (the parts' rows stacked in

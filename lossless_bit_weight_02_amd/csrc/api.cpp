@@ -210,8 +210,13 @@ int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, ui
 
 namespace {
 int run_top1(w12::Fmt f, const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val,
-             void* stream) {
+             uint32_t flags, void* stream) {
   if (!x || !idx || !val) return fail(W12_ERR_ARG, "x, idx or val is NULL");
+  if (f == w12::kFmtQ8 && flags == W12_Q8_MIDPOINT) {
+    f = w12::kFmtQ8M;
+    flags = 0;
+  }
+  if (flags != 0) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
   if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
@@ -223,16 +228,18 @@ int run_top1(w12::Fmt f, const uint16_t* x, int64_t m, const w12_weight* wt, int
 }
 }  // namespace
 
-int w12_gemm_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val, void* stream) {
+int w12_gemm_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val,
+                  uint32_t flags, void* stream) {
   int rc = check_record(wt, true);
   if (rc) return rc;
-  return run_top1(w12::kFmtW12, x, m, wt, idx, val, stream);
+  return run_top1(w12::kFmtW12, x, m, wt, idx, val, flags, stream);
 }
 
-int w12_q8_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val, void* stream) {
+int w12_q8_top1(const uint16_t* x, int64_t m, const w12_weight* wt, int32_t* idx, float* val,
+                uint32_t flags, void* stream) {
   int rc = check_record(wt, false);
   if (rc) return rc;
-  return run_top1(w12::kFmtQ8, x, m, wt, idx, val, stream);
+  return run_top1(w12::kFmtQ8, x, m, wt, idx, val, flags, stream);
 }
 
 int w12_concat_rows(const w12_weight* parts, int count, w12_weight* out, uint64_t* n_esc, void* stream) {

@@ -56,9 +56,9 @@ EXPORTS = {
     "w12_q8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                    ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_q8_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_gemm_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_concat_rows": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_int,
                                        ctypes.POINTER(_W12Weight), ctypes.POINTER(ctypes.c_uint64),
                                        ctypes.c_void_p]),
@@ -265,7 +265,7 @@ def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.
     return out
 
 
-def _top1(fn, x, wt, lo, out):
+def _top1(fn, x, wt, lo, out, flags=0):
     x = _bits16(x)
     if x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D CUDA tensor")
@@ -277,14 +277,15 @@ def _top1(fn, x, wt, lo, out):
     s = wt.c_struct()
     if not lo:
         s.lo = None
-    _check(fn(x.data_ptr(), m, ctypes.byref(s), out[0].data_ptr(), out[1].data_ptr(),
+    _check(fn(x.data_ptr(), m, ctypes.byref(s), out[0].data_ptr(), out[1].data_ptr(), flags,
               _stream_handle(x.device)))
     return out
 
 
-def q8_top1(x: torch.Tensor, wt: W12Weight, out=None):
-    """Top-1 of the Q pass per row of x: (index int32 [m], value float32 [m]), no logits written."""
-    return _top1(lib().w12_q8_top1, x, wt, False, out)
+def q8_top1(x: torch.Tensor, wt: W12Weight, out=None, midpoint: bool = False):
+    """Top-1 of the Q pass per row of x: (index int32 [m], value float32 [m]), no logits written;
+    ``midpoint`` reads the dropped nibble as 8 as in q8_gemm."""
+    return _top1(lib().w12_q8_top1, x, wt, False, out, Q8_MIDPOINT if midpoint else 0)
 
 
 def gemm_top1(x: torch.Tensor, wt: W12Weight, out=None):

@@ -111,12 +111,15 @@ def test_concat_rows_argument_errors_are_host_side():
 
 def test_top1_argument_errors_are_host_side():
     L = _lib()
-    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec()), None, 0x1000, None) == w12.W12_ERR_ARG
-    assert L.w12_gemm_top1(0x1000, 0, ctypes.byref(_rec()), 0x1000, 0x1000, None) == w12.W12_ERR_ARG
-    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec()), 0x1002, 0x1000, None) == w12.W12_ERR_ALIGN
-    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec(k=100)), 0x1000, 0x1000, None) == w12.W12_ERR_SHAPE
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec()), None, 0x1000, 0, None) == w12.W12_ERR_ARG
+    assert L.w12_gemm_top1(0x1000, 0, ctypes.byref(_rec()), 0x1000, 0x1000, 0, None) == w12.W12_ERR_ARG
+    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec()), 0x1002, 0x1000, 0, None) == w12.W12_ERR_ALIGN
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec(k=100)), 0x1000, 0x1000, 0, None) == w12.W12_ERR_SHAPE
     # the Q pass does not need the B plane, the exact pass does
-    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec(lo=None)), 0x1000, 0x1000, None) == w12.W12_ERR_ARG
+    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec(lo=None)), 0x1000, 0x1000, 0, None) == w12.W12_ERR_ARG
+    # flags: only the Q pass has a midpoint variant; path flags do not apply
+    assert L.w12_gemm_top1(0x1000, 1, ctypes.byref(_rec()), 0x1000, 0x1000, w12.Q8_MIDPOINT, None) == w12.W12_ERR_ARG
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec()), 0x1000, 0x1000, 1, None) == w12.W12_ERR_ARG
 
 
 def test_midpoint_flag_only_on_the_q_pass():

@@ -105,7 +105,10 @@ def test_lm_head_q_pass_top1(pool):
     # the top-1 entry points run the same matrix-core kernel as the full outputs above (a shape
     # this large does not split), so they must pick exactly those outputs' argmax (ties to the
     # lowest index) and report exactly that value
-    for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y)):
+    say("lm_head: q8 midpoint gemm m=16")
+    yqm = w12.q8_gemm(xd, rec, midpoint=True).cpu().numpy()
+    for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y),
+                         ("q8 midpoint", lambda xx, rr: w12.q8_top1(xx, rr, midpoint=True), yqm)):
         say(f"lm_head: {name} top-1 entry point")
         idx, val = (t.cpu().numpy() for t in fn(xd, rec))
         want = np.argmax(yy, axis=1)

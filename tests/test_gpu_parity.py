@@ -332,9 +332,11 @@ def test_top1_within_bound(n, k, ms):
     w[rng.random((n, k)) < 0.01] = 0
     rec = w12.encode(to_dev(w))
     q8w = oracle.q8_view_bits(oracle.encode(w))
+    q8m = oracle.q8_view_bits(oracle.encode(w), midpoint=True)
     for m in ms:
         x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
-        for fn, ref_w, what in ((w12.q8_top1, q8w, "q8"), (w12.gemm_top1, w, "exact")):
+        for fn, ref_w, what in ((w12.q8_top1, q8w, "q8"), (w12.gemm_top1, w, "exact"),
+                                (lambda xx, rr: w12.q8_top1(xx, rr, midpoint=True), q8m, "q8 midpoint")):
             say(f"top1 {what} n={n} k={k} m={m}")
             idx, val = (t.cpu().numpy() for t in fn(to_dev(x), rec))
             y64 = oracle.gemm64(x, ref_w)
