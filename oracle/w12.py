@@ -45,10 +45,11 @@ layout.  The readings used here (numbered as in the design notes):
 Parity status: every function below is pinned by the CPU tests against
 values fixed independently of this file (exhaustive round trip over all 65536
 bfloat16 patterns, brute-force window search, hand-worked examples of the
-readings, exact rational GEMMs, an arithmetic formulation of the truncated
-view, the bits-per-weight closed form).  The readings themselves (bit order,
-tie rule, placeholder) cannot be pinned to the pages, which print no layout
-or worked example.
+readings, exact rational GEMMs, arithmetic formulations of the truncated and
+midpoint views, the bits-per-weight closed form).  The readings themselves
+(bit order R1, tie rule R3, placeholder R5, escape layout R6, storage order
+R15, the midpoint value R8m) cannot be pinned to the pages, which print no
+layout or worked example: parity unpinned on those points.
 """
 from __future__ import annotations
 
