@@ -479,7 +479,7 @@ def main():
     n, k = spec.n, spec.k
     t0 = time.perf_counter()
     w_bits = synth.gen_weight(spec, 0, tid)
-    x_bits = synth.gen_x(64, k, tensor_id=tid)
+    x_bits = synth.gen_x(256, k, tensor_id=tid)
     t_gen = time.perf_counter() - t0
 
     def to_dev(bits):
@@ -591,11 +591,12 @@ def main():
     if not a.no_sweep:
         sweep = {}
         xs = to_dev(x_bits)
-        for m in (1, 4, 8, 16, 32, 64):
+        for m in (1, 4, 8, 16, 32, 64, 128, 256):
             xm = xs[:m].contiguous()
             ym = torch.empty((m, n), dtype=torch.float32, device=dev)
             row = {}
-            for path in ("gemv", "mfma"):
+            # above 64 rows only the matrix-core path (passes of 64 rows, each reading W once)
+            for path in (("gemv", "mfma") if m <= 64 else ("mfma",)):
                 for fmt in ("w12", "bf16"):
                     def run(r, fmt=fmt, path=path):
                         if fmt == "w12":
@@ -614,7 +615,8 @@ def main():
                     byt = w12_bytes(n, k, n_esc, m) if fmt == "w12" else bf16_bytes(n, k, m)
                     row[f"{fmt}_{path}_us"] = round(t * 1e6, 2)
                     row[f"{fmt}_{path}_gbs"] = round(byt / t / 1e9, 1)
-            row["best_w12_path"] = "gemv" if row["w12_gemv_us"] <= row["w12_mfma_us"] else "mfma"
+            row["best_w12_path"] = "gemv" if row.get("w12_gemv_us", 1e30) <= row["w12_mfma_us"] else "mfma"
+            row["w12_mfma_tflops"] = round(2 * m * n * k / (row["w12_mfma_us"] * 1e-6) / 1e12, 1)
             sweep[str(m)] = row
 
     # Context, not a metric: the vendor library's dense bf16 GEMM on the same weights (torch.mm,

@@ -319,6 +319,19 @@ def test_concat_rows_equals_encode_of_stacked(ns, k):
     for path in ("gemv", "mfma"):
         y = w12.gemm(to_dev(x), fused, path=path).cpu().numpy()
         check_gemm(y, x, stacked, f"concat gemm {path}")
+    # capacity protocol: too few escape slots in `out` -> W12_ERR_CAPACITY with the total reported
+    import ctypes
+    total = fused.n_esc
+    if total > 0:
+        small = w12.W12Weight(fused.n, k, torch.empty_like(fused.base), torch.empty_like(fused.ae),
+                              torch.empty_like(fused.lo), torch.empty_like(fused.esc_ptr),
+                              torch.empty(total, dtype=torch.int32, device="cuda")[:total - 1],
+                              torch.empty(total, dtype=torch.int16, device="cuda")[:total - 1])
+        arr = (w12._W12Weight * len(recs))(*[r.c_struct() for r in recs])
+        n_esc = ctypes.c_uint64(0)
+        st = w12.lib().w12_concat_rows(arr, len(recs), ctypes.byref(small.c_struct()), ctypes.byref(n_esc),
+                                       torch.cuda.current_stream().cuda_stream)
+        assert st == w12.W12_ERR_CAPACITY and n_esc.value == total
 
 
 @pytest.mark.parametrize("n,k,ms", [(300, 1152, (1, 5, 16)), (4099, 640, (17, 40)), (64, 5120, (16,))])
