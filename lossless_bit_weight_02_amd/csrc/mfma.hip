@@ -1,6 +1,6 @@
-// Skinny GEMM for up to 32 activation rows (one or two 16-row activation tiles) on the matrix
-// cores: y[m][n] = sum_k x[m][k] W[n][k].  Three and four tiles run the register-staged variant
-// in mfma_wide.hip.
+// Skinny GEMM on the matrix cores, y[m][n] = sum_k x[m][k] W[n][k], for one or two 16-row
+// activation tiles (up to 32 rows) and for eight (passes of 65..128 rows).  Three and four tiles
+// run the register-staged variant in mfma_wide.hip.
 //
 // From about 16 rows the product is a dense contraction again (SpecPilot, arXiv 2611.02501,
 // summary page, "Main Findings": the W12 GEMM is measured at 1 and at 32 rows), so the decoded
@@ -63,10 +63,13 @@ constexpr int kEscStage = 128;    // of which staged through registers with the 
 
 template <int FMT, int NT, int W>
 struct Shape {
-  static_assert(NT == 1 || NT == 2, "three and four tiles run k_mfma_wide");
+  static_assert(NT == 1 || NT == 2 || NT == 8, "three and four tiles run k_mfma_wide");
   static_assert(W == 12 || W == 8, "12 or 8 waves per workgroup");
-  static constexpr int D = W == 12 ? 4 : 8;           // blocks in flight per wave
-  static constexpr int S = W == 12 ? kChunkBlocks : 8;   // k-blocks per x chunk
+  static_assert(NT != 8 || W == 12, "eight tiles run with 12 waves");
+  // blocks in flight per wave, and k-blocks per x chunk (eight activation tiles: 128 rows of x,
+  // whose two 64 KiB chunk buffers fill most of the LDS, with a 2-deep ring)
+  static constexpr int D = NT == 8 ? 2 : W == 12 ? 4 : 8;
+  static constexpr int S = NT == 8 ? 2 : W == 12 ? kChunkBlocks : 8;
   static constexpr int FS = 4 * NT;                   // 1 KiB x fragments per k-block
   static constexpr int F = FS * S;                    // 1 KiB x fragments per chunk
   static constexpr int FW = (F + W - 1) / W;          // fragments a wave loads per chunk
@@ -92,15 +95,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W
 void k_mfma(MfmaArgs a) {
   using SH = Shape<FMT, NT, W>;
   constexpr int D = SH::D, S = SH::S, F = SH::F, FW = SH::FW, FPS = SH::FPS, LS = SH::LS;
-  constexpr bool kEsc = FMT != kFmtBF16;
-  // x sums of escaped slots in registers of their own (up to two activation tiles; beyond that
-  // the registers are not there and the placeholders come out of the accumulators directly)
-  constexpr bool kSepSx = true;    // escape x sums kept apart from the accumulators
+  // kScale: decoded weights are w' = w / 2^(base - 112) and the outputs take the row's scale.
+  // kEsc: escapes are patched chunk by chunk from x in LDS (up to two activation tiles); with
+  // eight, their per-row sums would not fit the registers during the loop, so kEscEpi patches
+  // them in the epilogue (registers free again) from the transposed x in memory.
+  constexpr bool kScale = FMT != kFmtBF16;
+  constexpr bool kEsc = kScale && NT <= 2;
+  constexpr bool kEscEpi = kScale && !kEsc;
+  constexpr bool kStage = kEsc || kEscEpi;       // the tile's escape list staged in LDS
   constexpr int kLoadsPerStep = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
   __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * W > F) ? 64 : 1];   // target of unused fragment loads
-  __shared__ uint32_t s_ecol[kEsc ? W : 1][kEsc ? kEscCapM : 1];   // per wave: tile escapes
-  __shared__ uint16_t s_eval[kEsc ? W : 1][kEsc ? kEscCapM : 1];
+  __shared__ uint32_t s_ecol[kStage ? W : 1][kStage ? kEscCapM : 1];   // per wave: tile escapes
+  __shared__ uint16_t s_eval[kStage ? W : 1][kStage ? kEscCapM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
@@ -175,11 +182,13 @@ void k_mfma(MfmaArgs a) {
 
     // ---- row bounds and window bottoms of the tile's escapes (oldest loads) ----
     uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0, t_cnt = 0;
-    if constexpr (kEsc) {
+    if constexpr (kScale) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
+      if constexpr (kStage) {
 #pragma unroll
-      for (int r = 0; r < 5; ++r) st[r] = ptr_at(rg + r);
+        for (int r = 0; r < 5; ++r) st[r] = ptr_at(rg + r);
+      }
       const Rsrc rb = make_rsrc(a.base, (uint32_t)a.n);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -212,7 +221,7 @@ void k_mfma(MfmaArgs a) {
     // ---- the tile's escape list into LDS (its loads go out after the ring's, so the ring is
     // not held behind the wait for the row bounds; waiting for them waits for the ring, which
     // the first step needs anyway) ----
-    if constexpr (kEsc) {
+    if constexpr (kStage) {
       // escape range of the tile: row0's start (lane 0, g = 0) and row0 + 16's (lane 48, g = 3)
       t_e0 = __builtin_amdgcn_readfirstlane(st[0]);
       const uint32_t t_e1 = valid ? (uint32_t)__builtin_amdgcn_readlane((int)st[4], 48) : t_e0;
@@ -339,8 +348,7 @@ void k_mfma(MfmaArgs a) {
             for (int cc = 0; cc < NT; ++cc) {
               const uint32_t at = x_slot(col >> 8, 16u * cc + (uint32_t)r16, (col >> 3) & 31u);
               const float xv = bf16_to_float(reinterpret_cast<const uint16_t*>(&s_x[b][at])[col & 7u]);
-              if constexpr (kSepSx) sx[cc][r] += xv;
-              else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+              sx[cc][r] += xv;
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -383,8 +391,7 @@ void k_mfma(MfmaArgs a) {
             const float v = bf16_to_float(vb[i]);
 #pragma unroll
             for (int cc = 0; cc < NT; ++cc) {
-              if constexpr (kSepSx) sx[cc][r] += xv[i][cc];
-              else acc[cc][r] = fmaf(-xv[i][cc], placeholder_of<FMT>(), acc[cc][r]);
+              sx[cc][r] += xv[i][cc];
               qv[cc][r] = fmaf(xv[i][cc], v, qv[cc][r]);
             }
           }
@@ -395,29 +402,82 @@ void k_mfma(MfmaArgs a) {
     uint64_t best[NT];
 #pragma unroll
     for (int cc = 0; cc < NT; ++cc) best[cc] = 0;
+    if constexpr (kEscEpi) {
+      // the escapes of the lane's four rows, four at a time: entries from the LDS copy (memory
+      // past it in a crowded tile), x values from the transposed x (the lane's eight x rows in
+      // one 16-byte load); the placeholder terms come out of acc, the escape values go to q, and
+      // the row's outputs are then final in acc
+      static_assert(NT == 8, "the transposed x holds eight activation tiles");
+      const uint32_t lds_lim = t_e0 + t_cnt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float q[NT];
+#pragma unroll
+        for (int cc = 0; cc < NT; ++cc) q[cc] = 0.f;
+        for (uint32_t e = st[r]; e < st[r + 1]; e += 4) {
+          uint32_t col[4];
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t ei = e + i;
+            const bool in = ei < st[r + 1];
+            const bool lds = ei < lds_lim;
+            const uint32_t at = lds ? ei - t_e0 : 0u;
+            col[i] = !in ? 0u : lds ? s_ecol[w][at] : a.esc_col[ei];
+            v[i] = !in ? 0.f : bf16_to_float(lds ? s_eval[w][at] : a.esc_val[ei]);
+          }
+          u32x4 xw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            xw[i] = e + i < st[r + 1]
+                        ? *reinterpret_cast<const u32x4*>(a.xt + (int64_t)col[i] * 128 + 8 * r16)
+                        : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (e + i >= st[r + 1]) break;
+#pragma unroll
+            for (int cc = 0; cc < NT; ++cc) {
+              const uint32_t wd = xw[i][cc >> 1];
+              const float xv = __builtin_bit_cast(float, (cc & 1) ? wd & 0xFFFF0000u : wd << 16);
+              acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+              q[cc] = fmaf(xv, v[i], q[cc]);
+            }
+          }
+        }
+        const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+#pragma unroll
+        for (int cc = 0; cc < NT; ++cc) acc[cc][r] = fmaf(sc, acc[cc][r], q[cc]);
+      }
+    }
     if constexpr (!TOP1) {
       // lane (g, r16) holds rows 4 g .. 4 g + 3 of x row 16 cc + r16: written to the wave's part of
       // the idle x buffer as [x row][20 floats] (4 of padding), read back so that lane l holds
       // rows 4 (l % 4) .. +3 of x row 16 j + l / 4, and stored as one 16-byte vector (or four
       // floats when y is not 16-byte aligned).  Every wave is past the last chunk's barrier, and
       // the next tile's loads into this buffer wait for the barrier at its start.
-      float* res = reinterpret_cast<float*>(&s_x[0][0]) + w * (16 * NT * 20);
+      // (two activation tiles at a time: the region of eight would not fit)
+      constexpr int CG = NT < 2 ? NT : 2;
+      float* res = reinterpret_cast<float*>(&s_x[0][0]) + w * (16 * CG * 20);
+      const int q = lane & 3;
 #pragma unroll
-      for (int cc = 0; cc < NT; ++cc) {
+      for (int c0g = 0; c0g < NT; c0g += CG) {
+      if (c0g > 0) __builtin_amdgcn_wave_barrier();   // the group before has read its region
+#pragma unroll
+      for (int cc = c0g; cc < c0g + CG; ++cc) {
         float v4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
-          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r]) : acc[cc][r];
+          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
+                       : acc[cc][r];
         }
-        *reinterpret_cast<floatx4*>(&res[(16 * cc + r16) * 20 + 4 * g]) = (floatx4){v4[0], v4[1], v4[2], v4[3]};
+        *reinterpret_cast<floatx4*>(&res[(16 * (cc - c0g) + r16) * 20 + 4 * g]) = (floatx4){v4[0], v4[1], v4[2], v4[3]};
       }
       __builtin_amdgcn_wave_barrier();
-      const int q = lane & 3;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
+      for (int j = c0g; j < c0g + CG; ++j) {
         const int mcol = 16 * j + (lane >> 2);
-        const floatx4 o = *reinterpret_cast<const floatx4*>(&res[mcol * 20 + 4 * q]);
+        const floatx4 o = *reinterpret_cast<const floatx4*>(&res[(16 * (j - c0g) + (lane >> 2)) * 20 + 4 * q]);
         const int64_t nrow = row0 + 4 * q;
         if (mcol < a.m) {
           float* yp = &yout[mcol * a.ldy + nrow];
@@ -430,6 +490,7 @@ void k_mfma(MfmaArgs a) {
           }
         }
       }
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -441,7 +502,7 @@ void k_mfma(MfmaArgs a) {
           const int mcol = 16 * cc + r16;
           if (mcol >= a.m) continue;
           const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
-                               : acc[cc][r];
+                               : acc[cc][r];   // (with kEscEpi acc is already final)
           const uint64_t key = top1_key(v, nrow);
           best[cc] = key > best[cc] ? key : best[cc];
         }
@@ -474,6 +535,8 @@ void k_mfma(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int FMT, int W>
 static MfmaKernel pick(int nt) {
+  if constexpr (W == 12)
+    if (nt == 8) return k_mfma<FMT, 8, W, false>;
   if (nt >= 3) return mfma_wide_kernel(static_cast<Fmt>(FMT), nt);
   return nt == 1 ? k_mfma<FMT, 1, W, false> : k_mfma<FMT, 2, W, false>;
 }
@@ -502,7 +565,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
                             size_t ws_off = 0) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   const int64_t kb = k / kTileCols;
-  const int nt = (mb + 15) / 16;
+  const int nt = mb > 64 ? 8 : (mb + 15) / 16;   // 65..128 rows: the eight-tile instantiation
   // Up to two activation tiles: the dense baseline runs 8 waves per CU with 8 blocks in flight
   // when every tile fits one round of them (measured faster there), the W12 and Q8 kernels
   // always 12 waves with 4 (their decode needs three waves per SIMD to hide: 8 waves measured
@@ -510,7 +573,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   // a tile when the shape has few tiles (and at least 3), with at least 8 blocks in each;
   // their partial outputs must fit the workspace.
   int waves = kWaves;
-  int64_t chunk_blocks = kChunkBlocks;
+  int64_t chunk_blocks = nt == 8 ? 2 : kChunkBlocks;
   int64_t ranges = 1;
   if (nt <= 2) {
     if (f == kFmtBF16 && tiles <= (int64_t)di.cus * 8) {
@@ -552,6 +615,17 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.ysplit = (int64_t)mb * n;
   a.top1 = nullptr;
   a.yvec = (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
+  a.xt = nullptr;
+  if (nt == 8 && f != kFmtBF16) {
+    // x transposed into the workspace for the epilogue's escape patch (no split here)
+    float* wsx = nullptr;
+    hipError_t e = workspace(s, &wsx);
+    if (e != hipSuccess) return e;
+    uint16_t* xt = reinterpret_cast<uint16_t*>(wsx);
+    e = launch_x_transpose(x, mb, k, xt, s);
+    if (e != hipSuccess) return e;
+    a.xt = xt;
+  }
   hipLaunchKernelGGL(pick_kernel(f, nt, waves), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
                      s, a);
   hipError_t err = hipGetLastError();
@@ -585,8 +659,12 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  for (int64_t m0 = 0; m0 < m; m0 += 64) {
-    const int mb = (int)((m - m0) < 64 ? (m - m0) : 64);
+  // passes of up to 128 rows of x (each reads the weights once); the W12 and Q8 passes of more
+  // than 64 rows need x transposed in the workspace, else they stay at 64
+  const int64_t max_step = f == kFmtBF16 || k * 128 * 2 <= (int64_t)kWorkspaceBytes ? 128 : 64;
+  for (int64_t m0 = 0, step = 0; m0 < m; m0 += step) {
+    step = (m - m0) < max_step ? (m - m0) : max_step;
+    const int mb = (int)step;
     // A shape with more tiles than the chip's waves runs in rounds of one tile per wave; when the
     // last round would keep at most half of the waves busy (the LM head: 9504 tiles = 3 rounds
     // of 3072 and 288), the full rounds run as one launch and the remaining tiles as a second,
@@ -643,6 +721,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     a.ysplit = 0;
     a.top1 = keys;
     a.yvec = 0;
+    a.xt = nullptr;
     hipLaunchKernelGGL(pick_top1(f, nt), dim3((unsigned)groups), dim3(64 * kWaves), 0, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -38,6 +38,9 @@ struct MfmaArgs {
   // y (or the range's workspace slice) is 16-byte aligned and ldy % 4 == 0: the epilogue stores
   // 16-byte vectors of 4 consecutive outputs (transposed through LDS)
   int yvec;
+  // eight activation tiles (W12 and Q8): x transposed, [k][128] bfloat16 (rows past m zero); the
+  // epilogue reads the escapes' x values from it
+  const uint16_t* xt;
 };
 
 // Ordered key of output v of row n: larger v gives a larger key, and for equal v the smaller n.

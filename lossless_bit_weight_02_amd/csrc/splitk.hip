@@ -8,6 +8,31 @@
 
 namespace w12 {
 
+// x [m][k] (bfloat16 bits) -> xt [k][16][8]: xt[c][r][t] = x[16 t + r][c] (0 past m), so the
+// eight-tile matrix-core kernel's lane r16 finds the x values of rows r16, 16 + r16, ..., 112 + r16
+// at one escape column in a single 16-byte load.
+// A workgroup takes 32 columns: the 128 x rows' runs over them into LDS (row-contiguous reads),
+// then the 32 x 128 outputs out in order (contiguous writes).
+__global__ __launch_bounds__(256) void k_x_transpose(const uint16_t* __restrict__ x, int m, int64_t k,
+                                                     uint16_t* __restrict__ xt) {
+  __shared__ uint16_t tile[128][34];
+  const int64_t c0 = (int64_t)blockIdx.x * 32;
+  for (int i = threadIdx.x; i < 128 * 32; i += 256) {
+    const int j = i >> 5, c = i & 31;
+    tile[j][c] = j < m && c0 + c < k ? x[(int64_t)j * k + c0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 32 * 128; i += 256) {
+    const int c = i >> 7, p = i & 127;
+    if (c0 + c < k) xt[(c0 + c) * 128 + p] = tile[16 * (p & 7) + (p >> 3)][c];
+  }
+}
+
+hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt, hipStream_t s) {
+  hipLaunchKernelGGL(k_x_transpose, dim3((unsigned)((k + 31) / 32)), dim3(256), 0, s, x, m, k, xt);
+  return hipGetLastError();
+}
+
 // The partial slices arrive from memory (written by the previous kernel): every thread issues
 // the loads of up to 16 slices at once -- buffer loads, which return 0 past the last slice
 // instead of needing a branch -- and then adds them in order.

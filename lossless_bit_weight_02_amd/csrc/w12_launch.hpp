@@ -46,6 +46,10 @@ struct Planes {
   const uint16_t* w = nullptr;  // kFmtBF16 only: the dense bfloat16 weight, tiled storage order
 };
 
+// x [m <= 128][k] bfloat16 -> xt [k][16][8], xt[c][r][t] = x[16 t + r][c] (rows past m zero),
+// for the eight-tile GEMM's escapes
+hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt, hipStream_t s);
+
 // encoder: window choice per row (writes base[n] and the escape count of row i to esc_ptr[i+1])
 hipError_t launch_analyze(const uint16_t* w, int64_t n, int64_t k, uint8_t* base, uint32_t* esc_ptr,
                           hipStream_t s);

@@ -461,3 +461,43 @@ def test_q8_midpoint_gemm(n, k, ms):
     for path in ("gemv", "mfma"):
         y = w12.q8_gemm(to_dev(x), rec, path=path, midpoint=True).cpu().numpy().astype(np.float64)
         assert np.array_equal(y, oracle.bf16_to_f64(qm[:, cols]).T), path
+
+
+@pytest.mark.parametrize("n,k,m", [(4099, 640, 128), (300, 1152, 200), (64, 5120, 100), (16, 128, 65)])
+def test_gemm_more_than_64_rows(n, k, m):
+    """65..128 rows of x per weight read (eight activation tiles; escapes patched by a second
+    kernel), passes of 128 above that; every format against the oracle."""
+    rng = np.random.default_rng(n + k + m)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[rng.random((n, k)) < 1e-3] = 0x4480                                # outliers far above the window
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    _gemm_case(w, x, f"m>64 {n}x{k}", paths=("mfma",))
+    w12 = _w12()
+    rec = w12.encode(to_dev(w))
+    y = w12.q8_gemm(to_dev(x), rec, midpoint=True).cpu().numpy()
+    check_gemm(y, x, oracle.q8_view_bits(oracle.encode(w), midpoint=True), f"m>64 {n}x{k} q8 midpoint")
+
+
+def test_gemm_more_than_64_rows_one_hot_exact():
+    """x = e_c for 100 columns (escaped ones included) through the eight-tile path: every output
+    is exactly one weight, on the exact pass and both Q passes."""
+    w12 = _w12()
+    n, k = 256, 1024
+    rng = np.random.default_rng(21)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.02] = 0
+    w[5, 17] = 0x4500
+    w[9, 700] = 0x0001                                                   # subnormal escape
+    rec = w12.encode(to_dev(w))
+    ref = oracle.encode(w)
+    cols = sorted(set(rng.choice(k, 97, replace=False).tolist()) | {17, 700, 0})[:100]
+    x = np.zeros((len(cols), k), np.uint16)
+    for i, c in enumerate(cols):
+        x[i, c] = 0x3F80
+    xd = to_dev(x)
+    for fn, wv in ((lambda: w12.gemm(xd, rec, path="mfma"), w),
+                   (lambda: w12.q8_gemm(xd, rec, path="mfma"), oracle.q8_view_bits(ref)),
+                   (lambda: w12.q8_gemm(xd, rec, path="mfma", midpoint=True), oracle.q8_view_bits(ref, midpoint=True))):
+        y = fn().cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, oracle.bf16_to_f64(wv[:, cols]).T)
