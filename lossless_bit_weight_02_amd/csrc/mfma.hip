@@ -570,8 +570,10 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   // when every tile fits one round of them (measured faster there), the W12 and Q8 kernels
   // always 12 waves with 4 (their decode needs three waves per SIMD to hide: 8 waves measured
   // 49 us against 39 us on W [17408, 5120] at 32 rows).  k ranges: as many as give every wave
-  // a tile when the shape has few tiles (and at least 3), with at least 8 blocks in each;
-  // their partial outputs must fit the workspace.
+  // a tile when the shape has few tiles (at least 2), with at least 4 blocks (W12, Q8: one
+  // chunk) or 8 (dense) in each; their partial outputs must fit the workspace.  (Longer W12
+  // ranges measured slower on every layer shape: at 32 rows, W [6144, 5120] 21.8 us with ranges
+  // of 8 blocks, 24.6 with 16, 30.5 with 24.)
   int waves = kWaves;
   int64_t chunk_blocks = nt == 8 ? 2 : kChunkBlocks;
   int64_t ranges = 1;
@@ -582,11 +584,11 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
     }
     const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
     ranges = (int64_t)di.cus * waves / tiles;
-    const int64_t cap = chunks * chunk_blocks / 8;
+    const int64_t cap = chunks * chunk_blocks / (f == kFmtBF16 ? 8 : 4);
     if (ranges > cap) ranges = cap;
     if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes - ws_off)
       ranges = (int64_t)((kWorkspaceBytes - ws_off) / ((size_t)mb * n * sizeof(float)));
-    if (ranges < 3) ranges = 1;
+    if (ranges < 2) ranges = 1;
   }
   const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
   const int64_t cps = (chunks + ranges - 1) / ranges;

@@ -11,25 +11,38 @@ namespace w12 {
 // x [m][k] (bfloat16 bits) -> xt [k][16][8]: xt[c][r][t] = x[16 t + r][c] (0 past m), so the
 // eight-tile matrix-core kernel's lane r16 finds the x values of rows r16, 16 + r16, ..., 112 + r16
 // at one escape column in a single 16-byte load.
-// A workgroup takes 32 columns: the 128 x rows' runs over them into LDS (row-contiguous reads),
-// then the 32 x 128 outputs out in order (contiguous writes).
+// A workgroup takes 16 columns: thread t reads 8 of them of x row t / 2 as one 16-byte load into
+// LDS, then writes the 8 entries of run t % 16 at column t / 16 as one 16-byte store.  (x and the
+// output are 16-byte aligned and k is a multiple of 128.)
 __global__ __launch_bounds__(256) void k_x_transpose(const uint16_t* __restrict__ x, int m, int64_t k,
                                                      uint16_t* __restrict__ xt) {
-  __shared__ uint16_t tile[128][34];
-  const int64_t c0 = (int64_t)blockIdx.x * 32;
-  for (int i = threadIdx.x; i < 128 * 32; i += 256) {
-    const int j = i >> 5, c = i & 31;
-    tile[j][c] = j < m && c0 + c < k ? x[(int64_t)j * k + c0 + c] : (uint16_t)0;
+  __shared__ uint16_t tile[128][18];
+  const int64_t c0 = (int64_t)blockIdx.x * 16;
+  const int t = threadIdx.x;
+  {
+    const int j = t >> 1, h = t & 1;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j < m) v = *reinterpret_cast<const u32x4*>(x + (int64_t)j * k + c0 + 8 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[j][8 * h + 2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+      tile[j][8 * h + 2 * i + 1] = (uint16_t)(v[i] >> 16);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 32 * 128; i += 256) {
-    const int c = i >> 7, p = i & 127;
-    if (c0 + c < k) xt[(c0 + c) * 128 + p] = tile[16 * (p & 7) + (p >> 3)][c];
+  {
+    const int c = t >> 4, r = t & 15;
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)tile[16 * (2 * i) + r][c] | (uint32_t)tile[16 * (2 * i + 1) + r][c] << 16;
+    *reinterpret_cast<u32x4*>(xt + (c0 + c) * 128 + 8 * r) = o;
   }
 }
 
 hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt, hipStream_t s) {
-  hipLaunchKernelGGL(k_x_transpose, dim3((unsigned)((k + 31) / 32)), dim3(256), 0, s, x, m, k, xt);
+  if (k % 16 != 0 || m > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_x_transpose, dim3((unsigned)(k / 16)), dim3(256), 0, s, x, m, k, xt);
   return hipGetLastError();
 }
 
