@@ -37,7 +37,9 @@
  *     it keeps no other per-call state.
  *   - GEMM workspace: a GEMM call whose shape has too few 16-row tiles to occupy the device
  *     (for example W [1024, 5120], or [5120, 17408] at up to 32 rows of x) splits each row into
- *     k ranges whose partial sums go to a 64 MiB device buffer, then adds them in range order.
+ *     k ranges whose partial sums go to a 64 MiB device buffer, then adds them in range order;
+ *     a W12 or Q8 call with more than 64 rows of x puts a transposed copy of each pass's (up to
+ *     128) rows there (k x 256 bytes; with k > 262144 the passes stay at 64 rows and need none).
  *     The buffer belongs to the (device, stream) pair, is allocated with hipMalloc on the first
  *     such call on that stream (also while the stream is being captured into a graph: the
  *     allocation is made under the relaxed capture mode) and is kept until the process ends.
