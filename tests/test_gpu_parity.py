@@ -170,6 +170,37 @@ def test_gemm_attn_m1():
     _gemm_case(w, x, "attn 5120x5120")
 
 
+def _seeded_shapes(count, seed):
+    """Shapes drawn once from a fixed seed: ragged n, k a multiple of 128, m up to 260 (so the
+    GEMV, the one-, two-, three/four- and eight-tile matrix-core kernels, split k and passes of
+    128 rows all occur)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        n = int(rng.integers(1, 900))
+        k = 128 * int(rng.integers(1, 24))
+        m = int(rng.choice([int(rng.integers(1, 9)), int(rng.integers(9, 65)), int(rng.integers(65, 261))]))
+        out.append((n, k, m))
+    return out
+
+
+@pytest.mark.parametrize("n,k,m", _seeded_shapes(16, 2027))
+def test_gemm_seeded_shapes_auto_path(n, k, m):
+    """The automatic kernel choice on seeded shapes: exact pass, Q pass (both views) and the dense
+    baseline against the oracle; zeros and far outliers make escapes in most tiles."""
+    rng = np.random.default_rng(n * 131 + k * 7 + m)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[rng.random((n, k)) < 5e-4] = 0x4400
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    _gemm_case(w, x, f"seeded {n}x{k}", paths=("auto",))
+    w12 = _w12()
+    rec = w12.encode(to_dev(w))
+    say(f"q8_gemm midpoint seeded {n}x{k} m={m}")
+    y = w12.q8_gemm(to_dev(x), rec, midpoint=True).cpu().numpy()
+    check_gemm(y, x, oracle.q8_view_bits(oracle.encode(w), midpoint=True), f"seeded {n}x{k} q8 midpoint")
+
+
 @pytest.mark.parametrize("n,k,m", [(1, 128, 1), (37, 256, 3), (129, 384, 16), (300, 1152, 8),
                                    (300, 1152, 40), (77, 4224, 1), (64, 9216, 8), (50, 640, 2),
                                    (33, 128, 64), (16, 3968, 5), (1000, 2176, 33), (8, 128, 100)])
