@@ -27,7 +27,7 @@ per projection and in the qkv / gate_up layout.  These are timed as captured HIP
 replays are checked bit for bit against eager launches; their outputs are sampled into the CPU
 oracle leg.
 
-Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  `--gpus N` with N > 1 exits: the kernels here run on one GPU.
 """
 from __future__ import annotations
 
