@@ -83,6 +83,15 @@ extern "C" {
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16
  * values the 8-bit view stands for) instead of 0; escapes stay exact */
 #define W12_Q8_MIDPOINT 0x10u
+/* flag for w12_gemm, w12_q8_gemm and w12_bf16_gemm: y is written as bfloat16 bits instead of
+ * float -- each output is the float result of the same call without the flag, rounded to nearest
+ * (ties to even; NaN stays NaN).  y then points to uint16_t [m][n] (2-byte aligned), passed as the
+ * float* argument.  The rounding happens where the output is stored (the GEMM's epilogue, or the
+ * ordered sum of a split-k launch), so no float copy of y is written; a GEMV whose x rows do not
+ * fit LDS in one piece (several k slices) adds them in float in the GEMM workspace first.  The
+ * error bound becomes 1e-3 * sum_k |x[m][k] * W[n][k]| plus half a bfloat16 unit in the last
+ * place of the output. */
+#define W12_OUT_BF16 0x20u
 
 /* A W12 tensor: a non-owning view.  Every pointer is device memory owned by the caller. */
 typedef struct w12_weight {

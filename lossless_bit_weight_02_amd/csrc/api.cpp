@@ -81,13 +81,19 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
     f = w12::kFmtQ8M;
     flags &= ~W12_Q8_MIDPOINT;
   }
+  const bool out16 = (flags & W12_OUT_BF16) != 0;
+  flags &= ~W12_OUT_BF16;
   if (flags > W12_PATH_MFMA) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
-  if (!aligned4(y)) return fail(W12_ERR_ALIGN, "y must be 4-byte aligned");
+  if (out16 ? (reinterpret_cast<uintptr_t>(y) & 1u) != 0 : !aligned4(y))
+    return fail(W12_ERR_ALIGN, out16 ? "y must be 2-byte aligned" : "y must be 4-byte aligned");
+  w12::YOut yo;
+  if (out16) yo.h = reinterpret_cast<uint16_t*>(y);
+  else yo.f = y;
   // GEMV up to 4 rows: from 5 rows on the matrix-core kernel is faster on the 27B-class shapes
   const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && m <= 4);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, y, s) : w12::launch_mfma(f, x, m, p, n, k, y, s);
+  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s) : w12::launch_mfma(f, x, m, p, n, k, yo, s);
   if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
   return ok();
 }

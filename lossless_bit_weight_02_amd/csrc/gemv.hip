@@ -56,6 +56,7 @@ struct GemvArgs {
   int splits;             // k ranges of the slice: workgroup b takes range b % splits
   int64_t kend;           // end of the slice (the last range may be shorter)
   int64_t ysplit;         // floats between the partial outputs of consecutive ranges
+  uint16_t* y16;          // set (one slice, one range): outputs as bfloat16 (nearest even) here
 };
 
 // One 128-column block of the lane's row: the raw 128-bit words it loads.
@@ -334,6 +335,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float v = FMT != kFmtBF16 ? fmaf(sc, acc[m], q[m]) : acc[m];
+        if (a.y16) {
+          a.y16[m * a.ldy + row] = float_to_bf16_rne(v);
+          continue;
+        }
         float* yp = yout + m * a.ldy + row;
         // later k-slices add to y; the read stays in its branch (a hoisted read would make every
         // tile wait for the whole stream in flight)
@@ -389,7 +394,7 @@ static GemvKernel pick_kernel(Fmt f, int m) {
 }
 
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       float* y, hipStream_t s) {
+                       YOut y, hipStream_t s) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
@@ -439,6 +444,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     a.ldy = n;
     a.n = n; a.k = k;
     a.x = x + m0 * k;
+    a.y16 = nullptr;
     if (ws) {
       // one launch over all ranges into the workspace, then the ordered sum into y
       int64_t groups = slots / ranges;
@@ -456,9 +462,18 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
       if (err != hipSuccess) return err;
       continue;
     }
-    // one range per launch: later slices add to y in slice order
+    // one range per launch: later slices add to y in slice order (bfloat16 output over several
+    // slices: they add in float in the workspace, then a one-range reduce rounds them into y)
     int64_t groups = passes < slots ? passes : slots;
-    a.y = y + m0 * n;
+    const YOut yp = y + m0 * n;
+    float* acc32 = nullptr;
+    if (yp.h && k > slice) {
+      if ((size_t)mb * n * sizeof(float) > kWorkspaceBytes) return hipErrorInvalidValue;
+      err = workspace(s, &acc32);
+      if (err != hipSuccess) return err;
+    }
+    a.y = yp.h ? acc32 : yp.f;
+    a.y16 = yp.h && !acc32 ? yp.h : nullptr;
     a.splits = 1;
     a.ysplit = 0;
     for (int64_t k0 = 0; k0 < k; k0 += slice) {
@@ -467,6 +482,10 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
       a.accumulate = k0 > 0;
       hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kBlock), (size_t)2 * mb * kn, s, a);
       err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    if (acc32) {
+      err = launch_split_reduce(acc32, 1, mb, n, yp, n, s);
       if (err != hipSuccess) return err;
     }
   }

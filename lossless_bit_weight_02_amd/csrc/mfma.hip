@@ -479,7 +479,12 @@ void k_mfma(MfmaArgs a) {
         const int mcol = 16 * j + (lane >> 2);
         const floatx4 o = *reinterpret_cast<const floatx4*>(&res[(16 * (j - c0g) + (lane >> 2)) * 20 + 4 * q]);
         const int64_t nrow = row0 + 4 * q;
-        if (mcol < a.m) {
+        if (mcol < a.m && a.y16) {
+          uint16_t* yq = &a.y16[mcol * a.ldy + nrow];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nrow + i < a.n) yq[i] = float_to_bf16_rne(o[i]);
+        } else if (mcol < a.m) {
           float* yp = &yout[mcol * a.ldy + nrow];
           if (a.yvec) {
             if (nrow < a.n) *reinterpret_cast<floatx4*>(yp) = o;
@@ -561,7 +566,7 @@ static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
 // y[j * ldy + 0 .. n).
 // Partial sums of a split go to the workspace from byte ws_off on.
 static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb, const Planes& p,
-                            int64_t n, int64_t k, float* y, int64_t ldy, hipStream_t s,
+                            int64_t n, int64_t k, YOut y, int64_t ldy, hipStream_t s,
                             size_t ws_off = 0) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   const int64_t kb = k / kTileCols;
@@ -608,7 +613,8 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.base = p.base; a.ae = p.ae; a.lo = p.lo;
   a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
   a.w = p.w;
-  a.y = ws ? ws : y;
+  a.y = ws ? ws : y.f;
+  a.y16 = ws ? nullptr : y.h;
   a.ldy = ws ? n : ldy;                        // partial slices are [mb][n], contiguous
   a.n = n; a.k = k;
   a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
@@ -616,7 +622,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.cps = (int)cps;
   a.ysplit = (int64_t)mb * n;
   a.top1 = nullptr;
-  a.yvec = (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
+  a.yvec = a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
   a.xt = nullptr;
   if (nt == 8 && f != kFmtBF16) {
     // x transposed into the workspace for the epilogue's escape patch (no split here)
@@ -656,7 +662,7 @@ static Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
 }
 
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       float* y, hipStream_t s) {
+                       YOut y, hipStream_t s) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
@@ -715,6 +721,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
     a.w = p.w;
     a.y = nullptr;
+    a.y16 = nullptr;
     a.ldy = nh;
     a.n = nh; a.k = k;
     a.rounds = (int)((th + groups * kWaves - 1) / (groups * kWaves));
@@ -729,7 +736,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     if (err != hipSuccess) return err;
     int g_all = (int)groups;
     if (r0 > 0) {
-      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, ytail, n - r0, s,
+      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, yout_f(ytail), n - r0, s,
                       size_t(4) << 20);
       if (err != hipSuccess) return err;
       err = launch_top1_rows(ytail, mb, n - r0, r0, keys + (int64_t)groups * 32, s);

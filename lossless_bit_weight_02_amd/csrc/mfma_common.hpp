@@ -38,6 +38,8 @@ struct MfmaArgs {
   // y (or the range's workspace slice) is 16-byte aligned and ldy % 4 == 0: the epilogue stores
   // 16-byte vectors of 4 consecutive outputs (transposed through LDS)
   int yvec;
+  // with y16 set (a single k range), the outputs go there as bfloat16 (nearest even) instead of y
+  uint16_t* y16;
   // eight activation tiles (W12 and Q8): x transposed, [k][128] bfloat16 (rows past m zero); the
   // epilogue reads the escapes' x values from it
   const uint16_t* xt;

@@ -321,7 +321,8 @@ void k_mfma_wide(MfmaArgs a) {
         if (mcol >= a.m) continue;
         const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
                              : acc[cc][r];
-        a.y[mcol * a.ldy + nrow] = v;
+        if (a.y16) a.y16[mcol * a.ldy + nrow] = float_to_bf16_rne(v);
+        else a.y[mcol * a.ldy + nrow] = v;
       }
     }
   }

@@ -51,7 +51,8 @@ hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt,
 // instead of needing a branch -- and then adds them in order.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits,
                                                       int64_t rows, int64_t cols,
-                                                      float* __restrict__ y, int64_t ldy) {
+                                                      float* __restrict__ y, uint16_t* __restrict__ y16,
+                                                      int64_t ldy) {
   const int64_t cnt = rows * cols;
   const Rsrc rp = make_rsrc(part, (uint32_t)((int64_t)splits * cnt * 4));
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
         if (j0 + j < splits) s = (j0 + j == 0) ? v[j] : s + v[j];
     }
     const int64_t r = i / cols;
-    y[r * ldy + (i - r * cols)] = s;
+    if (y16) y16[r * ldy + (i - r * cols)] = float_to_bf16_rne(s);
+    else y[r * ldy + (i - r * cols)] = s;
   }
 }
 
@@ -136,11 +138,12 @@ hipError_t launch_top1_final(const uint64_t* part, int groups, int m, int32_t* i
   return hipGetLastError();
 }
 
-hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, float* y,
+hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, YOut y,
                                int64_t ldy, hipStream_t s) {
   int64_t blocks = (rows * cols + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, rows, cols, y, ldy);
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, rows, cols,
+                     y.f, y.h, ldy);
   return hipGetLastError();
 }
 

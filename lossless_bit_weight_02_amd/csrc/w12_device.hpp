@@ -101,6 +101,13 @@ __device__ __forceinline__ void midpoint16(uint32_t p[16]) {
   for (int i = 0; i < 16; ++i) p[i] |= 0x00080008u;
 }
 
+// float -> bfloat16 bits, round to nearest, ties to even (NaN stays NaN, quieted)
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

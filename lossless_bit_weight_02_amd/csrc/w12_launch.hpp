@@ -22,9 +22,27 @@ hipError_t dev_info(DevInfo* out);
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
 hipError_t workspace(hipStream_t s, float** out);
 
+// Where a GEMM writes y: float (f), or bfloat16 bits rounded to nearest even from the float
+// result (h); exactly one of them is set.  Offsets count elements of either.
+struct YOut {
+  float* f = nullptr;
+  uint16_t* h = nullptr;
+  YOut operator+(int64_t off) const {
+    YOut r;
+    r.f = f ? f + off : nullptr;
+    r.h = h ? h + off : nullptr;
+    return r;
+  }
+};
+inline YOut yout_f(float* f) {
+  YOut r;
+  r.f = f;
+  return r;
+}
+
 // y[r * ldy + c] = sum over j = 0 .. splits-1 (in that order) of part[j * rows * cols + r * cols + c],
-// r < rows, c < cols
-hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, float* y,
+// r < rows, c < cols (splits = 1: a copy, or with y.h the rounding to bfloat16)
+hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, YOut y,
                                int64_t ldy, hipStream_t s);
 
 // best key of each row of y [m][cols] (row index row0 + column), into keys[0 .. m)
@@ -70,10 +88,10 @@ hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hi
 
 // GEMV family (wave-reduction kernel), any m (passes of <= 8 rows of x)
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       float* y, hipStream_t s);
+                       YOut y, hipStream_t s);
 // MFMA family (bf16 v_mfma_f32_16x16x32), any m (blocks of <= 64 rows of x)
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       float* y, hipStream_t s);
+                       YOut y, hipStream_t s);
 // top-1 over the n outputs of each x row (no y written), passes of <= 32 rows of x
 hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n,
                             int64_t k, int32_t* idx, float* val, hipStream_t s);

@@ -25,6 +25,7 @@ W12_ERR_HIP = -6
 
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 Q8_MIDPOINT = 0x10
+OUT_BF16 = 0x20
 _PATHS = {None: PATH_AUTO, "auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
 
 
@@ -234,32 +235,44 @@ def decode(wt: W12Weight) -> torch.Tensor:
     return decode_into(wt, torch.empty((wt.n, wt.k), dtype=torch.bfloat16, device=wt.device))
 
 
-def _gemm_out(x, n):
+def _gemm_out(x, n, bf16=False):
     x = _bits16(x)
     if x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D CUDA tensor")
-    return x.contiguous(), torch.empty((x.shape[0], n), dtype=torch.float32, device=x.device)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    return x.contiguous(), torch.empty((x.shape[0], n), dtype=dt, device=x.device)
 
 
-def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None):
-    """Exact pass: y = x W^T (fp32) with W read from its W12 record."""
+def _out_flag(out):
+    """float32 outputs, or bfloat16 ones (OUT_BF16: the float result rounded to nearest even)."""
+    if out.dtype == torch.bfloat16:
+        return OUT_BF16
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32 or bfloat16")
+    return 0
+
+
+def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None,
+         out_bf16: bool = False):
+    """Exact pass: y = x W^T (fp32, or bfloat16 with ``out_bf16`` / a bfloat16 ``out``) with W
+    read from its W12 record."""
     if out is None:
-        x, out = _gemm_out(x, wt.n)
+        x, out = _gemm_out(x, wt.n, out_bf16)
     s = wt.c_struct()
     _check(lib().w12_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
-                          _PATHS[path], _stream_handle(x.device)))
+                          _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
     return out
 
 
 def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None,
-            midpoint: bool = False):
+            midpoint: bool = False, out_bf16: bool = False):
     """Q pass: y = x W_q^T with W_q the 8-bit view (B plane taken as 0, or as 8 with
-    ``midpoint``), escapes exact."""
+    ``midpoint``), escapes exact; outputs as in gemm."""
     if out is None:
-        x, out = _gemm_out(x, wt.n)
+        x, out = _gemm_out(x, wt.n, out_bf16)
     s = wt.c_struct()
     s.lo = None
-    flags = _PATHS[path] | (Q8_MIDPOINT if midpoint else 0)
+    flags = _PATHS[path] | (Q8_MIDPOINT if midpoint else 0) | _out_flag(out)
     _check(lib().w12_q8_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
                              flags, _stream_handle(x.device)))
     return out
@@ -312,12 +325,14 @@ def bf16_tiles(w: torch.Tensor) -> Bf16Tiles:
     return Bf16Tiles(n, k, out)
 
 
-def bf16_gemm(x: torch.Tensor, wt: Bf16Tiles, path: str | None = None, out: torch.Tensor | None = None):
-    """Same-build dense baseline: y = x W^T with W plain bfloat16 (tiled storage)."""
+def bf16_gemm(x: torch.Tensor, wt: Bf16Tiles, path: str | None = None, out: torch.Tensor | None = None,
+              out_bf16: bool = False):
+    """Same-build dense baseline: y = x W^T with W plain bfloat16 (tiled storage); outputs as in
+    gemm."""
     if out is None:
-        x, out = _gemm_out(x, wt.n)
+        x, out = _gemm_out(x, wt.n, out_bf16)
     _check(lib().w12_bf16_gemm(x.data_ptr(), x.shape[0], wt.data.data_ptr(), wt.n, wt.k,
-                               out.data_ptr(), _PATHS[path], _stream_handle(x.device)))
+                               out.data_ptr(), _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
     return out
 
 

@@ -131,3 +131,20 @@ def test_midpoint_flag_only_on_the_q_pass():
     assert L.w12_q8_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1000, w12.Q8_MIDPOINT | 0x4, None) == w12.W12_ERR_ARG
     text = open(HEADER).read()
     assert int(re.search(r"#define W12_Q8_MIDPOINT (0x[0-9a-fA-F]+)u", text).group(1), 16) == w12.Q8_MIDPOINT
+
+
+def test_bf16_output_flag_host_checks():
+    """W12_OUT_BF16: the header's value is the binding's; with it y needs only 2-byte alignment,
+    an odd address is refused before anything runs, and it does not combine with top-1 calls."""
+    L = _lib()
+    text = open(HEADER).read()
+    assert int(re.search(r"#define W12_OUT_BF16 (0x[0-9a-fA-F]+)u", text).group(1), 16) == w12.OUT_BF16
+    for fl in (w12.OUT_BF16, w12.OUT_BF16 | 1, w12.OUT_BF16 | 2):
+        assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1001, fl, None) == w12.W12_ERR_ALIGN
+        assert L.w12_q8_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1001, fl | w12.Q8_MIDPOINT, None) == w12.W12_ERR_ALIGN
+        assert L.w12_bf16_gemm(0x1000, 1, 0x1000, 8, 128, 0x1001, fl, None) == w12.W12_ERR_ALIGN
+    # without the flag y stays a float array (4-byte alignment)
+    assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1002, 0, None) == w12.W12_ERR_ALIGN
+    # the exact pass still has no midpoint variant; top-1 calls write no y
+    assert L.w12_gemm(0x1000, 1, ctypes.byref(_rec()), 0x1000, w12.OUT_BF16 | w12.Q8_MIDPOINT, None) == w12.W12_ERR_ARG
+    assert L.w12_q8_top1(0x1000, 1, ctypes.byref(_rec()), 0x1000, 0x1000, w12.OUT_BF16, None) == w12.W12_ERR_ARG

@@ -535,3 +535,65 @@ def test_gemm_more_than_64_rows_one_hot_exact():
                    (lambda: w12.q8_gemm(xd, rec, path="mfma", midpoint=True), oracle.q8_view_bits(ref, midpoint=True))):
         y = fn().cpu().numpy().astype(np.float64)
         assert np.array_equal(y, oracle.bf16_to_f64(wv[:, cols]).T)
+
+
+def _check_bf16_out(y16, y32, x_bits, w_bits, what):
+    """y16 (bfloat16 output) is the float output of the same call rounded to nearest even
+    (torch's rounding on the CPU: bit for bit, NaN for NaN); with an oracle weight, also within the
+    GEMM bound plus half a bfloat16 unit in the last place."""
+    import torch
+    want = torch.from_numpy(np.ascontiguousarray(y32)).to(torch.bfloat16)
+    got = y16.cpu()
+    wn, gn = torch.isnan(want.float()), torch.isnan(got.float())
+    assert torch.equal(wn, gn), f"{what}: NaN positions differ"
+    assert torch.equal(want.view(torch.int16)[~wn], got.view(torch.int16)[~gn]), \
+        f"{what}: bfloat16 output is not the rounded float output"
+    if w_bits is None:
+        return
+    y = got.float().numpy().astype(np.float64)
+    y64 = oracle.gemm64(x_bits, w_bits)
+    b = 1e-3 * oracle.abs_bound64(x_bits, w_bits)
+    fin = np.isfinite(y64)
+    err = np.abs(y[fin] - y64[fin])
+    # round to nearest with 8 significant bits: relative error at most 2^-8
+    assert np.all(err <= b[fin] + 2.0 ** -8 * (np.abs(y64[fin]) + b[fin])), f"{what}: outside the bound"
+
+
+@pytest.mark.parametrize("n,k,m,path,oracle_check", [
+    (300, 1152, 1, "auto", True),          # GEMV
+    (300, 1152, 3, "gemv", True),
+    (100, 6144, 8, "gemv", True),          # GEMV over two k slices: float sum in the workspace
+    (64, 9216, 1, "gemv", True),           # GEMV split k: ordered sum rounds
+    (320, 2048, 16, "mfma", True),         # matrix-core split k
+    (24592, 256, 20, "mfma", False),       # matrix-core, one k range: the epilogue rounds
+    (300, 1152, 40, "mfma", True),         # three activation tiles
+    (300, 1152, 100, "mfma", True),        # eight activation tiles
+    (50752, 128, 16, "mfma", False),       # full rounds + the split tail launch
+])
+def test_gemm_bf16_output(n, k, m, path, oracle_check):
+    """W12_OUT_BF16 on every store site, for the exact pass, both Q-pass views and the baseline."""
+    import torch
+    w12 = _w12()
+    rng = np.random.default_rng(n + 3 * k + m)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[rng.random((n, k)) < 5e-4] = 0x4400
+    w[0, 0] = 0x7F80                                                       # +Inf weight: Inf output
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    rec = w12.encode(to_dev(w))
+    xd = to_dev(x)
+    dw = w12.bf16_tiles(to_dev(w))
+    ref = oracle.encode(w) if oracle_check else None
+    cases = [("w12", lambda **kw: w12.gemm(xd, rec, path=path, **kw), w),
+             ("q8", lambda **kw: w12.q8_gemm(xd, rec, path=path, **kw),
+              oracle.q8_view_bits(ref) if oracle_check else None),
+             ("q8 midpoint", lambda **kw: w12.q8_gemm(xd, rec, path=path, midpoint=True, **kw),
+              oracle.q8_view_bits(ref, midpoint=True) if oracle_check else None),
+             ("bf16", lambda **kw: w12.bf16_gemm(xd, dw, path=path, **kw), w)]
+    for name, fn, wv in cases:
+        what = f"bf16 out {name} {n}x{k} m={m} path={path}"
+        say(what)
+        y32 = fn().cpu().numpy()
+        y16 = fn(out_bf16=True)
+        assert y16.dtype == torch.bfloat16 and tuple(y16.shape) == (m, n)
+        _check_bf16_out(y16, y32, x, wv if oracle_check else None, what)
