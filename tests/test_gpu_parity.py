@@ -597,3 +597,27 @@ def test_gemm_bf16_output(n, k, m, path, oracle_check):
         y16 = fn(out_bf16=True)
         assert y16.dtype == torch.bfloat16 and tuple(y16.shape) == (m, n)
         _check_bf16_out(y16, y32, x, wv if oracle_check else None, what)
+
+
+def test_gemm_bf16_output_gemv_k_slices():
+    """The GEMV with bfloat16 outputs when its x rows need two k slices and the split-k partial
+    sums would not fit the workspace (8 rows of x, k = 6144, n = 2^20 + 16: 2 x 8 x n floats >
+    64 MiB), so the slices add in float in the workspace before one rounding: bit for bit against
+    the rounded float output of the same path."""
+    import torch
+    w12 = _w12()
+    n, k, m = (1 << 20) + 16, 6144, 8
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    w = (torch.randn((n, k), device="cuda:0", dtype=torch.float32, generator=g) * 0.02).to(torch.bfloat16)
+    x = torch.randn((m, k), device="cuda:0", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    rec = w12.encode(w)
+    del w
+    torch.cuda.empty_cache()
+    for name, fn in (("w12", lambda **kw: w12.gemm(x, rec, path="gemv", **kw)),
+                     ("q8", lambda **kw: w12.q8_gemm(x, rec, path="gemv", **kw))):
+        say(f"bf16 out gemv k slices {name} n={n}")
+        y32 = fn().cpu().numpy()
+        y16 = fn(out_bf16=True)
+        _check_bf16_out(y16, y32, None, None, f"gemv k slices {name}")
+    del rec
+    torch.cuda.empty_cache()
