@@ -77,7 +77,8 @@ extern "C" {
 #define W12_ERR_HIP      (-6)  /* HIP runtime or launch error; message from hipGetErrorString */
 
 /* flags for the GEMM calls: which kernel family runs */
-#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 4, bf16 MFMA for m >= 5 */
+#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 2, and for m <= 5 on shapes of at
+                           * most 1024 16-row tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16

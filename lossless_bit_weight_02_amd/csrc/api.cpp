@@ -90,8 +90,14 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   w12::YOut yo;
   if (out16) yo.h = reinterpret_cast<uint16_t*>(y);
   else yo.f = y;
-  // GEMV up to 4 rows: from 5 rows on the matrix-core kernel is faster on the 27B-class shapes
-  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && m <= 4);
+  // Automatic choice, from measurements on the 27B-class shapes (W12 / Q8, us, GEMV vs matrix
+  // core): the GEMV wins at 1-2 rows everywhere; at 3-5 rows it wins on shapes with few tiles and
+  // rows of at most 8192 (stacked qkv [8192, 5120], 5 rows: 18.2 vs 20.4) and loses on long rows
+  // (down [5120, 17408], 4 rows: 43.0 vs 32.1); on gate+up [34816, 5120] the two are within 1 us
+  // at 3-4 rows and the matrix cores win from 5 (58.6 vs 46.3).
+  const int64_t tiles = (n + 15) / 16;
+  const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
+  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s) : w12::launch_mfma(f, x, m, p, n, k, yo, s);
   if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
