@@ -231,55 +231,61 @@ __global__ __launch_bounds__(kBlock) void k_pack(const uint16_t* __restrict__ w,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decoder: one thread per aligned group of 8 weights of a real row.  The group's w' pairs
+// Decoder: one thread per aligned group of 16 weights of a real row (as two groups of 8).  The group's w' pairs
 // (exponent 112 + E) get (base - 112) added to both exponent fields at once:
 // (base - 112) * 0x00800080 mod 2^32.  Neither half can carry or borrow into the other because
 // base + E stays within 1..254.  Reads the tiled planes, writes row-major bf16.
 // ---------------------------------------------------------------------------------------------
-constexpr int kDecU = 4;   // tiles per workgroup pass of the decoder (loads issued together)
+constexpr int kDecU = 4;   // units of two tiles per workgroup pass of the decoder (loads issued together)
 
 __global__ __launch_bounds__(kBlock) void k_decode(const uint8_t* __restrict__ base,
                                                    const uint8_t* __restrict__ ae,
                                                    const uint8_t* __restrict__ lo, int64_t n,
                                                    int64_t k, uint16_t* __restrict__ out) {
-  // Thread u handles row r = u / 16 of a tile, columns 8 c8 .. 8 c8 + 7 (c8 = u % 16), so a
-  // wave writes four 256-byte row segments.  Those 8 AE bytes sit at 1024 h + 16 (r + 16 g) +
-  // 8 (c8 % 2) with g = c8 / 4, h = (c8 / 2) % 2, their B nibbles in the 4 bytes at
-  // 16 (r + 16 g) + 4 (c8 % 4) of the tile's B plane.  A workgroup takes kDecU tiles per pass
-  // and issues all their loads before decoding, so enough bytes are in flight per CU.
+  // A workgroup pass takes two tiles per unit; thread u works on tile 2 U + u / 128 of unit U,
+  // row r = (u % 128) / 8 of it, columns 16 j .. 16 j + 15 with j = u % 8 (g = j / 2, h = j % 2).
+  // Those 16 AE bytes sit at 1024 h + 16 (r + 16 g), their B nibbles in the 8 bytes at
+  // 16 (r + 16 g) + 8 h of the tile's B plane (one 16-byte and one 8-byte load), and eight
+  // lanes write one row's 256 output bytes.  A workgroup issues the loads of kDecU units before
+  // decoding, so enough bytes are in flight per CU.
   const int64_t ktiles = k / kTileCols;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows * ktiles;
+  const int64_t units = (tiles + 1) / 2;
   const uint32_t e112 = exp112_pair();
-  const int u = threadIdx.x, r = u >> 4, c8 = u & 15;
-  const int g = c8 >> 2, h = (c8 >> 1) & 1;
-  const uint32_t ae_off = 1024u * h + 16u * (r + 16 * g) + 8u * (c8 & 1);
-  const uint32_t lo_off = 16u * (r + 16 * g) + 4u * (c8 & 3);
+  const int u = threadIdx.x, sub = u >> 7, r = (u & 127) >> 3, j = u & 7;
+  const int g = j >> 1, h = j & 1;
+  const uint32_t ae_off = 1024u * h + 16u * (r + 16 * g);
+  const uint32_t lo_off = 16u * (r + 16 * g) + 8u * h;
   const int64_t step = (int64_t)gridDim.x * kDecU;
-  for (int64_t t0 = blockIdx.x; t0 < tiles; t0 += step) {
-    u32x2 a[kDecU];
-    uint32_t lw[kDecU], bs[kDecU];
+  for (int64_t u0 = blockIdx.x; u0 < units; u0 += step) {
+    u32x4 a[kDecU];
+    u32x2 lw[kDecU];
+    uint32_t bs[kDecU];
 #pragma unroll
     for (int i = 0; i < kDecU; ++i) {
-      const int64_t t = t0 + (int64_t)i * gridDim.x;
+      const int64_t t = 2 * (u0 + (int64_t)i * gridDim.x) + sub;
       const bool ok = t < tiles;
       const int64_t tt = ok ? t : 0;
       const int64_t row = (tt / ktiles) * kTileRows + r;
-      a[i] = load_nt(reinterpret_cast<const u32x2*>(ae + tt * kTileAE + ae_off));
-      lw[i] = load_nt(reinterpret_cast<const uint32_t*>(lo + tt * kTileLO + lo_off));
+      a[i] = load_nt(reinterpret_cast<const u32x4*>(ae + tt * kTileAE + ae_off));
+      lw[i] = load_nt(reinterpret_cast<const u32x2*>(lo + tt * kTileLO + lo_off));
       bs[i] = base[row < n ? row : n - 1];
     }
 #pragma unroll
     for (int i = 0; i < kDecU; ++i) {
-      const int64_t t = t0 + (int64_t)i * gridDim.x;
+      const int64_t t = 2 * (u0 + (int64_t)i * gridDim.x) + sub;
       const int64_t row = (t / ktiles) * kTileRows + r;
       if (t >= tiles || row >= n) continue;
-      const int64_t col = (t % ktiles) * kTileCols + 8 * c8;
+      const int64_t col = (t % ktiles) * kTileCols + 16 * j;
       const uint32_t shift = (bs[i] - 112u) * 0x00800080u;
-      uint32_t p[4];
-      window_group8(a[i].x, a[i].y, lw[i], e112, p);
-      const u32x4 res = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
-      // streaming store: the decoded matrix is not read back by this kernel
-      __builtin_nontemporal_store(res, reinterpret_cast<u32x4*>(out + row * k + col));
+      uint32_t p[8];
+      window_group8(a[i].x, a[i].y, lw[i].x, e112, p);
+      window_group8(a[i].z, a[i].w, lw[i].y, e112, p + 4);
+      const u32x4 r0 = {p[0] + shift, p[1] + shift, p[2] + shift, p[3] + shift};
+      const u32x4 r1 = {p[4] + shift, p[5] + shift, p[6] + shift, p[7] + shift};
+      // streaming stores: the decoded matrix is not read back by this kernel
+      __builtin_nontemporal_store(r0, reinterpret_cast<u32x4*>(out + row * k + col));
+      __builtin_nontemporal_store(r1, reinterpret_cast<u32x4*>(out + row * k + col + 8));
     }
   }
 }
@@ -409,7 +415,7 @@ hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, h
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows * (k / kTileCols);
   const int64_t cap = (int64_t)di.cus * 8;
-  const int64_t want = (tiles + kDecU - 1) / kDecU;
+  const int64_t want = ((tiles + 1) / 2 + kDecU - 1) / kDecU;
   hipLaunchKernelGGL(k_decode, dim3((unsigned)(want < cap ? want : cap)), dim3(kBlock), 0, s, p.base,
                      p.ae, p.lo, n, k, out);
   err = hipGetLastError();
