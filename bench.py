@@ -20,7 +20,8 @@ on; the per-launch time is the elapsed time / launches (the M=1 groups launch ev
 so the gap around an event pair weighs less).
 
 Beside the step (context, outside `value` and `ms_per_step`): an M sweep on gate+up (GEMV and MFMA
-families, W12 and BF16) and the vendor library's bf16 GEMM; the attention projection [5120, 5120]
+families, W12 and BF16, W12 with bfloat16 outputs at M = 1, 32, 128) and the vendor library's
+bf16 GEMM; the attention projection [5120, 5120]
 at M=1; the LM-head-like [152064, 5120] Q pass at M=16 (truncated and midpoint views, exact pass,
 top-1 entry points, BF16, top-1 agreement); and the 64-layer 27B-class stack at M=1 and M=32,
 per projection and in the qkv / gate_up layout.  These are timed as captured HIP graphs whose
@@ -595,7 +596,7 @@ def main():
             xm = xs[:m].contiguous()
             ym = torch.empty((m, n), dtype=torch.float32, device=dev)
             row = {}
-            # above 64 rows only the matrix-core path (passes of 64 rows, each reading W once)
+            # above 64 rows only the matrix-core path (passes of up to 128 rows, each reading W once)
             for path in (("gemv", "mfma") if m <= 64 else ("mfma",)):
                 for fmt in ("w12", "bf16"):
                     def run(r, fmt=fmt, path=path):
@@ -615,6 +616,21 @@ def main():
                     byt = w12_bytes(n, k, n_esc, m) if fmt == "w12" else bf16_bytes(n, k, m)
                     row[f"{fmt}_{path}_us"] = round(t * 1e6, 2)
                     row[f"{fmt}_{path}_gbs"] = round(byt / t / 1e9, 1)
+            if m in (1, 32, 128):
+                # the same W12 GEMM with bfloat16 outputs (rounded where they are stored)
+                path = "gemv" if m == 1 else "mfma"
+                ym16 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                w12.gemm(xm, recs[0], path=path, out=ym16)
+                reps = 2 * rot
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ea.record(stream)
+                for r in range(reps):
+                    w12.gemm(xm, recs[r % rot], path=path, out=ym16)
+                eb.record(stream)
+                torch.cuda.synchronize()
+                t = ea.elapsed_time(eb) * 1e-3 / reps
+                row["w12_bf16out_us"] = round(t * 1e6, 2)
+                row["w12_bf16out_gbs"] = round((w12_bytes(n, k, n_esc, m) - 2 * m * n) / t / 1e9, 1)
             row["best_w12_path"] = "gemv" if row.get("w12_gemv_us", 1e30) <= row["w12_mfma_us"] else "mfma"
             row["w12_mfma_tflops"] = round(2 * m * n * k / (row["w12_mfma_us"] * 1e-6) / 1e12, 1)
             sweep[str(m)] = row

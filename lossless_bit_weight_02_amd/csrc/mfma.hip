@@ -481,9 +481,15 @@ void k_mfma(MfmaArgs a) {
         const int64_t nrow = row0 + 4 * q;
         if (mcol < a.m && a.y16) {
           uint16_t* yq = &a.y16[mcol * a.ldy + nrow];
+          if (a.yvec && nrow + 3 < a.n) {
+            const u32x2 pk = {(uint32_t)float_to_bf16_rne(o[0]) | (uint32_t)float_to_bf16_rne(o[1]) << 16,
+                              (uint32_t)float_to_bf16_rne(o[2]) | (uint32_t)float_to_bf16_rne(o[3]) << 16};
+            *reinterpret_cast<u32x2*>(yq) = pk;
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (nrow + i < a.n) yq[i] = float_to_bf16_rne(o[i]);
+            for (int i = 0; i < 4; ++i)
+              if (nrow + i < a.n) yq[i] = float_to_bf16_rne(o[i]);
+          }
         } else if (mcol < a.m) {
           float* yp = &yout[mcol * a.ldy + nrow];
           if (a.yvec) {
@@ -622,7 +628,9 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.cps = (int)cps;
   a.ysplit = (int64_t)mb * n;
   a.top1 = nullptr;
-  a.yvec = a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
+  // vector stores: 16 bytes of float (y 16-byte aligned) or 8 of bfloat16 (y16 8-byte aligned)
+  a.yvec = a.y16 ? (reinterpret_cast<uintptr_t>(a.y16) & 7u) == 0 && a.ldy % 4 == 0
+                 : a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
   a.xt = nullptr;
   if (nt == 8 && f != kFmtBF16) {
     // x transposed into the workspace for the epilogue's escape patch (no split here)

@@ -565,10 +565,11 @@ def _check_bf16_out(y16, y32, x_bits, w_bits, what):
     (100, 6144, 8, "gemv", True),          # GEMV over two k slices: float sum in the workspace
     (64, 9216, 1, "gemv", True),           # GEMV split k: ordered sum rounds
     (320, 2048, 16, "mfma", True),         # matrix-core split k
-    (24592, 256, 20, "mfma", False),       # matrix-core, one k range: the epilogue rounds
+    (24593, 256, 20, "mfma", False),       # matrix-core, one k range: the epilogue rounds (n % 4 = 1:
+                                           # 2-byte stores)
     (300, 1152, 40, "mfma", True),         # three activation tiles
     (300, 1152, 100, "mfma", True),        # eight activation tiles
-    (50752, 128, 16, "mfma", False),       # full rounds + the split tail launch
+    (50752, 128, 16, "mfma", False),       # full rounds (8-byte stores) + the split tail launch
 ])
 def test_gemm_bf16_output(n, k, m, path, oracle_check):
     """W12_OUT_BF16 on every store site, for the exact pass, both Q-pass views and the baseline."""
