@@ -589,6 +589,7 @@ def main():
         del src, dst
 
     sweep = None
+    sweep_samples = []
     if not a.no_sweep:
         sweep = {}
         xs = to_dev(x_bits)
@@ -616,6 +617,11 @@ def main():
                     byt = w12_bytes(n, k, n_esc, m) if fmt == "w12" else bf16_bytes(n, k, m)
                     row[f"{fmt}_{path}_us"] = round(t * 1e6, 2)
                     row[f"{fmt}_{path}_gbs"] = round(byt / t / 1e9, 1)
+                    if m > 64:
+                        # the timed outputs of the passes of more than 64 rows: their first 128
+                        # weight rows go to the CPU-oracle leg for parity
+                        sweep_samples.append((f"sweep {fmt} m={m} (rows 0..127)", x_bits[:m],
+                                              w_bits[:128], ym[:, :128].cpu().numpy()))
             if m in (1, 32, 128):
                 # the same W12 GEMM with bfloat16 outputs (rounded where they are stored)
                 path = "gemv" if m == 1 else "mfma"
@@ -661,7 +667,7 @@ def main():
     # Context beside the step: the attention projection at M=1, and the whole 64-layer stack at
     # M=1 and M=32 (both also run as captured HIP graphs); their outputs are parity-checked in
     # the CPU-oracle leg.
-    samples = []
+    samples = list(sweep_samples)
     attn = None
     if not a.no_attn:
         attn, smp = attn_bench(dev, stream, a.min_rot_bytes, reps=20)

@@ -99,7 +99,9 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
   const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s) : w12::launch_mfma(f, x, m, p, n, k, yo, s);
+  w12::Scratch sc;
+  sc.s = s;
+  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s, sc) : w12::launch_mfma(f, x, m, p, n, k, yo, s, sc);
   if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
   return ok();
 }

@@ -1,9 +1,10 @@
 // Skinny GEMM for 1..8 activation rows: y[m][n] = sum_k x[m][k] * W[n][k].
 //
-// W12 records are decoded in registers (SpecPilot, arXiv 2611.02501, figure-captions page,
-// Fig. 5(b): the GEMM decodes W12 records in registers) -- here into bfloat16 pairs for
-// v_dot2_f32_bf16 instead of a matrix-unit operand, because at this many rows the product is a
-// bandwidth-bound matrix-vector stream, not a dense contraction.
+// The W12 planes are turned back into bfloat16 inside the kernel's registers, never through
+// memory (SpecPilot, arXiv 2611.02501, figure-captions page, Fig. 5(b)).  Here the decoded pairs
+// feed v_dot2_f32_bf16 rather than a matrix-unit operand: with this few rows of x the product is
+// a bandwidth-bound matrix-vector stream, not a dense contraction.  Rows are summed across lanes
+// with two cross-lane shuffles.
 //
 // Work split: persistent workgroups of 4 waves.  A workgroup copies its k-slice of x into LDS
 // once.  A wave owns one 16-row tile of the tiled plane storage (see w12_device.hpp) at a time
@@ -393,8 +394,17 @@ static GemvKernel pick_kernel(Fmt f, int m) {
   return pick<kFmtBF16>(m);
 }
 
+int64_t gemv_k_slice(const DevInfo& di, int mb) {
+  // longest k range whose x copy fits the LDS budget (2*m*k <= 80 KiB: the whole row)
+  const int64_t red_bytes = (int64_t)4 * mb * 64 * 4;
+  int64_t budget = 81920;
+  if (budget > di.max_lds - red_bytes) budget = di.max_lds - red_bytes;
+  int64_t slice = (budget / (2 * mb)) / kTileCols * kTileCols;
+  return slice < kTileCols ? kTileCols : slice;
+}
+
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       YOut y, hipStream_t s) {
+                       YOut y, hipStream_t s, const Scratch& sc) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
@@ -406,12 +416,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     const int ks = ks_for(mb);
     const int64_t tpb = 4 / ks;
     const int64_t passes = (tiles + tpb - 1) / tpb;
-    // longest k range whose x copy fits the LDS budget (2*m*k <= 80 KiB: the whole row)
-    const int64_t red_bytes = (int64_t)4 * mb * 64 * 4;
-    int64_t budget = 81920;
-    if (budget > di.max_lds - red_bytes) budget = di.max_lds - red_bytes;
-    int64_t slice = (budget / (2 * mb)) / kTileCols * kTileCols;
-    if (slice < kTileCols) slice = kTileCols;
+    int64_t slice = gemv_k_slice(di, mb);
     if (slice > k) slice = k;
     int occ = 0;
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kern),
@@ -432,8 +437,8 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     if (rlen > slice) rlen = slice;
     ranges = (k + rlen - 1) / rlen;
     float* ws = nullptr;
-    if (ranges > 1 && (size_t)ranges * mb * n * sizeof(float) <= kWorkspaceBytes) {
-      err = workspace(s, &ws);
+    if (ranges > 1 && (size_t)ranges * mb * n * sizeof(float) <= sc.bytes) {
+      err = sc.get(&ws);
       if (err != hipSuccess) return err;
     }
     GemvArgs a;
@@ -468,8 +473,8 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     const YOut yp = y + m0 * n;
     float* acc32 = nullptr;
     if (yp.h && k > slice) {
-      if ((size_t)mb * n * sizeof(float) > kWorkspaceBytes) return hipErrorInvalidValue;
-      err = workspace(s, &acc32);
+      if ((size_t)mb * n * sizeof(float) > sc.bytes) return hipErrorInvalidValue;
+      err = sc.get(&acc32);
       if (err != hipSuccess) return err;
     }
     a.y = yp.h ? acc32 : yp.f;

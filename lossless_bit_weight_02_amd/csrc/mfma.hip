@@ -573,7 +573,7 @@ static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
 // Partial sums of a split go to the workspace from byte ws_off on.
 static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb, const Planes& p,
                             int64_t n, int64_t k, YOut y, int64_t ldy, hipStream_t s,
-                            size_t ws_off = 0) {
+                            const Scratch& sc, size_t ws_off = 0) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   const int64_t kb = k / kTileCols;
   const int nt = mb > 64 ? 8 : (mb + 15) / 16;   // 65..128 rows: the eight-tile instantiation
@@ -597,8 +597,8 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
     ranges = (int64_t)di.cus * waves / tiles;
     const int64_t cap = chunks * chunk_blocks / (f == kFmtBF16 ? 8 : 4);
     if (ranges > cap) ranges = cap;
-    if ((size_t)ranges * mb * n * sizeof(float) > kWorkspaceBytes - ws_off)
-      ranges = (int64_t)((kWorkspaceBytes - ws_off) / ((size_t)mb * n * sizeof(float)));
+    if ((size_t)ranges * mb * n * sizeof(float) > sc.bytes - ws_off)
+      ranges = (int64_t)((sc.bytes - ws_off) / ((size_t)mb * n * sizeof(float)));
     if (ranges < 2) ranges = 1;
   }
   const int64_t chunks = (kb + chunk_blocks - 1) / chunk_blocks;
@@ -606,7 +606,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   ranges = (chunks + cps - 1) / cps;
   float* ws = nullptr;
   if (ranges > 1) {
-    hipError_t err = workspace(s, &ws);
+    hipError_t err = sc.get(&ws);
     if (err != hipSuccess) return err;
     ws += ws_off / sizeof(float);
   }
@@ -635,7 +635,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   if (nt == 8 && f != kFmtBF16) {
     // x transposed into the workspace for the epilogue's escape patch (no split here)
     float* wsx = nullptr;
-    hipError_t e = workspace(s, &wsx);
+    hipError_t e = sc.get(&wsx);
     if (e != hipSuccess) return e;
     uint16_t* xt = reinterpret_cast<uint16_t*>(wsx);
     e = launch_x_transpose(x, mb, k, xt, s);
@@ -670,14 +670,17 @@ static Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
 }
 
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       YOut y, hipStream_t s) {
+                       YOut y, hipStream_t s, const Scratch& sc) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   // passes of up to 128 rows of x (each reads the weights once); the W12 and Q8 passes of more
-  // than 64 rows need x transposed in the workspace, else they stay at 64
-  const int64_t max_step = f == kFmtBF16 || k * 128 * 2 <= (int64_t)kWorkspaceBytes ? 128 : 64;
+  // than 64 rows need x transposed in the workspace, else they stay at 64.  The kernels address
+  // x with 32-bit byte offsets (2 * rows * k), so a pass of 128 rows also needs 256 k < 2^32.
+  const bool wide_ok = f == kFmtBF16 ? 256 * k < (int64_t(1) << 32)
+                                     : k * 128 * 2 <= (int64_t)sc.bytes;
+  const int64_t max_step = wide_ok ? 128 : 64;
   for (int64_t m0 = 0, step = 0; m0 < m; m0 += step) {
     step = (m - m0) < max_step ? (m - m0) : max_step;
     const int mb = (int)step;
@@ -687,11 +690,11 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     // split-k launch over the same record's last rows, so they take a fraction of a round.
     const int64_t r0 = tail_split_row(di, mb, tiles);
     if (r0 > 0) {
-      err = mfma_pass(f, di, x + m0 * k, mb, p, r0, k, y + m0 * n, n, s);
+      err = mfma_pass(f, di, x + m0 * k, mb, p, r0, k, y + m0 * n, n, s, sc);
       if (err != hipSuccess) return err;
-      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, y + m0 * n + r0, n, s);
+      err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, y + m0 * n + r0, n, s, sc);
     } else {
-      err = mfma_pass(f, di, x + m0 * k, mb, p, n, k, y + m0 * n, n, s);
+      err = mfma_pass(f, di, x + m0 * k, mb, p, n, k, y + m0 * n, n, s, sc);
     }
     if (err != hipSuccess) return err;
   }
@@ -706,8 +709,10 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
   // workspace: per-workgroup keys [groups + 1][32] at 0 (at most 257 x 32 x 8 bytes); the tail's
   // outputs [32][n - r0] (at most 32 x 1536 tiles x 16 rows x 4 bytes) from 128 KiB; the tail's
   // split partial sums from 4 MiB
+  Scratch sc;
+  sc.s = s;
   float* ws = nullptr;
-  err = workspace(s, &ws);
+  err = sc.get(&ws);
   if (err != hipSuccess) return err;
   uint64_t* keys = reinterpret_cast<uint64_t*>(ws);
   float* ytail = ws + (size_t(128) << 10) / sizeof(float);
@@ -745,7 +750,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     int g_all = (int)groups;
     if (r0 > 0) {
       err = mfma_pass(f, di, x + m0 * k, mb, rows_from(p, r0, k), n - r0, k, yout_f(ytail), n - r0, s,
-                      size_t(4) << 20);
+                      sc, size_t(4) << 20);
       if (err != hipSuccess) return err;
       err = launch_top1_rows(ytail, mb, n - r0, r0, keys + (int64_t)groups * 32, s);
       if (err != hipSuccess) return err;

@@ -64,9 +64,6 @@ void k_mfma_wide(MfmaArgs a) {
   using SH = ShapeWide<FMT, NT>;
   constexpr int D = SH::D, S = SH::S, FS = SH::FS, F = SH::F, XL = SH::XL;
   constexpr bool kEsc = FMT != kFmtBF16;
-  // x sums of escaped slots in registers of their own (up to two activation tiles; beyond that
-  // the registers are not there and the placeholders come out of the accumulators directly)
-  constexpr bool kSepSx = false;   // escape x sums go straight into the accumulators
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
   __shared__ __attribute__((aligned(16))) u32x4 s_scratch[64];   // stores of waves with no piece
   __shared__ uint32_t s_ecol[kEsc ? kWaves : 1][kEsc ? kEscCap : 1];   // per wave: tile escapes
@@ -222,12 +219,12 @@ void k_mfma_wide(MfmaArgs a) {
     }
 
     floatx4 acc[NT];
-    float qv[NT][4], sx[NT][4];
+    float qv[NT][4];   // escape values times x; the placeholder terms go into acc directly
 #pragma unroll
     for (int cc = 0; cc < NT; ++cc) {
       acc[cc] = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qv[cc][r] = sx[cc][r] = 0.f;
+      for (int r = 0; r < 4; ++r) qv[cc][r] = 0.f;
     }
 
     for (uint32_t c = 0; c * S < KBp; ++c) {       // chunk c: k-blocks S c .. S c + S - 1
@@ -279,8 +276,7 @@ void k_mfma_wide(MfmaArgs a) {
             for (int cc = 0; cc < NT; ++cc) {
               const float xv = bf16_to_float(
                   reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
-              if constexpr (kSepSx) sx[cc][r] += xv;
-              else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+              acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -303,8 +299,7 @@ void k_mfma_wide(MfmaArgs a) {
           for (int cc = 0; cc < NT; ++cc) {
             const int mrow = 16 * cc + r16;
             const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
-            if constexpr (kSepSx) sx[cc][r] += xv;
-            else acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+            acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
             qv[cc][r] = fmaf(xv, v, qv[cc][r]);
           }
         }
@@ -319,8 +314,7 @@ void k_mfma_wide(MfmaArgs a) {
       for (int cc = 0; cc < NT; ++cc) {
         const int mcol = 16 * cc + r16;
         if (mcol >= a.m) continue;
-        const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
-                             : acc[cc][r];
+        const float v = kEsc ? fmaf(sc, acc[cc][r], qv[cc][r]) : acc[cc][r];
         if (a.y16) a.y16[mcol * a.ldy + nrow] = float_to_bf16_rne(v);
         else a.y[mcol * a.ldy + nrow] = v;
       }

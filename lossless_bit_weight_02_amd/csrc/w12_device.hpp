@@ -117,28 +117,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// DPP move of a float with row/bank masks; lanes not written keep `old`.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_f(float old, float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
-                                                               __builtin_bit_cast(int, v), CTRL,
-                                                               ROWMASK, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wave; the total lands in lane 63.
-//  quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: every lane of a row
-//  of 16 holds the row sum; row_bcast:15 (rows 1,3) and row_bcast:31 (rows 2,3) then fold the
-//  four row sums into row 3.
-__device__ __forceinline__ float wave_sum_to_lane63(float v) {
-  v += dpp_f<0xB1, 0xF>(0.0f, v);
-  v += dpp_f<0x4E, 0xF>(0.0f, v);
-  v += dpp_f<0x141, 0xF>(0.0f, v);
-  v += dpp_f<0x140, 0xF>(0.0f, v);
-  v += dpp_f<0x142, 0xA>(0.0f, v);
-  v += dpp_f<0x143, 0xC>(0.0f, v);
-  return v;
-}
-
 // Non-temporal 128-bit load: weight planes are streamed once, keep them out of the caches'
 // reuse set.
 template <typename T>

@@ -22,6 +22,23 @@ hipError_t dev_info(DevInfo* out);
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
 hipError_t workspace(hipStream_t s, float** out);
 
+// The scratch memory one GEMM call may use: the per-stream workspace above (allocated on first
+// use), or a fixed device buffer of `bytes` bytes (`fixed`, nothing is allocated).  Split-k
+// ranges and 128-row passes adapt to `bytes`; only the GEMV's bfloat16 outputs over several
+// k slices need a fixed amount (rows x n floats).
+struct Scratch {
+  hipStream_t s = nullptr;
+  void* fixed = nullptr;
+  size_t bytes = kWorkspaceBytes;
+  hipError_t get(float** out) const {
+    if (fixed) {
+      *out = static_cast<float*>(fixed);
+      return hipSuccess;
+    }
+    return workspace(s, out);
+  }
+};
+
 // Where a GEMM writes y: float (f), or bfloat16 bits rounded to nearest even from the float
 // result (h); exactly one of them is set.  Offsets count elements of either.
 struct YOut {
@@ -86,12 +103,14 @@ hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* o
 // bandwidth probe
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 
+// Columns of x one GEMV launch over mb (<= 8) rows holds in LDS: longer rows run as k slices.
+int64_t gemv_k_slice(const DevInfo& di, int mb);
 // GEMV family (wave-reduction kernel), any m (passes of <= 8 rows of x)
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       YOut y, hipStream_t s);
+                       YOut y, hipStream_t s, const Scratch& sc);
 // MFMA family (bf16 v_mfma_f32_16x16x32), any m (blocks of <= 64 rows of x)
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                       YOut y, hipStream_t s);
+                       YOut y, hipStream_t s, const Scratch& sc);
 // top-1 over the n outputs of each x row (no y written), passes of <= 32 rows of x
 hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n,
                             int64_t k, int32_t* idx, float* val, hipStream_t s);

@@ -235,29 +235,58 @@ def decode(wt: W12Weight) -> torch.Tensor:
     return decode_into(wt, torch.empty((wt.n, wt.k), dtype=torch.bfloat16, device=wt.device))
 
 
-def _gemm_out(x, n, bf16=False):
+def _prep_x(x: torch.Tensor, k: int, device) -> torch.Tensor:
+    """x as the kernels read it: 2-D, 16-bit (bfloat16 bits), contiguous, on the weights' device,
+    with k columns.  A wrong x raises here, before anything is launched."""
     x = _bits16(x)
     if x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D CUDA tensor")
-    dt = torch.bfloat16 if bf16 else torch.float32
-    return x.contiguous(), torch.empty((x.shape[0], n), dtype=dt, device=x.device)
+    if x.device != device:
+        raise ValueError(f"x is on {x.device}, the weights on {device}")
+    if x.shape[1] != k:
+        raise ValueError(f"x has {x.shape[1]} columns, the weights have k={k}")
+    return x.contiguous()
+
+
+def _check_out(out: torch.Tensor, shape, dtypes, device, what="out"):
+    """A caller-provided output: contiguous, on the weights' device, of the given shape, and of
+    one of the given dtypes (a wrong one would be written past its end or misread)."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if out.device != device:
+        raise ValueError(f"{what} is on {out.device}, the weights on {device}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.dtype not in dtypes:
+        raise ValueError(f"{what} has dtype {out.dtype}, expected one of {dtypes}")
+    if not out.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _gemm_io(x, n, k, device, out, out_bf16):
+    """Checked (x, out) of a GEMM call: out [m, n] float32, or bfloat16 (OUT_BF16: the float
+    result rounded to nearest even), allocated when not given."""
+    x = _prep_x(x, k, device)
+    if out is None:
+        dt = torch.bfloat16 if out_bf16 else torch.float32
+        out = torch.empty((x.shape[0], n), dtype=dt, device=device)
+    else:
+        _check_out(out, (x.shape[0], n), (torch.float32, torch.bfloat16), device)
+    return x, out
 
 
 def _out_flag(out):
     """float32 outputs, or bfloat16 ones (OUT_BF16: the float result rounded to nearest even)."""
-    if out.dtype == torch.bfloat16:
-        return OUT_BF16
-    if out.dtype != torch.float32:
-        raise ValueError("out must be float32 or bfloat16")
-    return 0
+    return OUT_BF16 if out.dtype == torch.bfloat16 else 0
 
 
 def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None,
          out_bf16: bool = False):
     """Exact pass: y = x W^T (fp32, or bfloat16 with ``out_bf16`` / a bfloat16 ``out``) with W
     read from its W12 record."""
-    if out is None:
-        x, out = _gemm_out(x, wt.n, out_bf16)
+    x, out = _gemm_io(x, wt.n, wt.k, wt.device, out, out_bf16)
+    if x.shape[0] == 0:
+        return out
     s = wt.c_struct()
     _check(lib().w12_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
                           _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
@@ -268,8 +297,9 @@ def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.
             midpoint: bool = False, out_bf16: bool = False):
     """Q pass: y = x W_q^T with W_q the 8-bit view (B plane taken as 0, or as 8 with
     ``midpoint``), escapes exact; outputs as in gemm."""
-    if out is None:
-        x, out = _gemm_out(x, wt.n, out_bf16)
+    x, out = _gemm_io(x, wt.n, wt.k, wt.device, out, out_bf16)
+    if x.shape[0] == 0:
+        return out
     s = wt.c_struct()
     s.lo = None
     flags = _PATHS[path] | (Q8_MIDPOINT if midpoint else 0) | _out_flag(out)
@@ -279,14 +309,18 @@ def q8_gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.
 
 
 def _top1(fn, x, wt, lo, out, flags=0):
-    x = _bits16(x)
-    if x.dim() != 2 or not x.is_cuda:
-        raise ValueError("x must be a 2-D CUDA tensor")
-    x = x.contiguous()
+    x = _prep_x(x, wt.k, wt.device)
     m = x.shape[0]
     if out is None:
         out = (torch.empty(m, dtype=torch.int32, device=x.device),
                torch.empty(m, dtype=torch.float32, device=x.device))
+    else:
+        if len(out) != 2:
+            raise ValueError("out must be a pair (index int32 [m], value float32 [m])")
+        _check_out(out[0], (m,), (torch.int32,), wt.device, "out[0]")
+        _check_out(out[1], (m,), (torch.float32,), wt.device, "out[1]")
+    if m == 0:
+        return out
     s = wt.c_struct()
     if not lo:
         s.lo = None
@@ -329,8 +363,9 @@ def bf16_gemm(x: torch.Tensor, wt: Bf16Tiles, path: str | None = None, out: torc
               out_bf16: bool = False):
     """Same-build dense baseline: y = x W^T with W plain bfloat16 (tiled storage); outputs as in
     gemm."""
-    if out is None:
-        x, out = _gemm_out(x, wt.n, out_bf16)
+    x, out = _gemm_io(x, wt.n, wt.k, wt.data.device, out, out_bf16)
+    if x.shape[0] == 0:
+        return out
     _check(lib().w12_bf16_gemm(x.data_ptr(), x.shape[0], wt.data.data_ptr(), wt.n, wt.k,
                                out.data_ptr(), _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
     return out

@@ -98,3 +98,23 @@ def check_top1(y_gpu: np.ndarray, y64: np.ndarray, absum: np.ndarray, what="", r
         assert y64[m, a] >= y64[m, b] - slack, (f"{what}: row {m}: GPU argmax {a} "
                                                 f"(y64 {y64[m, a]}) vs oracle {b} (y64 {y64[m, b]})")
     return agree
+
+
+def check_y_bf16(y16, y32: np.ndarray, y64: np.ndarray, absum: np.ndarray, what="", rel=1e-3):
+    """A bfloat16 output (W12_OUT_BF16) against the float output of the same call and the oracle:
+    bit for bit the float output rounded to nearest even (torch's rounding on the CPU, NaN where
+    NaN), and within the GEMM bound plus half a bfloat16 unit in the last place (relative 2^-8)."""
+    import torch
+    want = torch.from_numpy(np.ascontiguousarray(y32)).to(torch.bfloat16)
+    got = y16.cpu()
+    assert tuple(got.shape) == tuple(want.shape), f"{what}: shape {tuple(got.shape)}"
+    wn, gn = torch.isnan(want.float()), torch.isnan(got.float())
+    assert torch.equal(wn, gn), f"{what}: NaN positions differ"
+    assert torch.equal(want.view(torch.int16)[~wn], got.view(torch.int16)[~gn]), \
+        f"{what}: bfloat16 output is not the rounded float output"
+    y = got.float().numpy().astype(np.float64)
+    b = rel * absum
+    fin = np.isfinite(y64)
+    err = np.abs(y[fin] - y64[fin])
+    ok = err <= b[fin] + 2.0 ** -8 * (np.abs(y64[fin]) + b[fin])
+    assert np.all(ok), f"{what}: {np.count_nonzero(~ok)} elements outside the bound"

@@ -25,8 +25,8 @@ def _encode_chunk(w_chunk):
 
 def _gemm_chunk(args):
     x_bits, w_chunk, view = args
-    if view == "q8":
-        w_chunk = oracle.q8_view_bits(oracle.encode(w_chunk))
+    if view in ("q8", "q8m"):
+        w_chunk = oracle.q8_view_bits(oracle.encode(w_chunk), midpoint=view == "q8m")
     return oracle.gemm64(x_bits, w_chunk), oracle.abs_bound64(x_bits, w_chunk)
 
 
@@ -74,7 +74,8 @@ def encode(w_bits: np.ndarray, pool: ProcessPoolExecutor) -> oracle.W12Record:
 
 
 def gemm(x_bits: np.ndarray, w_bits: np.ndarray, pool: ProcessPoolExecutor, view: str = "exact"):
-    """(y64, sum |x w|) for y = x W^T over all rows of W; view "q8" uses the oracle's 8-bit view."""
+    """(y64, sum |x w|) for y = x W^T over all rows of W; view "q8" uses the oracle's 8-bit view,
+    "q8m" its midpoint view."""
     n = w_bits.shape[0]
     parts = list(pool.map(_gemm_chunk, [(x_bits, w_bits[a:b], view) for a, b in _chunks(n)]))
     return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)

@@ -1,7 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configurations bench.py times.
 
-gate+up [34816, 5120] (every M of its config, both kernel families), the LM-head-shaped Q pass
-[152064, 5120] at M=16 with top-1, and three layers (0, 31, 63) of the 64-layer 27B-class stack.
+gate+up [34816, 5120] (every M of its config, both kernel families, and 48, 128 and 256 rows of
+x, so the three- and eight-tile matrix-core kernels run with every wave busy), the LM-head-shaped
+Q pass [152064, 5120] at M=16 with top-1 and at 48 and 128 rows (several rounds of tiles per wave),
+and three layers (0, 31, 63) of the 64-layer 27B-class stack.
 The oracle runs over row chunks in spawned worker processes (tests/oracle_pool.py), so every
 output element and every stored byte is compared, not a sample.
 """
@@ -10,7 +12,8 @@ import pytest
 
 from lossless_bit_weight_02_amd import synth
 from tests import oracle_pool
-from tests.gpu_util import (assert_records_equal, check_top1, check_y, record_numpy, say, to_dev)
+from tests.gpu_util import (assert_records_equal, check_top1, check_y, check_y_bf16, record_numpy,
+                            say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +136,62 @@ def test_stack_layer(pool, layer):
             say(f"{label}: gemm m={m}")
             y = w12.gemm(to_dev(x[:m]), rec).cpu().numpy()
             check_y(y, y64[:m], absum[:m], f"{label} w12 m={m}")
+
+
+def _formats(w12, rec, bt):
+    """(name, call, oracle view) of the four GEMMs on one record: exact pass, both Q-pass views and
+    the dense baseline."""
+    return (("w12", lambda x, **kw: w12.gemm(x, rec, **kw), "exact"),
+            ("q8", lambda x, **kw: w12.q8_gemm(x, rec, **kw), "q8"),
+            ("q8 midpoint", lambda x, **kw: w12.q8_gemm(x, rec, midpoint=True, **kw), "q8m"),
+            ("bf16", lambda x, **kw: w12.bf16_gemm(x, bt, **kw), "exact"))
+
+
+def test_gate_up_many_rows(pool):
+    """gate+up [34816, 5120] at 48 rows of x (three-tile kernel: 2176 tiles, every wave of the chip
+    busy), 128 rows (one eight-tile pass: 9 busy waves per workgroup) and 256 rows (two passes), on
+    the automatic path bench.py times: exact pass, both Q-pass views and the baseline, float and
+    bfloat16 outputs, every element against the oracle."""
+    w12 = _w12()
+    w, spec, tid = synth.config_weight("gate_up")
+    dw = to_dev(w)
+    say("gate_up many rows: encode")
+    rec = w12.encode(dw)
+    bt = w12.bf16_tiles(dw)
+    del dw
+    x = synth.gen_x(256, spec.k, tensor_id=tid)
+    ref = {}
+    for view in ("exact", "q8", "q8m"):
+        say(f"gate_up many rows: oracle GEMM M=256 ({view})")
+        ref[view] = oracle_pool.gemm(x, w, pool, view=view)
+    for m in (48, 128, 256):
+        xd = to_dev(x[:m])
+        for name, fn, view in _formats(w12, rec, bt):
+            y64, absum = ref[view]
+            say(f"gate_up: {name} m={m} float out")
+            y = fn(xd).cpu().numpy()
+            check_y(y, y64[:m], absum[:m], f"gate_up {name} m={m}")
+            say(f"gate_up: {name} m={m} bfloat16 out")
+            y16 = fn(xd, out_bf16=True)
+            check_y_bf16(y16, y, y64[:m], absum[:m], f"gate_up {name} m={m} bf16 out")
+
+
+@pytest.mark.parametrize("m", [48, 128])
+def test_lm_head_many_rows(pool, m):
+    """LM head [152064, 5120] (9504 tiles: four rounds of tiles per wave) at 48 rows of x (the
+    three-tile kernel) and 128 rows (the eight-tile kernel): exact pass and Q pass, every element
+    against the oracle."""
+    w12 = _w12()
+    w, spec, tid = synth.config_weight("lm_head")
+    dw = to_dev(w)
+    say(f"lm_head m={m}: encode")
+    rec = w12.encode(dw)
+    del dw
+    x = synth.gen_x(m, spec.k, tensor_id=tid)
+    xd = to_dev(x)
+    for name, fn, view in (("w12", w12.gemm, "exact"), ("q8", w12.q8_gemm, "q8")):
+        say(f"lm_head: {name} m={m}")
+        y = fn(xd, rec).cpu().numpy()
+        say(f"lm_head: oracle GEMM m={m} ({view})")
+        y64, absum = oracle_pool.gemm(x, w, pool, view=view)
+        check_y(y, y64, absum, f"lm_head {name} m={m}")

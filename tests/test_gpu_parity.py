@@ -622,3 +622,51 @@ def test_gemm_bf16_output_gemv_k_slices():
         _check_bf16_out(y16, y32, None, None, f"gemv k slices {name}")
     del rec
     torch.cuda.empty_cache()
+
+
+def test_binding_rejects_bad_arguments():
+    """The binding checks x and caller-provided outputs before anything is launched: a float or
+    wrongly shaped x, an output of the wrong shape, dtype, device or layout raise; a strided x is
+    copied contiguous and gives the same result; an x with no rows gives an empty output."""
+    import torch
+    w12 = _w12()
+    rng = np.random.default_rng(5)
+    n, k = 64, 256
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((4, k)).astype(np.float32))
+    rec = w12.encode(to_dev(w))
+    bt = w12.bf16_tiles(to_dev(w))
+    xd = to_dev(x)
+    calls = (lambda xx, **kw: w12.gemm(xx, rec, **kw), lambda xx, **kw: w12.q8_gemm(xx, rec, **kw),
+             lambda xx, **kw: w12.bf16_gemm(xx, bt, **kw))
+    dev = xd.device
+    for fn in calls:
+        with pytest.raises(TypeError):
+            fn(xd.float())
+        with pytest.raises(ValueError):
+            fn(xd[:, :128])                                        # k mismatch
+        with pytest.raises(ValueError):
+            fn(xd.cpu())                                           # not on the GPU
+        with pytest.raises(ValueError):
+            fn(xd, out=torch.empty((4, n - 1), dtype=torch.float32, device=dev))
+        with pytest.raises(ValueError):
+            fn(xd, out=torch.empty((4, n), dtype=torch.float16, device=dev))
+        with pytest.raises(ValueError):
+            fn(xd, out=torch.empty((n, 4), dtype=torch.float32, device=dev).t())
+        with pytest.raises(ValueError):
+            fn(xd, out=torch.empty((4, n), dtype=torch.float32))  # host memory
+        y = fn(xd)
+        wide = torch.zeros((4, 2 * k), dtype=torch.bfloat16, device=dev)
+        wide[:, ::2] = xd
+        assert torch.equal(fn(wide[:, ::2]), y)                    # strided x: same result
+        assert fn(xd[:0]).shape == (0, n)
+    for fn in (w12.q8_top1, w12.gemm_top1):
+        with pytest.raises(ValueError):
+            fn(xd, rec, out=(torch.empty(4, dtype=torch.int64, device=dev),
+                             torch.empty(4, dtype=torch.float32, device=dev)))
+        with pytest.raises(ValueError):
+            fn(xd, rec, out=(torch.empty(4, dtype=torch.int32, device=dev),
+                             torch.empty(3, dtype=torch.float32, device=dev)))
+        with pytest.raises(ValueError):
+            fn(xd[:, :128], rec)
+    torch.cuda.synchronize()
