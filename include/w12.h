@@ -138,6 +138,26 @@ int w12_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint3
              void *stream);
 
 /*
+ * w12_gemm_noalloc -- w12_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments, flags,
+ * kernels and results as w12_gemm (bit-identical for every shape whose split-k partial sums and
+ * 128-row passes fit the fixed scratch below, which covers every 27B-class projection).  The
+ * scratch a call needs (split-k partial sums, the transposed x of passes of more than 64 rows)
+ * comes from a fixed 16 MiB array of device memory in the library (W12_NOALLOC_SCRATCH_BYTES),
+ * one per GPU, held from the library's first use on that GPU until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).  Split-k ranges and
+ * 128-row passes adapt to that size; a call that cannot fit -- bfloat16 outputs on the GEMV path
+ * whose x rows need several k slices, with more than 16 MiB of float partial outputs
+ * (min(m, 8) x n x 4 bytes) -- returns W12_ERR_RANGE before anything is enqueued.  Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on different streams, or
+ * graphs replayed concurrently) race on it and must be ordered by the caller.  Nothing in the
+ * array needs to start at zero; it keeps the last call's contents.
+ */
+#define W12_NOALLOC_SCRATCH_BYTES (16u << 20)
+int w12_gemm_noalloc(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, uint32_t flags,
+                     void *stream);
+
+/*
  * w12_q8_gemm -- the Q pass of two-level verification (figure-captions page, Fig. 7):
  * the same product with every in-window weight taken from the 8-bit view alone (A + E, the
  * B nibble read as 0, i.e. the bfloat16 bits & 0xFFF0) and escapes exact.  Reads base, ae

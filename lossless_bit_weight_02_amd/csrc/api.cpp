@@ -34,6 +34,8 @@ int hip_fail(hipError_t e, const char* where) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+static_assert(W12_NOALLOC_SCRATCH_BYTES == w12::kScratchBytes, "w12.h states the fixed scratch size");
+
 constexpr int64_t kMaxDim = int64_t(1) << 31;  // n and m below 2^31
 constexpr int64_t kMaxK = int64_t(1) << 24;    // k at most 2^24: 32-bit buffer offsets in kernels
 
@@ -72,8 +74,10 @@ w12::Planes planes_of(const w12_weight* wt) {
   return p;
 }
 
+// fixed_scratch: run on the library's fixed scratch (allocation-free entry point) instead of the
+// per-stream workspace
 int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n, int64_t k,
-             float* y, uint32_t flags, void* stream) {
+             float* y, uint32_t flags, void* stream, bool fixed_scratch = false) {
   if (!x || !y) return fail(W12_ERR_ARG, "x or y is NULL");
   if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
@@ -101,6 +105,25 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   w12::Scratch sc;
   sc.s = s;
+  if (fixed_scratch) {
+    // the one fixed use of scratch: a GEMV pass with bfloat16 outputs whose x rows need several k
+    // slices adds them in float (rows x n) before rounding; refused up front if too large (the
+    // first pass has the most rows and the shortest slices)
+    const int rows = (int)(m < 8 ? m : 8);
+    w12::DevInfo di;
+    hipError_t e = w12::dev_info(&di);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+    const uint64_t need = (uint64_t)rows * (uint64_t)n * 4u;
+    if (out16 && gemv && k > w12::gemv_k_slice(di, rows) && need > w12::kScratchBytes)
+      return fail(W12_ERR_RANGE, "bfloat16 outputs of %d rows x n=%lld over several k slices need "
+                  "%llu bytes of scratch, more than the fixed %llu", rows, (long long)n,
+                  (unsigned long long)need, (unsigned long long)w12::kScratchBytes);
+    void* ptr = nullptr;
+    e = w12::fixed_scratch(&ptr);
+    if (e != hipSuccess) return hip_fail(e, "fixed scratch lookup");
+    sc.fixed = ptr;
+    sc.bytes = w12::kScratchBytes;
+  }
   hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s, sc) : w12::launch_mfma(f, x, m, p, n, k, yo, s, sc);
   if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
   return ok();
@@ -214,6 +237,13 @@ int w12_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint3
   int rc = check_record(wt, true);
   if (rc) return rc;
   return run_gemm(w12::kFmtW12, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream);
+}
+
+int w12_gemm_noalloc(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint32_t flags,
+                     void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  return run_gemm(w12::kFmtW12, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream, true);
 }
 
 int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint32_t flags, void* stream) {

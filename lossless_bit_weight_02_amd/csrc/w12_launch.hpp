@@ -39,6 +39,11 @@ struct Scratch {
   }
 };
 
+// The fixed scratch of the allocation-free entry point: kScratchBytes of file-scope device memory
+// per device, looked up once per device (noalloc.hip).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t fixed_scratch(void** out);
+
 // Where a GEMM writes y: float (f), or bfloat16 bits rounded to nearest even from the float
 // result (h); exactly one of them is set.  Offsets count elements of either.
 struct YOut {

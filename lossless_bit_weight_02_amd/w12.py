@@ -54,6 +54,8 @@ EXPORTS = {
     "w12_decode": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_void_p, ctypes.c_void_p]),
     "w12_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                 ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                        ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_q8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                    ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_q8_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
@@ -290,6 +292,19 @@ def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Ten
     s = wt.c_struct()
     _check(lib().w12_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
                           _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
+    return out
+
+
+def gemm_noalloc(x: torch.Tensor, wt: W12Weight, out: torch.Tensor, path: str | None = None):
+    """gemm into a caller-provided ``out`` (float32 or bfloat16 [m, n]) through the allocation-free
+    entry point: the library allocates nothing; its scratch is a fixed per-GPU array shared by
+    every call on that GPU (calls overlapping in time on one GPU race)."""
+    x, out = _gemm_io(x, wt.n, wt.k, wt.device, out, False)
+    if x.shape[0] == 0:
+        return out
+    s = wt.c_struct()
+    _check(lib().w12_gemm_noalloc(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
+                                  _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
     return out
 
 
