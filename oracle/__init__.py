@@ -17,4 +17,6 @@ from .w12 import (  # noqa: F401
     gemm64, w12_gemm64, q8_gemm64, abs_bound64, top1, record_nbytes,
     bits_per_weight, lo_row_bytes, lo_position, to_storage, from_storage,
     bf16_to_storage, padded_rows, TILE_ROWS, TILE_COLS,
+    gemm64_f, abs_bound64_f, I8Copy, escaped_mask, i8_copy, i8_weights64, i8_gemm64,
+    SILU_GROUP, interleave_rows, silu_rows, silu64, silu_mul64, silu_mul_bound,
 )

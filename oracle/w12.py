@@ -42,6 +42,12 @@ layout.  The readings used here (numbered as in the design notes):
       columns [32g, 32g+32) sit at 16*(r + 16*g) .. +16.  This is only a
       permutation of the logical arrays above (see ``to_storage``).
 
+* R16 the separate 8-bit Q-pass copy (a next step the scope table lists):
+      per-row int8 with a float32 scale from the row's largest in-window
+      magnitude; escapes exact through the record's list (``i8_copy``).
+* R17 SiLU(gate) * up on the gate+up product, with gate and up rows
+      interleaved in groups of 8 in one record (``interleave_rows``).
+
 Parity status: every function below is pinned by the CPU tests against
 values fixed independently of this file (exhaustive round trip over all 65536
 bfloat16 patterns, brute-force window search, hand-worked examples of the
@@ -307,6 +313,139 @@ def q8_gemm64(x_bits, rec: W12Record, midpoint: bool = False) -> np.ndarray:
 def top1(y) -> np.ndarray:
     """argmax over n for each row m; ties go to the lowest n (R11)."""
     return np.argmax(np.asarray(y), axis=1)
+
+
+def gemm64_f(x_bits, w64) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * W[n, k] in float64 for a float64 weight matrix."""
+    return bf16_to_f64(np.atleast_2d(x_bits)) @ np.asarray(w64, dtype=np.float64).T
+
+
+def abs_bound64_f(x_bits, w64) -> np.ndarray:
+    """sum_k |x[m, k] * W[n, k]| in float64 for a float64 weight matrix."""
+    return np.abs(bf16_to_f64(np.atleast_2d(x_bits))) @ np.abs(np.asarray(w64, dtype=np.float64)).T
+
+
+# ----------------------------------------------------------------------------
+# A separate 8-bit copy for the Q pass (summary page, Main Findings: the port to
+# the RTX PRO 6000 reads an INT6/INT8 copy of the weights in the Q pass instead
+# of the zero-copy 8-bit view).  The pages give no quantiser; reading R16:
+#   * per output row n, M_n = the largest |w| among the row's in-window weights
+#     (2^(base_n - 127), the window's smallest magnitude, for a row that has
+#     none), and the row scale s_n = float32(M_n) / 127 in float32;
+#   * an in-window weight becomes q = round-half-even(float32(w) / s_n), the
+#     division in float32, clamped to [-127, 127];
+#   * escaped weights (the record's exact escape list) hold q = 0 and stay exact
+#     through the same escape list the exact pass uses;
+#   * the weight the Q pass sees is s_n * q (in-window) or the escape value.
+# ----------------------------------------------------------------------------
+@dataclass
+class I8Copy:
+    """The 8-bit Q-pass copy of a W12 record (R16)."""
+    n: int
+    k: int
+    q: np.ndarray         # int8    [n, k]
+    scale: np.ndarray     # float32 [n]
+
+
+def escaped_mask(rec: W12Record) -> np.ndarray:
+    """True at every (n, k) listed in the record's escape list."""
+    mask = np.zeros((rec.n, rec.k), dtype=bool)
+    mask[_escape_rows(rec), rec.esc_col.astype(np.int64)] = True
+    return mask
+
+
+def i8_copy(rec: W12Record) -> I8Copy:
+    """Quantise the record's in-window weights to int8 with one float32 scale per row (R16)."""
+    w = decode(rec)
+    esc = escaped_mask(rec)
+    mag = np.abs(bf16_to_f64(w))
+    mag[esc] = 0.0
+    floor = np.ldexp(1.0, rec.base.astype(np.int64) - 127)
+    big = np.maximum(mag.max(axis=1) if rec.k else floor, floor)
+    scale = (big.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    wf = bf16_to_f64(w).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ratio = (wf / scale[:, None]).astype(np.float32)
+    ratio[esc] = 0.0
+    q = np.clip(np.rint(ratio), -127, 127).astype(np.int8)
+    return I8Copy(rec.n, rec.k, q, scale)
+
+
+def i8_weights64(rec: W12Record, cp: I8Copy) -> np.ndarray:
+    """The weights the Q pass sees with the 8-bit copy: s_n * q, escapes exact (float64)."""
+    w = cp.scale.astype(np.float64)[:, None] * cp.q.astype(np.float64)
+    w[_escape_rows(rec), rec.esc_col.astype(np.int64)] = bf16_to_f64(rec.esc_val)
+    return w
+
+
+def i8_gemm64(x_bits, rec: W12Record, cp: I8Copy) -> np.ndarray:
+    """The Q pass on the 8-bit copy, float64."""
+    return gemm64_f(x_bits, i8_weights64(rec, cp))
+
+
+# ----------------------------------------------------------------------------
+# SiLU(gate) * up on a gate+up product (summary page, Main Findings: W12 also
+# speeds up plain autoregressive decoding, where the gate and up projections
+# feed SiLU(gate) * up).  Readings R17:
+#   * the gate and up weights [I, k] are stored as one record whose rows
+#     interleave in groups of 8: rows 16 t .. 16 t + 7 are gate rows
+#     8 t .. 8 t + 7 and rows 16 t + 8 .. 16 t + 15 are up rows 8 t .. 8 t + 7
+#     (I a multiple of 8), so both halves of one output sit in one 16-row tile;
+#   * h[m, i] = silu(g) * u with g = y[m, gate row of i], u = y[m, up row of i]
+#     and silu(z) = z / (1 + exp(-z)).
+# ----------------------------------------------------------------------------
+SILU_GROUP = 8
+
+
+def interleave_rows(gate_bits, up_bits) -> np.ndarray:
+    """The stacked weight of R17: groups of 8 gate rows and 8 up rows, alternating."""
+    g = np.atleast_2d(np.asarray(gate_bits))
+    u = np.atleast_2d(np.asarray(up_bits))
+    if g.shape != u.shape or g.shape[0] % SILU_GROUP:
+        raise ValueError("gate and up must have the same shape, rows a multiple of 8")
+    i, k = g.shape
+    out = np.empty((2 * i, k), dtype=g.dtype)
+    for t in range(i // SILU_GROUP):
+        out[16 * t:16 * t + 8] = g[8 * t:8 * t + 8]
+        out[16 * t + 8:16 * t + 16] = u[8 * t:8 * t + 8]
+    return out
+
+
+def silu_rows(i: int):
+    """(gate rows, up rows) of the interleaved product for outputs 0 .. i-1 (R17)."""
+    j = np.arange(i)
+    gate = 16 * (j // SILU_GROUP) + j % SILU_GROUP
+    return gate, gate + SILU_GROUP
+
+
+def silu64(z) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)) in float64 (exp overflow gives the limit -0)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def silu_mul64(y_gu) -> np.ndarray:
+    """h[m, i] = silu(y[m, gate row of i]) * y[m, up row of i] from the interleaved product."""
+    y = np.atleast_2d(np.asarray(y_gu, dtype=np.float64))
+    gate, up = silu_rows(y.shape[1] // 2)
+    return silu64(y[:, gate]) * y[:, up]
+
+
+# |d silu / dz| is at most 1.0998 (its maximum, near z = 2.4); 1.1 bounds it.
+SILU_SLOPE = 1.1
+
+
+def silu_mul_bound(y64, absum, rel=1e-3) -> np.ndarray:
+    """Error bound of a SiLU(gate) * up output whose gate and up values each carry the GEMM bound
+    B = rel * sum|x w|: |silu(g') u' - silu(g) u| <= 1.1 B_g (|u| + B_u) + |silu(g)| B_u, plus
+    2^-20 |h| for the float32 evaluation of silu and the product."""
+    y = np.atleast_2d(np.asarray(y64, dtype=np.float64))
+    b = rel * np.atleast_2d(np.asarray(absum, dtype=np.float64))
+    gate, up = silu_rows(y.shape[1] // 2)
+    g, u, bg, bu = y[:, gate], y[:, up], b[:, gate], b[:, up]
+    h = silu64(g) * u
+    return SILU_SLOPE * bg * (np.abs(u) + bu) + np.abs(silu64(g)) * bu + 2.0 ** -20 * np.abs(h)
 
 
 # ----------------------------------------------------------------------------
