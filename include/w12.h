@@ -188,6 +188,48 @@ int w12_gemm_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *i
                   uint32_t flags, void *stream);
 
 /*
+ * The separate 8-bit copy for the Q pass (summary page, Main Findings: the RTX PRO 6000 port reads
+ * an INT6/INT8 copy of the weights in the Q pass instead of the zero-copy 8-bit view).  It sits
+ * beside a W12 record and shares that record's exact escape list.  The pages give no quantiser;
+ * this one is linear per output row: M_n = the largest magnitude among the row's in-window
+ * weights (2^(base - 127), the window's smallest magnitude, for a row with none), scale
+ * s_n = M_n / 127 in float32, and every in-window weight becomes q = round-half-even(w / s_n)
+ * (float32 division), clamped to +-127; escaped slots hold q = 0.  The Q pass then sees s_n * q
+ * for in-window weights and the exact value for escapes.  1 byte per weight plus 4 per row, the
+ * same bytes per pass as the 8-bit view, and 1 extra byte per weight of memory.
+ */
+typedef struct w12_i8 {
+    int64_t  n;        /* rows of W (must equal the record's)    */
+    int64_t  k;        /* columns of W (must equal the record's) */
+    int8_t  *q;        /* [npad * k] codes, in the storage order of the record's AE plane (device, 16-byte aligned) */
+    float   *scale;    /* [n] per-row scale (device, 4-byte aligned) */
+} w12_i8;
+
+/*
+ * w12_i8_build -- the 8-bit copy of record `wt` into the caller's out->q and out->scale (out->n,
+ * out->k set by the caller to the record's).  Reads the whole record (planes and escape list);
+ * padding rows of the storage get code 0.  Enqueued on `stream`, no synchronisation.
+ */
+int w12_i8_build(const w12_weight *wt, w12_i8 *out, void *stream);
+
+/*
+ * w12_i8_gemm -- the Q pass on the 8-bit copy: y[m][n] = s_n * sum_k x[m][k] q[n][k] + the exact
+ * escapes' products, fp32 accumulate.  Reads cp->q, cp->scale and wt's escape arrays (wt->base,
+ * wt->ae and wt->lo are not read and may be NULL).  Same x, y, flags (W12_PATH_*, W12_OUT_BF16),
+ * kernel families and error bound as w12_q8_gemm, against the weights s_n * q; more than 64 rows
+ * of x run as passes of at most 64.  W12_Q8_MIDPOINT is W12_ERR_ARG.
+ */
+int w12_i8_gemm(const uint16_t *x, int64_t m, const w12_i8 *cp, const w12_weight *wt, float *y,
+                uint32_t flags, void *stream);
+
+/*
+ * w12_i8_top1 -- top-1 of the Q pass on the 8-bit copy per row of x, as w12_q8_top1 (idx int32,
+ * val float; ties to the smallest n); flags must be 0.
+ */
+int w12_i8_top1(const uint16_t *x, int64_t m, const w12_i8 *cp, const w12_weight *wt, int32_t *idx,
+                float *val, uint32_t flags, void *stream);
+
+/*
  * w12_concat_rows -- the record of W = [W_0; W_1; ...; W_{count-1}] (the parts' rows stacked in
  * order) built on the device from the parts' records, without decoding or re-encoding.  Windows
  * and escape lists are per output row (figure-captions page, Fig. 5(a)), so the stacked record is

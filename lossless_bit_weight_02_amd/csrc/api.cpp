@@ -189,6 +189,35 @@ hipError_t workspace(hipStream_t s, float** out) {
 
 }  // namespace w12
 
+namespace {
+// The 8-bit copy and the record whose escape list it shares: same shape, codes 16-byte aligned.
+int check_i8(const w12_i8* cp, const w12_weight* wt) {
+  if (!cp || !wt) return fail(W12_ERR_ARG, "the 8-bit copy or the record is NULL");
+  int rc = check_nk(wt->n, wt->k);
+  if (rc) return rc;
+  if (cp->n != wt->n || cp->k != wt->k)
+    return fail(W12_ERR_ARG, "the 8-bit copy is [%lld, %lld], the record [%lld, %lld]", (long long)cp->n,
+                (long long)cp->k, (long long)wt->n, (long long)wt->k);
+  if (!cp->q || !cp->scale || !wt->esc_ptr) return fail(W12_ERR_ARG, "q, scale or esc_ptr is NULL");
+  if (wt->esc_cap > 0 && (!wt->esc_col || !wt->esc_val))
+    return fail(W12_ERR_ARG, "escape arrays are NULL but esc_cap > 0");
+  if (!aligned16(cp->q) || !aligned4(cp->scale)) return fail(W12_ERR_ALIGN, "q must be 16-byte and scale 4-byte aligned");
+  if (!aligned4(wt->esc_ptr) || (wt->esc_col && !aligned4(wt->esc_col)) ||
+      (wt->esc_val && (reinterpret_cast<uintptr_t>(wt->esc_val) & 1u)))
+    return fail(W12_ERR_ALIGN, "escape arrays must be naturally aligned");
+  return W12_OK;
+}
+
+w12::Planes planes_i8(const w12_i8* cp, const w12_weight* wt) {
+  w12::Planes p = planes_of(wt);
+  p.base = nullptr;
+  p.ae = reinterpret_cast<const uint8_t*>(cp->q);
+  p.lo = nullptr;
+  p.scale = cp->scale;
+  return p;
+}
+}  // namespace
+
 extern "C" {
 
 int w12_abi_version(void) { return W12_ABI_VERSION; }
@@ -343,6 +372,46 @@ int w12_concat_rows(const w12_weight* parts, int count, w12_weight* out, uint64_
     r0 += p.n;
     e0 += tot[i];
   }
+  return ok();
+}
+
+
+int w12_i8_build(const w12_weight* wt, w12_i8* out, void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  if (!out) return fail(W12_ERR_ARG, "out is NULL");
+  if (out->n != wt->n || out->k != wt->k)
+    return fail(W12_ERR_ARG, "out is [%lld, %lld], the record [%lld, %lld]", (long long)out->n,
+                (long long)out->k, (long long)wt->n, (long long)wt->k);
+  if (!out->q || !out->scale) return fail(W12_ERR_ARG, "out->q or out->scale is NULL");
+  if (!aligned16(out->q) || !aligned4(out->scale)) return fail(W12_ERR_ALIGN, "q must be 16-byte and scale 4-byte aligned");
+  hipError_t e = w12::launch_i8_build(planes_of(wt), wt->n, wt->k, out->q, out->scale,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "8-bit copy launch");
+  return ok();
+}
+
+int w12_i8_gemm(const uint16_t* x, int64_t m, const w12_i8* cp, const w12_weight* wt, float* y,
+                uint32_t flags, void* stream) {
+  int rc = check_i8(cp, wt);
+  if (rc) return rc;
+  if (flags & W12_Q8_MIDPOINT) return fail(W12_ERR_ARG, "W12_Q8_MIDPOINT does not apply to the 8-bit copy");
+  return run_gemm(w12::kFmtI8, x, m, planes_i8(cp, wt), wt->n, wt->k, y, flags, stream);
+}
+
+int w12_i8_top1(const uint16_t* x, int64_t m, const w12_i8* cp, const w12_weight* wt, int32_t* idx,
+                float* val, uint32_t flags, void* stream) {
+  int rc = check_i8(cp, wt);
+  if (rc) return rc;
+  if (!x || !idx || !val) return fail(W12_ERR_ARG, "x, idx or val is NULL");
+  if (flags != 0) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
+  if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
+  if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
+  if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned4(idx) || !aligned4(val)) return fail(W12_ERR_ALIGN, "idx and val must be 4-byte aligned");
+  hipError_t e = w12::launch_mfma_top1(w12::kFmtI8, x, m, planes_i8(cp, wt), wt->n, wt->k, idx, val,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "top-1 launch");
   return ok();
 }
 

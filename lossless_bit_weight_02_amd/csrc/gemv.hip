@@ -48,6 +48,7 @@ struct GemvArgs {
   const uint32_t* esc_col;
   const uint16_t* esc_val;
   const uint16_t* w;      // dense bfloat16 W (baseline), tiled storage
+  const float* scale;     // per-row scale of the 8-bit copy (its codes are in `ae`)
   float* y;               // y[m][ldy]; with splits > 1, range j writes y + j * ysplit
   int64_t ldy;
   int64_t n, k;           // rows of W, row length
@@ -117,6 +118,9 @@ __device__ __forceinline__ void block_pairs(const BlockRegs<FMT>& r, uint32_t e1
     window_group8(r.v[0].z, r.v[0].w, r.v[2].y, e112, p + 4);
     window_group8(r.v[1].x, r.v[1].y, r.v[2].z, e112, p + 8);
     window_group8(r.v[1].z, r.v[1].w, r.v[2].w, e112, p + 12);
+  } else if constexpr (FMT == kFmtI8) {
+    i8_group16(r.v[0], p);
+    i8_group16(r.v[1], p + 8);
   } else {
     window_group8_q(r.v[0].x, r.v[0].y, e112, p);
     window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
@@ -175,14 +179,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
   constexpr bool kEsc = FMT != kFmtBF16;
   uint32_t ce0 = 0, ce1 = 0, ecol[kEscPre], evalv[kEscPre];   // current tile
   uint32_t ne0 = 0, ne1 = 0, nte0 = 0;                         // next tile (bounds only)
-  uint32_t cbase = 0, nbase = 0;                               // window bottom of the row
+  uint32_t cbase = 0, nbase = 0;        // window bottom of the row (float bits of the 8-bit copy's scale)
   const auto esc_bounds = [&](int64_t ps, uint32_t& e0, uint32_t& e1, uint32_t& te0, uint32_t& bs) {
     const int64_t t = tile_of(ps);
     const bool use = kEsc && part == 0 && ps < passes && t < tiles;
     const int64_t r = use ? t * kTileRows + r16 : 0;
     e0 = use ? a.esc_ptr[r < a.n ? r : a.n] : 0u;
     e1 = use ? a.esc_ptr[r + 1 < a.n ? r + 1 : a.n] : 0u;
-    bs = use ? a.base[r < a.n ? r : a.n - 1] : 0u;
+    if constexpr (FMT == kFmtI8) bs = use ? __float_as_uint(a.scale[r < a.n ? r : a.n - 1]) : 0u;
+    else bs = use ? a.base[r < a.n ? r : a.n - 1] : 0u;
     te0 = use ? a.esc_ptr[t * kTileRows] : 0u;   // made uniform only when used, a tile later:
   };                                              // a uniform copy now would wait for the ring
   const auto esc_entries = [&](uint32_t e0, uint32_t e1, uint32_t te0v) {
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             const float xv = bf16_to_float(xs16[m * kn + c]);
-            acc[m] = fmaf(-xv, placeholder_of<FMT>(), acc[m]);
+            if constexpr (has_placeholder<FMT>()) acc[m] = fmaf(-xv, placeholder_of<FMT>(), acc[m]);
             q[m] = fmaf(xv, v, q[m]);
           }
         }
@@ -332,7 +337,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
 
     if (part == 0 && valid && g == 0 && row < a.n) {
       float sc = 1.0f;
-      if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
+      if constexpr (FMT == kFmtI8) sc = __uint_as_float(cbase);
+      else if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float v = FMT != kFmtBF16 ? fmaf(sc, acc[m], q[m]) : acc[m];
@@ -391,6 +397,7 @@ static GemvKernel pick_kernel(Fmt f, int m) {
   if (f == kFmtW12) return pick<kFmtW12>(m);
   if (f == kFmtQ8) return pick<kFmtQ8>(m);
   if (f == kFmtQ8M) return pick<kFmtQ8M>(m);
+  if (f == kFmtI8) return pick<kFmtI8>(m);
   return pick<kFmtBF16>(m);
 }
 
@@ -446,6 +453,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     a.base = p.base; a.ae = p.ae; a.lo = p.lo;
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
     a.w = p.w;
+    a.scale = p.scale;
     a.ldy = n;
     a.n = n; a.k = k;
     a.x = x + m0 * k;

@@ -181,7 +181,8 @@ void k_mfma(MfmaArgs a) {
     lds_barrier();                                 // the previous tile no longer reads LDS
 
     // ---- row bounds and window bottoms of the tile's escapes (oldest loads) ----
-    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0, t_cnt = 0;
+    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, t_cnt = 0;
+    RowScales<FMT> rsc;
     if constexpr (kScale) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
@@ -189,10 +190,7 @@ void k_mfma(MfmaArgs a) {
 #pragma unroll
         for (int r = 0; r < 5; ++r) st[r] = ptr_at(rg + r);
       }
-      const Rsrc rb = make_rsrc(a.base, (uint32_t)a.n);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
+      rsc.load(a, rg);
     }
 
     // ---- the range's first chunk of x, straight into LDS buffer 0 ----
@@ -439,12 +437,12 @@ void k_mfma(MfmaArgs a) {
             for (int cc = 0; cc < NT; ++cc) {
               const uint32_t wd = xw[i][cc >> 1];
               const float xv = __builtin_bit_cast(float, (cc & 1) ? wd & 0xFFFF0000u : wd << 16);
-              acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+              if constexpr (has_placeholder<FMT>()) acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
               q[cc] = fmaf(xv, v[i], q[cc]);
             }
           }
         }
-        const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+        const float sc = rsc.get(r);
 #pragma unroll
         for (int cc = 0; cc < NT; ++cc) acc[cc][r] = fmaf(sc, acc[cc][r], q[cc]);
       }
@@ -467,8 +465,8 @@ void k_mfma(MfmaArgs a) {
         float v4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
-          v4[r] = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
+          v4[r] = kEsc ? fmaf(rsc.get(r), has_placeholder<FMT>() ? fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r])
+                                                                  : acc[cc][r], qv[cc][r])
                        : acc[cc][r];
         }
         *reinterpret_cast<floatx4*>(&res[(16 * (cc - c0g) + r16) * 20 + 4 * g]) = (floatx4){v4[0], v4[1], v4[2], v4[3]};
@@ -507,12 +505,13 @@ void k_mfma(MfmaArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int64_t nrow = row0 + 4 * g + r;
         if (nrow >= a.n) continue;
-        const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+        const float sc = rsc.get(r);
 #pragma unroll
         for (int cc = 0; cc < NT; ++cc) {
           const int mcol = 16 * cc + r16;
           if (mcol >= a.m) continue;
-          const float v = kEsc ? fmaf(sc, fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r]), qv[cc][r])
+          const float v = kEsc ? fmaf(sc, has_placeholder<FMT>() ? fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r])
+                                                                 : acc[cc][r], qv[cc][r])
                                : acc[cc][r];   // (with kEscEpi acc is already final)
           const uint64_t key = top1_key(v, nrow);
           best[cc] = key > best[cc] ? key : best[cc];
@@ -546,7 +545,7 @@ void k_mfma(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int FMT, int W>
 static MfmaKernel pick(int nt) {
-  if constexpr (W == 12)
+  if constexpr (W == 12 && FMT != kFmtI8)   // the 8-bit copy runs passes of at most 64 rows
     if (nt == 8) return k_mfma<FMT, 8, W, false>;
   if (nt >= 3) return mfma_wide_kernel(static_cast<Fmt>(FMT), nt);
   return nt == 1 ? k_mfma<FMT, 1, W, false> : k_mfma<FMT, 2, W, false>;
@@ -557,6 +556,7 @@ static MfmaKernel pick(int nt) {
 static MfmaKernel pick_top1(Fmt f, int nt) {
   if (f == kFmtW12) return nt == 1 ? k_mfma<kFmtW12, 1, kWaves, true> : k_mfma<kFmtW12, 2, kWaves, true>;
   if (f == kFmtQ8M) return nt == 1 ? k_mfma<kFmtQ8M, 1, kWaves, true> : k_mfma<kFmtQ8M, 2, kWaves, true>;
+  if (f == kFmtI8) return nt == 1 ? k_mfma<kFmtI8, 1, kWaves, true> : k_mfma<kFmtI8, 2, kWaves, true>;
   return nt == 1 ? k_mfma<kFmtQ8, 1, kWaves, true> : k_mfma<kFmtQ8, 2, kWaves, true>;
 }
 
@@ -565,6 +565,7 @@ static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
   if (f == kFmtW12) return pick<kFmtW12, 12>(nt);
   if (f == kFmtQ8) return pick<kFmtQ8, 12>(nt);
   if (f == kFmtQ8M) return pick<kFmtQ8M, 12>(nt);
+  if (f == kFmtI8) return pick<kFmtI8, 12>(nt);
   return pick<kFmtBF16, 12>(nt);
 }
 
@@ -619,6 +620,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.base = p.base; a.ae = p.ae; a.lo = p.lo;
   a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
   a.w = p.w;
+  a.scale = p.scale;
   a.y = ws ? ws : y.f;
   a.y16 = ws ? nullptr : y.h;
   a.ldy = ws ? n : ldy;                        // partial slices are [mb][n], contiguous
@@ -666,6 +668,7 @@ static Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
   if (t.lo) t.lo += r0 * k / 2;
   if (t.esc_ptr) t.esc_ptr += r0;
   if (t.w) t.w += r0 * k;
+  if (t.scale) t.scale += r0;
   return t;
 }
 
@@ -679,7 +682,8 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   // than 64 rows need x transposed in the workspace, else they stay at 64.  The kernels address
   // x with 32-bit byte offsets (2 * rows * k), so a pass of 128 rows also needs 256 k < 2^32.
   const bool wide_ok = f == kFmtBF16 ? 256 * k < (int64_t(1) << 32)
-                                     : k * 128 * 2 <= (int64_t)sc.bytes;
+                      : f == kFmtI8   ? false
+                                      : k * 128 * 2 <= (int64_t)sc.bytes;
   const int64_t max_step = wide_ok ? 128 : 64;
   for (int64_t m0 = 0, step = 0; m0 < m; m0 += step) {
     step = (m - m0) < max_step ? (m - m0) : max_step;
@@ -733,6 +737,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     a.base = p.base; a.ae = p.ae; a.lo = p.lo;
     a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
     a.w = p.w;
+    a.scale = p.scale;
     a.y = nullptr;
     a.y16 = nullptr;
     a.ldy = nh;

@@ -24,6 +24,7 @@ struct MfmaArgs {
   const uint32_t* esc_col;
   const uint16_t* esc_val;
   const uint16_t* w;   // dense bfloat16 W (baseline), tiled storage
+  const float* scale;  // per-row scale of the 8-bit copy (its codes are in `ae`)
   float* y;            // y[m][ldy]; with splits > 1, split j writes y + j * ysplit
   int64_t ldy;
   int64_t n, k;
@@ -90,6 +91,9 @@ __device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112
     window_group8(r.v[0].z, r.v[0].w, r.v[2].y, e112, p + 4);
     window_group8(r.v[1].x, r.v[1].y, r.v[2].z, e112, p + 8);
     window_group8(r.v[1].z, r.v[1].w, r.v[2].w, e112, p + 12);
+  } else if constexpr (FMT == kFmtI8) {
+    i8_group16(r.v[0], p);
+    i8_group16(r.v[1], p + 8);
   } else {
     window_group8_q(r.v[0].x, r.v[0].y, e112, p);
     window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
@@ -98,6 +102,32 @@ __device__ __forceinline__ void ablock_pairs(const ABlock<FMT>& r, uint32_t e112
     if constexpr (FMT == kFmtQ8M) midpoint16(p);
   }
 }
+
+// The scales of a lane's four output rows rg .. rg + 3: the window bottoms of the W12 record
+// (packed bytes; the scale is 2^(base - 112)) or the float scales of the 8-bit copy.  Rows past
+// n read 0.
+template <int FMT>
+struct RowScales {
+  uint32_t bases = 0;
+  float f[FMT == kFmtI8 ? 4 : 1] = {};
+  __device__ __forceinline__ void load(const MfmaArgs& a, int64_t rg) {
+    if constexpr (FMT == kFmtI8) {
+      const Rsrc rs = make_rsrc(a.scale, (uint32_t)a.n * 4u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(rg + r) * 4u, 0, 0));
+    } else {
+      const Rsrc rb = make_rsrc(a.base, (uint32_t)a.n);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
+    }
+  }
+  __device__ __forceinline__ float get(int r) const {
+    if constexpr (FMT == kFmtI8) return f[r];
+    else return window_scale((bases >> (8 * r)) & 0xFFu);
+  }
+};
 
 typedef void (*MfmaKernel)(MfmaArgs);
 

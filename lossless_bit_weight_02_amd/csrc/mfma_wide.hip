@@ -141,17 +141,15 @@ void k_mfma_wide(MfmaArgs a) {
     lds_barrier();                                 // the previous tile no longer reads LDS
 
     // ---- escape list of the tile (oldest loads: waited for before the loop) ----
-    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, bases = 0;
+    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0;
+    RowScales<FMT> rsc;
     uint32_t ecol[kEscCap / 64], evalv[kEscCap / 64];
     if constexpr (kEsc) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
 #pragma unroll
       for (int r = 0; r < 5; ++r) st[r] = ptr_at(rg + r);
-      const Rsrc rb = make_rsrc(a.base, (uint32_t)a.n);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        bases |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rb, (uint32_t)(rg + r), 0, 0) << (8 * r);
+      rsc.load(a, rg);
       t_e0 = __builtin_amdgcn_readfirstlane(a.esc_ptr[row0]);
       const uint32_t t_e1 = __builtin_amdgcn_readfirstlane(valid ? ptr_at(row0 + kTileRows) : t_e0);
       const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCap ? t_e1 - t_e0 : (uint32_t)kEscCap;
@@ -276,7 +274,7 @@ void k_mfma_wide(MfmaArgs a) {
             for (int cc = 0; cc < NT; ++cc) {
               const float xv = bf16_to_float(
                   reinterpret_cast<const uint16_t*>(&s_x[b][(f0 + cc) * 64 + ln])[col & 7u]);
-              acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+              if constexpr (has_placeholder<FMT>()) acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
               qv[cc][r] = fmaf(xv, v, qv[cc][r]);
             }
             cur[r] += 1;
@@ -299,7 +297,7 @@ void k_mfma_wide(MfmaArgs a) {
           for (int cc = 0; cc < NT; ++cc) {
             const int mrow = 16 * cc + r16;
             const float xv = mrow < a.m ? bf16_to_float(a.x[(int64_t)mrow * a.k + col]) : 0.0f;
-            acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
+            if constexpr (has_placeholder<FMT>()) acc[cc][r] = fmaf(-xv, placeholder_of<FMT>(), acc[cc][r]);
             qv[cc][r] = fmaf(xv, v, qv[cc][r]);
           }
         }
@@ -309,7 +307,7 @@ void k_mfma_wide(MfmaArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int64_t nrow = row0 + 4 * g + r;
       if (nrow >= a.n) continue;
-      const float sc = window_scale((bases >> (8 * r)) & 0xFFu);
+      const float sc = rsc.get(r);
 #pragma unroll
       for (int cc = 0; cc < NT; ++cc) {
         const int mcol = 16 * cc + r16;
@@ -329,6 +327,7 @@ MfmaKernel mfma_wide_kernel(Fmt f, int nt) {
   if (f == kFmtW12) return nt == 3 ? k_mfma_wide<kFmtW12, 3> : k_mfma_wide<kFmtW12, 4>;
   if (f == kFmtQ8) return nt == 3 ? k_mfma_wide<kFmtQ8, 3> : k_mfma_wide<kFmtQ8, 4>;
   if (f == kFmtQ8M) return nt == 3 ? k_mfma_wide<kFmtQ8M, 3> : k_mfma_wide<kFmtQ8M, 4>;
+  if (f == kFmtI8) return nt == 3 ? k_mfma_wide<kFmtI8, 3> : k_mfma_wide<kFmtI8, 4>;
   return nt == 3 ? k_mfma_wide<kFmtBF16, 3> : k_mfma_wide<kFmtBF16, 4>;
 }
 

@@ -94,6 +94,27 @@ constexpr float kPlaceholder = 3.0517578125e-05f;
 constexpr float kPlaceholderMid = 3.24249267578125e-05f;
 template <int FMT>
 constexpr float placeholder_of() { return FMT == 3 ? kPlaceholderMid : kPlaceholder; }
+// Whether an escaped slot contributes a placeholder that the escape patch must take back out:
+// every format but the 8-bit copy (format 4), whose escaped slots hold the code 0.
+template <int FMT>
+constexpr bool has_placeholder() { return FMT != 4; }
+
+// Sixteen signed 8-bit codes (one 128-bit word, columns in order) -> eight dwords of bfloat16
+// pairs (c0, c1) (c2, c3) ...: each code converts exactly to float (a sign-extended byte select),
+// and a code of magnitude <= 127 has at most 7 significant bits, so the float's high half is the
+// exact bfloat16; one byte permute packs two of them.
+__device__ __forceinline__ void i8_group16(u32x4 v, uint32_t out[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wd = v[i];
+    const float f0 = (float)(int8_t)(wd & 0xFFu);
+    const float f1 = (float)(int8_t)((wd >> 8) & 0xFFu);
+    const float f2 = (float)(int8_t)((wd >> 16) & 0xFFu);
+    const float f3 = (float)(int8_t)(wd >> 24);
+    out[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    out[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  }
+}
 
 // Midpoint Q pass: the B nibble of both bfloat16 halves of each decoded pair set to 8.
 __device__ __forceinline__ void midpoint16(uint32_t p[16]) {

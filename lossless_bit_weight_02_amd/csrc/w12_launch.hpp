@@ -6,8 +6,10 @@
 
 namespace w12 {
 
-// kFmtQ8M: the Q pass with the dropped B nibble read as 8 (the midpoint of its 16 values)
-enum Fmt : int { kFmtW12 = 0, kFmtQ8 = 1, kFmtBF16 = 2, kFmtQ8M = 3 };
+// kFmtQ8M: the Q pass with the dropped B nibble read as 8 (the midpoint of its 16 values);
+// kFmtI8: the Q pass on the separate 8-bit copy (int8 codes in the AE plane's storage order, one
+// float scale per row, escapes exact from the record's list)
+enum Fmt : int { kFmtW12 = 0, kFmtQ8 = 1, kFmtBF16 = 2, kFmtQ8M = 3, kFmtI8 = 4 };
 
 struct DevInfo {
   int device = -1;
@@ -84,6 +86,7 @@ struct Planes {
   const uint32_t* esc_col = nullptr;
   const uint16_t* esc_val = nullptr;
   const uint16_t* w = nullptr;  // kFmtBF16 only: the dense bfloat16 weight, tiled storage order
+  const float* scale = nullptr; // kFmtI8 only: per-row scale (the codes are in `ae`)
 };
 
 // x [m <= 128][k] bfloat16 -> xt [k][16][8], xt[c][r][t] = x[16 t + r][c] (rows past m zero),
@@ -103,6 +106,8 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
 hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
 // dst[i] = src[i] + add, i < cnt (escape offsets of a part placed after earlier parts)
 hipError_t launch_rebase(const uint32_t* src, int64_t cnt, uint32_t add, uint32_t* dst, hipStream_t s);
+// 8-bit Q-pass copy of a record: per-row scales, codes in the AE storage order, escaped slots 0
+hipError_t launch_i8_build(const Planes& p, int64_t n, int64_t k, int8_t* q, float* scale, hipStream_t s);
 // dense bf16 [n][k] -> tiled storage order (baseline layout)
 hipError_t launch_bf16_tile(const uint16_t* w, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
 // bandwidth probe

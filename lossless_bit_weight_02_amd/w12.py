@@ -42,6 +42,11 @@ class _W12Weight(ctypes.Structure):
                 ("esc_val", ctypes.c_void_p), ("esc_cap", ctypes.c_uint64)]
 
 
+class _W12I8(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -62,6 +67,13 @@ EXPORTS = {
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_gemm_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_i8_build": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.POINTER(_W12I8), ctypes.c_void_p]),
+    "w12_i8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12I8),
+                                   ctypes.POINTER(_W12Weight), ctypes.c_void_p, ctypes.c_uint32,
+                                   ctypes.c_void_p]),
+    "w12_i8_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12I8),
+                                   ctypes.POINTER(_W12Weight), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_uint32, ctypes.c_void_p]),
     "w12_concat_rows": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.c_int,
                                        ctypes.POINTER(_W12Weight), ctypes.POINTER(ctypes.c_uint64),
                                        ctypes.c_void_p]),
@@ -353,6 +365,61 @@ def q8_top1(x: torch.Tensor, wt: W12Weight, out=None, midpoint: bool = False):
 def gemm_top1(x: torch.Tensor, wt: W12Weight, out=None):
     """Top-1 of the exact pass per row of x: (index int32 [m], value float32 [m])."""
     return _top1(lib().w12_gemm_top1, x, wt, True, out)
+
+
+class I8Copy:
+    """The separate 8-bit Q-pass copy of a W12 record: int8 codes in the AE plane's storage order
+    (padded_rows(n) * k) and a float32 scale per row; it shares ``rec``'s escape list."""
+
+    def __init__(self, rec: W12Weight, q, scale):
+        self.rec, self.q, self.scale = rec, q, scale
+        self.n, self.k = rec.n, rec.k
+
+    @property
+    def device(self):
+        return self.q.device
+
+    def nbytes(self) -> int:
+        return self.q.numel() + self.scale.numel() * 4
+
+    def c_struct(self) -> _W12I8:
+        return _W12I8(self.n, self.k, self.q.data_ptr(), self.scale.data_ptr())
+
+    def to_numpy(self) -> dict:
+        import numpy as np
+        return dict(q_s=self.q.cpu().numpy().view(np.int8), scale=self.scale.cpu().numpy())
+
+
+def i8_build(rec: W12Weight) -> I8Copy:
+    """The 8-bit Q-pass copy of ``rec`` (per-row scale from the largest in-window magnitude / 127,
+    codes rounded to nearest even, escaped slots 0), built on the device."""
+    q = torch.empty(padded_rows(rec.n) * rec.k, dtype=torch.int8, device=rec.device)
+    scale = torch.empty(rec.n, dtype=torch.float32, device=rec.device)
+    cp = I8Copy(rec, q, scale)
+    s, c = rec.c_struct(), cp.c_struct()
+    _check(lib().w12_i8_build(ctypes.byref(s), ctypes.byref(c), _stream_handle(rec.device)))
+    return cp
+
+
+def i8_gemm(x: torch.Tensor, cp: I8Copy, path: str | None = None, out: torch.Tensor | None = None,
+            out_bf16: bool = False):
+    """Q pass on the 8-bit copy: y = x (s q)^T with the record's escapes exact; outputs as in gemm."""
+    x, out = _gemm_io(x, cp.n, cp.k, cp.device, out, out_bf16)
+    if x.shape[0] == 0:
+        return out
+    c, s = cp.c_struct(), cp.rec.c_struct()
+    s.ae = None
+    s.lo = None
+    _check(lib().w12_i8_gemm(x.data_ptr(), x.shape[0], ctypes.byref(c), ctypes.byref(s), out.data_ptr(),
+                             _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
+    return out
+
+
+def i8_top1(x: torch.Tensor, cp: I8Copy, out=None):
+    """Top-1 of the Q pass on the 8-bit copy per row of x: (index int32 [m], value float32 [m])."""
+    c = cp.c_struct()
+    return _top1(lambda xp, m, s, ip, vp, fl, st: lib().w12_i8_top1(xp, m, ctypes.byref(c), s, ip, vp, fl, st),
+                 x, cp.rec, False, out)
 
 
 class Bf16Tiles:

@@ -11,6 +11,8 @@ import multiprocessing as mp
 import os
 from concurrent.futures import ProcessPoolExecutor
 
+import dataclasses
+
 import numpy as np
 
 import oracle
@@ -79,3 +81,19 @@ def gemm(x_bits: np.ndarray, w_bits: np.ndarray, pool: ProcessPoolExecutor, view
     n = w_bits.shape[0]
     parts = list(pool.map(_gemm_chunk, [(x_bits, w_bits[a:b], view) for a, b in _chunks(n)]))
     return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
+
+
+def _i8_chunk(args):
+    """(scale, codes in the storage order, y64, sum |x w|) of the 8-bit Q-pass copy of one row
+    chunk (a whole number of 16-row tiles, so the chunks' storage orders concatenate)."""
+    x_bits, w_chunk = args
+    ref = oracle.encode(w_chunk)
+    cp = oracle.i8_copy(ref)
+    q_s = oracle.to_storage(dataclasses.replace(ref, ae=cp.q.view(np.uint8)))[0].view(np.int8)
+    wq = oracle.i8_weights64(ref, cp)
+    return cp.scale, q_s, oracle.gemm64_f(x_bits, wq), oracle.abs_bound64_f(x_bits, wq)
+
+
+def i8_chunks(x_bits: np.ndarray, w_bits: np.ndarray, pool: ProcessPoolExecutor):
+    """_i8_chunk over the row chunks of W, in order."""
+    return list(pool.map(_i8_chunk, [(x_bits, w_bits[a:b]) for a, b in _chunks(w_bits.shape[0])]))
