@@ -188,6 +188,35 @@ int w12_gemm_top1(const uint16_t *x, int64_t m, const w12_weight *wt, int32_t *i
                   uint32_t flags, void *stream);
 
 /*
+ * w12_interleave_rows -- the record of the gate and up projections of an MLP stacked with their
+ * rows interleaved in groups of 8: output rows 16 t .. 16 t + 7 are gate rows 8 t .. 8 t + 7 and
+ * rows 16 t + 8 .. 16 t + 15 are up rows 8 t .. 8 t + 7, so the two inputs of one
+ * SiLU(gate) * up output sit in one 16-row tile (summary page, Main Findings: W12 also speeds up
+ * plain decoding, where gate and up feed SiLU(gate) * up).  Built on the device from the two
+ * records without decoding (windows and escape lists are per row); byte-identical to w12_encode
+ * of the interleaved matrix.  gate and up: same [I, k], I % 8 == 0.  out: a record of
+ * [2 I, k] sized for it.  Synchronises `stream` once to read the parts' escape totals into
+ * *n_esc (host); if out->esc_cap is smaller, returns W12_ERR_CAPACITY before writing anything.
+ */
+int w12_interleave_rows(const w12_weight *gate, const w12_weight *up, w12_weight *out, uint64_t *n_esc,
+                        void *stream);
+
+/*
+ * w12_gemm_silu_mul -- the exact pass on row-interleaved gate+up weights (w12_interleave_rows)
+ * with the MLP activation applied where the outputs are stored: h[j][i] = silu(g) * u, where
+ * g = y[j][16 (i / 8) + i % 8] and u = y[j][16 (i / 8) + i % 8 + 8] are the gate and up outputs of
+ * w12_gemm on the same record and silu(z) = z / (1 + exp(-z)) in float.  x bfloat16 [m, k]; h is
+ * float [m, n / 2] (or bfloat16 bits with W12_OUT_BF16: each h rounded to nearest even), fully
+ * overwritten; wt->n % 16 == 0 (W12_ERR_SHAPE otherwise).  flags: W12_PATH_*, W12_OUT_BF16.
+ * The y values are never written to memory except as split-k partial sums in the GEMM workspace.
+ * Error bound per output, with B = 1e-3 * sum_k |x[j][k] W[row][k]| of each input row:
+ * 1.1 B_g (|u| + B_u) + |silu(g)| B_u + 2^-20 |h| (1.1 bounds the slope of silu), plus half a
+ * bfloat16 unit in the last place with W12_OUT_BF16.
+ */
+int w12_gemm_silu_mul(const uint16_t *x, int64_t m, const w12_weight *wt, float *h, uint32_t flags,
+                      void *stream);
+
+/*
  * The separate 8-bit copy for the Q pass (summary page, Main Findings: the RTX PRO 6000 port reads
  * an INT6/INT8 copy of the weights in the Q pass instead of the zero-copy 8-bit view).  It sits
  * beside a W12 record and shares that record's exact escape list.  The pages give no quantiser;

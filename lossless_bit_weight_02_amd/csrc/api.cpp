@@ -77,7 +77,7 @@ w12::Planes planes_of(const w12_weight* wt) {
 // fixed_scratch: run on the library's fixed scratch (allocation-free entry point) instead of the
 // per-stream workspace
 int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n, int64_t k,
-             float* y, uint32_t flags, void* stream, bool fixed_scratch = false) {
+             float* y, uint32_t flags, void* stream, bool fixed_scratch = false, bool silu = false) {
   if (!x || !y) return fail(W12_ERR_ARG, "x or y is NULL");
   if (m <= 0) return fail(W12_ERR_ARG, "m must be positive (m=%lld)", (long long)m);
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
@@ -94,6 +94,7 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   w12::YOut yo;
   if (out16) yo.h = reinterpret_cast<uint16_t*>(y);
   else yo.f = y;
+  yo.silu = silu;
   // Automatic choice, from measurements on the 27B-class shapes (W12 / Q8, us, GEMV vs matrix
   // core): the GEMV wins at 1-2 rows everywhere; at 3-5 rows it wins on shapes with few tiles and
   // rows of at most 8192 (stacked qkv [8192, 5120], 5 rows: 18.2 vs 20.4) and loses on long rows
@@ -273,6 +274,46 @@ int w12_gemm_noalloc(const uint16_t* x, int64_t m, const w12_weight* wt, float* 
   int rc = check_record(wt, true);
   if (rc) return rc;
   return run_gemm(w12::kFmtW12, x, m, planes_of(wt), wt->n, wt->k, y, flags, stream, true);
+}
+
+int w12_gemm_silu_mul(const uint16_t* x, int64_t m, const w12_weight* wt, float* h, uint32_t flags,
+                      void* stream) {
+  int rc = check_record(wt, true);
+  if (rc) return rc;
+  if (wt->n % 16 != 0)
+    return fail(W12_ERR_SHAPE, "row-interleaved gate+up weights need n %% 16 == 0 (n=%lld)", (long long)wt->n);
+  return run_gemm(w12::kFmtW12, x, m, planes_of(wt), wt->n, wt->k, h, flags, stream, false, true);
+}
+
+int w12_interleave_rows(const w12_weight* gate, const w12_weight* up, w12_weight* out, uint64_t* n_esc,
+                        void* stream) {
+  if (!gate || !up || !out || !n_esc) return fail(W12_ERR_ARG, "gate, up, out or n_esc is NULL");
+  int rc = check_record(gate, true);
+  if (!rc) rc = check_record(up, true);
+  if (!rc) rc = check_record(out, true);
+  if (rc) return rc;
+  if (gate->n != up->n || gate->k != up->k || gate->n % 8 != 0)
+    return fail(W12_ERR_SHAPE, "gate and up must have the same shape with n %% 8 == 0 (gate [%lld, %lld], up "
+                "[%lld, %lld])", (long long)gate->n, (long long)gate->k, (long long)up->n, (long long)up->k);
+  if (out->n != 2 * gate->n || out->k != gate->k)
+    return fail(W12_ERR_ARG, "out must be [%lld, %lld]", (long long)(2 * gate->n), (long long)gate->k);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t tot[2];
+  hipError_t e = hipMemcpyAsync(&tot[0], gate->esc_ptr + gate->n, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&tot[1], up->esc_ptr + up->n, 4, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "escape total copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "interleave synchronisation");
+  const uint64_t total = (uint64_t)tot[0] + tot[1];
+  *n_esc = total;
+  if (total >= 0xFFFFFFFFull) return fail(W12_ERR_RANGE, "escape total does not fit the 32-bit CSR");
+  if (out->esc_cap < total)
+    return fail(W12_ERR_CAPACITY, "esc_cap %llu < escape total %llu", (unsigned long long)out->esc_cap,
+                (unsigned long long)total);
+  e = w12::launch_interleave(planes_of(gate), planes_of(up), out->n, out->k, out->base, out->ae, out->lo,
+                             out->esc_ptr, out->esc_col, out->esc_val, s);
+  if (e != hipSuccess) return hip_fail(e, "interleave launch");
+  return ok();
 }
 
 int w12_q8_gemm(const uint16_t* x, int64_t m, const w12_weight* wt, float* y, uint32_t flags, void* stream) {

@@ -59,6 +59,7 @@ struct GemvArgs {
   int64_t kend;           // end of the slice (the last range may be shorter)
   int64_t ysplit;         // floats between the partial outputs of consecutive ranges
   uint16_t* y16;          // set (one slice, one range): outputs as bfloat16 (nearest even) here
+  int silu;               // (one slice, one range) y / y16 hold h = silu(gate) * up, [m][ldy / 2]
 };
 
 // One 128-column block of the lane's row: the raw 128-bit words it loads.
@@ -335,7 +336,24 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
       lds_barrier();
     }
 
-    if (part == 0 && valid && g == 0 && row < a.n) {
+    if (a.silu && part == 0 && valid) {
+      // SiLU(gate) * up: rows r16 < 8 of the tile are gate rows, r16 + 8 the matching up rows
+      // (lane ^ 8 of the same wave); h [m][ldy / 2] gets 8 outputs per tile
+      float sc = 1.0f;
+      if constexpr (FMT == kFmtI8) sc = __uint_as_float(cbase);
+      else if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = FMT != kFmtBF16 ? fmaf(sc, acc[m], q[m]) : acc[m];
+        const float up = __shfl_xor(v, 8);
+        if (g == 0 && r16 < 8) {
+          const float hv = silu(v) * up;
+          const int64_t at = m * (a.ldy >> 1) + tile * 8 + r16;
+          if (a.y16) a.y16[at] = float_to_bf16_rne(hv);
+          else yout[at] = hv;
+        }
+      }
+    } else if (part == 0 && valid && g == 0 && row < a.n) {
       float sc = 1.0f;
       if constexpr (FMT == kFmtI8) sc = __uint_as_float(cbase);
       else if constexpr (FMT != kFmtBF16) sc = window_scale(cbase);
@@ -458,6 +476,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     a.n = n; a.k = k;
     a.x = x + m0 * k;
     a.y16 = nullptr;
+    a.silu = 0;
     if (ws) {
       // one launch over all ranges into the workspace, then the ordered sum into y
       int64_t groups = slots / ranges;
@@ -480,13 +499,16 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
     int64_t groups = passes < slots ? passes : slots;
     const YOut yp = y + m0 * n;
     float* acc32 = nullptr;
-    if (yp.h && k > slice) {
+    if ((yp.h || yp.silu) && k > slice) {
       if ((size_t)mb * n * sizeof(float) > sc.bytes) return hipErrorInvalidValue;
       err = sc.get(&acc32);
       if (err != hipSuccess) return err;
     }
-    a.y = yp.h ? acc32 : yp.f;
-    a.y16 = yp.h && !acc32 ? yp.h : nullptr;
+    // (several slices with bfloat16 or SiLU outputs: float sums in the workspace, then a
+    // one-range reduce rounds or pairs them into y)
+    a.y = acc32 ? acc32 : yp.f;
+    a.y16 = acc32 ? nullptr : yp.h;
+    a.silu = acc32 ? 0 : (int)yp.silu;
     a.splits = 1;
     a.ysplit = 0;
     for (int64_t k0 = 0; k0 < k; k0 += slice) {

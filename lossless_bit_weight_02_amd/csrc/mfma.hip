@@ -447,7 +447,42 @@ void k_mfma(MfmaArgs a) {
         for (int cc = 0; cc < NT; ++cc) acc[cc][r] = fmaf(sc, acc[cc][r], q[cc]);
       }
     }
-    if constexpr (!TOP1) {
+    if (!TOP1 && a.silu) {
+      // SiLU(gate) * up: lanes g = 0, 1 hold gate rows 4 g .. 4 g + 3 of x row 16 cc + r16, lanes
+      // g + 2 (lane ^ 32) the matching up rows; h gets 4 consecutive outputs per lane
+      const int64_t ldh = a.ldy >> 1;
+#pragma unroll
+      for (int cc = 0; cc < NT; ++cc) {
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = kEsc ? fmaf(rsc.get(r), has_placeholder<FMT>() ? fmaf(-sx[cc][r], placeholder_of<FMT>(), acc[cc][r])
+                                                                       : acc[cc][r], qv[cc][r])
+                               : acc[cc][r];
+          const float up = __shfl_xor(v, 32);
+          hv[r] = silu(v) * up;
+        }
+        const int mcol = 16 * cc + r16;
+        if (g < 2 && mcol < a.m) {
+          const int64_t at = mcol * ldh + row0 / 2 + 4 * g;
+          if (a.y16) {
+            const u32x2 pk = {(uint32_t)float_to_bf16_rne(hv[0]) | (uint32_t)float_to_bf16_rne(hv[1]) << 16,
+                              (uint32_t)float_to_bf16_rne(hv[2]) | (uint32_t)float_to_bf16_rne(hv[3]) << 16};
+            if (a.yvec) {
+              *reinterpret_cast<u32x2*>(&a.y16[at]) = pk;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a.y16[at + i] = float_to_bf16_rne(hv[i]);
+            }
+          } else if (a.yvec) {
+            *reinterpret_cast<floatx4*>(&yout[at]) = (floatx4){hv[0], hv[1], hv[2], hv[3]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yout[at + i] = hv[i];
+          }
+        }
+      }
+    } else if constexpr (!TOP1) {
       // lane (g, r16) holds rows 4 g .. 4 g + 3 of x row 16 cc + r16: written to the wave's part of
       // the idle x buffer as [x row][20 floats] (4 of padding), read back so that lane l holds
       // rows 4 (l % 4) .. +3 of x row 16 j + l / 4, and stored as one 16-byte vector (or four
@@ -623,6 +658,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.scale = p.scale;
   a.y = ws ? ws : y.f;
   a.y16 = ws ? nullptr : y.h;
+  a.silu = ws ? 0 : (int)y.silu;               // a split pairs the outputs in its sum instead
   a.ldy = ws ? n : ldy;                        // partial slices are [mb][n], contiguous
   a.n = n; a.k = k;
   a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
@@ -631,8 +667,11 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.ysplit = (int64_t)mb * n;
   a.top1 = nullptr;
   // vector stores: 16 bytes of float (y 16-byte aligned) or 8 of bfloat16 (y16 8-byte aligned)
-  a.yvec = a.y16 ? (reinterpret_cast<uintptr_t>(a.y16) & 7u) == 0 && a.ldy % 4 == 0
-                 : a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 4 == 0;
+  {
+    const int64_t ld_out = a.silu ? a.ldy / 2 : a.ldy;   // row stride of what is stored
+    a.yvec = a.y16 ? (reinterpret_cast<uintptr_t>(a.y16) & 7u) == 0 && ld_out % 4 == 0
+                   : a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && ld_out % 4 == 0;
+  }
   a.xt = nullptr;
   if (nt == 8 && f != kFmtBF16) {
     // x transposed into the workspace for the epilogue's escape patch (no split here)
@@ -740,6 +779,7 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     a.scale = p.scale;
     a.y = nullptr;
     a.y16 = nullptr;
+    a.silu = 0;
     a.ldy = nh;
     a.n = nh; a.k = k;
     a.rounds = (int)((th + groups * kWaves - 1) / (groups * kWaves));

@@ -41,6 +41,9 @@ struct MfmaArgs {
   int yvec;
   // with y16 set (a single k range), the outputs go there as bfloat16 (nearest even) instead of y
   uint16_t* y16;
+  // (a single k range) the weights are row-interleaved gate+up (rows 0..7 of a tile gate, 8..15
+  // up): y / y16 hold h = silu(gate) * up, [m][ldy / 2], 8 outputs per tile
+  int silu;
   // eight activation tiles (W12 and Q8): x transposed, [k][128] bfloat16 (rows past m zero); the
   // epilogue reads the escapes' x values from it
   const uint16_t* xt;

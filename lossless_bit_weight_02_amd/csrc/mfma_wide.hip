@@ -303,6 +303,26 @@ void k_mfma_wide(MfmaArgs a) {
         }
       }
     }
+    if (a.silu) {
+      // SiLU(gate) * up: lanes g = 0, 1 hold gate rows 4 g .. 4 g + 3, lane ^ 32 the up rows
+      const int64_t ldh = a.ldy >> 1;
+#pragma unroll
+      for (int cc = 0; cc < NT; ++cc) {
+        const int mcol = 16 * cc + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = kEsc ? fmaf(rsc.get(r), acc[cc][r], qv[cc][r]) : acc[cc][r];
+          const float up = __shfl_xor(v, 32);
+          const float hv = silu(v) * up;
+          const int64_t at = mcol * ldh + row0 / 2 + 4 * g + r;
+          if (g < 2 && mcol < a.m) {
+            if (a.y16) a.y16[at] = float_to_bf16_rne(hv);
+            else a.y[at] = hv;
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t nrow = row0 + 4 * g + r;

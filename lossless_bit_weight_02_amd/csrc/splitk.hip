@@ -49,28 +49,45 @@ hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt,
 // The partial slices arrive from memory (written by the previous kernel): every thread issues
 // the loads of up to 16 slices at once -- buffer loads, which return 0 past the last slice
 // instead of needing a branch -- and then adds them in order.
+// The ordered sum over the k ranges of element i of the [rows][cols] partial slices.
+__device__ __forceinline__ float range_sum(const Rsrc& rp, int splits, int64_t cnt, int64_t i) {
+  float s = 0.0f;
+  for (int j0 = 0; j0 < splits; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rp, (uint32_t)(((int64_t)(j0 + j) * cnt + i) * 4), 0, 0));
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j0 + j < splits) s = (j0 + j == 0) ? v[j] : s + v[j];
+  }
+  return s;
+}
+
+// silu: the gate and up sums of output i (row r, column c of h [rows][cols / 2]) are the slices'
+// columns 16 (c / 8) + c % 8 and that + 8; h = silu(gate) * up goes to r * (ldy / 2) + c.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int splits,
                                                       int64_t rows, int64_t cols,
                                                       float* __restrict__ y, uint16_t* __restrict__ y16,
-                                                      int64_t ldy) {
+                                                      int64_t ldy, int silu_pairs) {
   const int64_t cnt = rows * cols;
   const Rsrc rp = make_rsrc(part, (uint32_t)((int64_t)splits * cnt * 4));
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += step) {
-    float s = 0.0f;
-    for (int j0 = 0; j0 < splits; j0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             rp, (uint32_t)(((int64_t)(j0 + j) * cnt + i) * 4), 0, 0));
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j0 + j < splits) s = (j0 + j == 0) ? v[j] : s + v[j];
+  const int64_t oc = silu_pairs ? cols / 2 : cols, ld = silu_pairs ? ldy / 2 : ldy;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * oc; i += step) {
+    const int64_t r = i / oc, c = i - r * oc;
+    float v;
+    if (silu_pairs) {
+      const int64_t gc = 16 * (c / 8) + c % 8;
+      const float gate = range_sum(rp, splits, cnt, r * cols + gc);
+      const float up = range_sum(rp, splits, cnt, r * cols + gc + 8);
+      v = silu(gate) * up;
+    } else {
+      v = range_sum(rp, splits, cnt, i);
     }
-    const int64_t r = i / cols;
-    if (y16) y16[r * ldy + (i - r * cols)] = float_to_bf16_rne(s);
-    else y[r * ldy + (i - r * cols)] = s;
+    if (y16) y16[r * ld + c] = float_to_bf16_rne(v);
+    else y[r * ld + c] = v;
   }
 }
 
@@ -143,7 +160,7 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int6
   int64_t blocks = (rows * cols + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, splits, rows, cols,
-                     y.f, y.h, ldy);
+                     y.f, y.h, ldy, y.silu ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -129,6 +129,9 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// silu(z) = z / (1 + e^-z) in float (e^-z overflowing to +Inf gives the limit -0)
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -47,14 +47,21 @@ constexpr size_t kScratchBytes = size_t(16) << 20;
 hipError_t fixed_scratch(void** out);
 
 // Where a GEMM writes y: float (f), or bfloat16 bits rounded to nearest even from the float
-// result (h); exactly one of them is set.  Offsets count elements of either.
+// result (h); exactly one of them is set.  With `silu`, the n outputs of a row pair up as the
+// gate and up halves of row-interleaved gate+up weights (rows 16 t .. 16 t + 7 gate, 16 t + 8 ..
+// 16 t + 15 up) and the array holds h[j][i] = silu(y[j][gate row of i]) * y[j][up row of i],
+// [m][n / 2]; offsets are still given in elements of y (multiples of 16 within a row), so they
+// halve.  Offsets count elements of either.
 struct YOut {
   float* f = nullptr;
   uint16_t* h = nullptr;
+  bool silu = false;
   YOut operator+(int64_t off) const {
     YOut r;
-    r.f = f ? f + off : nullptr;
-    r.h = h ? h + off : nullptr;
+    const int64_t o = silu ? off / 2 : off;
+    r.f = f ? f + o : nullptr;
+    r.h = h ? h + o : nullptr;
+    r.silu = silu;
     return r;
   }
 };
@@ -65,7 +72,8 @@ inline YOut yout_f(float* f) {
 }
 
 // y[r * ldy + c] = sum over j = 0 .. splits-1 (in that order) of part[j * rows * cols + r * cols + c],
-// r < rows, c < cols (splits = 1: a copy, or with y.h the rounding to bfloat16)
+// r < rows, c < cols (splits = 1: a copy, or with y.h the rounding to bfloat16); with y.silu the
+// sums pair up into h[r * ldy / 2 + i], i < cols / 2 (see YOut)
 hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int64_t cols, YOut y,
                                int64_t ldy, hipStream_t s);
 
@@ -106,6 +114,11 @@ hipError_t launch_pack(const uint16_t* w, int64_t n, int64_t k, const uint8_t* b
 hipError_t launch_decode(const Planes& p, int64_t n, int64_t k, uint16_t* out, hipStream_t s);
 // dst[i] = src[i] + add, i < cnt (escape offsets of a part placed after earlier parts)
 hipError_t launch_rebase(const uint32_t* src, int64_t cnt, uint32_t add, uint32_t* dst, hipStream_t s);
+// record of the row-interleaved gate+up weights (rows 16 t .. +7 = gate rows 8 t .. +7, rows
+// 16 t + 8 .. +15 = up rows 8 t .. +7) from the two records; esc_total[2] = the parts' escape totals
+hipError_t launch_interleave(const Planes& gate, const Planes& up, int64_t rows, int64_t k, uint8_t* base,
+                             uint8_t* ae, uint8_t* lo, uint32_t* esc_ptr, uint32_t* esc_col, uint16_t* esc_val,
+                             hipStream_t s);
 // 8-bit Q-pass copy of a record: per-row scales, codes in the AE storage order, escaped slots 0
 hipError_t launch_i8_build(const Planes& p, int64_t n, int64_t k, int8_t* q, float* scale, hipStream_t s);
 // dense bf16 [n][k] -> tiled storage order (baseline layout)

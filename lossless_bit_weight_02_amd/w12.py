@@ -67,6 +67,11 @@ EXPORTS = {
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
     "w12_gemm_top1": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_gemm_silu_mul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12Weight),
+                                         ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]),
+    "w12_interleave_rows": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.POINTER(_W12Weight),
+                                           ctypes.POINTER(_W12Weight), ctypes.POINTER(ctypes.c_uint64),
+                                           ctypes.c_void_p]),
     "w12_i8_build": (ctypes.c_int, [ctypes.POINTER(_W12Weight), ctypes.POINTER(_W12I8), ctypes.c_void_p]),
     "w12_i8_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_W12I8),
                                    ctypes.POINTER(_W12Weight), ctypes.c_void_p, ctypes.c_uint32,
@@ -235,6 +240,27 @@ def concat_rows(parts) -> W12Weight:
     return out
 
 
+def interleave_rows(gate: W12Weight, up: W12Weight) -> W12Weight:
+    """Record of the gate and up projections with rows interleaved in groups of 8 (rows 16t..16t+7
+    gate rows 8t..8t+7, rows 16t+8..16t+15 up rows 8t..8t+7), built on the device without
+    re-encoding; the input of gemm_silu_mul."""
+    dev, k, n = gate.device, gate.k, 2 * gate.n
+    ne = gate.n_esc + up.n_esc
+    npad = padded_rows(n)
+    u8 = torch.uint8
+    out = W12Weight(n, k, torch.empty(n, dtype=u8, device=dev), torch.empty(npad * k, dtype=u8, device=dev),
+                    torch.empty(npad * k // 2, dtype=u8, device=dev),
+                    torch.empty(n + 1, dtype=torch.int32, device=dev),
+                    torch.empty(max(1, ne), dtype=torch.int32, device=dev)[:ne],
+                    torch.empty(max(1, ne), dtype=torch.int16, device=dev)[:ne])
+    g, u, o = gate.c_struct(), up.c_struct(), out.c_struct()
+    o.esc_cap = ne
+    n_esc = ctypes.c_uint64(0)
+    _check(lib().w12_interleave_rows(ctypes.byref(g), ctypes.byref(u), ctypes.byref(o), ctypes.byref(n_esc),
+                                     _stream_handle(dev)))
+    return out
+
+
 def decode_into(wt: W12Weight, out: torch.Tensor) -> torch.Tensor:
     """Decode into a preallocated contiguous bfloat16 [n, k] tensor."""
     if out.numel() != wt.n * wt.k or not out.is_contiguous() or out.element_size() != 2:
@@ -304,6 +330,19 @@ def gemm(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Ten
     s = wt.c_struct()
     _check(lib().w12_gemm(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
                           _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
+    return out
+
+
+def gemm_silu_mul(x: torch.Tensor, wt: W12Weight, path: str | None = None, out: torch.Tensor | None = None,
+                  out_bf16: bool = False):
+    """Exact pass on row-interleaved gate+up weights (interleave_rows) with SiLU(gate) * up
+    applied where the outputs are stored: h [m, n / 2] float32 (or bfloat16)."""
+    x, out = _gemm_io(x, wt.n // 2, wt.k, wt.device, out, out_bf16)
+    if x.shape[0] == 0:
+        return out
+    s = wt.c_struct()
+    _check(lib().w12_gemm_silu_mul(x.data_ptr(), x.shape[0], ctypes.byref(s), out.data_ptr(),
+                                   _PATHS[path] | _out_flag(out), _stream_handle(x.device)))
     return out
 
 
