@@ -186,10 +186,11 @@ def attn_bench(dev, stream, min_rot_bytes, reps):
 
 
 def lm_head_bench(dev, stream, reps):
-    """LM-head-like W [152064, 5120] at M=16: the Q pass on the 8-bit view and the exact pass, as
-    full outputs and as top-1 per row (no logits written), and the same-build BF16 kernel; each
-    timed as a captured HIP graph of back-to-back launches (the 1.17 GB record streams from HBM
-    on every launch).  Reports the Q pass's top-1 agreement with the exact pass on these inputs.
+    """LM-head-like W [152064, 5120] at M=16: the Q pass on the 8-bit view (truncated and midpoint)
+    and on the separate 8-bit copy, and the exact pass, as full outputs and as top-1 per row (no
+    logits written), and the same-build BF16 kernel; each timed as a captured HIP graph of
+    back-to-back launches (the 1.17 GB record streams from HBM on every launch).  Reports each Q
+    pass's top-1 agreement with the exact pass on these inputs and over 1024 rows of x.
     Weights drawn on the GPU (synth.gen_weight_torch)."""
     import torch
     from lossless_bit_weight_02_amd import synth, w12
@@ -201,6 +202,13 @@ def lm_head_bench(dev, stream, reps):
     tiles = w12.bf16_tiles(w)
     keep = w[:128].view(torch.int16).cpu().numpy().view(np.uint16)
     del w
+    # the separate 8-bit copy (one more byte per weight of memory), built on the device
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    cp = w12.i8_build(rec)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_build = ev0.elapsed_time(ev1) * 1e-3
     x_bits = synth.gen_x(m, k, tensor_id=tid)
     x = to_dev_bits(x_bits, dev)
     yq = torch.empty((m, n), dtype=torch.float32, device=dev)
@@ -210,6 +218,9 @@ def lm_head_bench(dev, stream, reps):
     tq = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     te = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
     tm = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
+    yi = torch.empty_like(yq)
+    ti = (torch.empty(m, dtype=torch.int32, device=dev), torch.empty(m, dtype=torch.float32, device=dev))
+    i8_byt = n * k + 4 * n + 4 * (n + 1) + 6 * rec.n_esc + 2 * m * k + 4 * m * n
     cases = (("q8_m16", lambda: w12.q8_gemm(x, rec, out=yq), [yq], q8_bytes(n, k, rec.n_esc, m)),
              ("q8_midpoint_m16", lambda: w12.q8_gemm(x, rec, out=ym, midpoint=True), [ym],
               q8_bytes(n, k, rec.n_esc, m)),
@@ -220,8 +231,11 @@ def lm_head_bench(dev, stream, reps):
               q8_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
              ("w12_top1_m16", lambda: w12.gemm_top1(x, rec, out=te), list(te),
               w12_bytes(n, k, rec.n_esc, m) - 4 * m * n + 8 * m),
+             ("i8_copy_m16", lambda: w12.i8_gemm(x, cp, out=yi), [yi], i8_byt),
+             ("i8_copy_top1_m16", lambda: w12.i8_top1(x, cp, out=ti), list(ti), i8_byt - 4 * m * n + 8 * m),
              ("bf16_m16", lambda: w12.bf16_gemm(x, tiles, out=yb), [yb], bf16_bytes(n, k, m)))
-    out = {"n": n, "k": k, "m": m, "escapes": rec.n_esc, "launches_per_graph": 8}
+    out = {"n": n, "k": k, "m": m, "escapes": rec.n_esc, "launches_per_graph": 8,
+           "i8_copy_bytes": cp.nbytes(), "i8_copy_build_us": round(t_build * 1e6, 1)}
     for name, fn, outs, byt in cases:
         g = capture_graph([fn] * 8, outs)
         t = time_graph(g, stream, reps) / 8
@@ -230,7 +244,9 @@ def lm_head_bench(dev, stream, reps):
         out[f"{name}_gbs"] = round(byt / t / 1e9, 1)
     out["q8_frac_hbm"] = round(out["q8_m16_gbs"] / HBM_PEAK_GBS, 4)
     out["w12_frac_hbm"] = round(out["w12_m16_gbs"] / HBM_PEAK_GBS, 4)
+    out["i8_copy_frac_hbm"] = round(out["i8_copy_m16_gbs"] / HBM_PEAK_GBS, 4)
     out["q8_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["q8_m16_us"], 4)
+    out["i8_copy_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["i8_copy_m16_us"], 4)
     out["w12_speedup_vs_bf16"] = round(out["bf16_m16_us"] / out["w12_m16_us"], 4)
     iq, ie = tq[0].cpu().numpy(), te[0].cpu().numpy()
     out["top1_agreement_q8_vs_exact"] = f"{int((iq == ie).sum())}/{m}"
@@ -239,13 +255,72 @@ def lm_head_bench(dev, stream, reps):
     scale = float(ye.abs().mean())
     out["q8_mean_abs_err_rel"] = round(float((yq - ye).abs().mean()) / scale, 6)
     out["q8_midpoint_mean_abs_err_rel"] = round(float((ym - ye).abs().mean()) / scale, 6)
+    out["i8_copy_mean_abs_err_rel"] = round(float((yi - ye).abs().mean()) / scale, 6)
+    # top-1 agreement with the exact pass over many rows of x (passes of 32 through the top-1
+    # entry points; the first 16 rows are the timed x)
+    rows = 1024
+    xa = to_dev_bits(synth.gen_x(rows, k, tensor_id=tid), dev)
+    agree = {"q8": 0, "q8_midpoint": 0, "i8_copy": 0}
+    for r0 in range(0, rows, 32):
+        xr = xa[r0:r0 + 32]
+        ie32 = w12.gemm_top1(xr, rec)[0]
+        for name, fn in (("q8", lambda: w12.q8_top1(xr, rec)), ("q8_midpoint", lambda: w12.q8_top1(xr, rec, midpoint=True)),
+                         ("i8_copy", lambda: w12.i8_top1(xr, cp))):
+            agree[name] += int((fn()[0] == ie32).sum())
+    for name, v in agree.items():
+        out[f"top1_agreement_{name}_vs_exact_{rows}_rows"] = f"{v}/{rows}"
     # the top-1 entry points against the argmax of the full outputs of the same kernels
     out["top1_matches_full_outputs"] = bool(
         np.array_equal(iq, yq.argmax(dim=1).cpu().numpy()) and np.array_equal(ie, ye.argmax(dim=1).cpu().numpy())
         and np.array_equal(tm[0].cpu().numpy(), im))
     samples = [("lm_head q8 m=16 (rows 0..127)", x_bits, keep, yq[:, :128].cpu().numpy(), "q8"),
                ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy()),
-               ("lm_head q8 midpoint m=16 (rows 0..127)", x_bits, keep, ym[:, :128].cpu().numpy(), "q8m")]
+               ("lm_head q8 midpoint m=16 (rows 0..127)", x_bits, keep, ym[:, :128].cpu().numpy(), "q8m"),
+               ("lm_head i8 copy m=16 (rows 0..127)", x_bits, keep, yi[:, :128].cpu().numpy(), "i8")]
+    return out, samples
+
+
+def silu_bench(w_bits, x_bits, dev, stream, rot):
+    """The gate+up shape as an MLP's two [17408, 5120] halves, row-interleaved
+    (w12_interleave_rows), at M = 1 and 32: the exact pass with the SiLU(gate) * up epilogue
+    (h [m, 17408]: half the output bytes) against the plain exact pass on the same record, over
+    `rot` copies so every launch reads HBM.  Returns (results, parity samples)."""
+    import torch
+    from lossless_bit_weight_02_amd import w12
+
+    half = w_bits.shape[0] // 2
+    n, k = w_bits.shape
+    to_dev = lambda bits: to_dev_bits(bits, dev)
+    gr, ur = w12.encode(to_dev(w_bits[:half])), w12.encode(to_dev(w_bits[half:]))
+    rec0 = w12.interleave_rows(gr, ur)
+    del gr, ur
+    recs = [rec0] + [rec0.clone() for _ in range(rot - 1)]
+    out = {"n": n, "k": k, "i": half}
+    samples = []
+    for m in (1, 32):
+        xm = to_dev(x_bits[:m])
+        ys = torch.empty((m, n), dtype=torch.float32, device=dev)
+        hs = torch.empty((m, half), dtype=torch.float32, device=dev)
+        for name, fn in (("w12", lambda r: w12.gemm(xm, recs[r], out=ys)),
+                         ("w12_silu_mul", lambda r: w12.gemm_silu_mul(xm, recs[r], out=hs))):
+            fn(0)
+            reps = 2 * rot
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            for r in range(reps):
+                fn(r % rot)
+            eb.record(stream)
+            torch.cuda.synchronize()
+            t = ea.elapsed_time(eb) * 1e-3 / reps
+            byt = w12_bytes(n, k, rec0.n_esc, m) - (2 * m * n if name == "w12_silu_mul" else 0)
+            out[f"{name}_m{m}_us"] = round(t * 1e6, 2)
+            out[f"{name}_m{m}_gbs"] = round(byt / t / 1e9, 1)
+        # the first 64 outputs read interleaved rows 0..127: gate rows 0..63 and up rows 0..63
+        wi = np.empty((128, k), dtype=np.uint16)
+        for t in range(8):
+            wi[16 * t:16 * t + 8] = w_bits[8 * t:8 * t + 8]
+            wi[16 * t + 8:16 * t + 16] = w_bits[half + 8 * t:half + 8 * t + 8]
+        samples.append((f"silu_mul m={m} (outputs 0..63)", x_bits[:m], wi, hs[:, :64].cpu().numpy(), "silu"))
     return out, samples
 
 
@@ -424,10 +499,23 @@ def cpu_baseline(w_bits, x_bits, gpu_out, rows, samples=()):
             raise SystemExit(f"parity failure in {name}: GPU output outside the bound")
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
     for label, xb, wb, gy, *view in samples:
-        if view and view[0] in ("q8", "q8m"):
-            wb = oracle.q8_view_bits(oracle.encode(wb), midpoint=view[0] == "q8m")
-        y = oracle.gemm64(xb, wb)
-        bound = 1e-3 * oracle.abs_bound64(xb, wb)
+        if view and view[0] == "silu":
+            y64, ab = oracle.gemm64(xb, wb), oracle.abs_bound64(xb, wb)
+            err = np.abs(gy.astype(np.float64) - oracle.silu_mul64(y64))
+            bound = oracle.silu_mul_bound(y64, ab)
+            if not np.all(err <= bound):
+                raise SystemExit(f"parity failure in {label}: GPU output outside the bound")
+            worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+            continue
+        if view and view[0] == "i8":
+            ref = oracle.encode(wb)
+            wq = oracle.i8_weights64(ref, oracle.i8_copy(ref))
+            y, bound = oracle.gemm64_f(xb, wq), 1e-3 * oracle.abs_bound64_f(xb, wq)
+        else:
+            if view and view[0] in ("q8", "q8m"):
+                wb = oracle.q8_view_bits(oracle.encode(wb), midpoint=view[0] == "q8m")
+            y = oracle.gemm64(xb, wb)
+            bound = 1e-3 * oracle.abs_bound64(xb, wb)
         err = np.abs(gy.astype(np.float64) - y)
         if not np.all(err <= bound):
             raise SystemExit(f"parity failure in {label}: GPU output outside the bound")
@@ -641,6 +729,12 @@ def main():
             row["w12_mfma_tflops"] = round(2 * m * n * k / (row["w12_mfma_us"] * 1e-6) / 1e12, 1)
             sweep[str(m)] = row
 
+    silu = None
+    if not a.no_sweep:
+        silu, smp = silu_bench(w_bits, x_bits, dev, stream, rot)
+        sweep_samples += smp
+        torch.cuda.empty_cache()
+
     # Context, not a metric: the vendor library's dense bf16 GEMM on the same weights (torch.mm,
     # which dispatches to hipBLASLt/rocBLAS), computed as y^T = W x^T with both operands
     # contiguous; the pages compare W12 against the vendor library of their GPU.
@@ -727,6 +821,7 @@ def main():
         "vendor_bf16_torch_mm": vendor,
         "attn_m1": attn,
         "lm_head_q_pass": lm_head,
+        "silu_mul_gate_up": silu,
         "stack": stack,
         "setup_s": {"generate": round(t_gen, 2)},
         "kernel_source_sha256_16": kernel_source_hash(),

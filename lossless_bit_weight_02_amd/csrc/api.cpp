@@ -87,7 +87,7 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   }
   const bool out16 = (flags & W12_OUT_BF16) != 0;
   flags &= ~W12_OUT_BF16;
-  if (flags > W12_PATH_MFMA) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
+  if (flags > W12_PATH_STREAM) return fail(W12_ERR_ARG, "unknown flags 0x%x", flags);
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
   if (out16 ? (reinterpret_cast<uintptr_t>(y) & 1u) != 0 : !aligned4(y))
     return fail(W12_ERR_ALIGN, out16 ? "y must be 2-byte aligned" : "y must be 4-byte aligned");
@@ -101,8 +101,23 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   // (down [5120, 17408], 4 rows: 43.0 vs 32.1); on gate+up [34816, 5120] the two are within 1 us
   // at 3-4 rows and the matrix cores win from 5 (58.6 vs 46.3).
   const int64_t tiles = (n + 15) / 16;
+  w12::DevInfo dinfo;
+  {
+    hipError_t e = w12::dev_info(&dinfo);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+  }
+  const bool stream_ok = !silu && w12::stream_fits(dinfo, m, n, k);
+  if (flags == W12_PATH_STREAM && !stream_ok)
+    return fail(silu ? W12_ERR_ARG : W12_ERR_SHAPE, "the CU-streaming kernel does not take this call "
+                "(at most 48 16-row tiles per compute unit, x rows within the LDS, no SiLU epilogue)");
+  // The CU-streaming kernel from 3 rows on shapes with at least 2 tiles per compute unit (measured
+  // on 27B-class shapes, us, stream vs the best other family: [34816, 5120] at 4 rows 45.7 vs
+  // 47.6, at 8 rows 46.9 vs 47.8; [8192, 5120] at 8 rows 16.4 vs 21.9); at 1-2 rows the GEMV
+  // stays faster (43.1 vs 43.9 at 1 row on [34816, 5120]).
+  const bool stream_auto = stream_ok && m >= 3 && m <= 8 && tiles >= 2 * (int64_t)dinfo.cus;
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
-  const bool gemv = flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto);
+  const bool use_stream = flags == W12_PATH_STREAM || (flags == W12_PATH_AUTO && stream_auto);
+  const bool gemv = !use_stream && (flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   w12::Scratch sc;
   sc.s = s;
@@ -125,8 +140,10 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
     sc.fixed = ptr;
     sc.bytes = w12::kScratchBytes;
   }
-  hipError_t e = gemv ? w12::launch_gemv(f, x, m, p, n, k, yo, s, sc) : w12::launch_mfma(f, x, m, p, n, k, yo, s, sc);
-  if (e != hipSuccess) return hip_fail(e, gemv ? "gemv launch" : "mfma launch");
+  hipError_t e = use_stream ? w12::launch_stream(f, x, m, p, n, k, yo, s)
+                 : gemv     ? w12::launch_gemv(f, x, m, p, n, k, yo, s, sc)
+                            : w12::launch_mfma(f, x, m, p, n, k, yo, s, sc);
+  if (e != hipSuccess) return hip_fail(e, use_stream ? "stream launch" : gemv ? "gemv launch" : "mfma launch");
   return ok();
 }
 

@@ -89,8 +89,10 @@ __device__ __forceinline__ void vm_wait_le() {
 }
 
 // W waves (W / 4 per SIMD) on the CU: at most 168 VGPRs with 12, 256 with 8.
-// TOP1: the top-1 mode of MfmaArgs (no y; per-workgroup best keys).
-template <int FMT, int NT, int W, bool TOP1>
+// TOP1: the top-1 mode of MfmaArgs (no y; per-workgroup best keys).  SILU: the weights are
+// row-interleaved gate+up (rows 0..7 of a tile gate, 8..15 up) and y / y16 hold
+// h = silu(gate) * up, [m][ldy / 2], 8 outputs per tile (one k range only).
+template <int FMT, int NT, int W, bool TOP1, bool SILU = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W / 4, W / 4)))
 void k_mfma(MfmaArgs a) {
   using SH = Shape<FMT, NT, W>;
@@ -447,7 +449,7 @@ void k_mfma(MfmaArgs a) {
         for (int cc = 0; cc < NT; ++cc) acc[cc][r] = fmaf(sc, acc[cc][r], q[cc]);
       }
     }
-    if (!TOP1 && a.silu) {
+    if constexpr (SILU) {
       // SiLU(gate) * up: lanes g = 0, 1 hold gate rows 4 g .. 4 g + 3 of x row 16 cc + r16, lanes
       // g + 2 (lane ^ 32) the matching up rows; h gets 4 consecutive outputs per lane
       const int64_t ldh = a.ldy >> 1;
@@ -595,7 +597,16 @@ static MfmaKernel pick_top1(Fmt f, int nt) {
   return nt == 1 ? k_mfma<kFmtQ8, 1, kWaves, true> : k_mfma<kFmtQ8, 2, kWaves, true>;
 }
 
-static MfmaKernel pick_kernel(Fmt f, int nt, int waves) {
+// the exact pass with the SiLU(gate) * up epilogue (instantiated apart, so the other kernels keep
+// their registers)
+static MfmaKernel pick_silu(int nt) {
+  if (nt == 8) return k_mfma<kFmtW12, 8, kWaves, false, true>;
+  if (nt >= 3) return mfma_wide_kernel(kFmtW12, nt, true);
+  return nt == 1 ? k_mfma<kFmtW12, 1, kWaves, false, true> : k_mfma<kFmtW12, 2, kWaves, false, true>;
+}
+
+static MfmaKernel pick_kernel(Fmt f, int nt, int waves, bool silu) {
+  if (silu) return pick_silu(nt);
   if (waves == 8) return pick<kFmtBF16, 8>(nt);   // only the dense baseline runs 8 waves
   if (f == kFmtW12) return pick<kFmtW12, 12>(nt);
   if (f == kFmtQ8) return pick<kFmtQ8, 12>(nt);
@@ -658,7 +669,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.scale = p.scale;
   a.y = ws ? ws : y.f;
   a.y16 = ws ? nullptr : y.h;
-  a.silu = ws ? 0 : (int)y.silu;               // a split pairs the outputs in its sum instead
+  const bool silu = !ws && y.silu;             // a split pairs the outputs in its sum instead
   a.ldy = ws ? n : ldy;                        // partial slices are [mb][n], contiguous
   a.n = n; a.k = k;
   a.rounds = (int)((tiles + groups * waves - 1) / (groups * waves));
@@ -668,7 +679,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
   a.top1 = nullptr;
   // vector stores: 16 bytes of float (y 16-byte aligned) or 8 of bfloat16 (y16 8-byte aligned)
   {
-    const int64_t ld_out = a.silu ? a.ldy / 2 : a.ldy;   // row stride of what is stored
+    const int64_t ld_out = silu ? a.ldy / 2 : a.ldy;     // row stride of what is stored
     a.yvec = a.y16 ? (reinterpret_cast<uintptr_t>(a.y16) & 7u) == 0 && ld_out % 4 == 0
                    : a.y && (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && ld_out % 4 == 0;
   }
@@ -683,7 +694,7 @@ static hipError_t mfma_pass(Fmt f, const DevInfo& di, const uint16_t* x, int mb,
     if (e != hipSuccess) return e;
     a.xt = xt;
   }
-  hipLaunchKernelGGL(pick_kernel(f, nt, waves), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
+  hipLaunchKernelGGL(pick_kernel(f, nt, waves, silu), dim3((unsigned)(groups * ranges)), dim3(64 * waves), 0,
                      s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -779,7 +790,6 @@ hipError_t launch_mfma_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p
     a.scale = p.scale;
     a.y = nullptr;
     a.y16 = nullptr;
-    a.silu = 0;
     a.ldy = nh;
     a.n = nh; a.k = k;
     a.rounds = (int)((th + groups * kWaves - 1) / (groups * kWaves));

@@ -41,9 +41,6 @@ struct MfmaArgs {
   int yvec;
   // with y16 set (a single k range), the outputs go there as bfloat16 (nearest even) instead of y
   uint16_t* y16;
-  // (a single k range) the weights are row-interleaved gate+up (rows 0..7 of a tile gate, 8..15
-  // up): y / y16 hold h = silu(gate) * up, [m][ldy / 2], 8 outputs per tile
-  int silu;
   // eight activation tiles (W12 and Q8): x transposed, [k][128] bfloat16 (rows past m zero); the
   // epilogue reads the escapes' x values from it
   const uint16_t* xt;
@@ -134,7 +131,9 @@ struct RowScales {
 
 typedef void (*MfmaKernel)(MfmaArgs);
 
-// The register-staged kernel for nt = 3 or 4 activation tiles (mfma_wide.hip).
-MfmaKernel mfma_wide_kernel(Fmt f, int nt);
+// The register-staged kernel for nt = 3 or 4 activation tiles (mfma_wide.hip); silu: the exact
+// pass with the SiLU(gate) * up epilogue on row-interleaved gate+up weights (y / y16 then hold
+// h [m][ldy / 2], 8 outputs per 16-row tile).
+MfmaKernel mfma_wide_kernel(Fmt f, int nt, bool silu = false);
 
 }  // namespace w12

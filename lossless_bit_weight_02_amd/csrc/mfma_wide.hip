@@ -58,7 +58,7 @@ struct ShapeWide {
 };
 
 // Twelve waves (three per SIMD) on the CU: at most 168 VGPRs.
-template <int FMT, int NT>
+template <int FMT, int NT, bool SILU = false>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_mfma_wide(MfmaArgs a) {
   using SH = ShapeWide<FMT, NT>;
@@ -303,7 +303,7 @@ void k_mfma_wide(MfmaArgs a) {
         }
       }
     }
-    if (a.silu) {
+    if constexpr (SILU) {
       // SiLU(gate) * up: lanes g = 0, 1 hold gate rows 4 g .. 4 g + 3, lane ^ 32 the up rows
       const int64_t ldh = a.ldy >> 1;
 #pragma unroll
@@ -343,7 +343,8 @@ void k_mfma_wide(MfmaArgs a) {
 // ---------------------------------------------------------------------------------------------
 // instantiations for three and four activation tiles
 // ---------------------------------------------------------------------------------------------
-MfmaKernel mfma_wide_kernel(Fmt f, int nt) {
+MfmaKernel mfma_wide_kernel(Fmt f, int nt, bool silu) {
+  if (silu) return nt == 3 ? k_mfma_wide<kFmtW12, 3, true> : k_mfma_wide<kFmtW12, 4, true>;
   if (f == kFmtW12) return nt == 3 ? k_mfma_wide<kFmtW12, 3> : k_mfma_wide<kFmtW12, 4>;
   if (f == kFmtQ8) return nt == 3 ? k_mfma_wide<kFmtQ8, 3> : k_mfma_wide<kFmtQ8, 4>;
   if (f == kFmtQ8M) return nt == 3 ? k_mfma_wide<kFmtQ8M, 3> : k_mfma_wide<kFmtQ8M, 4>;

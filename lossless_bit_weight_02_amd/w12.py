@@ -23,10 +23,10 @@ W12_ERR_CAPACITY = -4
 W12_ERR_RANGE = -5
 W12_ERR_HIP = -6
 
-PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_STREAM = 0, 1, 2, 3
 Q8_MIDPOINT = 0x10
 OUT_BF16 = 0x20
-_PATHS = {None: PATH_AUTO, "auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA}
+_PATHS = {None: PATH_AUTO, "auto": PATH_AUTO, "gemv": PATH_GEMV, "mfma": PATH_MFMA, "stream": PATH_STREAM}
 
 
 class W12Error(RuntimeError):

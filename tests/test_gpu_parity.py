@@ -670,3 +670,75 @@ def test_binding_rejects_bad_arguments():
         with pytest.raises(ValueError):
             fn(xd[:, :128], rec)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,k,ms", [
+    (300, 1152, (1, 2, 3, 8)),            # 19 tiles: one tile per workgroup, waves with empty ranges
+    (4000, 1024, (1, 2, 4, 5, 8, 13)),    # 250 tiles; 13 rows: passes of 8 and 5
+    (20487, 512, (1, 3, 7)),              # 1281 tiles: 5-6 per workgroup, ragged last tile
+    (196600, 128, (1, 6)),                # 12288 tiles, one block each: 48 per workgroup
+    (3000, 5120, (1, 2, 8)),              # long ranges: a wave crosses several tiles
+    (8192, 5120, (9, 13, 16, 21)),        # x in two k phases; 21 rows: passes of 16 and 5
+    (4000, 10240, (16,)),                 # four k phases
+])
+def test_stream_path(n, k, ms):
+    """The CU-streaming kernel (W12_PATH_STREAM) on every format, 1..16 rows per pass (x staged in
+    k phases when it does not fit the LDS whole), against the oracle; bfloat16 outputs the rounding
+    of the float outputs."""
+    import torch
+    w12 = _w12()
+    rng = np.random.default_rng(n + k)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[rng.random((n, k)) < 3e-4] = 0x4400
+    x = synth.f32_to_bf16_bits(rng.standard_normal((max(ms), k)).astype(np.float32))
+    rec = w12.encode(to_dev(w))
+    ref = oracle.encode(w)
+    cp = w12.i8_build(rec)
+    wq8, wq8m = oracle.q8_view_bits(ref), oracle.q8_view_bits(ref, midpoint=True)
+    wi8 = oracle.i8_weights64(ref, oracle.i8_copy(ref))
+    dw = w12.bf16_tiles(to_dev(w))
+    for m in ms:
+        xd = to_dev(x[:m])
+        for name, fn, wv in (("w12", lambda **kw: w12.gemm(xd, rec, path="stream", **kw), w),
+                             ("q8", lambda **kw: w12.q8_gemm(xd, rec, path="stream", **kw), wq8),
+                             ("q8m", lambda **kw: w12.q8_gemm(xd, rec, path="stream", midpoint=True, **kw), wq8m),
+                             ("bf16", lambda **kw: w12.bf16_gemm(xd, dw, path="stream", **kw), w),
+                             ("i8", lambda **kw: w12.i8_gemm(xd, cp, path="stream", **kw), None)):
+            what = f"stream {name} {n}x{k} m={m}"
+            say(what)
+            y = fn().cpu().numpy()
+            if wv is None:
+                from tests.gpu_util import check_y
+                check_y(y, oracle.gemm64_f(x[:m], wi8), oracle.abs_bound64_f(x[:m], wi8), what)
+            else:
+                check_gemm(y, x[:m], wv, what)
+            if m in (1, 3):
+                y16 = fn(out_bf16=True)
+                _check_bf16_out(y16, y, x[:m], None, what + " bf16")
+
+
+def test_stream_one_hot_and_special_values():
+    """One-hot x returns every weight exactly through the streaming kernel (escapes included), and
+    Inf / NaN weights give Inf / NaN outputs."""
+    w12 = _w12()
+    rng = np.random.default_rng(8)
+    n, k = 2048, 384
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.02] = 0
+    w[5, 100] = 0x4700                     # far outside the window: an escape
+    rec = w12.encode(to_dev(w))
+    for kk in (0, 100, 127, 128, 255, 383):
+        x = np.zeros((3, k), dtype=np.uint16)
+        x[:, kk] = 0x3F80
+        y = w12.gemm(to_dev(x), rec, path="stream").cpu().numpy().astype(np.float64)
+        assert np.array_equal(y[0], oracle.bf16_to_f64(w[:, kk])), kk
+        assert np.array_equal(y[2], y[0])
+    w2 = w.copy()
+    w2[7, 9] = 0x7F80
+    w2[8, 9] = 0x7FC0
+    rec2 = w12.encode(to_dev(w2))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, k)).astype(np.float32))
+    y = w12.gemm(to_dev(x), rec2, path="stream").cpu().numpy()
+    assert np.all(np.isinf(y[:, 7])) and np.all(np.isnan(y[:, 8]))
+    check_gemm(np.delete(y, [7, 8], axis=1), x, np.delete(w2, [7, 8], axis=0), "stream special")
