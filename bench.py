@@ -19,8 +19,8 @@ Each op's back-to-back launches are bracketed by one pair of HIP events on the s
 on; the per-launch time is the elapsed time / launches (the M=1 groups launch every copy twice,
 so the gap around an event pair weighs less).
 
-Beside the step (context, outside `value` and `ms_per_step`): an M sweep on gate+up (GEMV and MFMA
-families, W12 and BF16, W12 with bfloat16 outputs at M = 1, 32, 128) and the vendor library's
+Beside the step (context, outside `value` and `ms_per_step`): an M sweep on gate+up (GEMV, MFMA and
+streaming families, W12 and BF16, W12 with bfloat16 outputs at M = 1, 32, 128) and the vendor library's
 bf16 GEMM; the attention projection [5120, 5120]
 at M=1; the LM-head-like [152064, 5120] Q pass at M=16 (truncated and midpoint views, exact pass,
 top-1 entry points, BF16, top-1 agreement); and the 64-layer 27B-class stack at M=1 and M=32,
@@ -50,7 +50,8 @@ MFMA_BF16_PEAK_TFS = 2500.0      # dense bf16
 K_HIDDEN = 5120
 N_GATE_UP = 34816
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w12_gemv_m1_gate_up_traffic.md")
-KERNEL_SOURCES = ["lossless_bit_weight_02_amd/csrc/gemv.hip", "lossless_bit_weight_02_amd/csrc/w12_device.hpp"]
+KERNEL_SOURCES = ["lossless_bit_weight_02_amd/csrc/gemv.hip", "lossless_bit_weight_02_amd/csrc/block.hpp",
+                  "lossless_bit_weight_02_amd/csrc/w12_device.hpp"]
 
 
 def w12_bytes(n, k, n_esc, m):
@@ -685,8 +686,10 @@ def main():
             xm = xs[:m].contiguous()
             ym = torch.empty((m, n), dtype=torch.float32, device=dev)
             row = {}
-            # above 64 rows only the matrix-core path (passes of up to 128 rows, each reading W once)
-            for path in (("gemv", "mfma") if m <= 64 else ("mfma",)):
+            # the streaming kernel up to 32 rows; above 64 rows only the matrix-core path (passes of
+            # up to 128 rows, each reading W once)
+            paths = ("gemv", "mfma", "stream") if m <= 32 else ("gemv", "mfma") if m <= 64 else ("mfma",)
+            for path in paths:
                 for fmt in ("w12", "bf16"):
                     def run(r, fmt=fmt, path=path):
                         if fmt == "w12":
@@ -705,10 +708,10 @@ def main():
                     byt = w12_bytes(n, k, n_esc, m) if fmt == "w12" else bf16_bytes(n, k, m)
                     row[f"{fmt}_{path}_us"] = round(t * 1e6, 2)
                     row[f"{fmt}_{path}_gbs"] = round(byt / t / 1e9, 1)
-                    if m > 64:
-                        # the timed outputs of the passes of more than 64 rows: their first 128
-                        # weight rows go to the CPU-oracle leg for parity
-                        sweep_samples.append((f"sweep {fmt} m={m} (rows 0..127)", x_bits[:m],
+                    if m > 64 or (path == "stream" and m in (16, 32)):
+                        # the timed outputs of the passes of more than 64 rows and of the
+                        # streaming kernel: their first 128 weight rows go to the CPU-oracle leg
+                        sweep_samples.append((f"sweep {fmt} {path} m={m} (rows 0..127)", x_bits[:m],
                                               w_bits[:128], ym[:, :128].cpu().numpy()))
             if m in (1, 32, 128):
                 # the same W12 GEMM with bfloat16 outputs (rounded where they are stored)
@@ -725,7 +728,7 @@ def main():
                 t = ea.elapsed_time(eb) * 1e-3 / reps
                 row["w12_bf16out_us"] = round(t * 1e6, 2)
                 row["w12_bf16out_gbs"] = round((w12_bytes(n, k, n_esc, m) - 2 * m * n) / t / 1e9, 1)
-            row["best_w12_path"] = "gemv" if row.get("w12_gemv_us", 1e30) <= row["w12_mfma_us"] else "mfma"
+            row["best_w12_path"] = min((p for p in paths), key=lambda p: row[f"w12_{p}_us"])
             row["w12_mfma_tflops"] = round(2 * m * n * k / (row["w12_mfma_us"] * 1e-6) / 1e12, 1)
             sweep[str(m)] = row
 

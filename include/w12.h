@@ -81,9 +81,10 @@ extern "C" {
                            * most 1024 16-row tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
-#define W12_PATH_STREAM 3u /* force the CU-streaming kernel (passes of <= 8 rows of x; shapes with
-                            * at most 48 16-row tiles per compute unit and x rows that fit the
-                            * LDS; W12_ERR_SHAPE otherwise) */
+#define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
+                            * tiles, every wave of it an equal share of their 128-column blocks;
+                            * passes of <= 32 rows of x; shapes with at most 16 tiles per compute
+                            * unit, 12 above 16 rows of x; W12_ERR_SHAPE otherwise) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16
  * values the 8-bit view stands for) instead of 0; escapes stay exact */
 #define W12_Q8_MIDPOINT 0x10u

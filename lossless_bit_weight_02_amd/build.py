@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw12.so")
 ARCH = "gfx950"
 
-SOURCES = ["codec.hip", "gemv.hip", "mfma.hip", "mfma_wide.hip", "splitk.hip", "i8copy.hip", "interleave.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["codec.hip", "gemv.hip", "stream.hip", "mfma.hip", "mfma_wide.hip", "splitk.hip", "i8copy.hip", "interleave.hip", "noalloc.hip", "api.cpp"]
 
 # Packed-FP32 instructions are disabled in device code (see the design notes); the host pass
 # reports the feature as unknown, which is harmless.

@@ -33,8 +33,7 @@
 // (see w12_device.hpp), so the row's dot product sum_k x w' is scaled once by 2^(base - 112)
 // at the end.  An escaped slot decodes to w' = 2^-15; its contribution x * 2^-15 is removed and
 // x * (exact value) is added in a separate sum, so y = 2^(base-112) P + Q.
-#include "w12_device.hpp"
-#include "w12_launch.hpp"
+#include "block.hpp"
 
 namespace w12 {
 
@@ -62,18 +61,6 @@ struct GemvArgs {
   int silu;               // (one slice, one range) y / y16 hold h = silu(gate) * up, [m][ldy / 2]
 };
 
-// One 128-column block of the lane's row: the raw 128-bit words it loads.
-template <int FMT>
-struct BlockRegs {
-  u32x4 v[FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2];
-};
-
-// Buffers over one tile's blocks of the planes (or the dense baseline); an absent tile reads zeros.
-template <int FMT>
-struct TileRsrc {
-  Rsrc r0, r1;
-};
-
 template <int FMT>
 __device__ __forceinline__ TileRsrc<FMT> tile_rsrc(const GemvArgs& a, int64_t tile, bool valid,
                                                    uint32_t ktiles) {
@@ -87,55 +74,6 @@ __device__ __forceinline__ TileRsrc<FMT> tile_rsrc(const GemvArgs& a, int64_t ti
     t.r1 = make_rsrc(a.lo + t0 * ktiles * kTileLO, valid ? ktiles * (uint32_t)kTileLO : 0u);
   }
   return t;
-}
-
-// Block `kb` of the tile (kb = ~0: nothing) into the lane's registers.
-template <int FMT>
-__device__ __forceinline__ void load_block(const TileRsrc<FMT>& t, uint32_t kb, uint32_t lane16,
-                                           BlockRegs<FMT>& r) {
-  if constexpr (FMT == kFmtBF16) {
-    const uint32_t off = kb == ~0u ? kOOB : kb * kTileBF + lane16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r.v[q] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off + 1024 * q, 0, kAuxNT);
-  } else {
-    const uint32_t off = kb == ~0u ? kOOB : kb * kTileAE + lane16;
-    r.v[0] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off, 0, kAuxNT);
-    r.v[1] = __builtin_amdgcn_raw_buffer_load_b128(t.r0, off + 1024, 0, kAuxNT);
-    if constexpr (FMT == kFmtW12)
-      r.v[2] = __builtin_amdgcn_raw_buffer_load_b128(t.r1, kb == ~0u ? kOOB : kb * kTileLO + lane16, 0, kAuxNT);
-  }
-}
-
-// The 16 dwords of bfloat16 pairs (w' for W12/Q8, w for the baseline) of columns 32g..32g+31.
-template <int FMT>
-__device__ __forceinline__ void block_pairs(const BlockRegs<FMT>& r, uint32_t e112, uint32_t p[16]) {
-  if constexpr (FMT == kFmtBF16) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      p[4 * q] = r.v[q].x; p[4 * q + 1] = r.v[q].y; p[4 * q + 2] = r.v[q].z; p[4 * q + 3] = r.v[q].w;
-    }
-  } else if constexpr (FMT == kFmtW12) {
-    window_group8(r.v[0].x, r.v[0].y, r.v[2].x, e112, p);
-    window_group8(r.v[0].z, r.v[0].w, r.v[2].y, e112, p + 4);
-    window_group8(r.v[1].x, r.v[1].y, r.v[2].z, e112, p + 8);
-    window_group8(r.v[1].z, r.v[1].w, r.v[2].w, e112, p + 12);
-  } else if constexpr (FMT == kFmtI8) {
-    i8_group16(r.v[0], p);
-    i8_group16(r.v[1], p + 8);
-  } else {
-    window_group8_q(r.v[0].x, r.v[0].y, e112, p);
-    window_group8_q(r.v[0].z, r.v[0].w, e112, p + 4);
-    window_group8_q(r.v[1].x, r.v[1].y, e112, p + 8);
-    window_group8_q(r.v[1].z, r.v[1].w, e112, p + 12);
-    if constexpr (FMT == kFmtQ8M) midpoint16(p);
-  }
-}
-
-// Sum over the 4 lanes r, r+16, r+32, r+48 (the column groups of one row).
-__device__ __forceinline__ float group_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
 }
 
 constexpr int kEscPre = 4;   // escapes per lane fetched ahead (16 per row)
@@ -383,333 +321,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// CU-streaming kernel for 1..16 rows of x on shapes with several tiles per CU
-// ---------------------------------------------------------------------------------------------
-// One workgroup of kSW waves per CU.  Workgroup c owns tiles c, c + G, c + 2G, ... (G workgroups):
-// T tiles of nkb 128-column blocks.  The blocks are taken in `nph` k phases of kbp = nkb / nph
-// blocks; in each phase the workgroup's T kbp (tile, block) units are split into kSW contiguous
-// ranges of equal length (to one unit), the same ranges of tiles in every phase, so every wave of
-// the chip streams the same number of bytes and none waits on another inside a phase.  The x
-// columns of the phase stay in LDS for the phase (rows one bank apart); a phase change is two
-// barriers and a reload of x, while the weight ring of every wave keeps streaming the next
-// phase's first blocks.  A wave's range crosses at most kSMaxSlots tiles; at every tile boundary
-// it adds the partial sums of the tile's 16 rows into LDS (one slot per wave and tile, written
-// only by that wave).  At the end of each phase, wave w patches the escapes of the phase's columns
-// for the tiles it finalises (w, w + kSW, ...: entries prefetched at the start), and after one
-// last barrier it adds the tile's partial sums in wave order (deterministic), applies the escapes
-// and the scale and stores y.  1-2 rows: dot2 (lane r16 + 16 g computes row r16 over columns
-// 32 g .. +31); 3-16 rows: the B operand of v_mfma_f32_16x16x32_bf16 (x rows past m are zero).
-// In the final pass lane r16 + 16 g owns the outputs of x rows g, g + 4, ...
-constexpr int kSW = 16;         // waves per workgroup
-constexpr int kSMaxSlots = 4;   // tiles one wave's range may touch (the launcher checks)
-
-struct StreamArgs {
-  const uint16_t* x;      // x[m][k]
-  const uint8_t* base;
-  const uint8_t* ae;
-  const uint8_t* lo;
-  const uint32_t* esc_ptr;
-  const uint32_t* esc_col;
-  const uint16_t* esc_val;
-  const uint16_t* w;
-  const float* scale;
-  float* y;               // y[m][ldy] (or y16)
-  uint16_t* y16;
-  int64_t ldy;
-  int64_t n, k;
-  int nph;                // k phases (nkb % nph == 0)
-};
-
-template <int FMT>
-__device__ __forceinline__ TileRsrc<FMT> stream_rsrc(const StreamArgs& a, int64_t tile, bool valid,
-                                                     uint32_t ktiles) {
-  TileRsrc<FMT> t;
-  const int64_t t0 = valid ? tile : 0;
-  if constexpr (FMT == kFmtBF16) {
-    t.r0 = make_rsrc(a.w + t0 * ktiles * (kTileBF / 2), valid ? ktiles * (uint32_t)kTileBF : 0u);
-    t.r1 = t.r0;
-  } else {
-    t.r0 = make_rsrc(a.ae + t0 * ktiles * kTileAE, valid ? ktiles * (uint32_t)kTileAE : 0u);
-    t.r1 = make_rsrc(a.lo + t0 * ktiles * kTileLO, valid ? ktiles * (uint32_t)kTileLO : 0u);
-  }
-  return t;
-}
-
-// SFIN: tiles one wave finalises at most (T <= kSW SFIN)
-template <int FMT, int M, int D, int SFIN>
-__global__ __launch_bounds__(64 * kSW) void k_stream(StreamArgs a) {
-  constexpr bool kMF = M > 2;                       // matrix cores for 3..16 rows
-  constexpr bool kEsc = FMT != kFmtBF16;
-  constexpr int MQ = (M + 3) / 4;                   // x rows a lane finalises: g, g + 4, ...
-  extern __shared__ u32x4 xs[];                    // x row m of the phase at word m * kxrow
-  __shared__ float s_part[kSW][kSMaxSlots][kTileRows][M];
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-  const uint32_t lane16 = 16u * lane;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t G = gridDim.x, c = blockIdx.x;
-  const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
-  const uint32_t nkb = (uint32_t)(a.k / kTileCols);
-  const int nph = a.nph;
-  const uint32_t kbp = nkb / (uint32_t)nph;        // blocks per phase
-  const int T = (int)((tiles - c + G - 1) / G);   // tiles c + j G, j < T (the grid keeps c < tiles)
-  const uint32_t U = (uint32_t)T * kbp;            // units per phase
-  const auto range_start = [&](int wv) { return (uint32_t)(((uint64_t)wv * U) / kSW); };
-  const uint32_t u0 = range_start(w), u1 = range_start(w + 1), L = u1 - u0;
-  const uint32_t s0 = u0 / kbp, k0l = u0 - s0 * kbp;   // first slot and its first block (in the phase)
-  const int kxrow = (int)(kbp * 16) + 1;           // 16-byte words per x row of a phase in LDS
-  const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(xs);
-  const uint32_t e112 = exp112_pair();
-
-  // ---- the tiles this wave finalises: bounds and scale of the lane's row, prefetched first ----
-  uint32_t fe0[SFIN], fe1[SFIN], fte0[SFIN], fsc[SFIN];
-#pragma unroll
-  for (int q = 0; q < SFIN; ++q) {
-    const int j = w + kSW * q;
-    const bool use = kEsc && j < T;
-    const int64_t t = c + (int64_t)j * G;
-    const int64_t r = use ? t * kTileRows + r16 : 0;
-    const int64_t rr = r < a.n ? r : a.n;
-    fe0[q] = use ? a.esc_ptr[rr] : 0u;
-    fe1[q] = use ? a.esc_ptr[r + 1 < a.n ? r + 1 : a.n] : 0u;
-    fte0[q] = use ? a.esc_ptr[t * kTileRows] : 0u;
-    if constexpr (FMT == kFmtI8) fsc[q] = use ? __float_as_uint(a.scale[rr < a.n ? rr : a.n - 1]) : 0u;
-    else if constexpr (kEsc) fsc[q] = use ? a.base[rr < a.n ? rr : a.n - 1] : 0u;
-    else fsc[q] = 0u;
-  }
-
-  // ---- x of phase 0 into LDS: loads first, then the ring, then the LDS writes ----
-  const int xw = (int)(kbp * 16);                  // 16-byte words of one x row per phase
-  const Rsrc r_x = make_rsrc(a.x, (uint32_t)(M * a.k * 2));
-  const auto x_word = [&](int ph, int i) {          // global offset of word i of the phase's x
-    const int m = i / xw, j = i - m * xw;
-    return i < M * xw ? (uint32_t)(2 * (m * a.k + (int64_t)ph * kbp * kTileCols + 8 * j)) : kOOB;
-  };
-  constexpr int kXF = 4;
-  u32x4 xv[kXF];
-#pragma unroll
-  for (int q = 0; q < kXF; ++q)
-    xv[q] = __builtin_amdgcn_raw_buffer_load_b128(r_x, x_word(0, tid + q * 64 * kSW), 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // the refill cursor: phase rp, slot rs, block rk (in the phase), position ri in the range
-  uint32_t rp = 0, rs = s0, rk = k0l, ri = 0;
-  const auto next_unit = [&](uint32_t& p_, uint32_t& s_, uint32_t& k_, uint32_t& i_) {
-    k_ += 1;
-    i_ += 1;
-    const bool wrap = k_ == kbp;
-    k_ = wrap ? 0u : k_;
-    s_ = wrap ? s_ + 1 : s_;
-    const bool pend = i_ == L;                       // the range ends: the next phase's range
-    p_ = pend ? p_ + 1 : p_;
-    s_ = pend ? s0 : s_;
-    k_ = pend ? k0l : k_;
-    i_ = pend ? 0u : i_;
-  };
-  const auto load_unit = [&](BlockRegs<FMT>& r) {
-    const bool have = rp < (uint32_t)nph && L > 0;
-    load_block<FMT>(stream_rsrc<FMT>(a, c + (int64_t)rs * G, have, nkb), have ? rp * kbp + rk : ~0u,
-                    lane16, r);
-    next_unit(rp, rs, rk, ri);
-  };
-  BlockRegs<FMT> buf[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_unit(buf[d]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int q = 0; q < kXF; ++q) {
-    const int i = tid + q * 64 * kSW, m = i / xw, j = i - m * xw;
-    if (i < M * xw) xs[m * kxrow + j] = xv[q];
-  }
-  for (int i = tid + kXF * 64 * kSW; i < M * xw; i += 64 * kSW) {
-    const int m = i / xw, j = i - m * xw;
-    xs[m * kxrow + j] = __builtin_amdgcn_raw_buffer_load_b128(r_x, x_word(0, i), 0, 0);
-  }
-  lds_barrier();
-
-  // ---- escape entries of the tiles to finalise (their bounds arrived before the first block) ----
-  uint32_t ecol[SFIN][kEscPre], evalv[SFIN][kEscPre];
-#pragma unroll
-  for (int q = 0; q < SFIN; ++q) {
-    const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0[q]);
-    const Rsrc rc = make_rsrc(a.esc_col + te0, 0x7FFFFFF0u), rv = make_rsrc(a.esc_val + te0, 0x7FFFFFF0u);
-#pragma unroll
-    for (int i = 0; i < kEscPre; ++i) {
-      const uint32_t e = fe0[q] + g + 4 * i;
-      const bool in = kEsc && e < fe1[q];
-      ecol[q][i] = __builtin_amdgcn_raw_buffer_load_b32(rc, in ? 4u * (e - te0) : kOOB, 0, 0);
-      evalv[q][i] = __builtin_amdgcn_raw_buffer_load_b16(rv, in ? 2u * (e - te0) : kOOB, 0, 0);
-    }
-  }
-  // escape corrections of the finalised tiles, over the phases: dP (placeholders) and Q (values)
-  float dP[SFIN][MQ], Qe[SFIN][MQ];
-#pragma unroll
-  for (int q = 0; q < SFIN; ++q)
-#pragma unroll
-    for (int i = 0; i < MQ; ++i) dP[q][i] = Qe[q][i] = 0.0f;
-  // the escapes of row r16 of each finalised tile whose column lies in phase ph: every lane of the
-  // row takes all of them (the prefetched entries of its three row-mates through shuffles) for its
-  // own x rows g + 4 i, x from the phase's LDS copy
-  const auto phase_escapes = [&](int ph) {
-    if constexpr (kEsc) {
-      const uint32_t c0 = (uint32_t)ph * kbp * kTileCols, c1 = c0 + kbp * kTileCols;
-#pragma unroll
-      for (int q = 0; q < SFIN; ++q) {
-        const auto patch = [&](uint32_t col, uint32_t vbits) {
-          if (col < c0 || col >= c1) return;
-          const float v = bf16_to_float(vbits);
-#pragma unroll
-          for (int i = 0; i < MQ; ++i) {
-            const int m = g + 4 * i;
-            if (m >= M) continue;
-            const float xv = bf16_to_float(xs16[(int64_t)m * kxrow * 8 + (col - c0)]);
-            if constexpr (has_placeholder<FMT>()) dP[q][i] = fmaf(-xv, placeholder_of<FMT>(), dP[q][i]);
-            Qe[q][i] = fmaf(xv, v, Qe[q][i]);
-          }
-        };
-#pragma unroll
-        for (int sg = 0; sg < 4; ++sg)
-#pragma unroll
-          for (int i = 0; i < kEscPre; ++i) {
-            const uint32_t col = (uint32_t)__shfl((int)ecol[q][i], r16 + 16 * sg, 64);
-            const uint32_t vb = (uint32_t)__shfl((int)evalv[q][i], r16 + 16 * sg, 64);
-            if (fe0[q] + (uint32_t)sg + 4 * i < fe1[q]) patch(col, vb);
-          }
-        for (uint32_t e = fe0[q] + 4 * kEscPre; e < fe1[q]; ++e) patch(a.esc_col[e], a.esc_val[e]);
-      }
-    }
-  };
-
-  // ---- the wave's ranges: ring of D blocks, partial sums added into LDS at every tile boundary ----
-  float acc[kMF ? 4 : M];
-#pragma unroll
-  for (int i = 0; i < (kMF ? 4 : M); ++i) acc[i] = 0.0f;
-  uint32_t cp = 0, cs = s0, ck = k0l, ci = 0;       // consumption cursor
-  const auto flush = [&]() {
-    const int i = (int)(cs - s0);
-    const bool first = cp == 0;
-    if constexpr (kMF) {
-      if (r16 < M) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float& dst = s_part[w][i][4 * g + r][r16];
-          dst = first ? acc[r] : dst + acc[r];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = 0.0f;
-    } else {
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float v = group_sum(acc[m]);
-        if (g == m) {
-          float& dst = s_part[w][i][r16][m];
-          dst = first ? v : dst + v;
-        }
-        acc[m] = 0.0f;
-      }
-    }
-  };
-  const uint32_t steps = L * (uint32_t)nph;
-  for (uint32_t ib = 0; ib < steps; ib += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const uint32_t it = ib + d;
-      uint32_t p[16];
-      block_pairs<FMT>(buf[d], e112, p);
-      if constexpr (FMT != kFmtBF16) pin16(p);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (FMT != kFmtBF16) load_unit(buf[d]);
-      if (it < steps) {
-        if constexpr (kMF) {
-          floatx4 acc4 = {acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
-            const u32x4 bv = r16 < M ? xs[r16 * kxrow + (kTileCols * ck + 32 * g + 8 * t) / 8]
-                                     : (u32x4){0u, 0u, 0u, 0u};
-            acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                           __builtin_bit_cast(bf16x8, bv), acc4, 0, 0, 0);
-          }
-          acc[0] = acc4[0]; acc[1] = acc4[1]; acc[2] = acc4[2]; acc[3] = acc4[3];
-        } else {
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const u32x4* xr = xs + m * kxrow + (kTileCols * ck + 32 * g) / 8;
-            const u32x4 x0 = xr[0], x1 = xr[1], x2 = xr[2], x3 = xr[3];
-            float sa = acc[m];
-            sa = dot2_bf16(p[0], x0.x, sa);  sa = dot2_bf16(p[1], x0.y, sa);
-            sa = dot2_bf16(p[2], x0.z, sa);  sa = dot2_bf16(p[3], x0.w, sa);
-            sa = dot2_bf16(p[4], x1.x, sa);  sa = dot2_bf16(p[5], x1.y, sa);
-            sa = dot2_bf16(p[6], x1.z, sa);  sa = dot2_bf16(p[7], x1.w, sa);
-            sa = dot2_bf16(p[8], x2.x, sa);  sa = dot2_bf16(p[9], x2.y, sa);
-            sa = dot2_bf16(p[10], x2.z, sa); sa = dot2_bf16(p[11], x2.w, sa);
-            sa = dot2_bf16(p[12], x3.x, sa); sa = dot2_bf16(p[13], x3.y, sa);
-            sa = dot2_bf16(p[14], x3.z, sa); sa = dot2_bf16(p[15], x3.w, sa);
-            acc[m] = sa;
-          }
-        }
-        if (ck + 1 == kbp || ci + 1 == L) flush();
-        const uint32_t cph = cp;
-        next_unit(cp, cs, ck, ci);
-        if (cp != cph) {
-          // end of the phase: its escapes, then the next phase's x (the ring keeps streaming)
-          phase_escapes((int)cph);
-          if (cp < (uint32_t)nph) {
-            lds_barrier();
-            for (int i = tid; i < M * xw; i += 64 * kSW) {
-              const int m = i / xw, j = i - m * xw;
-              xs[m * kxrow + j] = __builtin_amdgcn_raw_buffer_load_b128(r_x, x_word((int)cp, i), 0, 0);
-            }
-            lds_barrier();
-          }
-        }
-      }
-      if constexpr (FMT == kFmtBF16) load_unit(buf[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // a wave with an empty range (fewer units than waves: then one phase) still patches the escapes
-  // of the tiles it finalises
-  if (L == 0) phase_escapes(0);
-  lds_barrier();
-
-  // ---- finalise tiles w, w + kSW, ...: partial sums in wave order, escapes, scale, store ----
-  const auto wave_of = [&](uint32_t unit) {        // the wave whose range holds `unit`
-    return (int)(((uint64_t)kSW * (unit + 1) + U - 1) / U) - 1;
-  };
-#pragma unroll
-  for (int q = 0; q < SFIN; ++q) {
-    const int j = w + kSW * q;
-    if (j >= T) break;
-    const int64_t tile = c + (int64_t)j * G;
-    const int64_t row = tile * kTileRows + r16;
-    const int wf = wave_of((uint32_t)j * kbp), wl = wave_of((uint32_t)j * kbp + kbp - 1);
-    float P[MQ];
-#pragma unroll
-    for (int i = 0; i < MQ; ++i) P[i] = 0.0f;
-    for (int wv = wf; wv <= wl; ++wv) {
-      if (range_start(wv) == range_start(wv + 1)) continue;   // an empty range (U < kSW)
-      const int si = j - (int)(range_start(wv) / kbp);
-#pragma unroll
-      for (int i = 0; i < MQ; ++i)
-        if (g + 4 * i < M) P[i] += s_part[wv][si][r16][g + 4 * i];
-    }
-    float sc = 1.0f;
-    if constexpr (FMT == kFmtI8) sc = __uint_as_float(fsc[q]);
-    else if constexpr (kEsc) sc = window_scale(fsc[q]);
-#pragma unroll
-    for (int i = 0; i < MQ; ++i) {
-      const int m = g + 4 * i;
-      if (m >= M || row >= a.n) continue;
-      const float v = kEsc ? fmaf(sc, P[i] + dP[q][i], Qe[q][i]) : P[i];
-      if (a.y16) a.y16[m * a.ldy + row] = float_to_bf16_rne(v);
-      else a.y[m * a.ldy + row] = v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------------------
 typedef void (*GemvKernel)(GemvArgs);
@@ -747,99 +358,6 @@ static GemvKernel pick_kernel(Fmt f, int m) {
   if (f == kFmtQ8M) return pick<kFmtQ8M>(m);
   if (f == kFmtI8) return pick<kFmtI8>(m);
   return pick<kFmtBF16>(m);
-}
-
-// ---- the CU-streaming kernel's launcher ----
-typedef void (*StreamKernel)(StreamArgs);
-
-template <int FMT, int M>
-static StreamKernel stream_pick_m(int sfin) {
-  return sfin == 1 ? k_stream<FMT, M, 3, 1> : k_stream<FMT, M, 3, 3>;
-}
-
-template <int FMT>
-static StreamKernel stream_pick(int m, int sfin) {
-  switch (m) {
-    case 1: return stream_pick_m<FMT, 1>(sfin);
-    case 2: return stream_pick_m<FMT, 2>(sfin);
-    case 3: return stream_pick_m<FMT, 3>(sfin);
-    case 4: return stream_pick_m<FMT, 4>(sfin);
-    case 5: case 6: return stream_pick_m<FMT, 6>(sfin);
-    case 7: case 8: return stream_pick_m<FMT, 8>(sfin);
-    case 9: case 10: case 11: case 12: return stream_pick_m<FMT, 12>(sfin);
-    default: return stream_pick_m<FMT, 16>(sfin);
-  }
-}
-
-static StreamKernel stream_kernel(Fmt f, int m, int sfin) {
-  if (f == kFmtW12) return stream_pick<kFmtW12>(m, sfin);
-  if (f == kFmtQ8) return stream_pick<kFmtQ8>(m, sfin);
-  if (f == kFmtQ8M) return stream_pick<kFmtQ8M>(m, sfin);
-  if (f == kFmtI8) return stream_pick<kFmtI8>(m, sfin);
-  return stream_pick<kFmtBF16>(m, sfin);
-}
-
-// rows of x the kernel instance for mb rows is compiled for (x rows past mb read zeros)
-static int stream_rows(int mb) {
-  return mb <= 4 ? mb : mb <= 6 ? 6 : mb <= 8 ? 8 : mb <= 12 ? 12 : 16;
-}
-
-// k phases for mb rows: the fewest that divide the row's blocks and let one phase of x and the
-// partial sums fit the LDS; a phase change needs every wave busy in each phase (0: none fits)
-static int stream_phases(const DevInfo& di, int mb, int64_t k, int64_t tiles_min) {
-  const int64_t nkb = k / kTileCols;
-  const int rows = stream_rows(mb);
-  const int64_t part = (int64_t)kSW * kSMaxSlots * kTileRows * rows * 4;
-  for (int64_t ph = 1; ph <= nkb; ++ph) {
-    if (nkb % ph) continue;
-    const int64_t kbp = nkb / ph;
-    if (rows * (kbp * 16 + 1) * 16 + part > di.max_lds) continue;
-    if (ph > 1 && tiles_min * kbp < kSW) return 0;
-    return (int)ph;
-  }
-  return 0;
-}
-
-bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
-  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t g = tiles < di.cus ? tiles : di.cus;
-  const int mb = (int)(m < 16 ? m : 16);
-  return m >= 1 && (tiles + g - 1) / g <= 3 * kSW && k * 16 * 2 < (int64_t(1) << 32) &&
-         stream_phases(di, mb, k, tiles / g) > 0 && stream_phases(di, (int)((m - 1) % 16) + 1, k, tiles / g) > 0;
-}
-
-hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                         YOut y, hipStream_t s) {
-  DevInfo di;
-  hipError_t err = dev_info(&di);
-  if (err != hipSuccess) return err;
-  if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
-  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t g = tiles < di.cus ? tiles : di.cus;
-  const int sfin = (tiles + g - 1) / g <= kSW ? 1 : 3;
-  for (int64_t m0 = 0; m0 < m; m0 += 16) {
-    const int mb = (int)((m - m0) < 16 ? (m - m0) : 16);
-    const int rows = stream_rows(mb);
-    const int nph = stream_phases(di, mb, k, tiles / g);
-    StreamArgs a;
-    a.x = x + m0 * k;
-    a.base = p.base; a.ae = p.ae; a.lo = p.lo;
-    a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
-    a.w = p.w;
-    a.scale = p.scale;
-    const YOut yp = y + m0 * n;
-    a.y = yp.f;
-    a.y16 = yp.h;
-    a.ldy = n;
-    a.n = n; a.k = k;
-    a.nph = nph;
-    const int64_t kbp = k / kTileCols / nph;
-    hipLaunchKernelGGL(stream_kernel(f, mb, sfin), dim3((unsigned)g), dim3(64 * kSW),
-                       (size_t)(rows * (kbp * 16 + 1) * 16), s, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
 }
 
 int64_t gemv_k_slice(const DevInfo& di, int mb) {

@@ -1,0 +1,595 @@
+// Streaming GEMM for 1..32 rows of x, y[m][n] = sum_k x[m][k] W[n][k], with every wave of a CU
+// streaming the same number of weight blocks.
+//
+// One workgroup of W waves per CU (W = 16 up to 16 rows of x, 12 with 168 VGPRs and a deeper ring
+// for 17..32 rows).  Workgroup c owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so
+// every CU gets the same number of tiles to within one.  Inside the CU the work is dealt by
+// (tile, 128-column block) units rather than by tiles, so no wave idles while others stream:
+//
+// k phases.  x stays in LDS, but 32 rows of a 5120-column x do not fit, so the blocks run in
+// `nph` phases of kbp blocks each.  In phase q the CU's T kbp units (tile-major: blocks
+// q kbp .. q kbp + kbp - 1 of its T tiles) are split into W contiguous ranges, the same ranges of
+// tiles in every phase; the launcher picks kbp so that the ranges are equal (or nearly: the
+// busiest wave sets the phase's time).  x of phase q + 1 is loaded straight from memory into the
+// second of two LDS buffers (global-to-LDS loads dealt over the waves) while phase q runs, so a
+// phase change costs one barrier; the weight ring (D blocks in flight per wave) runs on across
+// phases.
+//
+// Partial sums.  A wave's range touches at most two tiles; it keeps one running sum per touched
+// tile in registers over all phases and adds them into LDS at the end.  Tile j of the CU is then
+// finalised by wave j % W: the partial sums of the waves that touch it, added in wave order
+// (deterministic), plus its escape corrections, collected during each phase from x in LDS.
+//
+// Decode and arithmetic as in the GEMV: 1-2 rows by dot2 (lane r16 + 16 g computes row r16 over
+// columns 32 g .. +31 of each block); 3-32 rows on the matrix cores, the decoded block as operand
+// A of v_mfma_f32_16x16x32_bf16 (one or two 16-row activation tiles as operand B, read from LDS).
+// Escapes as everywhere: y = 2^(base - 112) (P - 2^-15 sum_esc x) + sum_esc x v.
+#include "block.hpp"
+
+namespace w12 {
+
+constexpr int kSECap = 128;     // escapes of a finalised tile copied to LDS (more: read at the end)
+constexpr int kSPieces = 80;    // x pieces (1 KiB) per phase buffer at most
+
+struct StreamArgs {
+  const uint16_t* x;      // x [mrows][k] (this pass's rows)
+  int mrows;
+  const uint8_t* base;
+  const uint8_t* ae;
+  const uint8_t* lo;
+  const uint32_t* esc_ptr;
+  const uint32_t* esc_col;
+  const uint16_t* esc_val;
+  const uint16_t* w;
+  const float* scale;
+  float* y;               // y[m][ldy] (or y16)
+  uint16_t* y16;
+  int64_t ldy;
+  int64_t n, k;
+  uint32_t kbp;           // blocks per phase (kbp * nph = k / 128)
+  int nph;                // phases
+  uint32_t rs;            // 16-byte words per x row in LDS: 64 per 512-column segment
+  uint32_t xwords;        // 16-byte words of one x buffer: MR rows of rs
+  uint32_t eoff;          // 16-byte word offset of the escape copies [W][kSECap] cols, then values
+  int yvec;               // y 16-byte aligned and ldy % 4 == 0: 16-byte stores
+};
+
+template <int FMT>
+__device__ __forceinline__ TileRsrc<FMT> stream_rsrc(const StreamArgs& a, int64_t tile, bool valid,
+                                                     uint32_t nkb) {
+  TileRsrc<FMT> t;
+  const int64_t t0 = valid ? tile : 0;
+  if constexpr (FMT == kFmtBF16) {
+    t.r0 = make_rsrc(a.w + t0 * nkb * (kTileBF / 2), valid ? nkb * (uint32_t)kTileBF : 0u);
+    t.r1 = t.r0;
+  } else {
+    t.r0 = make_rsrc(a.ae + t0 * nkb * kTileAE, valid ? nkb * (uint32_t)kTileAE : 0u);
+    t.r1 = make_rsrc(a.lo + t0 * nkb * kTileLO, valid ? nkb * (uint32_t)kTileLO : 0u);
+  }
+  return t;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete in
+// issue order).
+template <int N>
+__device__ __forceinline__ void s_vm_wait_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Wait until at most min(L, D) ring steps of kLPS loads each are outstanding (L a runtime value).
+template <int D, int kLPS>
+__device__ __forceinline__ void s_vm_wait_steps(uint32_t L) {
+  if (L >= (uint32_t)D) s_vm_wait_le<D * kLPS>();
+  else if constexpr (D > 3) {
+    if (L == 3) s_vm_wait_le<3 * kLPS>();
+    else if (L == 2) s_vm_wait_le<2 * kLPS>();
+    else if (L == 1) s_vm_wait_le<kLPS>();
+    else s_vm_wait_le<0>();
+  } else {
+    if (L == 2) s_vm_wait_le<2 * kLPS>();
+    else if (L == 1) s_vm_wait_le<kLPS>();
+    else s_vm_wait_le<0>();
+  }
+}
+
+template <int W>
+struct StreamShape {
+  static_assert(W == 12 || W == 16, "12 or 16 waves per workgroup");
+  static constexpr int D = W == 12 ? 4 : 3;     // blocks in flight per wave
+  static constexpr int FW = (kSPieces + W - 1) / W;   // x pieces a wave may load per phase
+};
+
+// MR: rows of x the instance is built for (x rows mrows .. MR - 1 read zeros).
+template <int FMT, int MR, int W>
+__global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
+  constexpr int D = StreamShape<W>::D, FW = StreamShape<W>::FW;
+  constexpr int SL = 2;                              // tiles one wave's range touches at most
+  constexpr bool kMF = MR > 2;                       // matrix cores for 3..32 rows
+  constexpr int NT = MR > 16 ? 2 : 1;                // 16-row activation tiles
+  constexpr int NACC = kMF ? 4 * NT : MR;            // running sums per lane
+  constexpr int MP = MR + 1;                         // row stride of the LDS partial sums
+  constexpr bool kEsc = FMT != kFmtBF16;
+  constexpr int kLPS = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;   // loads per ring step
+  // LDS: x buffers [2][MR][rs] of 16-byte words; column word c16 (columns 8 c16 .. +7 of the
+  // phase) of x row r sits at r * rs + (c16 & ~15) + ((c16 & 15) ^ (r & 15)): the 16 rows an
+  // operand read takes then hit distinct banks.  At the end the partial sums [W][SL][16][MP]
+  // over them.
+  extern __shared__ u32x4 lds[];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const uint32_t lane16 = 16u * lane;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t G = gridDim.x, c = blockIdx.x;
+  const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
+  const uint32_t nkb = (uint32_t)(a.k / kTileCols);
+  const uint32_t kbp = a.kbp;
+  const int nph = a.nph;
+  const int T = (int)((tiles - c + G - 1) / G);     // tiles c + j G, j < T (the grid keeps c < tiles)
+  const uint32_t U = (uint32_t)T * kbp;              // units per phase of the CU
+  const auto rstart = [&](int wv) { return (uint32_t)(((uint64_t)wv * U) / W); };
+  const uint32_t r0 = rstart(w), r1 = rstart(w + 1);
+  const uint32_t L = r1 - r0;                        // units per phase of this wave
+  const uint32_t s0 = r0 / kbp, k0l = r0 - s0 * kbp; // the wave's first tile (local) and block
+  const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(lds);
+  const uint32_t e112 = exp112_pair();
+
+  // ---- the tile this wave finalises (local tile w) ----
+  // Lane layout of the finalisation (the matrix cores' output layout): lane r16 + 16 g owns
+  // weight rows wr(r) = 4 g + r (r < RW = 4) and x rows xm(cc) = 16 cc + r16 (cc < NX = NT);
+  // with dot2 (1-2 rows) weight row r16 (RW = 1) and x row g (NX = 1, lanes g >= MR idle).
+  constexpr int RW = kMF ? 4 : 1, NX = kMF ? NT : 1;
+  const auto wr = [&](int r) { return kMF ? 4 * g + r : r16; };
+  const auto xm = [&](int cc) { return kMF ? 16 * cc + r16 : g; };
+  const bool fin = w < T;
+  const int64_t ftile = c + (int64_t)w * G;
+  const int64_t row0 = (fin ? ftile : 0) * kTileRows;
+  // escape bounds of the lane's rows: row wr(r) holds entries [st[r], st[r + 1]) (kMF: rows
+  // 4 g .. 4 g + 3 are consecutive, so 5 bounds), and the window bottoms (or 8-bit scales)
+  uint32_t st[RW + 1], fsc[RW];
+#pragma unroll
+  for (int r = 0; r <= RW; ++r) {
+    const int64_t rr = row0 + (kMF ? 4 * g + r : r16 + r);
+    st[r] = kEsc && fin ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t rr = row0 + wr(r), rc = rr < a.n ? rr : a.n - 1;
+    if constexpr (FMT == kFmtI8) fsc[r] = fin ? __float_as_uint(a.scale[rc]) : 0u;
+    else if constexpr (kEsc) fsc[r] = fin ? a.base[rc] : 0u;
+    else fsc[r] = 0u;
+  }
+  // the tile's escape list [te0, te1): its first kSECap entries are copied to this wave's LDS
+  // slot (loaded after phase 0's x, written at the end of phase 0)
+  const uint32_t fte0 = kEsc && fin ? a.esc_ptr[row0] : 0u;
+
+  // ---- x of a phase into LDS buffer `buf`: piece P = (row, 512-column segment), one coalesced
+  // 1 KiB read of the row (lane j reads the column word its LDS slot holds), by wave P % W;
+  // columns past the phase read zeros into the row's last segment ----
+  const uint32_t rs = a.rs, segs = rs >> 6;
+  const Rsrc r_x = make_rsrc(a.x, (uint32_t)(a.mrows * a.k * 2));
+  const auto issue_x = [&](int ph, int buf) {
+#pragma unroll
+    for (int i = 0; i < FW; ++i) {
+      const uint32_t P = (uint32_t)(w + W * i);
+      if (P < MR * segs) {
+        const uint32_t row = P / segs, sg = P - row * segs;
+        const uint32_t c16 = 64u * sg + (((uint32_t)lane & ~15u) | (((uint32_t)lane & 15u) ^ (row & 15u)));
+        const bool ok = c16 < kbp * 16u && (int)row < a.mrows;
+        const uint32_t off = ok ? 2u * (row * (uint32_t)a.k + (uint32_t)ph * kbp * kTileCols + 8u * c16) : kOOB;
+        u32x4* dst = lds + buf * a.xwords + row * rs + 64u * sg;   // lane j at word j
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_x, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- ring cursors: phase, tile (local), block in the phase, index in the range ----
+  uint32_t rp = 0, rt = s0, rk = k0l, ri = 0;
+  const auto advance = [&](uint32_t& p_, uint32_t& t_, uint32_t& k_, uint32_t& i_) {
+    k_ += 1;
+    i_ += 1;
+    const bool wrap = k_ == kbp;
+    k_ = wrap ? 0u : k_;
+    t_ = wrap ? t_ + 1 : t_;
+    const bool pend = i_ == L;                       // the range ends: the next phase's range
+    p_ = pend ? p_ + 1 : p_;
+    t_ = pend ? s0 : t_;
+    k_ = pend ? k0l : k_;
+    i_ = pend ? 0u : i_;
+  };
+  const auto load_next = [&](BlockRegs<FMT>& r) {
+    const bool have = rp < (uint32_t)nph && L > 0;
+    load_block<FMT>(stream_rsrc<FMT>(a, c + (int64_t)rt * G, have, nkb), have ? rp * kbp + rk : ~0u, lane16, r);
+    advance(rp, rt, rk, ri);
+  };
+
+  issue_x(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  BlockRegs<FMT> buf[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_next(buf[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  s_vm_wait_le<D * kLPS>();                          // phase 0's x is in LDS
+  lds_barrier();
+  if (nph > 1) issue_x(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- escape entries of the tile to finalise (its bounds arrived before the x loads) ----
+  const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0);
+  uint32_t ldc[kSECap / 64], ldv[kSECap / 64];
+  {
+    const uint32_t te1 = kMF ? (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 48)
+                             : (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 15);
+    const uint32_t cnt = te1 - te0 < (uint32_t)kSECap ? te1 - te0 : (uint32_t)kSECap;
+    const Rsrc rc = make_rsrc(a.esc_col + te0, cnt * 4u), rv = make_rsrc(a.esc_val + te0, cnt * 2u);
+#pragma unroll
+    for (int i = 0; i < kSECap / 64; ++i) {
+      ldc[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, 4u * (lane + 64 * i), 0, 0);
+      ldv[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, 2u * (lane + 64 * i), 0, 0);
+    }
+  }
+  uint32_t* s_ecol = reinterpret_cast<uint32_t*>(lds + a.eoff) + w * kSECap;   // this wave's copy
+  uint16_t* s_eval = reinterpret_cast<uint16_t*>(lds + a.eoff + W * kSECap / 4) + w * kSECap;
+  const uint32_t lds_end = te0 + kSECap;              // entries past this stay in memory
+  const auto run_end = [&](int r) { return st[r + 1] < lds_end ? st[r + 1] : lds_end; };
+  // escape corrections of the finalised tile: dP (placeholders), Qe (values); per row a cursor
+  // (absolute entry index) with the column and value under it (column ~0: none left in LDS)
+  float dP[NX][RW], Qe[NX][RW];
+  uint32_t cur[RW], ncol[RW], nval[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    cur[r] = st[r];
+    ncol[r] = ~0u;
+    nval[r] = 0u;
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc) dP[cc][r] = Qe[cc][r] = 0.0f;
+  }
+  const bool xlane = kMF || g < MR;                   // the lane owns an x row
+  const auto entry_at = [&](int r) {                  // the entry under row r's cursor
+    const bool in = cur[r] < run_end(r);
+    const uint32_t at = in ? cur[r] - te0 : 0u;
+    ncol[r] = in ? s_ecol[at] : ~0u;
+    nval[r] = s_eval[at];
+  };
+  // the escapes of the lane's rows with a column in phase ph (runs are sorted by column), x from
+  // the phase's LDS buffer; the reads of the x values at an entry and of the row's next entry go
+  // out together.  The first call also puts the entries into LDS.
+  const auto phase_escapes = [&](int ph) {
+    if constexpr (kEsc) {
+      if (!fin) return;
+      if (ph == 0) {
+#pragma unroll
+        for (int i = 0; i < kSECap / 64; ++i) {
+          s_ecol[lane + 64 * i] = ldc[i];
+          s_eval[lane + 64 * i] = (uint16_t)ldv[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+        for (int r = 0; r < RW; ++r) entry_at(r);
+      }
+      const uint32_t c0 = (uint32_t)ph * kbp * kTileCols, c1 = c0 + kbp * kTileCols;
+      const uint16_t* xb = xs16 + (size_t)(ph & 1) * a.xwords * 8;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        while (ncol[r] < c1) {
+          const uint32_t cc0 = ncol[r] - c0, c16 = cc0 >> 3;
+          const float v = bf16_to_float(nval[r]);
+          float xv[NX];
+#pragma unroll
+          for (int cc = 0; cc < NX; ++cc) {
+            const int m = xm(cc) < MR ? xm(cc) : 0;
+            xv[cc] = bf16_to_float(
+                xb[(m * rs + (c16 & ~15u) + ((c16 & 15u) ^ (uint32_t)(m & 15))) * 8 + (cc0 & 7)]);
+          }
+          cur[r] += 1;
+          entry_at(r);
+#pragma unroll
+          for (int cc = 0; cc < NX; ++cc) {
+            if (!xlane || xm(cc) >= MR) continue;
+            if constexpr (has_placeholder<FMT>()) dP[cc][r] = fmaf(-xv[cc], placeholder_of<FMT>(), dP[cc][r]);
+            Qe[cc][r] = fmaf(xv[cc], v, Qe[cc][r]);
+          }
+        }
+      }
+    }
+  };
+  // end of phase ph: its escapes; then (not the last phase) wait for the next phase's x, the
+  // barrier that publishes it and frees buffer ph & 1, and the loads of phase ph + 2 into it.
+  // The next phase's x went out before the L ring refills of this phase, and loads complete in
+  // issue order, so waiting until at most min(L, D) refills are outstanding waits for it.
+  const auto phase_end = [&](int ph) {
+    __builtin_amdgcn_sched_barrier(0);
+    phase_escapes(ph);
+    if (ph + 1 < nph) {
+      __builtin_amdgcn_sched_barrier(0);
+      s_vm_wait_steps<D, kLPS>(L);
+      lds_barrier();
+      if (ph + 2 < nph) issue_x(ph + 2, ph & 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- the wave's ranges: ring of D blocks; a running sum per touched tile ----
+  float acc[NACC], tot[SL][NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) {
+    acc[i] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) tot[s][i] = 0.0f;
+  }
+  uint32_t cp = 0, ct = s0, ck = k0l, ci = 0;       // consumption cursor
+  const auto flush = [&]() {
+    const uint32_t slot = ct - s0;
+    // every slot takes acc or 0 (a select per element, so the slots stay in registers)
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) tot[s][i] += slot == (uint32_t)s ? acc[i] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = 0.0f;
+  };
+  const uint32_t steps = L * (uint32_t)nph;
+  for (uint32_t ib = 0; ib < steps; ib += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const uint32_t it = ib + d;
+      uint32_t p[16];
+      block_pairs<FMT>(buf[d], e112, p);
+      if constexpr (FMT != kFmtBF16) pin16(p);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (FMT != kFmtBF16) load_next(buf[d]);
+      if (it < steps) {
+        const u32x4* xb = lds + (cp & 1u) * a.xwords + ck * 16u;   // block ck of the phase
+        if constexpr (kMF) {
+#pragma unroll
+          for (int cc = 0; cc < NT; ++cc) {
+            floatx4 a4 = {acc[4 * cc], acc[4 * cc + 1], acc[4 * cc + 2], acc[4 * cc + 3]};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
+              const int xr = 16 * cc + r16;
+              const u32x4 bv = (MR >= 16 * (cc + 1) || xr < MR) ? xb[xr * rs + ((4 * g + t) ^ r16)]
+                                                                : (u32x4){0u, 0u, 0u, 0u};
+              a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, bv), a4, 0, 0, 0);
+            }
+            acc[4 * cc] = a4[0]; acc[4 * cc + 1] = a4[1]; acc[4 * cc + 2] = a4[2]; acc[4 * cc + 3] = a4[3];
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            const u32x4* xr = xb + m * rs;
+            const u32x4 x0 = xr[(4 * g) ^ m], x1 = xr[(4 * g + 1) ^ m];
+            const u32x4 x2 = xr[(4 * g + 2) ^ m], x3 = xr[(4 * g + 3) ^ m];
+            float sa = acc[m];
+            sa = dot2_bf16(p[0], x0.x, sa);  sa = dot2_bf16(p[1], x0.y, sa);
+            sa = dot2_bf16(p[2], x0.z, sa);  sa = dot2_bf16(p[3], x0.w, sa);
+            sa = dot2_bf16(p[4], x1.x, sa);  sa = dot2_bf16(p[5], x1.y, sa);
+            sa = dot2_bf16(p[6], x1.z, sa);  sa = dot2_bf16(p[7], x1.w, sa);
+            sa = dot2_bf16(p[8], x2.x, sa);  sa = dot2_bf16(p[9], x2.y, sa);
+            sa = dot2_bf16(p[10], x2.z, sa); sa = dot2_bf16(p[11], x2.w, sa);
+            sa = dot2_bf16(p[12], x3.x, sa); sa = dot2_bf16(p[13], x3.y, sa);
+            sa = dot2_bf16(p[14], x3.z, sa); sa = dot2_bf16(p[15], x3.w, sa);
+            acc[m] = sa;
+          }
+        }
+        if (ck + 1 == kbp || ci + 1 == L) flush();
+        const uint32_t cph = cp;
+        advance(cp, ct, ck, ci);
+        if (cp != cph) phase_end((int)cph);
+      }
+      if constexpr (FMT == kFmtBF16) load_next(buf[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // a wave with an empty range still takes part in every phase change and patches the escapes
+  // of the tile it finalises
+  if (L == 0)
+    for (int ph = 0; ph < nph; ++ph) phase_end(ph);
+
+  // ---- the running sums into LDS (over the x buffers, after the last phase's reads) ----
+  float* s_part = reinterpret_cast<float*>(lds);     // [W][SL][16][MP]
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    float* dst = s_part + ((w * SL + s) * kTileRows) * MP;
+    if constexpr (kMF) {
+#pragma unroll
+      for (int cc = 0; cc < NT; ++cc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (MR >= 16 * (cc + 1) || 16 * cc + r16 < MR) dst[(4 * g + r) * MP + 16 * cc + r16] = tot[s][4 * cc + r];
+    } else {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float v = group_sum(tot[s][m]);
+        if (g == m) dst[r16 * MP + m] = v;
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- finalise local tile w: partial sums in wave order, escapes, scale, store ----
+  if (!fin) return;
+  // escapes past the LDS copy of a crowded tile: entries and x from memory
+  if constexpr (kEsc) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      for (uint32_t e = cur[r] > lds_end ? cur[r] : lds_end; e < st[r + 1]; ++e) {
+        const uint32_t col = a.esc_col[e];
+        const float v = bf16_to_float(a.esc_val[e]);
+#pragma unroll
+        for (int cc = 0; cc < NX; ++cc) {
+          const int m = xm(cc);
+          if (!xlane || m >= a.mrows) continue;
+          const float xv = bf16_to_float(a.x[(int64_t)m * a.k + col]);
+          if constexpr (has_placeholder<FMT>()) dP[cc][r] = fmaf(-xv, placeholder_of<FMT>(), dP[cc][r]);
+          Qe[cc][r] = fmaf(xv, v, Qe[cc][r]);
+        }
+      }
+  }
+  const int j = w;
+  const auto owner = [&](uint32_t u) {               // the wave whose range holds unit u
+    return (int)(((uint64_t)W * (u + 1) + U - 1) / U) - 1;
+  };
+  const int wf = owner((uint32_t)j * kbp), wl = owner((uint32_t)j * kbp + kbp - 1);
+  float P[NX][RW];
+#pragma unroll
+  for (int cc = 0; cc < NX; ++cc)
+#pragma unroll
+    for (int r = 0; r < RW; ++r) P[cc][r] = 0.0f;
+  for (int wv = wf; wv <= wl; ++wv) {
+    const uint32_t v0 = rstart(wv);
+    if (v0 == rstart(wv + 1)) continue;              // an empty range
+    const int si = j - (int)(v0 / kbp);
+    const float* src = s_part + ((wv * SL + si) * kTileRows) * MP;
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+        if (xlane && xm(cc) < MR) P[cc][r] += src[wr(r) * MP + xm(cc)];
+  }
+  if (!xlane) return;
+#pragma unroll
+  for (int cc = 0; cc < NX; ++cc) {
+    const int m = xm(cc);
+    if (m >= a.mrows) continue;
+    float v[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float sc = 1.0f;
+      if constexpr (FMT == kFmtI8) sc = __uint_as_float(fsc[r]);
+      else if constexpr (kEsc) sc = window_scale(fsc[r]);
+      v[r] = kEsc ? fmaf(sc, P[cc][r] + dP[cc][r], Qe[cc][r]) : P[cc][r];
+    }
+    const int64_t rbase = row0 + wr(0);
+    if (a.y16) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+        if (rbase + r < a.n) a.y16[m * a.ldy + rbase + r] = float_to_bf16_rne(v[r]);
+    } else if (kMF && a.yvec && rbase + 3 < a.n) {
+      *reinterpret_cast<floatx4*>(a.y + m * a.ldy + rbase) = (floatx4){v[0], v[RW > 1 ? 1 : 0], v[RW > 2 ? 2 : 0], v[RW > 3 ? 3 : 0]};
+    } else {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+        if (rbase + r < a.n) a.y[m * a.ldy + rbase + r] = v[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------------------------
+typedef void (*StreamKernel)(StreamArgs);
+
+template <int FMT>
+static StreamKernel stream_pick(int mr) {
+  switch (mr) {
+    case 1: return k_stream<FMT, 1, 16>;
+    case 2: return k_stream<FMT, 2, 16>;
+    case 4: return k_stream<FMT, 4, 16>;
+    case 8: return k_stream<FMT, 8, 16>;
+    case 16: return k_stream<FMT, 16, 16>;
+    default: return k_stream<FMT, 32, 12>;
+  }
+}
+
+static StreamKernel stream_kernel(Fmt f, int mr) {
+  if (f == kFmtW12) return stream_pick<kFmtW12>(mr);
+  if (f == kFmtQ8) return stream_pick<kFmtQ8>(mr);
+  if (f == kFmtQ8M) return stream_pick<kFmtQ8M>(mr);
+  if (f == kFmtI8) return stream_pick<kFmtI8>(mr);
+  return stream_pick<kFmtBF16>(mr);
+}
+
+// rows of x the kernel instance for mb rows is built for, and its waves per workgroup
+static int stream_rows(int64_t mb) {
+  return mb <= 2 ? (int)mb : mb <= 4 ? 4 : mb <= 8 ? 8 : mb <= 16 ? 16 : 32;
+}
+static int stream_waves(int mr) { return mr > 16 ? 12 : 16; }
+
+struct StreamPlan {
+  int mr = 0, waves = 0, nph = 0;
+  int64_t G = 0;
+  uint32_t kbp = 0, rs = 0, xwords = 0, eoff = 0;
+  size_t lds = 0;
+};
+
+// The phase length for a pass of mb rows: among the divisors of the row's blocks whose x buffers
+// (two, one for a single phase) fit the LDS and that keep every wave's range within two tiles,
+// the one with the fewest blocks for the busiest wave over all phases (a phase change counted as
+// half a block).  False if none fits.
+static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, StreamPlan* out) {
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows, nkb = k / kTileCols;
+  const int mr = stream_rows(mb), W = stream_waves(mr);
+  const int64_t G = tiles < di.cus ? tiles : di.cus;
+  const int64_t tmax = (tiles + G - 1) / G;          // tiles of the busiest CU
+  double best = 0;
+  bool found = false;
+  for (int64_t kbp = nkb; kbp >= 1; --kbp) {
+    if (nkb % kbp) continue;
+    const int64_t nph = nkb / kbp;
+    const int64_t segs = (kbp + 3) / 4, rs = 64 * segs, xwords = mr * rs;
+    if (mr * segs > kSPieces) continue;
+    const int64_t U = tmax * kbp;
+    if (U >= (int64_t(1) << 31)) continue;
+    const int64_t lmax = (U + W - 1) / W;
+    if ((lmax - 1) / kbp + 2 > 2) continue;          // a range over at most two tiles
+    const int64_t part = (int64_t)W * 2 * kTileRows * (mr + 1) * 4;
+    const int64_t xb = (nph > 1 ? 2 : 1) * xwords * 16;
+    const int64_t body = ((xb > part ? xb : part) + 15) / 16 * 16;
+    const int64_t lds = body + (int64_t)W * kSECap * 6;   // then the escape copies
+    if (lds > di.max_lds) continue;
+    const double cost = (double)(lmax * nph) + 0.5 * (double)(nph - 1);
+    if (found && cost >= best) continue;
+    found = true;
+    best = cost;
+    out->mr = mr; out->waves = W; out->nph = (int)nph; out->G = G;
+    out->kbp = (uint32_t)kbp; out->rs = (uint32_t)rs; out->xwords = (uint32_t)xwords; out->lds = (size_t)lds;
+    out->eoff = (uint32_t)(body / 16);
+  }
+  return found;
+}
+
+bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || k * 32 * 2 >= (int64_t(1) << 32)) return false;
+  StreamPlan p;
+  const int64_t full = m < 32 ? m : 32, tail = (m - 1) % 32 + 1;
+  return stream_plan(di, full, n, k, &p) && stream_plan(di, tail, n, k, &p);
+}
+
+hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
+                         YOut y, hipStream_t s) {
+  DevInfo di;
+  hipError_t err = dev_info(&di);
+  if (err != hipSuccess) return err;
+  if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
+  for (int64_t m0 = 0; m0 < m; m0 += 32) {
+    const int64_t mb = (m - m0) < 32 ? (m - m0) : 32;
+    StreamPlan pl;
+    if (!stream_plan(di, mb, n, k, &pl)) return hipErrorInvalidValue;
+    StreamArgs a;
+    a.x = x + m0 * k;
+    a.mrows = (int)mb;
+    a.base = p.base; a.ae = p.ae; a.lo = p.lo;
+    a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
+    a.w = p.w;
+    a.scale = p.scale;
+    const YOut yp = y + m0 * n;
+    a.y = yp.f;
+    a.y16 = yp.h;
+    a.ldy = n;
+    a.n = n; a.k = k;
+    a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
+    a.yvec = yp.f && (reinterpret_cast<uintptr_t>(yp.f) & 15u) == 0 && n % 4 == 0;
+    hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)pl.G), dim3(64 * pl.waves), pl.lds, s, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace w12

@@ -131,9 +131,9 @@ int64_t gemv_k_slice(const DevInfo& di, int mb);
 // GEMV family (wave-reduction kernel), any m (passes of <= 8 rows of x)
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        YOut y, hipStream_t s, const Scratch& sc);
-// CU-streaming family (one workgroup of 16 waves per CU, equal block ranges per wave, x resident
-// in LDS): passes of <= 8 rows of x; stream_fits says whether a shape can run it (at most 48 tiles
-// per CU and x rows within the LDS); no SiLU pairing
+// Streaming family (one workgroup per CU owning whole tiles, every wave an equal share of their
+// blocks, x in LDS by k phases): passes of <= 32 rows of x; stream_fits says whether a shape can
+// run it (at most 16 tiles per CU, 12 above 16 rows); no SiLU pairing
 bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k);
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                          YOut y, hipStream_t s);

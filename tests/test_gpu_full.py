@@ -57,8 +57,9 @@ def _codec(w, what, pool):
 
 
 def test_gate_up_full(pool):
-    """Config gate+up: codec, exact GEMM at M = 1, 2, 4, 8, 16, 32, 64 on both kernel families, the
-    Q pass at M=16 and the dense baseline at M=1 and 32 -- every output element."""
+    """Config gate+up: codec, exact GEMM at M = 1, 2, 4, 8, 16, 32, 64 on the three kernel families
+    (the streaming kernel in passes of 32 rows), the Q pass at M=16 and the dense baseline at M=1
+    and 32 -- every output element."""
     w12 = _w12()
     w, spec, tid = synth.config_weight("gate_up")
     rec, dw = _codec(w, "gate_up", pool)
@@ -66,18 +67,18 @@ def test_gate_up_full(pool):
     say("gate_up: oracle GEMM M=64 (all rows)")
     y64, absum = oracle_pool.gemm(x, w, pool)
     for m in (1, 2, 4, 8, 16, 32, 64):
-        for path in ("gemv", "mfma"):
+        for path in ("gemv", "mfma", "stream"):
             say(f"gate_up: gemm m={m} path={path}")
             y = w12.gemm(to_dev(x[:m]), rec, path=path).cpu().numpy()
             check_y(y, y64[:m], absum[:m], f"gate_up w12 m={m} {path}")
     say("gate_up: oracle Q-pass GEMM M=16")
     yq64, qabs = oracle_pool.gemm(x[:16], w, pool, view="q8")
-    for path in ("gemv", "mfma"):
+    for path in ("gemv", "mfma", "stream"):
         say(f"gate_up: q8_gemm m=16 path={path}")
         yq = w12.q8_gemm(to_dev(x[:16]), rec, path=path).cpu().numpy()
         check_y(yq, yq64, qabs, f"gate_up q8 m=16 {path}")
     bt = w12.bf16_tiles(dw)
-    for m, path in ((1, "gemv"), (32, "mfma")):
+    for m, path in ((1, "gemv"), (32, "mfma"), (32, "stream")):
         say(f"gate_up: bf16_gemm m={m} path={path}")
         yb = w12.bf16_gemm(to_dev(x[:m]), bt, path=path).cpu().numpy()
         check_y(yb, y64[:m], absum[:m], f"gate_up bf16 m={m} {path}")

@@ -673,18 +673,21 @@ def test_binding_rejects_bad_arguments():
 
 
 @pytest.mark.parametrize("n,k,ms", [
-    (300, 1152, (1, 2, 3, 8)),            # 19 tiles: one tile per workgroup, waves with empty ranges
-    (4000, 1024, (1, 2, 4, 5, 8, 13)),    # 250 tiles; 13 rows: passes of 8 and 5
-    (20487, 512, (1, 3, 7)),              # 1281 tiles: 5-6 per workgroup, ragged last tile
-    (196600, 128, (1, 6)),                # 12288 tiles, one block each: 48 per workgroup
-    (3000, 5120, (1, 2, 8)),              # long ranges: a wave crosses several tiles
-    (8192, 5120, (9, 13, 16, 21)),        # x in two k phases; 21 rows: passes of 16 and 5
-    (4000, 10240, (16,)),                 # four k phases
+    (300, 1152, (1, 2, 3, 8)),            # 19 tiles: every tile shared by several CUs
+    (4000, 1024, (1, 2, 4, 5, 8, 13)),    # 250 tiles; 13 rows: the 16-row instance, rows 13..15 zero
+    (20487, 512, (1, 3, 7)),              # 1281 tiles: 5-6 per CU, ragged last tile
+    (40000, 128, (1, 6)),                 # 2500 tiles of one block each: 9-10 per CU
+    (3000, 5120, (1, 2, 8)),              # 188 tiles of 40 blocks: no tile inside one CU
+    (8192, 5120, (9, 13, 16, 21, 32)),    # 16 rows: 4 k phases; 21 and 32 rows: 5 phases of 8 blocks
+    (4000, 10240, (16,)),                 # 5 phases of 16 blocks
+    (1024, 5120, (1, 17, 32)),            # 64 tiles (a k/v projection): each tile over 4 CUs
+    (2000, 2048, (33, 40, 64)),           # passes of 32 rows and a ragged last pass
 ])
 def test_stream_path(n, k, ms):
-    """The CU-streaming kernel (W12_PATH_STREAM) on every format, 1..16 rows per pass (x staged in
-    k phases when it does not fit the LDS whole), against the oracle; bfloat16 outputs the rounding
-    of the float outputs."""
+    """The streaming kernel (W12_PATH_STREAM) on every format, 1..32 rows per pass (x staged in
+    k phases when it does not fit the LDS whole; tiles shared by neighbouring CUs added through the
+    workspace), against the oracle; bfloat16 outputs the rounding of the float outputs; a second
+    call gives the same bits (the shared tiles' sums are added in a fixed order)."""
     import torch
     w12 = _w12()
     rng = np.random.default_rng(n + k)
@@ -713,9 +716,12 @@ def test_stream_path(n, k, ms):
                 check_y(y, oracle.gemm64_f(x[:m], wi8), oracle.abs_bound64_f(x[:m], wi8), what)
             else:
                 check_gemm(y, x[:m], wv, what)
-            if m in (1, 3):
+            if m in (1, 3, 32):
                 y16 = fn(out_bf16=True)
                 _check_bf16_out(y16, y, x[:m], None, what + " bf16")
+            if name == "w12":
+                assert np.array_equal(fn().cpu().numpy().view(np.uint32), y.view(np.uint32)), \
+                    f"{what}: a second call differs"
 
 
 def test_stream_one_hot_and_special_values():
