@@ -77,8 +77,12 @@ extern "C" {
 #define W12_ERR_HIP      (-6)  /* HIP runtime or launch error; message from hipGetErrorString */
 
 /* flags for the GEMM calls: which kernel family runs */
-#define W12_PATH_AUTO 0u  /* GEMV with wave reductions for m <= 2, and for m <= 5 on shapes of at
-                           * most 1024 16-row tiles and k <= 8192; bf16 MFMA otherwise */
+#define W12_PATH_AUTO 0u  /* the family measured fastest for the shape: the streaming kernel for
+                           * 3 <= m <= 16 on shapes of at least 1.5 16-row tiles per compute unit
+                           * and k <= 8192, and for 17 <= m <= 32 on at least 2 tiles per unit
+                           * (the dense baseline: at most 6 tiles per unit); otherwise the GEMV
+                           * with wave reductions for m <= 2, and for m <= 5 on shapes of at most
+                           * 1024 tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row

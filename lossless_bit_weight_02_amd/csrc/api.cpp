@@ -110,19 +110,19 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   if (flags == W12_PATH_STREAM && !stream_ok)
     return fail(silu ? W12_ERR_ARG : W12_ERR_SHAPE, "the streaming kernel does not take this call "
                 "(at most 16 16-row tiles per compute unit, 12 above 16 rows of x; no SiLU epilogue)");
-  // The streaming kernel where it measured fastest (W12, us, stream vs the best other family, on
-  // 27B-class shapes): 3..16 rows on shapes of at least 1.5 tiles per CU and rows of at most 8192
-  // columns ([17408, 5120]: 4 rows 29.3 vs 31.4, 16 rows 29.5 vs 32.8; [8192, 5120]: 4 rows 17.5
-  // vs 18.3, 16 rows 20.6 vs 22.5; [6144, 5120], 8 rows: 18.2 vs 19.1; [34816, 5120], 16 rows:
-  // 46.9 vs 48.5), except 5..8 rows above 6 tiles per CU ([34816, 5120], 8 rows: 50.7 vs 47.8);
-  // 17..32 rows on 3..6 tiles per CU ([17408, 5120], 32 rows: 33.9 vs 38.0; [34816, 5120]: 54.5
-  // vs 53.6, [8192, 5120]: 26.8 vs 26.1).  Long rows ([5120, 17408]) and shapes of 1.25 tiles per
-  // CU or fewer run the other families.
+  // The streaming kernel where it measured fastest (us, streaming vs the best other family, on
+  // 27B-class shapes, W12): 3..16 rows on shapes of at least 1.5 tiles per CU with rows of at
+  // most 8192 columns ([34816, 5120]: 4 rows 46.4 vs 47.7, 8 rows 47.2 vs 47.9, 16 rows 46.8 vs
+  // 48.6; [17408, 5120], 16 rows: 29.3 vs 32.8; [8192, 5120], 4 rows: 15.8 vs 18.3; [6144, 5120],
+  // 16 rows: 17.8 vs 20.2), and 17..32 rows on at least 2 tiles per CU ([17408, 5120]: 34.2 vs
+  // 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
+  // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
+  // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
+  // 55.8, 32 rows 59.5 vs 57.8).
   const int64_t cus = dinfo.cus;
   const bool stream_auto =
-      stream_ok && k <= 8192 &&
-      ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus && !(m >= 5 && m <= 8 && tiles > 6 * cus)) ||
-       (m >= 17 && m <= 32 && tiles >= 3 * cus && tiles <= 6 * cus));
+      stream_ok && k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
+      ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus));
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
   const bool use_stream = flags == W12_PATH_STREAM || (flags == W12_PATH_AUTO && stream_auto);
   const bool gemv = !use_stream && (flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto));

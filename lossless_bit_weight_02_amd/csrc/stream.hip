@@ -51,7 +51,6 @@ struct StreamArgs {
   uint32_t rs;            // 16-byte words per x row in LDS: 64 per 512-column segment
   uint32_t xwords;        // 16-byte words of one x buffer: MR rows of rs
   uint32_t eoff;          // 16-byte word offset of the escape copies [W][kSECap] cols, then values
-  int yvec;               // y 16-byte aligned and ldy % 4 == 0: 16-byte stores
 };
 
 template <int FMT>
@@ -134,12 +133,11 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const uint32_t e112 = exp112_pair();
 
   // ---- the tile this wave finalises (local tile w) ----
-  // Lane layout of the finalisation (the matrix cores' output layout): lane r16 + 16 g owns
-  // weight rows wr(r) = 4 g + r (r < RW = 4) and x rows xm(cc) = 16 cc + r16 (cc < NX = NT);
-  // with dot2 (1-2 rows) weight row r16 (RW = 1) and x row g (NX = 1, lanes g >= MR idle).
-  constexpr int RW = kMF ? 4 : 1, NX = kMF ? NT : 1;
-  const auto wr = [&](int r) { return kMF ? 4 * g + r : r16; };
-  const auto xm = [&](int cc) { return kMF ? 16 * cc + r16 : g; };
+  // Lane layout of the finalisation: lane r16 + 16 g owns weight row r16 and x rows
+  // xm(i) = g + 4 i (i < NX; rows past MR idle), so a lane walks the escapes of one row.
+  constexpr int RW = 1, NX = (MR + 3) / 4;
+  const auto wr = [&](int r) { return r16 + r; };
+  const auto xm = [&](int i) { return g + 4 * i; };
   const bool fin = w < T;
   const int64_t ftile = c + (int64_t)w * G;
   const int64_t row0 = (fin ? ftile : 0) * kTileRows;
@@ -148,7 +146,7 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   uint32_t st[RW + 1], fsc[RW];
 #pragma unroll
   for (int r = 0; r <= RW; ++r) {
-    const int64_t rr = row0 + (kMF ? 4 * g + r : r16 + r);
+    const int64_t rr = row0 + r16 + r;
     st[r] = kEsc && fin ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
   }
 #pragma unroll
@@ -219,8 +217,7 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0);
   uint32_t ldc[kSECap / 64], ldv[kSECap / 64];
   {
-    const uint32_t te1 = kMF ? (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 48)
-                             : (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 15);
+    const uint32_t te1 = (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 15);   // row0 + 16
     const uint32_t cnt = te1 - te0 < (uint32_t)kSECap ? te1 - te0 : (uint32_t)kSECap;
     const Rsrc rc = make_rsrc(a.esc_col + te0, cnt * 4u), rv = make_rsrc(a.esc_val + te0, cnt * 2u);
 #pragma unroll
@@ -245,7 +242,7 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
 #pragma unroll
     for (int cc = 0; cc < NX; ++cc) dP[cc][r] = Qe[cc][r] = 0.0f;
   }
-  const bool xlane = kMF || g < MR;                   // the lane owns an x row
+  const bool xlane = g < MR;                          // the lane owns an x row
   const auto entry_at = [&](int r) {                  // the entry under row r's cursor
     const bool in = cur[r] < run_end(r);
     const uint32_t at = in ? cur[r] - te0 : 0u;
@@ -465,18 +462,10 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
       else if constexpr (kEsc) sc = window_scale(fsc[r]);
       v[r] = kEsc ? fmaf(sc, P[cc][r] + dP[cc][r], Qe[cc][r]) : P[cc][r];
     }
-    const int64_t rbase = row0 + wr(0);
-    if (a.y16) {
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-        if (rbase + r < a.n) a.y16[m * a.ldy + rbase + r] = float_to_bf16_rne(v[r]);
-    } else if (kMF && a.yvec && rbase + 3 < a.n) {
-      *reinterpret_cast<floatx4*>(a.y + m * a.ldy + rbase) = (floatx4){v[0], v[RW > 1 ? 1 : 0], v[RW > 2 ? 2 : 0], v[RW > 3 ? 3 : 0]};
-    } else {
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-        if (rbase + r < a.n) a.y[m * a.ldy + rbase + r] = v[r];
-    }
+    const int64_t row = row0 + wr(0);
+    if (row >= a.n) continue;
+    if (a.y16) a.y16[m * a.ldy + row] = float_to_bf16_rne(v[0]);
+    else a.y[m * a.ldy + row] = v[0];
   }
 }
 
@@ -584,7 +573,6 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
     a.ldy = n;
     a.n = n; a.k = k;
     a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
-    a.yvec = yp.f && (reinterpret_cast<uintptr_t>(yp.f) & 15u) == 0 && n % 4 == 0;
     hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)pl.G), dim3(64 * pl.waves), pl.lds, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
