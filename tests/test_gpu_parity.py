@@ -424,8 +424,9 @@ def test_top1_ties_go_to_the_lowest_row():
 
 
 def test_graph_capture_replays_match_eager():
-    """Split-k GEMMs (workspace), both kernel families, the Q pass and the top-1 entry points
-    captured in one HIP graph on a fresh stream (its workspace is allocated inside the capture):
+    """Split-k GEMMs (workspace), the three kernel families (the streaming kernel with float and
+    bfloat16 outputs), the Q pass and the top-1 entry points captured in one HIP graph on a fresh
+    stream (its workspace is allocated inside the capture):
     every replay, with eager work and cleared outputs in between, equals the eager launches bit
     for bit."""
     w12 = _w12()
@@ -438,13 +439,17 @@ def test_graph_capture_replays_match_eager():
     x16 = to_dev(synth.f32_to_bf16_bits(rng.standard_normal((16, k)).astype(np.float32)))
     outs = [torch.empty((1, n), dtype=torch.float32, device="cuda"),
             torch.empty((16, n), dtype=torch.float32, device="cuda"),
-            torch.empty((16, n), dtype=torch.float32, device="cuda")]
+            torch.empty((16, n), dtype=torch.float32, device="cuda"),
+            torch.empty((16, n), dtype=torch.float32, device="cuda"),
+            torch.empty((16, n), dtype=torch.bfloat16, device="cuda")]
     t1 = (torch.empty(16, dtype=torch.int32, device="cuda"), torch.empty(16, dtype=torch.float32, device="cuda"))
 
     def run():
         w12.gemm(x1, rec, path="gemv", out=outs[0])
         w12.gemm(x16, rec, path="mfma", out=outs[1])
         w12.q8_gemm(x16, rec, out=outs[2])
+        w12.gemm(x16, rec, path="stream", out=outs[3])
+        w12.gemm(x16, rec, path="stream", out=outs[4])
         w12.q8_top1(x16, rec, out=t1)
 
     run()
@@ -466,7 +471,7 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         got = outs + list(t1)
         for i, (a, b) in enumerate(zip(got, want)):
-            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, i)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (rep, i)
 
 
 @pytest.mark.parametrize("n,k,ms", [(256, 512, (1, 4, 16, 33)), (64, 5120, (1, 16, 32)), (4099, 640, (2, 17)),

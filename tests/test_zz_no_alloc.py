@@ -6,7 +6,8 @@ must give bit-identical outputs.  Calls come in a row on one record, each next o
 of x, so a call that read what the previous one left in the scratch would show.  Cases: the
 eight-tile pass (100 rows: x transposed into the scratch), the split-k matrix-core pass (32 rows
 on W [1024, 5120] and [5120, 17408]: partial sums in the scratch), the split-k GEMV (1 row on
-[5120, 17408]) and a GEMV with no scratch; float and bfloat16 outputs; plus the oracle bound on
+[5120, 17408]), a GEMV with no scratch and the streaming kernel (32, 16 and 4 rows on
+[8192, 5120]); float and bfloat16 outputs; plus the oracle bound on
 one case and the up-front refusal of a call that cannot fit.
 """
 import numpy as np
@@ -40,6 +41,7 @@ def _weight(n, k, seed):
 @pytest.mark.parametrize("n,k,ms,seed", [
     (1024, 5120, (100, 32, 1), 1),        # eight-tile pass, split-k matrix cores, GEMV
     (5120, 17408, (32, 1), 2),            # split-k matrix cores, split-k GEMV
+    (8192, 5120, (32, 16, 4), 3),         # the streaming kernel (no scratch)
 ])
 def test_noalloc_matches_gemm(n, k, ms, seed):
     from lossless_bit_weight_02_amd import w12
