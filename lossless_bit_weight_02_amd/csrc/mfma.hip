@@ -108,8 +108,11 @@ void k_mfma(MfmaArgs a) {
   constexpr int kLoadsPerStep = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;
   __shared__ __attribute__((aligned(16))) u32x4 s_x[2][F * 64];
   __shared__ __attribute__((aligned(16))) u32x4 s_dummy[(FW * W > F) ? 64 : 1];   // target of unused fragment loads
-  __shared__ uint32_t s_ecol[kStage ? W : 1][kStage ? kEscCapM : 1];   // per wave: tile escapes
-  __shared__ uint16_t s_eval[kStage ? W : 1][kStage ? kEscCapM : 1];
+  // per wave: the tile's escapes (with kEsc the values are copied in 4-byte pairs from an even
+  // entry, so their copy starts one slot early when the tile's first entry is odd)
+  constexpr int kValCap = kEsc ? kEscCapM + 128 : kEscCapM;
+  __shared__ __attribute__((aligned(16))) uint32_t s_ecol[kStage ? W : 1][kStage ? kEscCapM : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_eval[kStage ? W : 1][kStage ? kValCap : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
@@ -183,7 +186,7 @@ void k_mfma(MfmaArgs a) {
     lds_barrier();                                 // the previous tile no longer reads LDS
 
     // ---- row bounds and window bottoms of the tile's escapes (oldest loads) ----
-    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, t_cnt = 0;
+    uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, t_cnt = 0, t_vsh = 0;
     RowScales<FMT> rsc;
     if constexpr (kScale) {
       const int64_t rg = row0 + 4 * g;
@@ -219,38 +222,60 @@ void k_mfma(MfmaArgs a) {
     }
 
     // ---- the tile's escape list into LDS (its loads go out after the ring's, so the ring is
-    // not held behind the wait for the row bounds; waiting for them waits for the ring, which
-    // the first step needs anyway) ----
+    // not held behind the wait for the row bounds) ----
     if constexpr (kStage) {
       // escape range of the tile: row0's start (lane 0, g = 0) and row0 + 16's (lane 48, g = 3)
       t_e0 = __builtin_amdgcn_readfirstlane(st[0]);
       const uint32_t t_e1 = valid ? (uint32_t)__builtin_amdgcn_readlane((int)st[4], 48) : t_e0;
       const uint32_t cnt = t_e1 - t_e0 < (uint32_t)kEscCapM ? t_e1 - t_e0 : (uint32_t)kEscCapM;
       t_cnt = cnt;
-      const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
-      const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
-      uint32_t ecol[kEscStage / 64], evalv[kEscStage / 64];
+      if constexpr (kEsc) {
+        // global-to-LDS loads: no registers held and no wait here; the end of the range's first
+        // chunk waits for them (they went out before any of its loads).  Columns: 64 entries
+        // per load.  Values: 128 per load as 4-byte pairs from entry t_e0 rounded down to even
+        // (a 4-byte word holding one value of the list lies in the same page as that value).
+        t_vsh = t_e0 & 1u;
+        const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
+        const Rsrc r_val = make_rsrc(a.esc_val + (t_e0 - t_vsh), ((cnt + t_vsh) * 2u + 3u) & ~3u);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kEscStage / 64; ++i) {
-        ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
-        evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
-      }
+        for (int i = 0; i < kEscCapM / 64; ++i)
+          if (64u * i < cnt)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r_col, (__attribute__((address_space(3))) void*)&s_ecol[w][64 * i],
+                                                     4, 4u * (lane + 64 * i), 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < kEscStage / 64; ++i) {
-        s_ecol[w][lane + 64 * i] = ecol[i];
-        s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
-      }
-      // a crowded tile: the rest of the LDS copy
-      for (uint32_t i = kEscStage + (uint32_t)lane; i < t_cnt; i += 64) {
-        s_ecol[w][i] = a.esc_col[t_e0 + i];
-        s_eval[w][i] = a.esc_val[t_e0 + i];
+        for (int i = 0; i < kValCap / 128; ++i)
+          if (128u * i < cnt + t_vsh)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r_val, (__attribute__((address_space(3))) void*)&s_eval[w][128 * i],
+                                                     4, 4u * (lane + 64 * i), 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        const Rsrc r_col = make_rsrc(a.esc_col + t_e0, cnt * 4u);
+        const Rsrc r_val = make_rsrc(a.esc_val + t_e0, cnt * 2u);
+        uint32_t ecol[kEscStage / 64], evalv[kEscStage / 64];
+#pragma unroll
+        for (int i = 0; i < kEscStage / 64; ++i) {
+          ecol[i] = __builtin_amdgcn_raw_buffer_load_b32(r_col, 4u * (lane + 64 * i), 0, 0);
+          evalv[i] = __builtin_amdgcn_raw_buffer_load_b16(r_val, 2u * (lane + 64 * i), 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kEscStage / 64; ++i) {
+          s_ecol[w][lane + 64 * i] = ecol[i];
+          s_eval[w][lane + 64 * i] = (uint16_t)evalv[i];
+        }
+        // a crowded tile: the rest of the LDS copy
+        for (uint32_t i = kEscStage + (uint32_t)lane; i < t_cnt; i += 64) {
+          s_ecol[w][i] = a.esc_col[t_e0 + i];
+          s_eval[w][i] = a.esc_val[t_e0 + i];
+        }
       }
       if (!valid) {
 #pragma unroll
         for (int r = 0; r < 5; ++r) st[r] = t_e0;
       }
     }
-    vm_wait_le<D * kLoadsPerStep>();   // chunk 0 is in LDS
+    // chunk 0 is in LDS (its loads went out before the ring's, and the escape copy after them)
+    vm_wait_le<D * kLoadsPerStep>();
     lds_barrier();
 
     // per row r: cursor (absolute escape index) and the column under it (~0: none in LDS)
@@ -264,34 +289,6 @@ void k_mfma(MfmaArgs a) {
       cur[r] = st[r];
       ncol[r] = 0xFFFFFFFFu;
     }
-    if constexpr (kEsc) {
-      // first escape at or right of col0 of each row (runs are sorted by column): the four
-      // binary searches in lockstep, branch-free, so each halving issues its four LDS reads
-      // together (a run in LDS has at most kEscCapM < 2^9 entries); none for the first range
-      uint32_t hi[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hi[r] = run_end(r);
-#pragma unroll
-      for (int it = 0; it < (col0 > 0 ? 9 : 0); ++it) {
-        uint32_t v[4], mid[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          mid[r] = (cur[r] + hi[r]) >> 1;
-          const uint32_t at = mid[r] - t_e0;
-          v[r] = s_ecol[w][at < (uint32_t)kEscCapM ? at : 0u];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool open = cur[r] < hi[r];
-          const bool right = v[r] < col0;
-          cur[r] = open && right ? mid[r] + 1 : cur[r];
-          hi[r] = open && !right ? mid[r] : hi[r];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
-    }
-
     floatx4 acc[NT];
     float qv[NT][4], sx[NT][4];
 #pragma unroll
@@ -336,6 +333,41 @@ void k_mfma(MfmaArgs a) {
       }
 
       if constexpr (kEsc) {
+        if (c == c0) {
+          // the escape copy has landed: the chunk's steps issued FW fragment loads and S ring
+          // refills after it
+          vm_wait_le<FW + S * kLoadsPerStep>();
+          // first escape at or right of col0 of each row (runs are sorted by column): the four
+          // binary searches in lockstep, branch-free, so each halving issues its four LDS reads
+          // together, until every lane's searches have closed; none for the first range
+          uint32_t hi[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hi[r] = run_end(r);
+          if (col0 > 0) {
+            for (int it = 0; it < 10; ++it) {
+              bool open_any = false;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) open_any |= cur[r] < hi[r];
+              if (!__builtin_amdgcn_ballot_w64(open_any)) break;
+              uint32_t v[4], mid[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                mid[r] = (cur[r] + hi[r]) >> 1;
+                const uint32_t at = mid[r] - t_e0;
+                v[r] = s_ecol[w][at < (uint32_t)kEscCapM ? at : 0u];
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const bool open = cur[r] < hi[r];
+                const bool right = v[r] < col0;
+                cur[r] = open && right ? mid[r] + 1 : cur[r];
+                hi[r] = open && !right ? mid[r] : hi[r];
+              }
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ncol[r] = cur[r] < run_end(r) ? s_ecol[w][cur[r] - t_e0] : 0xFFFFFFFFu;
+        }
         // escapes of rows 4g..4g+3 with a column in this chunk, x from LDS buffer b
         const uint32_t lim = 128u * S * (c + 1);
 #pragma unroll
@@ -343,7 +375,7 @@ void k_mfma(MfmaArgs a) {
           while (ncol[r] < lim) {
             const uint32_t e = cur[r] - t_e0;
             const uint32_t col = ncol[r] - 128u * S * c;
-            const float v = bf16_to_float(s_eval[w][e]);
+            const float v = bf16_to_float(s_eval[w][e + t_vsh]);
 #pragma unroll
             for (int cc = 0; cc < NT; ++cc) {
               const uint32_t at = x_slot(col >> 8, 16u * cc + (uint32_t)r16, (col >> 3) & 31u);
@@ -365,10 +397,11 @@ void k_mfma(MfmaArgs a) {
     if (!valid) continue;
     if constexpr (kEsc) {
       // escapes beyond the LDS copy of a crowded tile, four at a time (their loads issued
-      // together, then the x values they select)
+      // together, then the x values they select).  A walk that stopped inside the copy stopped at
+      // a column past the range (runs are sorted) or at the row's end: nothing is left for it.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        for (uint32_t e = cur[r]; e < st[r + 1]; e += 4) {
+        for (uint32_t e = cur[r] >= lds_end ? cur[r] : st[r + 1]; e < st[r + 1]; e += 4) {
           uint32_t col[4], vb[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
