@@ -79,7 +79,7 @@ extern "C" {
 /* flags for the GEMM calls: which kernel family runs */
 #define W12_PATH_AUTO 0u  /* the family measured fastest for the shape: the streaming kernel for
                            * 3 <= m <= 16 on shapes of at least 1.5 16-row tiles per compute unit
-                           * and k <= 8192, and for 17 <= m <= 32 on at least 2 tiles per unit
+                           * and k <= 8192, and for 17 <= m <= 32 on 2 to 12 tiles per unit
                            * (the dense baseline: at most 6 tiles per unit); otherwise the GEMV
                            * with wave reductions for m <= 2, and for m <= 5 on shapes of at most
                            * 1024 tiles and k <= 8192; bf16 MFMA otherwise */
@@ -87,8 +87,9 @@ extern "C" {
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
                             * tiles, every wave of it an equal share of their 128-column blocks;
-                            * passes of <= 32 rows of x; shapes with at most 16 tiles per compute
-                            * unit, 12 above 16 rows of x; W12_ERR_SHAPE otherwise) */
+                            * passes of <= 32 rows of x; shapes with more tiles than waves on the
+                            * chip in equal row groups, one launch each; W12_ERR_SHAPE when k is
+                            * 2^26 or more or no phase length fits the LDS) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16
  * values the 8-bit view stands for) instead of 0; escapes stay exact */
 #define W12_Q8_MIDPOINT 0x10u

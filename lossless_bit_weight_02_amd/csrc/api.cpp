@@ -109,7 +109,7 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   const bool stream_ok = !silu && w12::stream_fits(dinfo, m, n, k);
   if (flags == W12_PATH_STREAM && !stream_ok)
     return fail(silu ? W12_ERR_ARG : W12_ERR_SHAPE, "the streaming kernel does not take this call "
-                "(at most 16 16-row tiles per compute unit, 12 above 16 rows of x; no SiLU epilogue)");
+                "(rows of fewer than 2^26 columns whose x phases fit the LDS; no SiLU epilogue)");
   // The streaming kernel where it measured fastest (us, streaming vs the best other family, on
   // 27B-class shapes, W12): 3..16 rows on shapes of at least 1.5 tiles per CU with rows of at
   // most 8192 columns ([34816, 5120]: 4 rows 46.4 vs 47.7, 8 rows 47.2 vs 47.9, 16 rows 46.8 vs
@@ -118,11 +118,14 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   // 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
   // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
   // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
-  // 55.8, 32 rows 59.5 vs 57.8).
+  // 55.8, 32 rows 59.5 vs 57.8).  Shapes with more tiles than waves on the chip run in row groups
+  // (one launch each): at 16 rows the LM-head-like [152064, 5120] takes 146.5 vs 153.1 (Q pass)
+  // and 197.1 vs 207.7 (exact), at 32 rows 192.5 vs 166.2 and 231.9 vs 220.8, so above 16 rows
+  // only shapes of one group do.
   const int64_t cus = dinfo.cus;
   const bool stream_auto =
       stream_ok && k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
-      ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus));
+      ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus));
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
   const bool use_stream = flags == W12_PATH_STREAM || (flags == W12_PATH_AUTO && stream_auto);
   const bool gemv = !use_stream && (flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto));

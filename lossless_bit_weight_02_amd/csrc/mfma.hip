@@ -742,19 +742,6 @@ static int64_t tail_split_row(const DevInfo& di, int mb, int64_t tiles) {
   return mb <= 32 && full >= 1 && tail > 0 && 2 * tail <= per_round ? full * per_round * kTileRows : 0;
 }
 
-// The record's rows r0 .. n as a record of their own (r0 a multiple of 16; escape offsets stay
-// absolute indices into the escape arrays).
-static Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
-  Planes t = p;
-  if (t.base) t.base += r0;
-  if (t.ae) t.ae += r0 * k;
-  if (t.lo) t.lo += r0 * k / 2;
-  if (t.esc_ptr) t.esc_ptr += r0;
-  if (t.w) t.w += r0 * k;
-  if (t.scale) t.scale += r0;
-  return t;
-}
-
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        YOut y, hipStream_t s, const Scratch& sc) {
   DevInfo di;

@@ -543,11 +543,26 @@ static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, Str
   return found;
 }
 
+// Row groups of a shape with more 16-row tiles than waves on the chip: as few as keep every
+// CU at one tile per wave or fewer, of equal size (whole tiles).
+static int64_t stream_group_rows(const DevInfo& di, int64_t mb, int64_t n) {
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  const int64_t cap = (int64_t)stream_waves(stream_rows(mb)) * di.cus;
+  const int64_t groups = (tiles + cap - 1) / cap;
+  return (tiles + groups - 1) / groups * kTileRows;
+}
+
 bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || k * 32 * 2 >= (int64_t(1) << 32)) return false;
+  if (m < 1 || n < 1 || k * 32 * 2 >= (int64_t(1) << 32)) return false;
   StreamPlan p;
   const int64_t full = m < 32 ? m : 32, tail = (m - 1) % 32 + 1;
-  return stream_plan(di, full, n, k, &p) && stream_plan(di, tail, n, k, &p);
+  for (const int64_t mb : {full, tail}) {
+    const int64_t gr = stream_group_rows(di, mb, n);
+    // the groups' sizes: gr rows, and the rest of n in the last one
+    const int64_t last = n - (n - 1) / gr * gr;
+    if (!stream_plan(di, mb, gr < n ? gr : n, k, &p) || !stream_plan(di, mb, last, k, &p)) return false;
+  }
+  return true;
 }
 
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
@@ -558,24 +573,29 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
   if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int64_t mb = (m - m0) < 32 ? (m - m0) : 32;
-    StreamPlan pl;
-    if (!stream_plan(di, mb, n, k, &pl)) return hipErrorInvalidValue;
-    StreamArgs a;
-    a.x = x + m0 * k;
-    a.mrows = (int)mb;
-    a.base = p.base; a.ae = p.ae; a.lo = p.lo;
-    a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
-    a.w = p.w;
-    a.scale = p.scale;
-    const YOut yp = y + m0 * n;
-    a.y = yp.f;
-    a.y16 = yp.h;
-    a.ldy = n;
-    a.n = n; a.k = k;
-    a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
-    hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)pl.G), dim3(64 * pl.waves), pl.lds, s, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    const int64_t gr = stream_group_rows(di, mb, n);
+    for (int64_t r0 = 0; r0 < n; r0 += gr) {
+      const int64_t rows = (n - r0) < gr ? (n - r0) : gr;
+      StreamPlan pl;
+      if (!stream_plan(di, mb, rows, k, &pl)) return hipErrorInvalidValue;
+      const Planes pg = rows_from(p, r0, k);
+      StreamArgs a;
+      a.x = x + m0 * k;
+      a.mrows = (int)mb;
+      a.base = pg.base; a.ae = pg.ae; a.lo = pg.lo;
+      a.esc_ptr = pg.esc_ptr; a.esc_col = pg.esc_col; a.esc_val = pg.esc_val;
+      a.w = pg.w;
+      a.scale = pg.scale;
+      const YOut yp = y + (m0 * n + r0);
+      a.y = yp.f;
+      a.y16 = yp.h;
+      a.ldy = n;
+      a.n = rows; a.k = k;
+      a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
+      hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)pl.G), dim3(64 * pl.waves), pl.lds, s, a);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   return hipSuccess;
 }

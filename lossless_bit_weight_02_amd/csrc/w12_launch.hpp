@@ -97,6 +97,19 @@ struct Planes {
   const float* scale = nullptr; // kFmtI8 only: per-row scale (the codes are in `ae`)
 };
 
+// The record's rows r0 .. n as a record of their own (r0 a multiple of 16; escape offsets stay
+// absolute indices into the escape arrays).
+inline Planes rows_from(const Planes& p, int64_t r0, int64_t k) {
+  Planes t = p;
+  if (t.base) t.base += r0;
+  if (t.ae) t.ae += r0 * k;
+  if (t.lo) t.lo += r0 * k / 2;
+  if (t.esc_ptr) t.esc_ptr += r0;
+  if (t.w) t.w += r0 * k;
+  if (t.scale) t.scale += r0;
+  return t;
+}
+
 // x [m <= 128][k] bfloat16 -> xt [k][16][8], xt[c][r][t] = x[16 t + r][c] (rows past m zero),
 // for the eight-tile GEMM's escapes
 hipError_t launch_x_transpose(const uint16_t* x, int m, int64_t k, uint16_t* xt, hipStream_t s);
@@ -132,8 +145,9 @@ int64_t gemv_k_slice(const DevInfo& di, int mb);
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        YOut y, hipStream_t s, const Scratch& sc);
 // Streaming family (one workgroup per CU owning whole tiles, every wave an equal share of their
-// blocks, x in LDS by k phases): passes of <= 32 rows of x; stream_fits says whether a shape can
-// run it (at most 16 tiles per CU, 12 above 16 rows); no SiLU pairing
+// blocks, x in LDS by k phases): passes of <= 32 rows of x, and shapes with more tiles than one
+// per wave of the chip in equal groups of rows, one launch each; stream_fits says whether a shape
+// can run it; no SiLU pairing
 bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k);
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                          YOut y, hipStream_t s);

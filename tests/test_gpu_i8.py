@@ -157,7 +157,8 @@ def test_i8_top1_and_bf16_out():
 
 def test_i8_full_lm_head():
     """LM head [152064, 5120] at M=16 (the Q-pass config): the copy byte-identical to the oracle's,
-    every output within the bound, top-1 exactly the argmax of the full outputs."""
+    every output within the bound (automatic path and matrix cores), top-1 exactly the argmax of
+    the matrix-core kernel's full outputs (the kernel the top-1 entry point runs)."""
     from tests import oracle_pool
     w12 = _w12()
     w, spec, tid = synth.config_weight("lm_head")
@@ -167,6 +168,7 @@ def test_i8_full_lm_head():
     x_bits = synth.gen_x(16, spec.k, tensor_id=tid)
     x = to_dev(x_bits)
     y = w12.i8_gemm(x, cp).cpu().numpy()
+    y_mf = w12.i8_gemm(x, cp, path="mfma").cpu().numpy()
     idx, val = (t.cpu().numpy() for t in w12.i8_top1(x, cp))
     got = cp.to_numpy()
     ex = oracle_pool.make_pool()
@@ -182,7 +184,8 @@ def test_i8_full_lm_head():
     assert np.array_equal(got["scale"].view(np.uint32), scale.view(np.uint32))
     assert np.array_equal(got["q_s"], q_s)
     check_y(y, y64, absum, "lm_head i8")
-    want = np.argmax(y, axis=1)
+    check_y(y_mf, y64, absum, "lm_head i8 matrix cores")
+    want = np.argmax(y_mf, axis=1)
     assert np.array_equal(idx, want)
-    assert np.array_equal(val.view(np.uint32), y[np.arange(16), want].view(np.uint32))
+    assert np.array_equal(val.view(np.uint32), y_mf[np.arange(16), want].view(np.uint32))
 

@@ -687,12 +687,14 @@ def test_binding_rejects_bad_arguments():
     (4000, 10240, (16,)),                 # 5 phases of 16 blocks
     (1024, 5120, (1, 17, 32)),            # 64 tiles (a k/v projection): each tile over 4 CUs
     (2000, 2048, (33, 40, 64)),           # passes of 32 rows and a ragged last pass
+    (70003, 256, (1, 4, 16, 32)),         # 4376 tiles: two row groups (one launch each), ragged
 ])
 def test_stream_path(n, k, ms):
     """The streaming kernel (W12_PATH_STREAM) on every format, 1..32 rows per pass (x staged in
-    k phases when it does not fit the LDS whole; tiles shared by neighbouring CUs added through the
-    workspace), against the oracle; bfloat16 outputs the rounding of the float outputs; a second
-    call gives the same bits (the shared tiles' sums are added in a fixed order)."""
+    k phases when it does not fit the LDS whole; a tile's blocks shared by several waves of its CU,
+    their sums added in wave order; shapes with more tiles than waves on the chip in row groups),
+    against the oracle; bfloat16 outputs the rounding of the float outputs; a second call gives the
+    same bits."""
     import torch
     w12 = _w12()
     rng = np.random.default_rng(n + k)
