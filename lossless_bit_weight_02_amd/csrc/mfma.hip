@@ -185,9 +185,17 @@ void k_mfma(MfmaArgs a) {
 
     lds_barrier();                                 // the previous tile no longer reads LDS
 
-    // ---- row bounds and window bottoms of the tile's escapes (oldest loads) ----
     uint32_t st[5] = {0, 0, 0, 0, 0}, t_e0 = 0, t_cnt = 0, t_vsh = 0;
     RowScales<FMT> rsc;
+
+    // ---- the range's first chunk of x, straight into LDS buffer 0 (the oldest loads: the
+    // first barrier waits for them, not for the escape metadata) ----
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FW; ++i) x_fetch_one(c0, 0u, i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- row bounds and window bottoms of the tile's escapes ----
     if constexpr (kScale) {
       const int64_t rg = row0 + 4 * g;
       const auto ptr_at = [&](int64_t r) { return a.esc_ptr[r < a.n ? r : a.n]; };
@@ -197,11 +205,6 @@ void k_mfma(MfmaArgs a) {
       }
       rsc.load(a, rg);
     }
-
-    // ---- the range's first chunk of x, straight into LDS buffer 0 ----
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < FW; ++i) x_fetch_one(c0, 0u, i);
 
     // ---- D virtual steps -D .. -1: the same load pattern as a loop step ----
     // (buffers over the range's blocks only: the ring's refills past the range read zeros)
@@ -274,7 +277,8 @@ void k_mfma(MfmaArgs a) {
         for (int r = 0; r < 5; ++r) st[r] = t_e0;
       }
     }
-    // chunk 0 is in LDS (its loads went out before the ring's, and the escape copy after them)
+    // chunk 0 is in LDS (its loads went out before the escape metadata and the ring, and the
+    // escape copy after them)
     vm_wait_le<D * kLoadsPerStep>();
     lds_barrier();
 

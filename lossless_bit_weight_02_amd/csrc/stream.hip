@@ -141,24 +141,27 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const bool fin = w < T;
   const int64_t ftile = c + (int64_t)w * G;
   const int64_t row0 = (fin ? ftile : 0) * kTileRows;
-  // escape bounds of the lane's rows: row wr(r) holds entries [st[r], st[r + 1]) (kMF: rows
-  // 4 g .. 4 g + 3 are consecutive, so 5 bounds), and the window bottoms (or 8-bit scales)
+  // escape bounds of the lane's rows: row wr(r) holds entries [st[r], st[r + 1]), and the
+  // window bottoms (or 8-bit scales); loaded after phase 0's x (the first barrier waits for x)
   uint32_t st[RW + 1], fsc[RW];
-#pragma unroll
-  for (int r = 0; r <= RW; ++r) {
-    const int64_t rr = row0 + r16 + r;
-    st[r] = kEsc && fin ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
-  }
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int64_t rr = row0 + wr(r), rc = rr < a.n ? rr : a.n - 1;
-    if constexpr (FMT == kFmtI8) fsc[r] = fin ? __float_as_uint(a.scale[rc]) : 0u;
-    else if constexpr (kEsc) fsc[r] = fin ? a.base[rc] : 0u;
-    else fsc[r] = 0u;
-  }
   // the tile's escape list [te0, te1): its first kSECap entries are copied to this wave's LDS
-  // slot (loaded after phase 0's x, written at the end of phase 0)
-  const uint32_t fte0 = kEsc && fin ? a.esc_ptr[row0] : 0u;
+  // slot (loaded after the ring's first blocks, written at the end of phase 0)
+  uint32_t fte0 = 0;
+  const auto load_meta = [&]() {
+#pragma unroll
+    for (int r = 0; r <= RW; ++r) {
+      const int64_t rr = row0 + r16 + r;
+      st[r] = kEsc && fin ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t rr = row0 + wr(r), rc = rr < a.n ? rr : a.n - 1;
+      if constexpr (FMT == kFmtI8) fsc[r] = fin ? __float_as_uint(a.scale[rc]) : 0u;
+      else if constexpr (kEsc) fsc[r] = fin ? a.base[rc] : 0u;
+      else fsc[r] = 0u;
+    }
+    fte0 = kEsc && fin ? a.esc_ptr[row0] : 0u;
+  };
 
   // ---- x of a phase into LDS buffer `buf`: piece P = (row, 512-column segment), one coalesced
   // 1 KiB read of the row (lane j reads the column word its LDS slot holds), by wave P % W;
@@ -202,6 +205,8 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
 
   issue_x(0, 0);
   __builtin_amdgcn_sched_barrier(0);
+  load_meta();
+  __builtin_amdgcn_sched_barrier(0);
   BlockRegs<FMT> buf[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -213,7 +218,8 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   if (nph > 1) issue_x(1, 1);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- escape entries of the tile to finalise (its bounds arrived before the x loads) ----
+  // ---- escape entries of the tile to finalise (its bounds went out right after phase 0's x,
+  // before the ring, so the wait for x covered them) ----
   const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0);
   uint32_t ldc[kSECap / 64], ldv[kSECap / 64];
   {
