@@ -119,9 +119,9 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
   // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
   // 55.8, 32 rows 59.5 vs 57.8).  Shapes with more tiles than waves on the chip run in row groups
-  // (one launch each): at 16 rows the LM-head-like [152064, 5120] takes 146.5 vs 153.1 (Q pass)
-  // and 197.1 vs 207.7 (exact), at 32 rows 192.5 vs 166.2 and 231.9 vs 220.8, so above 16 rows
-  // only shapes of one group do.
+  // (one launch): the LM-head-like [152064, 5120] takes 137.8 vs 151 (Q pass) and 188.7 vs 213
+  // (exact) at 4 rows, 142.4 vs 149.5 and 198.6 vs 212.9 at 16 rows, but 179.3 vs 165.8 and
+  // 227.9 vs 220.2 at 32 rows, so above 16 rows only shapes of one group do.
   const int64_t cus = dinfo.cus;
   const bool stream_auto =
       stream_ok && k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&

@@ -3,8 +3,10 @@
 //
 // One workgroup of W waves per CU (W = 16 up to 16 rows of x, 12 with 168 VGPRs and a deeper ring
 // for 17..32 rows).  Workgroup c owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so
-// every CU gets the same number of tiles to within one.  Inside the CU the work is dealt by
-// (tile, 128-column block) units rather than by tiles, so no wave idles while others stream:
+// every CU gets the same number of tiles to within one; a shape with more tiles than waves on
+// the chip runs as row groups of such workgroups in one launch (workgroup b: group b / G).
+// Inside the CU the work is dealt by (tile, 128-column block) units rather than by tiles, so no
+// wave idles while others stream:
 //
 // k phases.  x stays in LDS, but 32 rows of a 5120-column x do not fit, so the blocks run in
 // `nph` phases of kbp blocks each.  In phase q the CU's T kbp units (tile-major: blocks
@@ -51,6 +53,8 @@ struct StreamArgs {
   uint32_t rs;            // 16-byte words per x row in LDS: 64 per 512-column segment
   uint32_t xwords;        // 16-byte words of one x buffer: MR rows of rs
   uint32_t eoff;          // 16-byte word offset of the escape copies [W][kSECap] cols, then values
+  int64_t gtiles;         // 16-row tiles per row group (workgroup b takes group b / G)
+  int64_t G;              // workgroups per group
 };
 
 template <int FMT>
@@ -118,12 +122,15 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const uint32_t lane16 = 16u * lane;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t G = gridDim.x, c = blockIdx.x;
-  const int64_t tiles = (a.n + kTileRows - 1) / kTileRows;
+  // row group b / G (its tiles tb .. tb + tiles - 1), workgroup c of it
+  const int64_t G = a.G, c = blockIdx.x % G, tb = (blockIdx.x / G) * a.gtiles;
+  const int64_t tiles_all = (a.n + kTileRows - 1) / kTileRows;
+  const int64_t tiles = tiles_all - tb < a.gtiles ? tiles_all - tb : a.gtiles;
+  if (c >= tiles) return;                            // a last group with fewer tiles than G
   const uint32_t nkb = (uint32_t)(a.k / kTileCols);
   const uint32_t kbp = a.kbp;
   const int nph = a.nph;
-  const int T = (int)((tiles - c + G - 1) / G);     // tiles c + j G, j < T (the grid keeps c < tiles)
+  const int T = (int)((tiles - c + G - 1) / G);     // tiles tb + c + j G, j < T
   const uint32_t U = (uint32_t)T * kbp;              // units per phase of the CU
   const auto rstart = [&](int wv) { return (uint32_t)(((uint64_t)wv * U) / W); };
   const uint32_t r0 = rstart(w), r1 = rstart(w + 1);
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const auto wr = [&](int r) { return r16 + r; };
   const auto xm = [&](int i) { return g + 4 * i; };
   const bool fin = w < T;
-  const int64_t ftile = c + (int64_t)w * G;
+  const int64_t ftile = tb + c + (int64_t)w * G;
   const int64_t row0 = (fin ? ftile : 0) * kTileRows;
   // escape bounds of the lane's rows: row wr(r) holds entries [st[r], st[r + 1]), and the
   // window bottoms (or 8-bit scales); loaded after phase 0's x (the first barrier waits for x)
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   };
   const auto load_next = [&](BlockRegs<FMT>& r) {
     const bool have = rp < (uint32_t)nph && L > 0;
-    load_block<FMT>(stream_rsrc<FMT>(a, c + (int64_t)rt * G, have, nkb), have ? rp * kbp + rk : ~0u, lane16, r);
+    load_block<FMT>(stream_rsrc<FMT>(a, tb + c + (int64_t)rt * G, have, nkb), have ? rp * kbp + rk : ~0u, lane16, r);
     advance(rp, rt, rk, ri);
   };
 
@@ -550,7 +557,9 @@ static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, Str
 }
 
 // Row groups of a shape with more 16-row tiles than waves on the chip: as few as keep every
-// CU at one tile per wave or fewer, of equal size (whole tiles).
+// CU at one tile per wave or fewer, of equal size (whole tiles).  One launch runs them all,
+// group after group in workgroup order, so a CU that finishes its workgroup of one group takes
+// one of the next without waiting for a kernel boundary.
 static int64_t stream_group_rows(const DevInfo& di, int64_t mb, int64_t n) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   const int64_t cap = (int64_t)stream_waves(stream_rows(mb)) * di.cus;
@@ -564,9 +573,8 @@ bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
   const int64_t full = m < 32 ? m : 32, tail = (m - 1) % 32 + 1;
   for (const int64_t mb : {full, tail}) {
     const int64_t gr = stream_group_rows(di, mb, n);
-    // the groups' sizes: gr rows, and the rest of n in the last one
-    const int64_t last = n - (n - 1) / gr * gr;
-    if (!stream_plan(di, mb, gr < n ? gr : n, k, &p) || !stream_plan(di, mb, last, k, &p)) return false;
+    // the plan of a full group (a smaller last group runs the same plan with fewer tiles)
+    if (!stream_plan(di, mb, gr < n ? gr : n, k, &p)) return false;
   }
   return true;
 }
@@ -579,29 +587,28 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
   if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int64_t mb = (m - m0) < 32 ? (m - m0) : 32;
-    const int64_t gr = stream_group_rows(di, mb, n);
-    for (int64_t r0 = 0; r0 < n; r0 += gr) {
-      const int64_t rows = (n - r0) < gr ? (n - r0) : gr;
-      StreamPlan pl;
-      if (!stream_plan(di, mb, rows, k, &pl)) return hipErrorInvalidValue;
-      const Planes pg = rows_from(p, r0, k);
-      StreamArgs a;
-      a.x = x + m0 * k;
-      a.mrows = (int)mb;
-      a.base = pg.base; a.ae = pg.ae; a.lo = pg.lo;
-      a.esc_ptr = pg.esc_ptr; a.esc_col = pg.esc_col; a.esc_val = pg.esc_val;
-      a.w = pg.w;
-      a.scale = pg.scale;
-      const YOut yp = y + (m0 * n + r0);
-      a.y = yp.f;
-      a.y16 = yp.h;
-      a.ldy = n;
-      a.n = rows; a.k = k;
-      a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
-      hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)pl.G), dim3(64 * pl.waves), pl.lds, s, a);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
+    const int64_t gr = stream_group_rows(di, mb, n);   // a multiple of 16
+    StreamPlan pl;
+    if (!stream_plan(di, mb, gr < n ? gr : n, k, &pl)) return hipErrorInvalidValue;
+    const int64_t groups = (n + gr - 1) / gr;
+    StreamArgs a;
+    a.x = x + m0 * k;
+    a.mrows = (int)mb;
+    a.base = p.base; a.ae = p.ae; a.lo = p.lo;
+    a.esc_ptr = p.esc_ptr; a.esc_col = p.esc_col; a.esc_val = p.esc_val;
+    a.w = p.w;
+    a.scale = p.scale;
+    const YOut yp = y + m0 * n;
+    a.y = yp.f;
+    a.y16 = yp.h;
+    a.ldy = n;
+    a.n = n; a.k = k;
+    a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
+    a.gtiles = gr / kTileRows;                         // (the last group may be smaller)
+    a.G = pl.G;
+    hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)(groups * pl.G)), dim3(64 * pl.waves), pl.lds, s, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
