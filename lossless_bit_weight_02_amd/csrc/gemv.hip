@@ -6,8 +6,10 @@
 // a bandwidth-bound matrix-vector stream, not a dense contraction.  Rows are summed across lanes
 // with two cross-lane shuffles.
 //
-// Work split: persistent workgroups of 4 waves.  A workgroup copies its k-slice of x into LDS
-// once.  A wave owns one 16-row tile of the tiled plane storage (see w12_device.hpp) at a time
+// Work split: workgroups of 4 waves, one per pass of tiles (a workgroup loops over several
+// passes only in the split-k launch below, whose grid is the resident slots).  A workgroup copies
+// its k-slice of x into LDS.  A wave owns one 16-row tile of the tiled plane storage (see
+// w12_device.hpp) at a time
 // and, with KS > 1, only every KS-th 128-column block of it (the KS waves of a tile are in the same
 // workgroup and add their partial sums through LDS in a fixed order).  Lane l = r + 16g works on
 // row r, columns 32g..32g+31 of each block: its AE (2 x 128-bit) and B (1 x 128-bit) loads are
@@ -436,8 +438,12 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
       continue;
     }
     // one range per launch: later slices add to y in slice order (bfloat16 output over several
-    // slices: they add in float in the workspace, then a one-range reduce rounds them into y)
-    int64_t groups = passes < slots ? passes : slots;
+    // slices: they add in float in the workspace, then a one-range reduce rounds them into y).
+    // One workgroup per tile pass, not a persistent grid of the resident slots: the hardware
+    // starts each further workgroup on the first CU with a free slot, so CUs that finish early
+    // take more tiles (gate+up [34816, 5120] at one row: 44.6 -> 43.6 us on one box, 43.0 ->
+    // 42.3 on another; the LM-head-like [152064, 5120]: 173.6 -> 166.8 us).
+    const int64_t groups = passes;
     const YOut yp = y + m0 * n;
     float* acc32 = nullptr;
     if ((yp.h || yp.silu) && k > slice) {
