@@ -328,43 +328,52 @@ __global__ __launch_bounds__(64 * NW) void k_gemv(GemvArgs a) {
 typedef void (*GemvKernel)(GemvArgs);
 
 // Blocks in flight per wave (D), k-split per tile (KS) and waves per workgroup (NW), by rows of
-// x: 1-2 rows split the blocks of a tile over all kNWSmall waves of the workgroup (more waves in
-// flight per tile), 3-4 over 2 of 4, 5-8 keep one wave per tile.
+// x: 1-2 rows split the blocks of a tile over all waves of the workgroup (more waves in flight
+// per tile), 3-4 over 2 of 4, 5-8 keep one wave per tile.
 constexpr int kNWSmall = 4;
+// Shapes of at most one tile per CU at 1-2 rows (a layer's k and v projections): 8 waves per
+// tile, so the blocks in flight per tile double (us, [1024, 5120], 4 / 8 waves: W12 6.57 / 6.23
+// at one row, 7.77 / 6.74 at two; Q8 6.11 / 5.43; the dense baseline 5.69 / 5.94 at one row and
+// 6.64 / 6.17 at two, so it keeps 4 waves at one row).  More tiles: 8 waves lose ([5120, 5120]:
+// W12 11.05 / 11.86 us).
+constexpr int kNWFew = 8;
+static bool few_tiles(Fmt f, int m, int64_t tiles, const DevInfo& di) {
+  return m <= 2 && tiles <= di.cus && (f != kFmtBF16 || m == 2);
+}
 template <int FMT, int M>
-static GemvKernel pick_m() {
-  if constexpr (M <= 2) return k_gemv<FMT, M, 3, kNWSmall, kNWSmall>;
+static GemvKernel pick_m(bool few) {
+  if constexpr (M <= 2) return few ? k_gemv<FMT, M, 3, kNWFew, kNWFew> : k_gemv<FMT, M, 3, kNWSmall, kNWSmall>;
   else if constexpr (M <= 4) return k_gemv<FMT, M, 4, 2, 4>;
   else return k_gemv<FMT, M, 4, 1, 4>;
 }
-static int ks_for(int m) { return m <= 2 ? kNWSmall : m <= 4 ? 2 : 1; }
-static int nw_for(int m) { return m <= 2 ? kNWSmall : 4; }
+static int ks_for(int m, bool few) { return m <= 2 ? (few ? kNWFew : kNWSmall) : m <= 4 ? 2 : 1; }
+static int nw_for(int m, bool few) { return m <= 2 ? (few ? kNWFew : kNWSmall) : 4; }
 
 template <int FMT>
-static GemvKernel pick(int m) {
+static GemvKernel pick(int m, bool few) {
   switch (m) {
-    case 1: return pick_m<FMT, 1>();
-    case 2: return pick_m<FMT, 2>();
-    case 3: return pick_m<FMT, 3>();
-    case 4: return pick_m<FMT, 4>();
-    case 5: return pick_m<FMT, 5>();
-    case 6: return pick_m<FMT, 6>();
-    case 7: return pick_m<FMT, 7>();
-    default: return pick_m<FMT, 8>();
+    case 1: return pick_m<FMT, 1>(few);
+    case 2: return pick_m<FMT, 2>(few);
+    case 3: return pick_m<FMT, 3>(few);
+    case 4: return pick_m<FMT, 4>(few);
+    case 5: return pick_m<FMT, 5>(few);
+    case 6: return pick_m<FMT, 6>(few);
+    case 7: return pick_m<FMT, 7>(few);
+    default: return pick_m<FMT, 8>(few);
   }
 }
 
-static GemvKernel pick_kernel(Fmt f, int m) {
-  if (f == kFmtW12) return pick<kFmtW12>(m);
-  if (f == kFmtQ8) return pick<kFmtQ8>(m);
-  if (f == kFmtQ8M) return pick<kFmtQ8M>(m);
-  if (f == kFmtI8) return pick<kFmtI8>(m);
-  return pick<kFmtBF16>(m);
+static GemvKernel pick_kernel(Fmt f, int m, bool few) {
+  if (f == kFmtW12) return pick<kFmtW12>(m, few);
+  if (f == kFmtQ8) return pick<kFmtQ8>(m, few);
+  if (f == kFmtQ8M) return pick<kFmtQ8M>(m, few);
+  if (f == kFmtI8) return pick<kFmtI8>(m, few);
+  return pick<kFmtBF16>(m, few);
 }
 
 int64_t gemv_k_slice(const DevInfo& di, int mb) {
   // longest k range whose x copy fits the LDS budget (2*m*k <= 80 KiB: the whole row)
-  const int64_t red_bytes = (int64_t)4 * mb * 64 * 4;
+  const int64_t red_bytes = (int64_t)kNWFew * mb * 64 * 4;
   int64_t budget = 81920;
   if (budget > di.max_lds - red_bytes) budget = di.max_lds - red_bytes;
   int64_t slice = (budget / (2 * mb)) / kTileCols * kTileCols;
@@ -380,8 +389,9 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   const int64_t nkb = k / kTileCols;
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int mb = (int)((m - m0) < 8 ? (m - m0) : 8);
-    GemvKernel kern = pick_kernel(f, mb);
-    const int ks = ks_for(mb), nw = nw_for(mb);
+    const bool few = few_tiles(f, mb, tiles, di);
+    GemvKernel kern = pick_kernel(f, mb, few);
+    const int ks = ks_for(mb, few), nw = nw_for(mb, few);
     const int64_t tpb = nw / ks;
     const int64_t passes = (tiles + tpb - 1) / tpb;
     int64_t slice = gemv_k_slice(di, mb);
