@@ -13,8 +13,9 @@ Infinity Cache):
   cached read of 512 MiB (writes back the dirty lines the encoder and decoder left in the
   caches; the streaming kernels' non-temporal loads do not, and a GEMM launched right after the
   decoder pays several microseconds for that write-back) -> read probe over 2 GiB (measured
-  ceiling) -> exact W12 GEMM M=1 (GEMV) x 2R -> exact W12 GEMM M=32 (MFMA) x R -> Q-pass GEMM on
-  the 8-bit view M=16 x R -> same-build BF16 GEMM M=1 x 2R and M=32 x R.
+  ceiling) -> exact W12 GEMM M=1 (GEMV) x 2R -> exact W12 GEMM M=32 x R -> Q-pass GEMM on the
+  8-bit view M=16 x R -> same-build BF16 GEMM M=1 x 2R and M=32 x R (M = 16 and 32 on the
+  automatic path: the streaming kernel for W12 and Q8, the matrix cores for BF16).
 Each op's back-to-back launches are bracketed by one pair of HIP events on the stream they run
 on; the per-launch time is the elapsed time / launches (the M=1 groups launch every copy twice,
 so the gap around an event pair weighs less).
@@ -637,10 +638,10 @@ def main():
         ("cache_flush", 1, lambda r: flush_buf.sum()),
         ("read_probe", 1, lambda r: w12.read_probe(probe_buf, sink)),
         ("w12_m1", 2 * rot, lambda r: w12.gemm(x1, recs[r % rot], path="gemv", out=y1)),
-        ("w12_m32", rot, lambda r: w12.gemm(x32, recs[r], path="mfma", out=y32)),
-        ("q8_m16", rot, lambda r: w12.q8_gemm(x16, recs[r], path="mfma", out=y16)),
+        ("w12_m32", rot, lambda r: w12.gemm(x32, recs[r], out=y32)),
+        ("q8_m16", rot, lambda r: w12.q8_gemm(x16, recs[r], out=y16)),
         ("bf16_m1", 2 * rot, lambda r: w12.bf16_gemm(x1, btiles[r % rot], path="gemv", out=yb1)),
-        ("bf16_m32", rot, lambda r: w12.bf16_gemm(x32, btiles[r], path="mfma", out=yb32)),
+        ("bf16_m32", rot, lambda r: w12.bf16_gemm(x32, btiles[r], out=yb32)),
     ]
 
     def step(evs=None):
