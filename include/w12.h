@@ -42,7 +42,8 @@
  *     128) rows there (k x 256 bytes; with k > 262144 the passes stay at 64 rows and need none).
  *     The buffer belongs to the (device, stream) pair, is allocated with hipMalloc on the first
  *     such call on that stream (also while the stream is being captured into a graph: the
- *     allocation is made under the relaxed capture mode) and is kept until the process ends.
+ *     allocation is made under the relaxed capture mode) and is kept until the process ends
+ *     or w12_release_workspace(stream).
  *     Calls on one stream are ordered by the stream; a captured graph uses the buffer of the
  *     stream it was captured on, so replaying it concurrently with other GEMM calls on that
  *     stream races.  Whether a shape splits depends only on the shape and the device, so
@@ -305,6 +306,17 @@ int w12_bf16_to_tiles(const uint16_t *w, int64_t n, int64_t k, uint16_t *out, vo
  * checksum to `sink` (device, at least 4096 u32).  Measures the achievable HBM read rate.
  */
 int w12_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, void *stream);
+
+/*
+ * w12_release_workspace -- frees the GEMM workspace of (current device, `stream`), if the
+ * library allocated one (see the conventions above), for callers that create and destroy
+ * streams (per request or per thread): without it a destroyed stream's 64 MiB stay allocated
+ * until the process ends.  Waits for the stream's work first (hipStreamSynchronize), then frees
+ * the buffer; a later GEMM call on the stream allocates a new one.  Graphs captured on the
+ * stream still point at the freed buffer: do not replay them after this call.  Returns W12_OK
+ * whether or not there was a buffer; not for use while `stream` is being captured.
+ */
+int w12_release_workspace(void *stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char *w12_last_error(void);

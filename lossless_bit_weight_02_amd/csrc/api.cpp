@@ -183,19 +183,24 @@ hipError_t dev_info(DevInfo* out) {
   return hipSuccess;
 }
 
+namespace {
+struct WsEntry {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+};
+std::mutex ws_mu;
+std::vector<WsEntry> ws_table;   // the workspaces, one per (device, stream)
+}  // namespace
+
 hipError_t workspace(hipStream_t s, float** out) {
-  struct Entry {
-    int device;
-    hipStream_t stream;
-    void* ptr;
-  };
-  static std::mutex mu;
-  static std::vector<Entry> table;
+  std::mutex& mu = ws_mu;
+  std::vector<WsEntry>& table = ws_table;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& en : table)
+  for (const WsEntry& en : table)
     if (en.device == dev && en.stream == s) {
       *out = static_cast<float*>(en.ptr);
       return hipSuccess;
@@ -211,7 +216,7 @@ hipError_t workspace(hipStream_t s, float** out) {
   hipError_t e2 = hipThreadExchangeStreamCaptureMode(&mode);
   if (e != hipSuccess) return e;
   if (e2 != hipSuccess) return e2;
-  table.push_back(Entry{dev, s, p});
+  table.push_back(WsEntry{dev, s, p});
   *out = static_cast<float*>(p);
   return hipSuccess;
 }
@@ -248,6 +253,29 @@ w12::Planes planes_i8(const w12_i8* cp, const w12_weight* wt) {
 }  // namespace
 
 extern "C" {
+
+int w12_release_workspace(void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(w12::ws_mu);
+    for (size_t i = 0; i < w12::ws_table.size(); ++i)
+      if (w12::ws_table[i].device == dev && w12::ws_table[i].stream == s) {
+        p = w12::ws_table[i].ptr;
+        w12::ws_table.erase(w12::ws_table.begin() + (ptrdiff_t)i);
+        break;
+      }
+  }
+  if (!p) return W12_OK;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  e = hipFree(p);
+  if (e != hipSuccess) return hip_fail(e, "hipFree");
+  return W12_OK;
+}
 
 int w12_abi_version(void) { return W12_ABI_VERSION; }
 

@@ -53,6 +53,7 @@ _lock = threading.Lock()
 # name -> (restype, argtypes)
 EXPORTS = {
     "w12_abi_version": (ctypes.c_int, []),
+    "w12_release_workspace": (ctypes.c_int, [ctypes.c_void_p]),
     "w12_last_error": (ctypes.c_char_p, []),
     "w12_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(_W12Weight),
                                   ctypes.POINTER(ctypes.c_uint64), ctypes.c_void_p]),
@@ -499,3 +500,13 @@ def read_probe(buf: torch.Tensor, sink: torch.Tensor | None = None):
     _check(lib().w12_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                 _stream_handle(buf.device)))
     return sink
+
+
+def release_workspace(stream: "torch.cuda.Stream | None" = None, device=None):
+    """Free the library's GEMM workspace of ``stream`` (default: the current stream of
+    ``device``) on its device; waits for the stream's work first.  A later GEMM call on the
+    stream allocates a new one."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    with torch.cuda.device(stream.device):
+        _check(lib().w12_release_workspace(stream.cuda_stream))

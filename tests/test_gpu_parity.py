@@ -755,3 +755,30 @@ def test_stream_one_hot_and_special_values():
     y = w12.gemm(to_dev(x), rec2, path="stream").cpu().numpy()
     assert np.all(np.isinf(y[:, 7])) and np.all(np.isnan(y[:, 8]))
     check_gemm(np.delete(y, [7, 8], axis=1), x, np.delete(w2, [7, 8], axis=0), "stream special")
+
+
+def test_release_workspace_on_a_side_stream():
+    """w12_release_workspace: a split-k GEMM on a stream of its own (W [1024, 2048] at 32 rows
+    splits k, so its partial sums use that stream's workspace) is right before and after the
+    stream's workspace is freed (the next call allocates a new one); releasing a stream that has
+    none, or twice, is a no-op."""
+    w12 = _w12()
+    rng = np.random.default_rng(77)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((1024, 2048)) * 0.02).astype(np.float32))
+    w[rng.random(w.shape) < 0.01] = 0
+    x = synth.f32_to_bf16_bits(rng.standard_normal((32, 2048)).astype(np.float32))
+    rec = w12.encode(to_dev(w))
+    xd = to_dev(x)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        with torch.cuda.stream(side):
+            say(f"side-stream split GEMM, call {rep}")
+            y = w12.gemm(xd, rec, path="mfma")
+        side.synchronize()
+        check_gemm(y.cpu().numpy(), x, w, f"side stream call {rep}")
+        w12.release_workspace(side)
+        w12.release_workspace(side)
+    fresh = torch.cuda.Stream()
+    w12.release_workspace(fresh)
+    torch.cuda.synchronize()
