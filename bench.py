@@ -705,7 +705,7 @@ def main():
             row = {}
             # the streaming kernel up to 32 rows; above 64 rows only the matrix-core path (passes of
             # up to 128 rows, each reading W once)
-            paths = ("gemv", "mfma", "stream") if m <= 32 else ("gemv", "mfma") if m <= 64 else ("mfma",)
+            paths = ("gemv", "mfma", "stream") if m <= 64 else ("mfma",)
             for path in paths:
                 for fmt in ("w12", "bf16"):
                     def run(r, fmt=fmt, path=path):

@@ -80,15 +80,17 @@ extern "C" {
 /* flags for the GEMM calls: which kernel family runs */
 #define W12_PATH_AUTO 0u  /* the family measured fastest for the shape: the streaming kernel for
                            * 3 <= m <= 16 on shapes of at least 1.5 16-row tiles per compute unit
-                           * and k <= 8192, and for 17 <= m <= 32 on 2 to 12 tiles per unit
-                           * (the dense baseline: at most 6 tiles per unit); otherwise the GEMV
+                           * and k <= 8192, for 17 <= m <= 32 on 2 to 12 tiles per unit
+                           * (the dense baseline: at most 6 tiles per unit), and for
+                           * 33 <= m <= 64 on at most 3 tiles per unit (the dense baseline:
+                           * 5); otherwise the GEMV
                            * with wave reductions for m <= 2, and for m <= 5 on shapes of at most
                            * 1024 tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
                             * tiles, every wave of it an equal share of their 128-column blocks;
-                            * passes of <= 32 rows of x; shapes with more tiles than waves on the
+                            * passes of <= 64 rows of x; shapes with more tiles than waves on the
                             * chip in equal row groups, one launch each; W12_ERR_SHAPE when k is
                             * 2^26 or more or no phase length fits the LDS) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16

@@ -122,10 +122,18 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   // (one launch): the LM-head-like [152064, 5120] takes 137.8 vs 151 (Q pass) and 188.7 vs 213
   // (exact) at 4 rows, 142.4 vs 149.5 and 198.6 vs 212.9 at 16 rows, but 179.3 vs 165.8 and
   // 227.9 vs 220.2 at 32 rows, so above 16 rows only shapes of one group do.
+  // At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
+  // the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64
+  // rows: [1024, 5120] 28.2 vs 46.7, [6144, 5120] 37.1 vs 48.7, [5120, 6144] 41.0 vs 63.5,
+  // [5120, 17408] 98.0 vs 209.0, [12288, 5120] 44.8 vs 51.0; at 40 rows the last ties, 44.5 vs
+  // 44.1), the dense baseline up to 5 ([17408, 5120]: 40.7 vs 47.7); above that the matrix cores
+  // ([34816, 5120]: W12 70.9 vs 100.9, [17408, 5120] 55.4 vs 56.6).
   const int64_t cus = dinfo.cus;
   const bool stream_auto =
-      stream_ok && k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
-      ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus));
+      stream_ok &&
+      ((k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
+        ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus))) ||
+       (m >= 33 && m <= 64 && tiles <= (f == w12::kFmtBF16 ? 5 : 3) * cus));
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
   const bool use_stream = flags == W12_PATH_STREAM || (flags == W12_PATH_AUTO && stream_auto);
   const bool gemv = !use_stream && (flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto));

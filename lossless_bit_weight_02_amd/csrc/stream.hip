@@ -1,10 +1,11 @@
-// Streaming GEMM for 1..32 rows of x, y[m][n] = sum_k x[m][k] W[n][k], with every wave of a CU
+// Streaming GEMM for 1..64 rows of x, y[m][n] = sum_k x[m][k] W[n][k], with every wave of a CU
 // streaming the same number of weight blocks.
 //
 // One workgroup of W waves per CU (W = 16 up to 16 rows of x, 12 with 168 VGPRs and a deeper ring
-// for 17..32 rows).  Workgroup c owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so
-// every CU gets the same number of tiles to within one; a shape with more tiles than waves on
-// the chip runs as row groups of such workgroups in one launch (workgroup b: group b / G).
+// for 17..32 rows, 8 with 256 VGPRs for 33..64, whose ranges may touch three tiles).  Workgroup c
+// owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so every CU gets the same number
+// of tiles to within one; a shape with more tiles than waves on the chip runs as row groups of
+// such workgroups in one launch (workgroup b: group b / G).
 // Inside the CU the work is dealt by (tile, 128-column block) units rather than by tiles, so no
 // wave idles while others stream:
 //
@@ -17,20 +18,21 @@
 // phase change costs one barrier; the weight ring (D blocks in flight per wave) runs on across
 // phases.
 //
-// Partial sums.  A wave's range touches at most two tiles; it keeps one running sum per touched
-// tile in registers over all phases and adds them into LDS at the end.  Tile j of the CU is then
-// finalised by wave j % W: the partial sums of the waves that touch it, added in wave order
-// (deterministic), plus its escape corrections, collected during each phase from x in LDS.
+// Partial sums.  A wave's range touches at most two tiles (three at 64 rows); it keeps one running
+// sum per touched tile in registers over all phases and adds them into LDS at the end.  Tile j of
+// the CU is then finalised by wave j: the partial sums of the waves that touch it, added in wave
+// order (deterministic), plus its escape corrections, collected during each phase from x in LDS.
 //
 // Decode and arithmetic as in the GEMV: 1-2 rows by dot2 (lane r16 + 16 g computes row r16 over
-// columns 32 g .. +31 of each block); 3-32 rows on the matrix cores, the decoded block as operand
-// A of v_mfma_f32_16x16x32_bf16 (one or two 16-row activation tiles as operand B, read from LDS).
+// columns 32 g .. +31 of each block); 3-64 rows on the matrix cores, the decoded block as operand
+// A of v_mfma_f32_16x16x32_bf16 (one to four 16-row activation tiles as operand B, read from LDS).
 // Escapes as everywhere: y = 2^(base - 112) (P - 2^-15 sum_esc x) + sum_esc x v.
 #include "block.hpp"
 
 namespace w12 {
 
-constexpr int kSECap = 128;     // escapes of a finalised tile copied to LDS (more: read at the end)
+constexpr int kSECap = 384;     // escapes of a finalised tile copied to LDS (more: read at the end)
+constexpr int kSEVal = kSECap + 128;   // value slots: copied as 4-byte pairs from an even entry
 constexpr int kSPieces = 80;    // x pieces (1 KiB) per phase buffer at most
 
 struct StreamArgs {
@@ -52,7 +54,8 @@ struct StreamArgs {
   int nph;                // phases
   uint32_t rs;            // 16-byte words per x row in LDS: 64 per 512-column segment
   uint32_t xwords;        // 16-byte words of one x buffer: MR rows of rs
-  uint32_t eoff;          // 16-byte word offset of the escape copies [W][kSECap] cols, then values
+  uint32_t eoff;          // 16-byte word offset of the escape copies: [W][kSECap] columns, then
+                          // [W][kSEVal] values
   int64_t gtiles;         // 16-row tiles per row group (workgroup b takes group b / G)
   int64_t G;              // workgroups per group
 };
@@ -98,8 +101,8 @@ __device__ __forceinline__ void s_vm_wait_steps(uint32_t L) {
 
 template <int W>
 struct StreamShape {
-  static_assert(W == 12 || W == 16, "12 or 16 waves per workgroup");
-  static constexpr int D = W == 12 ? 4 : 3;     // blocks in flight per wave
+  static_assert(W == 8 || W == 12 || W == 16, "8, 12 or 16 waves per workgroup");
+  static constexpr int D = W == 16 ? 3 : 4;     // blocks in flight per wave
   static constexpr int FW = (kSPieces + W - 1) / W;   // x pieces a wave may load per phase
 };
 
@@ -107,9 +110,9 @@ struct StreamShape {
 template <int FMT, int MR, int W>
 __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   constexpr int D = StreamShape<W>::D, FW = StreamShape<W>::FW;
-  constexpr int SL = 2;                              // tiles one wave's range touches at most
-  constexpr bool kMF = MR > 2;                       // matrix cores for 3..32 rows
-  constexpr int NT = MR > 16 ? 2 : 1;                // 16-row activation tiles
+  constexpr int SL = MR > 32 ? 3 : 2;                // tiles one wave's range touches at most
+  constexpr bool kMF = MR > 2;                       // matrix cores for 3..64 rows
+  constexpr int NT = (MR + 15) / 16;                 // 16-row activation tiles
   constexpr int NACC = kMF ? 4 * NT : MR;            // running sums per lane
   constexpr int MP = MR + 1;                         // row stride of the LDS partial sums
   constexpr bool kEsc = FMT != kFmtBF16;
@@ -227,20 +230,33 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
 
   // ---- escape entries of the tile to finalise (its bounds went out right after phase 0's x,
   // before the ring, so the wait for x covered them) ----
+  // The copy goes straight to the wave's LDS slot with global-to-LDS loads (no registers held;
+  // the first phase's escape walk waits for them): columns 64 per load, values 128 per load as
+  // 4-byte pairs from the even entry at or below te0 (a 4-byte word holding one value of the list
+  // lies in the same page as that value), so the value copy starts one slot early for an odd te0.
   const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0);
-  uint32_t ldc[kSECap / 64], ldv[kSECap / 64];
-  {
+  const uint32_t tvsh = te0 & 1u;
+  uint32_t* s_ecol = reinterpret_cast<uint32_t*>(lds + a.eoff) + w * kSECap;   // this wave's copy
+  uint16_t* s_evalb = reinterpret_cast<uint16_t*>(lds + a.eoff + W * kSECap / 4) + w * kSEVal;
+  uint16_t* s_eval = s_evalb + tvsh;                  // entry te0 + i at s_eval[i]
+  if (kEsc && fin) {
     const uint32_t te1 = (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 15);   // row0 + 16
     const uint32_t cnt = te1 - te0 < (uint32_t)kSECap ? te1 - te0 : (uint32_t)kSECap;
-    const Rsrc rc = make_rsrc(a.esc_col + te0, cnt * 4u), rv = make_rsrc(a.esc_val + te0, cnt * 2u);
+    const Rsrc rc = make_rsrc(a.esc_col + te0, cnt * 4u);
+    const Rsrc rv = make_rsrc(a.esc_val + (te0 - tvsh), ((cnt + tvsh) * 2u + 3u) & ~3u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kSECap / 64; ++i) {
-      ldc[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, 4u * (lane + 64 * i), 0, 0);
-      ldv[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, 2u * (lane + 64 * i), 0, 0);
-    }
+    for (int i = 0; i < kSECap / 64; ++i)
+      if (64u * i < cnt)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(s_ecol + 64 * i), 4,
+                                                 4u * (lane + 64 * i), 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kSEVal / 128; ++i)
+      if (128u * i < cnt + tvsh)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(s_evalb + 128 * i), 4,
+                                                 4u * (lane + 64 * i), 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  uint32_t* s_ecol = reinterpret_cast<uint32_t*>(lds + a.eoff) + w * kSECap;   // this wave's copy
-  uint16_t* s_eval = reinterpret_cast<uint16_t*>(lds + a.eoff + W * kSECap / 4) + w * kSECap;
   const uint32_t lds_end = te0 + kSECap;              // entries past this stay in memory
   const auto run_end = [&](int r) { return st[r + 1] < lds_end ? st[r + 1] : lds_end; };
   // escape corrections of the finalised tile: dP (placeholders), Qe (values); per row a cursor
@@ -269,14 +285,10 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
     if constexpr (kEsc) {
       if (!fin) return;
       if (ph == 0) {
-#pragma unroll
-        for (int i = 0; i < kSECap / 64; ++i) {
-          s_ecol[lane + 64 * i] = ldc[i];
-          s_eval[lane + 64 * i] = (uint16_t)ldv[i];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        // the escape copy has landed: it went out before every refill of this phase, so waiting
+        // until at most min(L, D) refills are outstanding covers it (the phase change waits the
+        // same for the next phase's x)
+        s_vm_wait_steps<D, kLPS>(L);
 #pragma unroll
         for (int r = 0; r < RW; ++r) entry_at(r);
       }
@@ -495,7 +507,8 @@ static StreamKernel stream_pick(int mr) {
     case 4: return k_stream<FMT, 4, 16>;
     case 8: return k_stream<FMT, 8, 16>;
     case 16: return k_stream<FMT, 16, 16>;
-    default: return k_stream<FMT, 32, 12>;
+    case 32: return k_stream<FMT, 32, 12>;
+    default: return k_stream<FMT, 64, 8>;
   }
 }
 
@@ -507,11 +520,16 @@ static StreamKernel stream_kernel(Fmt f, int mr) {
   return stream_pick<kFmtBF16>(mr);
 }
 
-// rows of x the kernel instance for mb rows is built for, and its waves per workgroup
+constexpr int64_t kPassRows = 64;   // rows of x per pass (per weight read)
+
+// rows of x the kernel instance for mb rows is built for, its waves per workgroup (16 of up to
+// 128 VGPRs, 12 of up to 168, 8 of up to 256 for the accumulators of 64 rows) and the tiles one
+// wave's range may touch
 static int stream_rows(int64_t mb) {
-  return mb <= 2 ? (int)mb : mb <= 4 ? 4 : mb <= 8 ? 8 : mb <= 16 ? 16 : 32;
+  return mb <= 2 ? (int)mb : mb <= 4 ? 4 : mb <= 8 ? 8 : mb <= 16 ? 16 : mb <= 32 ? 32 : 64;
 }
-static int stream_waves(int mr) { return mr > 16 ? 12 : 16; }
+static int stream_waves(int mr) { return mr > 32 ? 8 : mr > 16 ? 12 : 16; }
+static int stream_slots(int mr) { return mr > 32 ? 3 : 2; }
 
 struct StreamPlan {
   int mr = 0, waves = 0, nph = 0;
@@ -539,11 +557,12 @@ static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, Str
     const int64_t U = tmax * kbp;
     if (U >= (int64_t(1) << 31)) continue;
     const int64_t lmax = (U + W - 1) / W;
-    if ((lmax - 1) / kbp + 2 > 2) continue;          // a range over at most two tiles
-    const int64_t part = (int64_t)W * 2 * kTileRows * (mr + 1) * 4;
+    const int SL = stream_slots(mr);
+    if ((lmax - 1) / kbp + 2 > SL) continue;         // a range over at most SL tiles
+    const int64_t part = (int64_t)W * SL * kTileRows * (mr + 1) * 4;
     const int64_t xb = (nph > 1 ? 2 : 1) * xwords * 16;
     const int64_t body = ((xb > part ? xb : part) + 15) / 16 * 16;
-    const int64_t lds = body + (int64_t)W * kSECap * 6;   // then the escape copies
+    const int64_t lds = body + (int64_t)W * (kSECap * 4 + kSEVal * 2);   // then the escape copies
     if (lds > di.max_lds) continue;
     const double cost = (double)(lmax * nph) + 0.5 * (double)(nph - 1);
     if (found && cost >= best) continue;
@@ -568,9 +587,9 @@ static int64_t stream_group_rows(const DevInfo& di, int64_t mb, int64_t n) {
 }
 
 bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || n < 1 || k * 32 * 2 >= (int64_t(1) << 32)) return false;
+  if (m < 1 || n < 1 || k * kPassRows * 2 >= (int64_t(1) << 32)) return false;
   StreamPlan p;
-  const int64_t full = m < 32 ? m : 32, tail = (m - 1) % 32 + 1;
+  const int64_t full = m < kPassRows ? m : kPassRows, tail = (m - 1) % kPassRows + 1;
   for (const int64_t mb : {full, tail}) {
     const int64_t gr = stream_group_rows(di, mb, n);
     // the plan of a full group (a smaller last group runs the same plan with fewer tiles)
@@ -585,8 +604,8 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
   if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
-  for (int64_t m0 = 0; m0 < m; m0 += 32) {
-    const int64_t mb = (m - m0) < 32 ? (m - m0) : 32;
+  for (int64_t m0 = 0; m0 < m; m0 += kPassRows) {
+    const int64_t mb = (m - m0) < kPassRows ? (m - m0) : kPassRows;
     const int64_t gr = stream_group_rows(di, mb, n);   // a multiple of 16
     StreamPlan pl;
     if (!stream_plan(di, mb, gr < n ? gr : n, k, &pl)) return hipErrorInvalidValue;

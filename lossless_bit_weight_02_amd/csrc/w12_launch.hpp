@@ -145,7 +145,7 @@ int64_t gemv_k_slice(const DevInfo& di, int mb);
 hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        YOut y, hipStream_t s, const Scratch& sc);
 // Streaming family (one workgroup per CU owning whole tiles, every wave an equal share of their
-// blocks, x in LDS by k phases): passes of <= 32 rows of x, and shapes with more tiles than one
+// blocks, x in LDS by k phases): passes of <= 64 rows of x, and shapes with more tiles than one
 // per wave of the chip in equal groups of rows, one launch each; stream_fits says whether a shape
 // can run it; no SiLU pairing
 bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k);
