@@ -106,7 +106,7 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
     hipError_t e = w12::dev_info(&dinfo);
     if (e != hipSuccess) return hip_fail(e, "device query");
   }
-  const bool stream_ok = !silu && w12::stream_fits(dinfo, m, n, k);
+  const bool stream_ok = !silu && w12::stream_fits(dinfo, f, m, n, k);
   if (flags == W12_PATH_STREAM && !stream_ok)
     return fail(silu ? W12_ERR_ARG : W12_ERR_SHAPE, "the streaming kernel does not take this call "
                 "(rows of fewer than 2^26 columns whose x phases fit the LDS; no SiLU epilogue)");

@@ -31,8 +31,9 @@
 
 namespace w12 {
 
-constexpr int kSECap = 384;     // escapes of a finalised tile copied to LDS (more: read at the end)
-constexpr int kSEVal = kSECap + 128;   // value slots: copied as 4-byte pairs from an even entry
+// escapes of a finalised tile copied to LDS (more: read at the end), with one and with three
+// tiles finalised per wave; value slots 128 more (copied as 4-byte pairs from an even entry)
+constexpr int kSECap = 384, kSECap3 = 128;
 constexpr int kSPieces = 80;    // x pieces (1 KiB) per phase buffer at most
 
 struct StreamArgs {
@@ -54,8 +55,8 @@ struct StreamArgs {
   int nph;                // phases
   uint32_t rs;            // 16-byte words per x row in LDS: 64 per 512-column segment
   uint32_t xwords;        // 16-byte words of one x buffer: MR rows of rs
-  uint32_t eoff;          // 16-byte word offset of the escape copies: [W][kSECap] columns, then
-                          // [W][kSEVal] values
+  uint32_t eoff;          // 16-byte word offset of the escape copies: [W FT][cap] columns, then
+                          // [W FT][cap + 128] values
   int64_t gtiles;         // 16-row tiles per row group (workgroup b takes group b / G)
   int64_t G;              // workgroups per group
 };
@@ -106,16 +107,22 @@ struct StreamShape {
   static constexpr int FW = (kSPieces + W - 1) / W;   // x pieces a wave may load per phase
 };
 
-// MR: rows of x the instance is built for (x rows mrows .. MR - 1 read zeros).
-template <int FMT, int MR, int W>
+// MR: rows of x the instance is built for (x rows mrows .. MR - 1 read zeros).  FT: tiles a wave
+// finalises at most (1: the CU has at most W tiles, whose escapes the waves walk phase by phase
+// from LDS; 3: up to 3 W tiles, so a shape of up to 3 W tiles per CU needs no row groups, with
+// the escapes patched at the end from memory).
+template <int FMT, int MR, int W, int FT>
 __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   constexpr int D = StreamShape<W>::D, FW = StreamShape<W>::FW;
-  constexpr int SL = MR > 32 ? 3 : 2;                // tiles one wave's range touches at most
+  static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16), "FT 3: up to 16 rows, 16 waves");
+  // tiles one wave's range touches at most: its length is at most FT kbp units + 1
+  constexpr int SL = FT == 3 ? 4 : MR > 32 ? 3 : 2;
   constexpr bool kMF = MR > 2;                       // matrix cores for 3..64 rows
   constexpr int NT = (MR + 15) / 16;                 // 16-row activation tiles
   constexpr int NACC = kMF ? 4 * NT : MR;            // running sums per lane
   constexpr int MP = MR + 1;                         // row stride of the LDS partial sums
   constexpr bool kEsc = FMT != kFmtBF16;
+  constexpr int ECAP = FT == 1 ? kSECap : kSECap3, EVAL = ECAP + 128;
   constexpr int kLPS = FMT == kFmtBF16 ? 4 : FMT == kFmtW12 ? 3 : 2;   // loads per ring step
   // LDS: x buffers [2][MR][rs] of 16-byte words; column word c16 (columns 8 c16 .. +7 of the
   // phase) of x row r sits at r * rs + (c16 & ~15) + ((c16 & 15) ^ (r & 15)): the 16 rows an
@@ -142,35 +149,38 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(lds);
   const uint32_t e112 = exp112_pair();
 
-  // ---- the tile this wave finalises (local tile w) ----
-  // Lane layout of the finalisation: lane r16 + 16 g owns weight row r16 and x rows
-  // xm(i) = g + 4 i (i < NX; rows past MR idle), so a lane walks the escapes of one row.
-  constexpr int RW = 1, NX = (MR + 3) / 4;
-  const auto wr = [&](int r) { return r16 + r; };
+  // ---- the tiles this wave finalises: local tiles w + f W, f < FT ----
+  // Lane layout of the finalisation: lane r16 + 16 g owns weight row r16 of each and x rows
+  // xm(i) = g + 4 i (i < NX; rows past MR idle), so a lane walks the escapes of one row per tile.
+  constexpr int NX = (MR + 3) / 4;
   const auto xm = [&](int i) { return g + 4 * i; };
-  const bool fin = w < T;
-  const int64_t ftile = tb + c + (int64_t)w * G;
-  const int64_t row0 = (fin ? ftile : 0) * kTileRows;
-  // escape bounds of the lane's rows: row wr(r) holds entries [st[r], st[r + 1]), and the
-  // window bottoms (or 8-bit scales); loaded after phase 0's x (the first barrier waits for x)
-  uint32_t st[RW + 1], fsc[RW];
-  // the tile's escape list [te0, te1): its first kSECap entries are copied to this wave's LDS
-  // slot (loaded after the ring's first blocks, written at the end of phase 0)
-  uint32_t fte0 = 0;
+  bool fin[FT];
+  int64_t row0[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    fin[f] = w + f * W < T;
+    row0[f] = (fin[f] ? tb + c + (int64_t)(w + f * W) * G : 0) * kTileRows;
+  }
+  // escape bounds of the lane's row r16 of tile f: entries [st[f][0], st[f][1]), and its window
+  // bottom (or 8-bit scale); loaded after phase 0's x (the first barrier waits for x)
+  uint32_t st[FT][2], fsc[FT];
+  // tile f's escape list [te0, te1): its first ECAP entries are copied to this wave's LDS slot f
+  // (loaded after the ring's first blocks, waited for before phase 0's walk)
+  uint32_t fte0[FT];
   const auto load_meta = [&]() {
 #pragma unroll
-    for (int r = 0; r <= RW; ++r) {
-      const int64_t rr = row0 + r16 + r;
-      st[r] = kEsc && fin ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
-    }
+    for (int f = 0; f < FT; ++f) {
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const int64_t rr = row0 + wr(r), rc = rr < a.n ? rr : a.n - 1;
-      if constexpr (FMT == kFmtI8) fsc[r] = fin ? __float_as_uint(a.scale[rc]) : 0u;
-      else if constexpr (kEsc) fsc[r] = fin ? a.base[rc] : 0u;
-      else fsc[r] = 0u;
+      for (int r = 0; r < 2; ++r) {
+        const int64_t rr = row0[f] + r16 + r;
+        st[f][r] = kEsc && fin[f] ? a.esc_ptr[rr < a.n ? rr : a.n] : 0u;
+      }
+      const int64_t rr = row0[f] + r16, rc = rr < a.n ? rr : a.n - 1;
+      if constexpr (FMT == kFmtI8) fsc[f] = fin[f] ? __float_as_uint(a.scale[rc]) : 0u;
+      else if constexpr (kEsc) fsc[f] = fin[f] ? a.base[rc] : 0u;
+      else fsc[f] = 0u;
+      fte0[f] = kEsc && fin[f] ? a.esc_ptr[row0[f]] : 0u;
     }
-    fte0 = kEsc && fin ? a.esc_ptr[row0] : 0u;
   };
 
   // ---- x of a phase into LDS buffer `buf`: piece P = (row, 512-column segment), one coalesced
@@ -228,77 +238,93 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   if (nph > 1) issue_x(1, 1);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- escape entries of the tile to finalise (its bounds went out right after phase 0's x,
+  // ---- escape entries of the tiles to finalise (their bounds went out right after phase 0's x,
   // before the ring, so the wait for x covered them) ----
-  // The copy goes straight to the wave's LDS slot with global-to-LDS loads (no registers held;
+  // The copy goes straight to the wave's LDS slots with global-to-LDS loads (no registers held;
   // the first phase's escape walk waits for them): columns 64 per load, values 128 per load as
   // 4-byte pairs from the even entry at or below te0 (a 4-byte word holding one value of the list
   // lies in the same page as that value), so the value copy starts one slot early for an odd te0.
-  const uint32_t te0 = __builtin_amdgcn_readfirstlane(fte0);
-  const uint32_t tvsh = te0 & 1u;
-  uint32_t* s_ecol = reinterpret_cast<uint32_t*>(lds + a.eoff) + w * kSECap;   // this wave's copy
-  uint16_t* s_evalb = reinterpret_cast<uint16_t*>(lds + a.eoff + W * kSECap / 4) + w * kSEVal;
-  uint16_t* s_eval = s_evalb + tvsh;                  // entry te0 + i at s_eval[i]
-  if (kEsc && fin) {
-    const uint32_t te1 = (uint32_t)__builtin_amdgcn_readlane((int)st[RW], 15);   // row0 + 16
-    const uint32_t cnt = te1 - te0 < (uint32_t)kSECap ? te1 - te0 : (uint32_t)kSECap;
-    const Rsrc rc = make_rsrc(a.esc_col + te0, cnt * 4u);
-    const Rsrc rv = make_rsrc(a.esc_val + (te0 - tvsh), ((cnt + tvsh) * 2u + 3u) & ~3u);
-    __builtin_amdgcn_sched_barrier(0);
+  uint32_t te0[FT], lds_end[FT];
+  uint32_t* s_ecol[FT];
+  uint16_t* s_eval[FT];
 #pragma unroll
-    for (int i = 0; i < kSECap / 64; ++i)
-      if (64u * i < cnt)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(s_ecol + 64 * i), 4,
-                                                 4u * (lane + 64 * i), 0, 0, 0);
+  for (int f = 0; f < FT; ++f) {
+    te0[f] = __builtin_amdgcn_readfirstlane(fte0[f]);
+    const uint32_t tvsh = te0[f] & 1u;
+    const int sl = w * FT + f;                          // this wave's slot f
+    s_ecol[f] = reinterpret_cast<uint32_t*>(lds + a.eoff) + sl * ECAP;
+    uint16_t* s_evalb = reinterpret_cast<uint16_t*>(lds + a.eoff + W * FT * ECAP / 4) + sl * EVAL;
+    s_eval[f] = s_evalb + tvsh;                         // entry te0 + i at s_eval[f][i]
+    lds_end[f] = te0[f] + ECAP;                         // entries past this stay in memory
+    if (kEsc && fin[f]) {
+      const uint32_t te1 = (uint32_t)__builtin_amdgcn_readlane((int)st[f][1], 15);   // row0 + 16
+      const uint32_t cnt = te1 - te0[f] < (uint32_t)ECAP ? te1 - te0[f] : (uint32_t)ECAP;
+      const Rsrc rc = make_rsrc(a.esc_col + te0[f], cnt * 4u);
+      const Rsrc rv = make_rsrc(a.esc_val + (te0[f] - tvsh), ((cnt + tvsh) * 2u + 3u) & ~3u);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kSEVal / 128; ++i)
-      if (128u * i < cnt + tvsh)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(s_evalb + 128 * i), 4,
-                                                 4u * (lane + 64 * i), 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < ECAP / 64; ++i)
+        if (64u * i < cnt)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)(s_ecol[f] + 64 * i), 4,
+                                                   4u * (lane + 64 * i), 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < EVAL / 128; ++i)
+        if (128u * i < cnt + tvsh)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(s_evalb + 128 * i), 4,
+                                                   4u * (lane + 64 * i), 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  const uint32_t lds_end = te0 + kSECap;              // entries past this stay in memory
-  const auto run_end = [&](int r) { return st[r + 1] < lds_end ? st[r + 1] : lds_end; };
-  // escape corrections of the finalised tile: dP (placeholders), Qe (values); per row a cursor
-  // (absolute entry index) with the column and value under it (column ~0: none left in LDS)
-  float dP[NX][RW], Qe[NX][RW];
-  uint32_t cur[RW], ncol[RW], nval[RW];
+  const auto run_end = [&](int f) { return st[f][1] < lds_end[f] ? st[f][1] : lds_end[f]; };
+  // escape corrections: with one tile per wave dP (placeholders) and Qe (values) apart, with three
+  // Qe[f] alone, the placeholder terms scaled into it (x v - x 2^(base - 112) ph per entry); per
+  // tile a cursor (absolute entry index) with the column and value under it (column ~0: none left
+  // in LDS)
+  float dP[FT == 1 ? NX : 1], Qe[FT][NX];
+  uint32_t cur[FT], ncol[FT], nval[FT];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    cur[r] = st[r];
-    ncol[r] = ~0u;
-    nval[r] = 0u;
+  for (int cc = 0; cc < (FT == 1 ? NX : 1); ++cc) dP[cc] = 0.0f;
 #pragma unroll
-    for (int cc = 0; cc < NX; ++cc) dP[cc][r] = Qe[cc][r] = 0.0f;
+  for (int f = 0; f < FT; ++f) {
+    cur[f] = st[f][0];
+    ncol[f] = ~0u;
+    nval[f] = 0u;
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc) Qe[f][cc] = 0.0f;
   }
   const bool xlane = g < MR;                          // the lane owns an x row
-  const auto entry_at = [&](int r) {                  // the entry under row r's cursor
-    const bool in = cur[r] < run_end(r);
-    const uint32_t at = in ? cur[r] - te0 : 0u;
-    ncol[r] = in ? s_ecol[at] : ~0u;
-    nval[r] = s_eval[at];
+  const auto entry_at = [&](int f) {                  // the entry under tile f's cursor
+    const bool in = cur[f] < run_end(f);
+    const uint32_t at = in ? cur[f] - te0[f] : 0u;
+    ncol[f] = in ? s_ecol[f][at] : ~0u;
+    nval[f] = s_eval[f][at];
   };
   // the escapes of the lane's rows with a column in phase ph (runs are sorted by column), x from
   // the phase's LDS buffer; the reads of the x values at an entry and of the row's next entry go
-  // out together.  The first call also puts the entries into LDS.
+  // out together.
   const auto phase_escapes = [&](int ph) {
     if constexpr (kEsc) {
-      if (!fin) return;
+      if (!fin[0]) return;
       if (ph == 0) {
-        // the escape copy has landed: it went out before every refill of this phase, so waiting
-        // until at most min(L, D) refills are outstanding covers it (the phase change waits the
-        // same for the next phase's x)
+        // the escape copies have landed: they went out before every refill of this phase, so
+        // waiting until at most min(L, D) refills are outstanding covers them (the phase change
+        // waits the same for the next phase's x)
         s_vm_wait_steps<D, kLPS>(L);
 #pragma unroll
-        for (int r = 0; r < RW; ++r) entry_at(r);
+        for (int f = 0; f < FT; ++f) entry_at(f);
       }
       const uint32_t c0 = (uint32_t)ph * kbp * kTileCols, c1 = c0 + kbp * kTileCols;
       const uint16_t* xb = xs16 + (size_t)(ph & 1) * a.xwords * 8;
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        while (ncol[r] < c1) {
-          const uint32_t cc0 = ncol[r] - c0, c16 = cc0 >> 3;
-          const float v = bf16_to_float(nval[r]);
+      for (int f = 0; f < FT; ++f) {
+        float scph = 0.0f;                            // 2^(base - 112) ph (three tiles per wave)
+        if constexpr (FT > 1 && has_placeholder<FMT>()) {
+          if constexpr (FMT == kFmtI8) scph = __uint_as_float(fsc[f]) * placeholder_of<FMT>();
+          else scph = window_scale(fsc[f]) * placeholder_of<FMT>();
+        }
+        while (ncol[f] < c1) {
+          const uint32_t cc0 = ncol[f] - c0, c16 = cc0 >> 3;
+          const float v = bf16_to_float(nval[f]);
           float xv[NX];
 #pragma unroll
           for (int cc = 0; cc < NX; ++cc) {
@@ -306,13 +332,18 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
             xv[cc] = bf16_to_float(
                 xb[(m * rs + (c16 & ~15u) + ((c16 & 15u) ^ (uint32_t)(m & 15))) * 8 + (cc0 & 7)]);
           }
-          cur[r] += 1;
-          entry_at(r);
+          cur[f] += 1;
+          entry_at(f);
 #pragma unroll
           for (int cc = 0; cc < NX; ++cc) {
             if (!xlane || xm(cc) >= MR) continue;
-            if constexpr (has_placeholder<FMT>()) dP[cc][r] = fmaf(-xv[cc], placeholder_of<FMT>(), dP[cc][r]);
-            Qe[cc][r] = fmaf(xv[cc], v, Qe[cc][r]);
+            if constexpr (FT == 1) {
+              if constexpr (has_placeholder<FMT>()) dP[cc] = fmaf(-xv[cc], placeholder_of<FMT>(), dP[cc]);
+              Qe[f][cc] = fmaf(xv[cc], v, Qe[f][cc]);
+            } else {
+              Qe[f][cc] = fmaf(xv[cc], v, Qe[f][cc]);
+              if constexpr (has_placeholder<FMT>()) Qe[f][cc] = fmaf(-xv[cc], scph, Qe[f][cc]);
+            }
           }
         }
       }
@@ -434,13 +465,21 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   }
   lds_barrier();
 
-  // ---- finalise local tile w: partial sums in wave order, escapes, scale, store ----
-  if (!fin) return;
-  // escapes past the LDS copy of a crowded tile: entries and x from memory
-  if constexpr (kEsc) {
+  // ---- finalise local tiles w + f W: partial sums in wave order, escapes, scale, store ----
+  const auto owner = [&](uint32_t u) {               // the wave whose range holds unit u
+    return (int)(((uint64_t)W * (u + 1) + U - 1) / U) - 1;
+  };
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
-      for (uint32_t e = cur[r] > lds_end ? cur[r] : lds_end; e < st[r + 1]; ++e) {
+  for (int f = 0; f < FT; ++f) {
+    if (!fin[f]) break;
+    // escapes past the LDS copy of a crowded tile: entries and x from memory
+    if constexpr (kEsc) {
+      float scph = 0.0f;
+      if constexpr (FT > 1 && has_placeholder<FMT>()) {
+        if constexpr (FMT == kFmtI8) scph = __uint_as_float(fsc[f]) * placeholder_of<FMT>();
+        else scph = window_scale(fsc[f]) * placeholder_of<FMT>();
+      }
+      for (uint32_t e = cur[f] > lds_end[f] ? cur[f] : lds_end[f]; e < st[f][1]; ++e) {
         const uint32_t col = a.esc_col[e];
         const float v = bf16_to_float(a.esc_val[e]);
 #pragma unroll
@@ -448,49 +487,48 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
           const int m = xm(cc);
           if (!xlane || m >= a.mrows) continue;
           const float xv = bf16_to_float(a.x[(int64_t)m * a.k + col]);
-          if constexpr (has_placeholder<FMT>()) dP[cc][r] = fmaf(-xv, placeholder_of<FMT>(), dP[cc][r]);
-          Qe[cc][r] = fmaf(xv, v, Qe[cc][r]);
+          if constexpr (FT == 1) {
+            if constexpr (has_placeholder<FMT>()) dP[cc] = fmaf(-xv, placeholder_of<FMT>(), dP[cc]);
+            Qe[f][cc] = fmaf(xv, v, Qe[f][cc]);
+          } else {
+            Qe[f][cc] = fmaf(xv, v, Qe[f][cc]);
+            if constexpr (has_placeholder<FMT>()) Qe[f][cc] = fmaf(-xv, scph, Qe[f][cc]);
+          }
         }
       }
-  }
-  const int j = w;
-  const auto owner = [&](uint32_t u) {               // the wave whose range holds unit u
-    return (int)(((uint64_t)W * (u + 1) + U - 1) / U) - 1;
-  };
-  const int wf = owner((uint32_t)j * kbp), wl = owner((uint32_t)j * kbp + kbp - 1);
-  float P[NX][RW];
-#pragma unroll
-  for (int cc = 0; cc < NX; ++cc)
-#pragma unroll
-    for (int r = 0; r < RW; ++r) P[cc][r] = 0.0f;
-  for (int wv = wf; wv <= wl; ++wv) {
-    const uint32_t v0 = rstart(wv);
-    if (v0 == rstart(wv + 1)) continue;              // an empty range
-    const int si = j - (int)(v0 / kbp);
-    const float* src = s_part + ((wv * SL + si) * kTileRows) * MP;
-#pragma unroll
-    for (int cc = 0; cc < NX; ++cc)
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-        if (xlane && xm(cc) < MR) P[cc][r] += src[wr(r) * MP + xm(cc)];
-  }
-  if (!xlane) return;
-#pragma unroll
-  for (int cc = 0; cc < NX; ++cc) {
-    const int m = xm(cc);
-    if (m >= a.mrows) continue;
-    float v[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      float sc = 1.0f;
-      if constexpr (FMT == kFmtI8) sc = __uint_as_float(fsc[r]);
-      else if constexpr (kEsc) sc = window_scale(fsc[r]);
-      v[r] = kEsc ? fmaf(sc, P[cc][r] + dP[cc][r], Qe[cc][r]) : P[cc][r];
     }
-    const int64_t row = row0 + wr(0);
+    // the partial sums of the tile for the lane's row, in wave order
+    const int j = w + f * W;
+    const int wf = owner((uint32_t)j * kbp), wl = owner((uint32_t)j * kbp + kbp - 1);
+    float P[NX];
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc) P[cc] = 0.0f;
+    for (int wv = wf; wv <= wl; ++wv) {
+      const uint32_t v0 = rstart(wv);
+      if (v0 == rstart(wv + 1)) continue;            // an empty range
+      const int si = j - (int)(v0 / kbp);
+      const float* src = s_part + ((wv * SL + si) * kTileRows) * MP;
+#pragma unroll
+      for (int cc = 0; cc < NX; ++cc)
+        if (xlane && xm(cc) < MR) P[cc] += src[r16 * MP + xm(cc)];
+    }
+    if (!xlane) continue;
+    // y = 2^(base - 112) (P + dP) + Qe (the 8-bit copy: its row scale; three tiles per wave: the
+    // placeholder terms are in Qe), or P for the dense baseline
+    const int64_t row = row0[f] + r16;
     if (row >= a.n) continue;
-    if (a.y16) a.y16[m * a.ldy + row] = float_to_bf16_rne(v[0]);
-    else a.y[m * a.ldy + row] = v[0];
+    float sc = 1.0f;
+    if constexpr (FMT == kFmtI8) sc = __uint_as_float(fsc[f]);
+    else if constexpr (kEsc) sc = window_scale(fsc[f]);
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc) {
+      const int m = xm(cc);
+      if (m >= a.mrows) continue;
+      float v = P[cc];
+      if constexpr (kEsc) v = FT == 1 ? fmaf(sc, P[cc] + dP[cc], Qe[f][cc]) : fmaf(sc, P[cc], Qe[f][cc]);
+      if (a.y16) a.y16[m * a.ldy + row] = float_to_bf16_rne(v);
+      else a.y[m * a.ldy + row] = v;
+    }
   }
 }
 
@@ -500,24 +538,34 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
 typedef void (*StreamKernel)(StreamArgs);
 
 template <int FMT>
-static StreamKernel stream_pick(int mr) {
+static StreamKernel stream_pick(int mr, int ft) {
+  if (ft == 3) {
+    switch (mr) {
+      case 4: return k_stream<FMT, 4, 16, 3>;
+      case 8: return k_stream<FMT, 8, 16, 3>;
+      default:
+        // (W12 takes three tiles per wave only up to 8 rows)
+        if constexpr (FMT == kFmtW12) return nullptr;
+        else return k_stream<FMT, 16, 16, 3>;
+    }
+  }
   switch (mr) {
-    case 1: return k_stream<FMT, 1, 16>;
-    case 2: return k_stream<FMT, 2, 16>;
-    case 4: return k_stream<FMT, 4, 16>;
-    case 8: return k_stream<FMT, 8, 16>;
-    case 16: return k_stream<FMT, 16, 16>;
-    case 32: return k_stream<FMT, 32, 12>;
-    default: return k_stream<FMT, 64, 8>;
+    case 1: return k_stream<FMT, 1, 16, 1>;
+    case 2: return k_stream<FMT, 2, 16, 1>;
+    case 4: return k_stream<FMT, 4, 16, 1>;
+    case 8: return k_stream<FMT, 8, 16, 1>;
+    case 16: return k_stream<FMT, 16, 16, 1>;
+    case 32: return k_stream<FMT, 32, 12, 1>;
+    default: return k_stream<FMT, 64, 8, 1>;
   }
 }
 
-static StreamKernel stream_kernel(Fmt f, int mr) {
-  if (f == kFmtW12) return stream_pick<kFmtW12>(mr);
-  if (f == kFmtQ8) return stream_pick<kFmtQ8>(mr);
-  if (f == kFmtQ8M) return stream_pick<kFmtQ8M>(mr);
-  if (f == kFmtI8) return stream_pick<kFmtI8>(mr);
-  return stream_pick<kFmtBF16>(mr);
+static StreamKernel stream_kernel(Fmt f, int mr, int ft) {
+  if (f == kFmtW12) return stream_pick<kFmtW12>(mr, ft);
+  if (f == kFmtQ8) return stream_pick<kFmtQ8>(mr, ft);
+  if (f == kFmtQ8M) return stream_pick<kFmtQ8M>(mr, ft);
+  if (f == kFmtI8) return stream_pick<kFmtI8>(mr, ft);
+  return stream_pick<kFmtBF16>(mr, ft);
 }
 
 constexpr int64_t kPassRows = 64;   // rows of x per pass (per weight read)
@@ -529,71 +577,90 @@ static int stream_rows(int64_t mb) {
   return mb <= 2 ? (int)mb : mb <= 4 ? 4 : mb <= 8 ? 8 : mb <= 16 ? 16 : mb <= 32 ? 32 : 64;
 }
 static int stream_waves(int mr) { return mr > 32 ? 8 : mr > 16 ? 12 : 16; }
-static int stream_slots(int mr) { return mr > 32 ? 3 : 2; }
+// tiles a wave finalises: 3 for 3..16 rows on shapes with more tiles than waves on the chip
+// (instances for 4, 8 and 16 rows; W12 up to 8: its 16-row instance would spill, and row groups
+// of one tile per wave measured faster there), else 1
+static int stream_ft(const DevInfo& di, Fmt f, int mr, int64_t tiles) {
+  return mr >= 3 && mr <= (f == kFmtW12 ? 8 : 16) && tiles > (int64_t)stream_waves(mr) * di.cus ? 3 : 1;
+}
+static int stream_slots(int mr, int ft) { return ft == 3 ? 4 : mr > 32 ? 3 : 2; }
 
 struct StreamPlan {
-  int mr = 0, waves = 0, nph = 0;
+  int mr = 0, waves = 0, nph = 0, ft = 1;
   int64_t G = 0;
   uint32_t kbp = 0, rs = 0, xwords = 0, eoff = 0;
   size_t lds = 0;
 };
 
-// The phase length for a pass of mb rows: among the divisors of the row's blocks whose x buffers
-// (two, one for a single phase) fit the LDS and that keep every wave's range within two tiles,
-// the one with the fewest blocks for the busiest wave over all phases (a phase change counted as
-// half a block).  False if none fits.
-static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, StreamPlan* out) {
+// The phase length for a pass of mb rows over a group of n rows, with ft tiles finalised per
+// wave: among the divisors of the row's blocks whose x buffers (two, one for a single phase) fit
+// the LDS and that keep every wave's range within the kernel's tile slots, the one with the
+// fewest blocks for the busiest wave over all phases (a phase change counted as half a block).
+// A CU with 8 or more tiles of 16 or more blocks takes 4 to 10 phases where one fits: its waves
+// then walk the escapes phase by phase while their next blocks load, rather than all at the end
+// (gate+up [34816, 5120], 4 rows: Q8 36.0 -> 33.8 us, W12 46.7 -> 46.0; the LM head [152064,
+// 5120]: Q8 139.7 -> 133.2; with fewer tiles per CU the extra barriers cost more: [8192, 5120]
+// W12 15.9 -> 17.4).  False if none fits.
+static bool stream_plan(const DevInfo& di, int64_t mb, int64_t n, int64_t k, int ft, StreamPlan* out) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows, nkb = k / kTileCols;
   const int mr = stream_rows(mb), W = stream_waves(mr);
   const int64_t G = tiles < di.cus ? tiles : di.cus;
   const int64_t tmax = (tiles + G - 1) / G;          // tiles of the busiest CU
+  const int64_t minph = tmax >= 8 && nkb >= 16 ? 4 : 1;
   double best = 0;
   bool found = false;
+  for (int pass = 0; pass < 2 && !found; ++pass)
   for (int64_t kbp = nkb; kbp >= 1; --kbp) {
     if (nkb % kbp) continue;
     const int64_t nph = nkb / kbp;
+    if (pass == 0 && minph > 1 && (nph < minph || nph > 10)) continue;
     const int64_t segs = (kbp + 3) / 4, rs = 64 * segs, xwords = mr * rs;
     if (mr * segs > kSPieces) continue;
     const int64_t U = tmax * kbp;
     if (U >= (int64_t(1) << 31)) continue;
     const int64_t lmax = (U + W - 1) / W;
-    const int SL = stream_slots(mr);
+    if (tmax > (int64_t)ft * W) continue;            // the waves finalise every tile
+    const int SL = stream_slots(mr, ft);
     if ((lmax - 1) / kbp + 2 > SL) continue;         // a range over at most SL tiles
     const int64_t part = (int64_t)W * SL * kTileRows * (mr + 1) * 4;
     const int64_t xb = (nph > 1 ? 2 : 1) * xwords * 16;
     const int64_t body = ((xb > part ? xb : part) + 15) / 16 * 16;
-    const int64_t lds = body + (int64_t)W * (kSECap * 4 + kSEVal * 2);   // then the escape copies
+    // then the escape copies (walked per phase with one tile per wave)
+    const int64_t cap = ft == 1 ? kSECap : kSECap3;
+    const int64_t lds = body + (int64_t)W * ft * (cap * 4 + (cap + 128) * 2);
     if (lds > di.max_lds) continue;
     const double cost = (double)(lmax * nph) + 0.5 * (double)(nph - 1);
     if (found && cost >= best) continue;
     found = true;
     best = cost;
-    out->mr = mr; out->waves = W; out->nph = (int)nph; out->G = G;
+    out->mr = mr; out->waves = W; out->nph = (int)nph; out->G = G; out->ft = ft;
     out->kbp = (uint32_t)kbp; out->rs = (uint32_t)rs; out->xwords = (uint32_t)xwords; out->lds = (size_t)lds;
     out->eoff = (uint32_t)(body / 16);
   }
   return found;
 }
 
-// Row groups of a shape with more 16-row tiles than waves on the chip: as few as keep every
-// CU at one tile per wave or fewer, of equal size (whole tiles).  One launch runs them all,
-// group after group in workgroup order, so a CU that finishes its workgroup of one group takes
-// one of the next without waiting for a kernel boundary.
-static int64_t stream_group_rows(const DevInfo& di, int64_t mb, int64_t n) {
+// Row groups of a shape with more 16-row tiles than the waves on the chip finalise: as few as
+// keep every CU at ft tiles per wave or fewer, of equal size (whole tiles).  One launch runs
+// them all, group after group in workgroup order, so a CU that finishes its workgroup of one
+// group takes one of the next without waiting for a kernel boundary.
+static int64_t stream_group_rows(const DevInfo& di, int64_t mb, int64_t n, int ft) {
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  const int64_t cap = (int64_t)stream_waves(stream_rows(mb)) * di.cus;
+  const int64_t cap = (int64_t)stream_waves(stream_rows(mb)) * ft * di.cus;
   const int64_t groups = (tiles + cap - 1) / cap;
   return (tiles + groups - 1) / groups * kTileRows;
 }
 
-bool stream_fits(const DevInfo& di, int64_t m, int64_t n, int64_t k) {
+bool stream_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k) {
   if (m < 1 || n < 1 || k * kPassRows * 2 >= (int64_t(1) << 32)) return false;
   StreamPlan p;
   const int64_t full = m < kPassRows ? m : kPassRows, tail = (m - 1) % kPassRows + 1;
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
   for (const int64_t mb : {full, tail}) {
-    const int64_t gr = stream_group_rows(di, mb, n);
+    const int ft = stream_ft(di, f, stream_rows(mb), tiles);
+    const int64_t gr = stream_group_rows(di, mb, n, ft);
     // the plan of a full group (a smaller last group runs the same plan with fewer tiles)
-    if (!stream_plan(di, mb, gr < n ? gr : n, k, &p)) return false;
+    if (!stream_plan(di, mb, gr < n ? gr : n, k, ft, &p)) return false;
   }
   return true;
 }
@@ -603,12 +670,13 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
-  if (!stream_fits(di, m, n, k) || y.silu) return hipErrorInvalidValue;
+  if (!stream_fits(di, f, m, n, k) || y.silu) return hipErrorInvalidValue;
   for (int64_t m0 = 0; m0 < m; m0 += kPassRows) {
     const int64_t mb = (m - m0) < kPassRows ? (m - m0) : kPassRows;
-    const int64_t gr = stream_group_rows(di, mb, n);   // a multiple of 16
+    const int ft = stream_ft(di, f, stream_rows(mb), (n + kTileRows - 1) / kTileRows);
+    const int64_t gr = stream_group_rows(di, mb, n, ft);   // a multiple of 16
     StreamPlan pl;
-    if (!stream_plan(di, mb, gr < n ? gr : n, k, &pl)) return hipErrorInvalidValue;
+    if (!stream_plan(di, mb, gr < n ? gr : n, k, ft, &pl)) return hipErrorInvalidValue;
     const int64_t groups = (n + gr - 1) / gr;
     StreamArgs a;
     a.x = x + m0 * k;
@@ -625,7 +693,7 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
     a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
     a.gtiles = gr / kTileRows;                         // (the last group may be smaller)
     a.G = pl.G;
-    hipLaunchKernelGGL(stream_kernel(f, pl.mr), dim3((unsigned)(groups * pl.G)), dim3(64 * pl.waves), pl.lds, s, a);
+    hipLaunchKernelGGL(stream_kernel(f, pl.mr, pl.ft), dim3((unsigned)(groups * pl.G)), dim3(64 * pl.waves), pl.lds, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

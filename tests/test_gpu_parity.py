@@ -686,11 +686,12 @@ def test_binding_rejects_bad_arguments():
     (8192, 5120, (9, 13, 16, 21, 32)),    # 16 rows: 4 k phases; 21 and 32 rows: 5 phases of 8 blocks
     (4000, 10240, (16,)),                 # 5 phases of 16 blocks
     (1024, 5120, (1, 17, 32)),            # 64 tiles (a k/v projection): each tile over 4 CUs
-    (2000, 2048, (33, 40, 64)),           # passes of 32 rows and a ragged last pass
-    (70003, 256, (1, 4, 16, 32)),         # 4376 tiles: two row groups (one launch each), ragged
+    (2000, 2048, (33, 40, 64)),           # 33..64 rows: the 64-row instance, ranges over 3 tiles
+    (70003, 256, (1, 4, 16, 32)),         # 4376 tiles: 1 and 32 rows two row groups; 4 and 16
+                                          # rows one group, up to three tiles finalised per wave
 ])
 def test_stream_path(n, k, ms):
-    """The streaming kernel (W12_PATH_STREAM) on every format, 1..32 rows per pass (x staged in
+    """The streaming kernel (W12_PATH_STREAM) on every format, 1..64 rows per pass (x staged in
     k phases when it does not fit the LDS whole; a tile's blocks shared by several waves of its CU,
     their sums added in wave order; shapes with more tiles than waves on the chip in row groups),
     against the oracle; bfloat16 outputs the rounding of the float outputs; a second call gives the
@@ -729,6 +730,38 @@ def test_stream_path(n, k, ms):
             if name == "w12":
                 assert np.array_equal(fn().cpu().numpy().view(np.uint32), y.view(np.uint32)), \
                     f"{what}: a second call differs"
+
+
+@pytest.mark.parametrize("n,k,ms", [
+    (197000, 128, (4, 16)),               # 12313 tiles: two row groups of up to 3 tiles per wave
+    (66000, 2816, (8, 16)),               # 4125 tiles; 16 rows: two k phases of 11 blocks
+])
+def test_stream_three_tiles_per_wave(n, k, ms):
+    """The streaming kernel on shapes with more tiles than waves on the chip at 3..16 rows, where
+    every wave finalises up to three tiles and patches their escapes at the end from memory: W12
+    and the dense baseline against the oracle product (the plain definition), bfloat16 outputs the
+    rounding of the float outputs, a second call the same bits."""
+    w12 = _w12()
+    rng = np.random.default_rng(n + k)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[rng.random((n, k)) < 3e-4] = 0x4400
+    x = synth.f32_to_bf16_bits(rng.standard_normal((max(ms), k)).astype(np.float32))
+    wd = to_dev(w)
+    rec = w12.encode(wd)
+    dw = w12.bf16_tiles(wd)
+    del wd
+    for m in ms:
+        xd = to_dev(x[:m])
+        for name, fn in (("w12", lambda **kw: w12.gemm(xd, rec, path="stream", **kw)),
+                         ("bf16", lambda **kw: w12.bf16_gemm(xd, dw, path="stream", **kw))):
+            what = f"stream {name} {n}x{k} m={m}"
+            say(what)
+            y = fn().cpu().numpy()
+            check_gemm(y, x[:m], w, what)
+            _check_bf16_out(fn(out_bf16=True), y, x[:m], None, what + " bf16")
+            assert np.array_equal(fn().cpu().numpy().view(np.uint32), y.view(np.uint32)), \
+                f"{what}: a second call differs"
 
 
 def test_stream_one_hot_and_special_values():
