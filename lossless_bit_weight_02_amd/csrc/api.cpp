@@ -74,6 +74,47 @@ w12::Planes planes_of(const w12_weight* wt) {
   return p;
 }
 
+// The streaming kernel where it measured fastest (us, streaming vs the best other family, on
+// 27B-class shapes, W12): 3..16 rows on shapes of at least 1.5 tiles per CU with rows of at
+// most 8192 columns ([34816, 5120]: 4 rows 46.4 vs 47.7, 8 rows 47.2 vs 47.9, 16 rows 46.8 vs
+// 48.6; [17408, 5120], 16 rows: 29.3 vs 32.8; [8192, 5120], 4 rows: 15.8 vs 18.3; [6144, 5120],
+// 16 rows: 17.8 vs 20.2), and 17..32 rows on at least 2 tiles per CU ([17408, 5120]: 34.2 vs
+// 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
+// ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
+// the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
+// 55.8, 32 rows 59.5 vs 57.8).  Up to 16 rows a wave finalises up to three tiles (W12 up to 8
+// rows; with more, row groups in one launch): the LM-head-like [152064, 5120] takes 133.3 vs
+// 138.8 (Q pass) and 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 199.3 vs 206.7 at 16
+// rows; at 32 rows (one tile per wave, row groups) 179.3 vs 165.8 and 227.9 vs 220.2, so above
+// 16 rows only shapes of one group do.
+// At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
+// the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64
+// rows: [1024, 5120] 28.2 vs 46.7, [6144, 5120] 37.1 vs 48.7, [5120, 6144] 41.0 vs 63.5,
+// [5120, 17408] 98.0 vs 209.0, [12288, 5120] 44.8 vs 51.0; at 40 rows the last ties, 44.5 vs
+// 44.1), the dense baseline up to 5 ([17408, 5120]: 40.7 vs 47.7); above that the matrix cores
+// ([34816, 5120]: W12 70.9 vs 100.9, [17408, 5120] 55.4 vs 56.6).
+bool stream_auto_pick(w12::Fmt f, int64_t m, int64_t tiles, int64_t k, int64_t cus) {
+  return (k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
+          ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) ||
+           (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus))) ||
+         (m >= 33 && m <= 64 && tiles <= (f == w12::kFmtBF16 ? 5 : 3) * cus);
+}
+
+// Top-1 on the family the GEMM's automatic path takes for the shape: the streaming kernel (its
+// outputs into the workspace, then a scan) where that rule picks it for all m rows at once and
+// the kernel runs in one row group, else the matrix-core kernel's top-1 mode in passes of 32
+// rows (LM head [152064, 5120], Q pass, 16 rows: 139.6 vs 147.6 us).
+hipError_t launch_top1_auto(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n,
+                            int64_t k, int32_t* idx, float* val, hipStream_t s) {
+  w12::DevInfo di;
+  hipError_t e = w12::dev_info(&di);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = (n + 15) / 16;
+  if (w12::stream_top1_fits(di, f, m, n, k) && stream_auto_pick(f, m, tiles, k, di.cus))
+    return w12::launch_stream_top1(f, x, m, p, n, k, idx, val, s);
+  return w12::launch_mfma_top1(f, x, m, p, n, k, idx, val, s);
+}
+
 // fixed_scratch: run on the library's fixed scratch (allocation-free entry point) instead of the
 // per-stream workspace
 int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n, int64_t k,
@@ -110,30 +151,7 @@ int run_gemm(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int
   if (flags == W12_PATH_STREAM && !stream_ok)
     return fail(silu ? W12_ERR_ARG : W12_ERR_SHAPE, "the streaming kernel does not take this call "
                 "(rows of fewer than 2^26 columns whose x phases fit the LDS; no SiLU epilogue)");
-  // The streaming kernel where it measured fastest (us, streaming vs the best other family, on
-  // 27B-class shapes, W12): 3..16 rows on shapes of at least 1.5 tiles per CU with rows of at
-  // most 8192 columns ([34816, 5120]: 4 rows 46.4 vs 47.7, 8 rows 47.2 vs 47.9, 16 rows 46.8 vs
-  // 48.6; [17408, 5120], 16 rows: 29.3 vs 32.8; [8192, 5120], 4 rows: 15.8 vs 18.3; [6144, 5120],
-  // 16 rows: 17.8 vs 20.2), and 17..32 rows on at least 2 tiles per CU ([17408, 5120]: 34.2 vs
-  // 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
-  // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
-  // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
-  // 55.8, 32 rows 59.5 vs 57.8).  Shapes with more tiles than waves on the chip run in row groups
-  // (one launch): the LM-head-like [152064, 5120] takes 137.8 vs 151 (Q pass) and 188.7 vs 213
-  // (exact) at 4 rows, 142.4 vs 149.5 and 198.6 vs 212.9 at 16 rows, but 179.3 vs 165.8 and
-  // 227.9 vs 220.2 at 32 rows, so above 16 rows only shapes of one group do.
-  // At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
-  // the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64
-  // rows: [1024, 5120] 28.2 vs 46.7, [6144, 5120] 37.1 vs 48.7, [5120, 6144] 41.0 vs 63.5,
-  // [5120, 17408] 98.0 vs 209.0, [12288, 5120] 44.8 vs 51.0; at 40 rows the last ties, 44.5 vs
-  // 44.1), the dense baseline up to 5 ([17408, 5120]: 40.7 vs 47.7); above that the matrix cores
-  // ([34816, 5120]: W12 70.9 vs 100.9, [17408, 5120] 55.4 vs 56.6).
-  const int64_t cus = dinfo.cus;
-  const bool stream_auto =
-      stream_ok &&
-      ((k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
-        ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) || (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus))) ||
-       (m >= 33 && m <= 64 && tiles <= (f == w12::kFmtBF16 ? 5 : 3) * cus));
+  const bool stream_auto = stream_ok && stream_auto_pick(f, m, tiles, k, dinfo.cus);
   const bool gemv_auto = m <= 2 || (m <= 5 && tiles <= 1024 && k <= 8192);
   const bool use_stream = flags == W12_PATH_STREAM || (flags == W12_PATH_AUTO && stream_auto);
   const bool gemv = !use_stream && (flags == W12_PATH_GEMV || (flags == W12_PATH_AUTO && gemv_auto));
@@ -399,8 +417,8 @@ int run_top1(w12::Fmt f, const uint16_t* x, int64_t m, const w12_weight* wt, int
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned4(idx) || !aligned4(val)) return fail(W12_ERR_ALIGN, "idx and val must be 4-byte aligned");
-  hipError_t e = w12::launch_mfma_top1(f, x, m, planes_of(wt), wt->n, wt->k, idx, val,
-                                       reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_top1_auto(f, x, m, planes_of(wt), wt->n, wt->k, idx, val,
+                                  reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "top-1 launch");
   return ok();
 }
@@ -514,8 +532,8 @@ int w12_i8_top1(const uint16_t* x, int64_t m, const w12_i8* cp, const w12_weight
   if (m >= kMaxDim) return fail(W12_ERR_RANGE, "m too large");
   if (!aligned16(x)) return fail(W12_ERR_ALIGN, "x must be 16-byte aligned");
   if (!aligned4(idx) || !aligned4(val)) return fail(W12_ERR_ALIGN, "idx and val must be 4-byte aligned");
-  hipError_t e = w12::launch_mfma_top1(w12::kFmtI8, x, m, planes_i8(cp, wt), wt->n, wt->k, idx, val,
-                                       reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_top1_auto(w12::kFmtI8, x, m, planes_i8(cp, wt), wt->n, wt->k, idx, val,
+                                  reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "top-1 launch");
   return ok();
 }

@@ -116,14 +116,16 @@ __global__ __launch_bounds__(64) void k_top1_final(const uint64_t* __restrict__ 
   }
 }
 
-// Best key of each row j < m of y [m][cols] (row index = row0 + column), into keys[j].
-__global__ __launch_bounds__(256) void k_top1_rows(const float* __restrict__ y, int64_t cols, int64_t row0,
-                                                   uint64_t* __restrict__ keys) {
+// The best key over columns c0 .. c1 - 1 of one row of outputs (value order of the float bits,
+// NaN above +Inf; ties to the lowest index row0 + column), reduced over the 256 threads of the
+// workgroup (thread 0 returns it).
+__device__ __forceinline__ uint64_t block_best_key(const float* __restrict__ yr, int64_t c0, int64_t c1,
+                                                   int64_t row0) {
   __shared__ uint64_t s_b[4];
-  const int j = blockIdx.x, t = threadIdx.x;
+  const int t = threadIdx.x;
   uint64_t b = 0;
-  for (int64_t c = t; c < cols; c += 256) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, y[(int64_t)j * cols + c]);
+  for (int64_t c = c0 + t; c < c1; c += 256) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, yr[c]);
     const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     const uint64_t key = ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(row0 + c));
     b = key > b ? key : b;
@@ -137,15 +139,42 @@ __global__ __launch_bounds__(256) void k_top1_rows(const float* __restrict__ y, 
   }
   if ((t & 63) == 0) s_b[t >> 6] = b;
   __syncthreads();
-  if (t == 0) {
-    for (int i = 1; i < 4; ++i) b = s_b[i] > b ? s_b[i] : b;
-    b = s_b[0] > b ? s_b[0] : b;
-    keys[j] = b;
-  }
+  if (t == 0)
+    for (int i = 0; i < 4; ++i) b = s_b[i] > b ? s_b[i] : b;
+  return b;
+}
+
+// Best key of each row j < m of y [m][cols] (row index = row0 + column), into keys[j].
+__global__ __launch_bounds__(256) void k_top1_rows(const float* __restrict__ y, int64_t cols, int64_t row0,
+                                                   uint64_t* __restrict__ keys) {
+  const int j = blockIdx.x;
+  const uint64_t b = block_best_key(y + (int64_t)j * cols, 0, cols, row0);
+  if (threadIdx.x == 0) keys[j] = b;
+}
+
+// Best key of row j = blockIdx.y of y [m][n] over the columns of chunk c = blockIdx.x, into
+// keys[c * 32 + j] (the [groups][32] layout k_top1_final reads, one group per chunk).
+__global__ __launch_bounds__(256) void k_top1_chunks(const float* __restrict__ y, int64_t n, int64_t chunk,
+                                                     uint64_t* __restrict__ keys) {
+  const int64_t c = blockIdx.x, j = blockIdx.y;
+  const int64_t c0 = c * chunk, c1 = c0 + chunk < n ? c0 + chunk : n;
+  const uint64_t b = block_best_key(y + j * n, c0, c1, 0);
+  if (threadIdx.x == 0) keys[c * 32 + j] = b;
 }
 
 hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s) {
   hipLaunchKernelGGL(k_top1_rows, dim3((unsigned)m), dim3(256), 0, s, y, cols, row0, keys);
+  return hipGetLastError();
+}
+
+// chunks of at least 256 columns, at most 256 of them (every chunk holds a column)
+hipError_t launch_top1_chunks(const float* y, int m, int64_t n, uint64_t* keys, int* groups, hipStream_t s) {
+  if (m < 1 || m > 32 || n < 1) return hipErrorInvalidValue;
+  int64_t chunk = (n + 255) / 256;
+  chunk = chunk < 256 ? 256 : chunk;
+  const int64_t chunks = (n + chunk - 1) / chunk;
+  hipLaunchKernelGGL(k_top1_chunks, dim3((unsigned)chunks, (unsigned)m), dim3(256), 0, s, y, n, chunk, keys);
+  *groups = (int)chunks;
   return hipGetLastError();
 }
 

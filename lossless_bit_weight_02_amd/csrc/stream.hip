@@ -4,8 +4,10 @@
 // One workgroup of W waves per CU (W = 16 up to 16 rows of x, 12 with 168 VGPRs and a deeper ring
 // for 17..32 rows, 8 with 256 VGPRs for 33..64, whose ranges may touch three tiles).  Workgroup c
 // owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so every CU gets the same number
-// of tiles to within one; a shape with more tiles than waves on the chip runs as row groups of
-// such workgroups in one launch (workgroup b: group b / G).
+// of tiles to within one.  Each wave finalises up to FT of the CU's tiles (FT = 3 for 3..16 rows
+// of x on shapes with more tiles than waves on the chip, W12 up to 8 rows; else 1); a shape with
+// more tiles than FT W per CU runs as row groups of such workgroups in one launch (workgroup b:
+// group b / G).
 // Inside the CU the work is dealt by (tile, 128-column block) units rather than by tiles, so no
 // wave idles while others stream:
 //
@@ -18,10 +20,11 @@
 // phase change costs one barrier; the weight ring (D blocks in flight per wave) runs on across
 // phases.
 //
-// Partial sums.  A wave's range touches at most two tiles (three at 64 rows); it keeps one running
-// sum per touched tile in registers over all phases and adds them into LDS at the end.  Tile j of
-// the CU is then finalised by wave j: the partial sums of the waves that touch it, added in wave
-// order (deterministic), plus its escape corrections, collected during each phase from x in LDS.
+// Partial sums.  A wave's range touches at most two tiles (three at 64 rows, four with FT = 3); it
+// keeps one running sum per touched tile in registers over all phases and adds them into LDS at
+// the end.  Tile j of the CU is then finalised by wave j % W: the partial sums of the waves that
+// touch it, added in wave order (deterministic), plus its escape corrections, collected during
+// each phase from x in LDS.
 //
 // Decode and arithmetic as in the GEMV: 1-2 rows by dot2 (lane r16 + 16 g computes row r16 over
 // columns 32 g .. +31 of each block); 3-64 rows on the matrix cores, the decoded block as operand
@@ -698,6 +701,44 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+constexpr size_t kTop1KeyBytes = size_t(128) << 10;   // keys at the start of the workspace
+
+// Only shapes of one row group: where the kernel runs in several (W12 at 9..16 rows on the LM
+// head), the matrix cores' top-1 mode, which writes no outputs, is faster than the streaming
+// GEMM plus the scan (LM head [152064, 5120], 16 rows, W12: 207.7 vs 199-203 us; the Q pass in
+// one group: 139.6 vs 147.6).
+bool stream_top1_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > 32 || (uint64_t)m * (uint64_t)n * 4u > kWorkspaceBytes - kTop1KeyBytes ||
+      !stream_fits(di, f, m, n, k))
+    return false;
+  const int mr = stream_rows(m);
+  const int64_t tiles = (n + kTileRows - 1) / kTileRows;
+  return stream_group_rows(di, m, n, stream_ft(di, f, mr, tiles)) >= n;
+}
+
+hipError_t launch_stream_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
+                              int32_t* idx, float* val, hipStream_t s) {
+  DevInfo di;
+  hipError_t err = dev_info(&di);
+  if (err != hipSuccess) return err;
+  if (!stream_top1_fits(di, f, m, n, k)) return hipErrorInvalidValue;
+  Scratch sc;
+  sc.s = s;
+  float* ws = nullptr;
+  err = sc.get(&ws);
+  if (err != hipSuccess) return err;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws);                 // [<= 256][32]
+  float* yb = ws + kTop1KeyBytes / sizeof(float);                   // [m][n]
+  YOut yo;
+  yo.f = yb;
+  err = launch_stream(f, x, m, p, n, k, yo, s);
+  if (err != hipSuccess) return err;
+  int groups = 0;
+  err = launch_top1_chunks(yb, (int)m, n, keys, &groups, s);
+  if (err != hipSuccess) return err;
+  return launch_top1_final(keys, groups, (int)m, idx, val, s);
 }
 
 }  // namespace w12

@@ -79,7 +79,11 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int6
 
 // best key of each row of y [m][cols] (row index row0 + column), into keys[0 .. m)
 hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s);
-// top-1 per x row from the per-workgroup keys of the matrix-core kernel's top-1 mode
+// best key of each row j < m (<= 32) of y [m][n] per chunk of columns, into keys[c * 32 + j];
+// *groups = the number of chunks (<= 256)
+hipError_t launch_top1_chunks(const float* y, int m, int64_t n, uint64_t* keys, int* groups, hipStream_t s);
+// top-1 per x row from per-group keys [groups][32] (the matrix-core kernel's top-1 mode, or the
+// chunks above)
 hipError_t launch_top1_final(const uint64_t* part, int groups, int m, int32_t* idx, float* val,
                              hipStream_t s);
 
@@ -151,6 +155,12 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
 bool stream_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k);
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                          YOut y, hipStream_t s);
+// Top-1 per row of x through the streaming kernel: the float outputs into the workspace, then a
+// chunked scan and the per-row reduction; m <= 32 and m n floats within the workspace past its
+// first 128 KiB (stream_top1_fits)
+bool stream_top1_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k);
+hipError_t launch_stream_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
+                              int32_t* idx, float* val, hipStream_t s);
 // MFMA family (bf16 v_mfma_f32_16x16x32), any m (blocks of <= 64 rows of x)
 hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                        YOut y, hipStream_t s, const Scratch& sc);

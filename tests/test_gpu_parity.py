@@ -423,6 +423,39 @@ def test_top1_ties_go_to_the_lowest_row():
     assert w12.gemm_top1(to_dev(x), rec)[0].cpu().numpy()[2] == 100
 
 
+@pytest.mark.parametrize("m", [3, 16, 24])
+def test_top1_streaming_route(m):
+    """On a shape where the automatic path takes the streaming kernel (8192 rows: 2 tiles per CU),
+    the top-1 entry points run it too (outputs into the workspace, then a chunked scan): per row
+    exactly the first maximum of the automatic path's full outputs and its value, bit for bit, on
+    planted exact ties as well, and within the bound of the oracle's maximum."""
+    w12 = _w12()
+    n, k = 8192, 512
+    rng = np.random.default_rng(31 + m)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[[7, 4000, 8191], 5] = 0x4000                     # 2.0 three times: an exact tie for x = e_5
+    rec = w12.encode(to_dev(w))
+    q8w = oracle.q8_view_bits(oracle.encode(w))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    x[0] = 0
+    x[0, 5] = 0x3F80
+    xd = to_dev(x)
+    rows = np.arange(m)
+    for name, top1, full, ref_w in (("q8", w12.q8_top1, w12.q8_gemm, q8w), ("exact", w12.gemm_top1, w12.gemm, w)):
+        say(f"top1 streaming route {name} m={m}")
+        y = full(xd, rec).cpu().numpy()
+        idx, val = (t.cpu().numpy() for t in top1(xd, rec))
+        want = np.argmax(y, axis=1)
+        assert np.array_equal(idx, want), name
+        assert np.array_equal(val.view(np.uint32), y[rows, want].view(np.uint32)), name
+        if name == "exact":
+            assert idx[0] == 7
+        y64 = oracle.gemm64(x, ref_w)
+        bound = 1e-3 * oracle.abs_bound64(x, ref_w)
+        assert np.all(y64[rows, idx] + bound[rows, idx] >= y64.max(axis=1) - bound.max(axis=1)), name
+
+
 def test_graph_capture_replays_match_eager():
     """Split-k GEMMs (workspace), the three kernel families (the streaming kernel with float and
     bfloat16 outputs), the Q pass and the top-1 entry points captured in one HIP graph on a fresh
