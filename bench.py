@@ -231,8 +231,8 @@ def lm_head_bench(dev, stream, reps):
              ("q8_midpoint_m16", lambda: w12.q8_gemm(x, rec, out=ym, midpoint=True), [ym],
               q8_bytes(n, k, rec.n_esc, m)),
              ("w12_m16", lambda: w12.gemm(x, rec, out=ye), [ye], w12_bytes(n, k, rec.n_esc, m)),
-             # the matrix-core path, for comparison (the automatic path runs the streaming
-             # kernel at this size; the exact top-1 runs the matrix cores)
+             # the matrix-core path, for comparison (the automatic path and the top-1 entry
+             # points run the streaming kernel at this size)
              ("q8_m16_mfma", lambda: w12.q8_gemm(x, rec, out=yq_mf, path="mfma"), [yq_mf],
               q8_bytes(n, k, rec.n_esc, m)),
              ("q8_midpoint_m16_mfma", lambda: w12.q8_gemm(x, rec, out=ym_mf, midpoint=True, path="mfma"), [ym_mf],
@@ -286,15 +286,14 @@ def lm_head_bench(dev, stream, reps):
     for name, v in agree.items():
         out[f"top1_agreement_{name}_vs_exact_{rows}_rows"] = f"{v}/{rows}"
     # the top-1 entry points against the first maximum of the full outputs of the same kernel
-    # (the automatic path's streaming kernel where it runs in one row group: the Q passes and the
-    # copy; the matrix cores for the exact pass, whose 16 rows run in row groups), and their
+    # (the automatic path's: the streaming kernel in one row group at this size), and their
     # values bit for bit
     def same_top1(t, yy):
         want = yy.cpu().numpy().argmax(axis=1)
         got_v = t[1].cpu().numpy()
         return bool(np.array_equal(t[0].cpu().numpy(), want)
                     and np.array_equal(got_v.view(np.uint32), yy.cpu().numpy()[np.arange(m), want].view(np.uint32)))
-    out["top1_matches_full_outputs"] = (same_top1(tq, yq) and same_top1(te, ye_mf) and same_top1(tm, ym)
+    out["top1_matches_full_outputs"] = (same_top1(tq, yq) and same_top1(te, ye) and same_top1(tm, ym)
                                         and same_top1(ti, yi))
     samples = [("lm_head q8 m=16 (rows 0..127)", x_bits, keep, yq[:, :128].cpu().numpy(), "q8"),
                ("lm_head w12 m=16 (rows 0..127)", x_bits, keep, ye[:, :128].cpu().numpy()),

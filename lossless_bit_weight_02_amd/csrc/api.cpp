@@ -82,10 +82,9 @@ w12::Planes planes_of(const w12_weight* wt) {
 // 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
 // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
 // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
-// 55.8, 32 rows 59.5 vs 57.8).  Up to 16 rows a wave finalises up to three tiles (W12 up to 8
-// rows; with more, row groups in one launch): the LM-head-like [152064, 5120] takes 133.3 vs
-// 138.8 (Q pass) and 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 199.3 vs 206.7 at 16
-// rows; at 32 rows (one tile per wave, row groups) 179.3 vs 165.8 and 227.9 vs 220.2, so above
+// 55.8, 32 rows 59.5 vs 57.8).  Up to 16 rows a wave finalises up to three tiles (with more,
+// row groups in one launch): the LM-head-like [152064, 5120] takes 133.3 vs 138.8 (Q pass) and
+// 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 183.1 vs 206.7 at 16 rows; at 32 rows (one tile per wave, row groups) 179.3 vs 165.8 and 227.9 vs 220.2, so above
 // 16 rows only shapes of one group do.
 // At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
 // the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64

@@ -116,7 +116,11 @@ struct StreamShape {
 // the escapes patched at the end from memory).
 template <int FMT, int MR, int W, int FT>
 __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
-  constexpr int D = StreamShape<W>::D, FW = StreamShape<W>::FW;
+  // W12 with three tiles per wave at 8 and 16 rows: a 2-deep ring keeps the escape walk's
+  // registers within the 16-wave budget (3 deep spilled; LM head [152064, 5120], 16 rows: 183.1
+  // us against 198.7 in row groups of one tile per wave)
+  constexpr int D = (FMT == kFmtW12 && FT == 3 && MR >= 8) ? 2 : StreamShape<W>::D;
+  constexpr int FW = StreamShape<W>::FW;
   static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16), "FT 3: up to 16 rows, 16 waves");
   // tiles one wave's range touches at most: its length is at most FT kbp units + 1
   constexpr int SL = FT == 3 ? 4 : MR > 32 ? 3 : 2;
@@ -400,19 +404,28 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
       if (it < steps) {
         const u32x4* xb = lds + (cp & 1u) * a.xwords + ck * 16u;   // block ck of the phase
         if constexpr (kMF) {
+          // k-group t outer, activation tile cc inner: the NT accumulators' chains interleave, so
+          // no product waits on the one before it
+          floatx4 a4[NT];
 #pragma unroll
-          for (int cc = 0; cc < NT; ++cc) {
-            floatx4 a4 = {acc[4 * cc], acc[4 * cc + 1], acc[4 * cc + 2], acc[4 * cc + 3]};
+          for (int cc = 0; cc < NT; ++cc)
+            a4[cc] = (floatx4){acc[4 * cc], acc[4 * cc + 1], acc[4 * cc + 2], acc[4 * cc + 3]};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
+          for (int t = 0; t < 4; ++t) {
+            const u32x4 av = {p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
+#pragma unroll
+            for (int cc = 0; cc < NT; ++cc) {
               const int xr = 16 * cc + r16;
               const u32x4 bv = (MR >= 16 * (cc + 1) || xr < MR) ? xb[xr * rs + ((4 * g + t) ^ r16)]
                                                                 : (u32x4){0u, 0u, 0u, 0u};
-              a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                           __builtin_bit_cast(bf16x8, bv), a4, 0, 0, 0);
+              a4[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, bv), a4[cc], 0, 0, 0);
             }
-            acc[4 * cc] = a4[0]; acc[4 * cc + 1] = a4[1]; acc[4 * cc + 2] = a4[2]; acc[4 * cc + 3] = a4[3];
+          }
+#pragma unroll
+          for (int cc = 0; cc < NT; ++cc) {
+            acc[4 * cc] = a4[cc][0]; acc[4 * cc + 1] = a4[cc][1];
+            acc[4 * cc + 2] = a4[cc][2]; acc[4 * cc + 3] = a4[cc][3];
           }
         } else {
 #pragma unroll
@@ -546,10 +559,7 @@ static StreamKernel stream_pick(int mr, int ft) {
     switch (mr) {
       case 4: return k_stream<FMT, 4, 16, 3>;
       case 8: return k_stream<FMT, 8, 16, 3>;
-      default:
-        // (W12 takes three tiles per wave only up to 8 rows)
-        if constexpr (FMT == kFmtW12) return nullptr;
-        else return k_stream<FMT, 16, 16, 3>;
+      default: return k_stream<FMT, 16, 16, 3>;
     }
   }
   switch (mr) {
@@ -581,10 +591,9 @@ static int stream_rows(int64_t mb) {
 }
 static int stream_waves(int mr) { return mr > 32 ? 8 : mr > 16 ? 12 : 16; }
 // tiles a wave finalises: 3 for 3..16 rows on shapes with more tiles than waves on the chip
-// (instances for 4, 8 and 16 rows; W12 up to 8: its 16-row instance would spill, and row groups
-// of one tile per wave measured faster there), else 1
-static int stream_ft(const DevInfo& di, Fmt f, int mr, int64_t tiles) {
-  return mr >= 3 && mr <= (f == kFmtW12 ? 8 : 16) && tiles > (int64_t)stream_waves(mr) * di.cus ? 3 : 1;
+// (instances for 4, 8 and 16 rows), else 1
+static int stream_ft(const DevInfo& di, Fmt, int mr, int64_t tiles) {
+  return mr >= 3 && mr <= 16 && tiles > (int64_t)stream_waves(mr) * di.cus ? 3 : 1;
 }
 static int stream_slots(int mr, int ft) { return ft == 3 ? 4 : mr > 32 ? 3 : 2; }
 
@@ -705,10 +714,9 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
 
 constexpr size_t kTop1KeyBytes = size_t(128) << 10;   // keys at the start of the workspace
 
-// Only shapes of one row group: where the kernel runs in several (W12 at 9..16 rows on the LM
-// head), the matrix cores' top-1 mode, which writes no outputs, is faster than the streaming
-// GEMM plus the scan (LM head [152064, 5120], 16 rows, W12: 207.7 vs 199-203 us; the Q pass in
-// one group: 139.6 vs 147.6).
+// Only shapes of one row group: with several, the matrix cores' top-1 mode, which writes no
+// outputs, can be faster than the streaming GEMM plus the scan (LM head [152064, 5120], 16 rows,
+// W12 in three row groups: 207.7 vs 199-203 us; the Q pass in one group: 139.6 vs 147.6).
 bool stream_top1_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k) {
   if (m < 1 || m > 32 || (uint64_t)m * (uint64_t)n * 4u > kWorkspaceBytes - kTop1KeyBytes ||
       !stream_fits(di, f, m, n, k))

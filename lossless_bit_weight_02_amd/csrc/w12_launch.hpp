@@ -150,7 +150,7 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
                        YOut y, hipStream_t s, const Scratch& sc);
 // Streaming family (one workgroup per CU owning whole tiles, every wave an equal share of their
 // blocks, x in LDS by k phases): passes of <= 64 rows of x, and shapes with more tiles than one
-// per wave of the chip (three for 3..16 rows, W12 up to 8) in equal groups of rows, one launch
+// per wave of the chip (three for 3..16 rows) in equal groups of rows, one launch
 // for all; stream_fits says whether a shape can run it; no SiLU pairing
 bool stream_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k);
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,

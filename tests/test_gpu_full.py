@@ -107,16 +107,15 @@ def test_lm_head_q_pass_top1(pool):
     agree = check_top1(y, y64, absum, "lm_head exact top-1")
     say(f"lm_head: top-1 exact agreement q8 {agree_q}/16, exact {agree}/16")
     # the top-1 entry points run the streaming kernel where the automatic path runs it in one row
-    # group (the Q pass here, three tiles per wave) and the matrix cores otherwise (the exact pass
-    # at 16 rows runs the streaming kernel in row groups), so they must pick exactly the argmax
-    # of that family's full outputs (ties to the lowest index) and report exactly that value
+    # group (both passes here, three tiles per wave), so they must pick exactly the argmax of its
+    # full outputs (ties to the lowest index) and report exactly that value
     say("lm_head: matrix-core gemm m=16 (q8, exact); automatic q8 midpoint")
     yq_mf = w12.q8_gemm(xd, rec, path="mfma").cpu().numpy()
     y_mf = w12.gemm(xd, rec, path="mfma").cpu().numpy()
     yqm = w12.q8_gemm(xd, rec, midpoint=True).cpu().numpy()
     check_y(yq_mf, yq64, qabs, "lm_head q8 matrix cores")
     check_y(y_mf, y64, absum, "lm_head exact matrix cores")
-    for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y_mf),
+    for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y),
                          ("q8 midpoint", lambda xx, rr: w12.q8_top1(xx, rr, midpoint=True), yqm)):
         say(f"lm_head: {name} top-1 entry point")
         idx, val = (t.cpu().numpy() for t in fn(xd, rec))
