@@ -85,8 +85,10 @@ def test_gate_up_full(pool):
 
 
 def test_lm_head_q_pass_top1(pool):
-    """Config LM head [152064, 5120], M=16: Q pass and exact pass on every output, and the top-1
-    token of each row within the error bound (a near-tie may resolve either way)."""
+    """Config LM head [152064, 5120], M=16: Q pass (truncated and midpoint views) and exact pass on
+    every output, on the automatic path (the streaming kernel, three tiles per wave) and the
+    matrix cores; the top-1 token of each row within the error bound (a near-tie may resolve
+    either way) and the top-1 entry points equal to the argmax of the same kernel's outputs."""
     w12 = _w12()
     w, spec, tid = synth.config_weight("lm_head")
     rec, dw = _codec(w, "lm_head", pool)
@@ -115,6 +117,9 @@ def test_lm_head_q_pass_top1(pool):
     yqm = w12.q8_gemm(xd, rec, midpoint=True).cpu().numpy()
     check_y(yq_mf, yq64, qabs, "lm_head q8 matrix cores")
     check_y(y_mf, y64, absum, "lm_head exact matrix cores")
+    say("lm_head: oracle midpoint-view GEMM (all rows)")
+    yqm64, qmabs = oracle_pool.gemm(x, w, pool, view="q8m")
+    check_y(yqm, yqm64, qmabs, "lm_head q8 midpoint")
     for name, fn, yy in (("q8", w12.q8_top1, yq), ("exact", w12.gemm_top1, y),
                          ("q8 midpoint", lambda xx, rr: w12.q8_top1(xx, rr, midpoint=True), yqm)):
         say(f"lm_head: {name} top-1 entry point")
