@@ -83,15 +83,16 @@ extern "C" {
                            * and k <= 8192, for 17 <= m <= 32 on 2 to 12 tiles per unit
                            * (the dense baseline: at most 6 tiles per unit), and for
                            * 33 <= m <= 64 on at most 3 tiles per unit (the dense baseline:
-                           * 5); otherwise the GEMV
+                           * every shape); otherwise the GEMV
                            * with wave reductions for m <= 2, and for m <= 5 on shapes of at most
                            * 1024 tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
 #define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
                             * tiles, every wave of it an equal share of their 128-column blocks;
-                            * passes of <= 64 rows of x; shapes with more tiles than waves on the
-                            * chip in equal row groups, one launch each; W12_ERR_SHAPE when k is
+                            * passes of <= 64 rows of x; a wave finalises up to three tiles at
+                            * 3..16 rows and two at 33..64 rows, and shapes with more tiles than
+                            * that in equal row groups, all in one launch; W12_ERR_SHAPE when k is
                             * 2^26 or more or no phase length fits the LDS) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16
  * values the 8-bit view stands for) instead of 0; escapes stay exact */

@@ -90,13 +90,14 @@ w12::Planes planes_of(const w12_weight* wt) {
 // the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64
 // rows: [1024, 5120] 28.2 vs 46.7, [6144, 5120] 37.1 vs 48.7, [5120, 6144] 41.0 vs 63.5,
 // [5120, 17408] 98.0 vs 209.0, [12288, 5120] 44.8 vs 51.0; at 40 rows the last ties, 44.5 vs
-// 44.1), the dense baseline up to 5 ([17408, 5120]: 40.7 vs 47.7); above that the matrix cores
-// ([34816, 5120]: W12 70.9 vs 100.9, [17408, 5120] 55.4 vs 56.6).
+// 44.1); above that the matrix cores ([34816, 5120]: W12 69.7 vs 80.8 with up to two tiles per
+// wave, [17408, 5120] 54.8 vs 55.1).  The dense baseline takes it at every size ([17408, 5120]:
+// 40.5 vs 48.4, [34816, 5120] 65.5 vs 65.6, [152064, 5120] 277.6 vs 312.4).
 bool stream_auto_pick(w12::Fmt f, int64_t m, int64_t tiles, int64_t k, int64_t cus) {
   return (k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
           ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) ||
            (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus))) ||
-         (m >= 33 && m <= 64 && tiles <= (f == w12::kFmtBF16 ? 5 : 3) * cus);
+         (m >= 33 && m <= 64 && (f == w12::kFmtBF16 || tiles <= 3 * cus));
 }
 
 // Top-1 on the family the GEMM's automatic path takes for the shape: the streaming kernel (its

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   // us against 198.7 in row groups of one tile per wave)
   constexpr int D = (FMT == kFmtW12 && FT == 3 && MR >= 8) ? 2 : StreamShape<W>::D;
   constexpr int FW = StreamShape<W>::FW;
-  static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16), "FT 3: up to 16 rows, 16 waves");
+  static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16) || (FT == 2 && W == 8 && MR == 64),
+                "FT 3: up to 16 rows, 16 waves; FT 2: 64 rows, 8 waves");
   // tiles one wave's range touches at most: its length is at most FT kbp units + 1
   constexpr int SL = FT == 3 ? 4 : MR > 32 ? 3 : 2;
   constexpr bool kMF = MR > 2;                       // matrix cores for 3..64 rows
@@ -555,6 +556,7 @@ typedef void (*StreamKernel)(StreamArgs);
 
 template <int FMT>
 static StreamKernel stream_pick(int mr, int ft) {
+  if (ft == 2) return k_stream<FMT, 64, 8, 2>;
   if (ft == 3) {
     switch (mr) {
       case 4: return k_stream<FMT, 4, 16, 3>;
@@ -590,10 +592,12 @@ static int stream_rows(int64_t mb) {
   return mb <= 2 ? (int)mb : mb <= 4 ? 4 : mb <= 8 ? 8 : mb <= 16 ? 16 : mb <= 32 ? 32 : 64;
 }
 static int stream_waves(int mr) { return mr > 32 ? 8 : mr > 16 ? 12 : 16; }
-// tiles a wave finalises: 3 for 3..16 rows on shapes with more tiles than waves on the chip
-// (instances for 4, 8 and 16 rows), else 1
+// tiles a wave finalises on shapes with more tiles than waves on the chip: 3 for 3..16 rows
+// (instances for 4, 8 and 16 rows), 2 for 33..64 rows (each row group re-reads all of x through
+// the CU, as much as the CU's weights at 64 rows); else 1
 static int stream_ft(const DevInfo& di, Fmt, int mr, int64_t tiles) {
-  return mr >= 3 && mr <= 16 && tiles > (int64_t)stream_waves(mr) * di.cus ? 3 : 1;
+  if (tiles <= (int64_t)stream_waves(mr) * di.cus) return 1;
+  return mr >= 3 && mr <= 16 ? 3 : mr > 32 ? 2 : 1;
 }
 static int stream_slots(int mr, int ft) { return ft == 3 ? 4 : mr > 32 ? 3 : 2; }
 

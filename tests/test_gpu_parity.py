@@ -768,12 +768,14 @@ def test_stream_path(n, k, ms):
 @pytest.mark.parametrize("n,k,ms", [
     (197000, 128, (4, 16)),               # 12313 tiles: two row groups of up to 3 tiles per wave
     (66000, 2816, (8, 16)),               # 4125 tiles; 16 rows: two k phases of 11 blocks
+    (40000, 640, (40, 64)),               # 2500 tiles, 64-row instance: up to 2 tiles per wave
+    (70000, 128, (33,)),                  # 4375 tiles: two row groups of up to 2 tiles per wave
 ])
-def test_stream_three_tiles_per_wave(n, k, ms):
-    """The streaming kernel on shapes with more tiles than waves on the chip at 3..16 rows, where
-    every wave finalises up to three tiles and patches their escapes at the end from memory: W12
-    and the dense baseline against the oracle product (the plain definition), bfloat16 outputs the
-    rounding of the float outputs, a second call the same bits."""
+def test_stream_several_tiles_per_wave(n, k, ms):
+    """The streaming kernel on shapes with more tiles than waves on the chip (3..16 rows: up to
+    three tiles finalised per wave; 33..64 rows: up to two), every wave walking the escapes of all
+    its tiles phase by phase: W12 and the dense baseline against the oracle product (the plain
+    definition), bfloat16 outputs the rounding of the float outputs, a second call the same bits."""
     w12 = _w12()
     rng = np.random.default_rng(n + k)
     w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
