@@ -188,11 +188,11 @@ int w12_q8_gemm(const uint16_t *x, int64_t m, const w12_weight *wt, float *y, ui
  * (figure-captions page, Fig. 7; summary page, Main Findings: 98.7% top-1 agreement).
  * idx[j] (int32, device) = the n at which y[j][n] is largest, ties to the smallest n; val[j]
  * (float, device) = that y[j][n] (a NaN output counts as the largest).  Where the automatic path
- * of w12_q8_gemm / w12_gemm takes the streaming kernel for all m <= 32 rows in one row group, y
- * is exactly that path's output: the kernel writes it into the workspace and two small kernels
- * scan it; otherwise y is computed exactly as the matrix-core path computes it for a shape too
- * large to split, in passes of up to 32 rows of x (each pass reads the weights once) plus one
- * small kernel per pass, with no outputs written.  Uses the GEMM workspace (see the conventions
+ * of w12_q8_gemm / w12_gemm takes the streaming kernel for all m <= 32 rows, y is exactly that
+ * path's output; otherwise y is computed exactly as the matrix-core path computes it for a shape
+ * too large to split, in passes of up to 32 rows of x (each pass reads the weights once).  Either
+ * kernel reduces its outputs to per-workgroup keys in the workspace instead of writing them, and
+ * one small kernel per pass picks the winners.  Uses the GEMM workspace (see the conventions
  * above).
  * Same record checks as w12_q8_gemm / w12_gemm; idx and val 4-byte aligned.  flags: 0, or for
  * w12_q8_top1 W12_Q8_MIDPOINT (the midpoint view, as in w12_q8_gemm); anything else is

@@ -100,10 +100,9 @@ bool stream_auto_pick(w12::Fmt f, int64_t m, int64_t tiles, int64_t k, int64_t c
          (m >= 33 && m <= 64 && (f == w12::kFmtBF16 || tiles <= 3 * cus));
 }
 
-// Top-1 on the family the GEMM's automatic path takes for the shape: the streaming kernel (its
-// outputs into the workspace, then a scan) where that rule picks it for all m rows at once and
-// the kernel runs in one row group, else the matrix-core kernel's top-1 mode in passes of 32
-// rows (LM head [152064, 5120], Q pass, 16 rows: 139.6 vs 147.6 us).
+// Top-1 on the family the GEMM's automatic path takes for the shape: the streaming kernel's
+// top-1 mode (each workgroup reduces its outputs to one key per x row) where that rule picks it
+// for all m <= 32 rows at once, else the matrix-core kernel's top-1 mode in passes of 32 rows.
 hipError_t launch_top1_auto(w12::Fmt f, const uint16_t* x, int64_t m, const w12::Planes& p, int64_t n,
                             int64_t k, int32_t* idx, float* val, hipStream_t s) {
   w12::DevInfo di;

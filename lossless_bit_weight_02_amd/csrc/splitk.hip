@@ -152,29 +152,8 @@ __global__ __launch_bounds__(256) void k_top1_rows(const float* __restrict__ y, 
   if (threadIdx.x == 0) keys[j] = b;
 }
 
-// Best key of row j = blockIdx.y of y [m][n] over the columns of chunk c = blockIdx.x, into
-// keys[c * 32 + j] (the [groups][32] layout k_top1_final reads, one group per chunk).
-__global__ __launch_bounds__(256) void k_top1_chunks(const float* __restrict__ y, int64_t n, int64_t chunk,
-                                                     uint64_t* __restrict__ keys) {
-  const int64_t c = blockIdx.x, j = blockIdx.y;
-  const int64_t c0 = c * chunk, c1 = c0 + chunk < n ? c0 + chunk : n;
-  const uint64_t b = block_best_key(y + j * n, c0, c1, 0);
-  if (threadIdx.x == 0) keys[c * 32 + j] = b;
-}
-
 hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s) {
   hipLaunchKernelGGL(k_top1_rows, dim3((unsigned)m), dim3(256), 0, s, y, cols, row0, keys);
-  return hipGetLastError();
-}
-
-// chunks of at least 256 columns, at most 256 of them (every chunk holds a column)
-hipError_t launch_top1_chunks(const float* y, int m, int64_t n, uint64_t* keys, int* groups, hipStream_t s) {
-  if (m < 1 || m > 32 || n < 1) return hipErrorInvalidValue;
-  int64_t chunk = (n + 255) / 256;
-  chunk = chunk < 256 ? 256 : chunk;
-  const int64_t chunks = (n + chunk - 1) / chunk;
-  hipLaunchKernelGGL(k_top1_chunks, dim3((unsigned)chunks, (unsigned)m), dim3(256), 0, s, y, n, chunk, keys);
-  *groups = (int)chunks;
   return hipGetLastError();
 }
 

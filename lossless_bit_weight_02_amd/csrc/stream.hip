@@ -62,6 +62,8 @@ struct StreamArgs {
                           // [W FT][cap + 128] values
   int64_t gtiles;         // 16-row tiles per row group (workgroup b takes group b / G)
   int64_t G;              // workgroups per group
+  uint64_t* keys;         // top-1 mode (y not written): workgroup b's best key of x row j at
+                          // keys[32 b + j], j < 32 (0 for rows past mrows and idle workgroups)
 };
 
 template <int FMT>
@@ -144,7 +146,10 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const int64_t G = a.G, c = blockIdx.x % G, tb = (blockIdx.x / G) * a.gtiles;
   const int64_t tiles_all = (a.n + kTileRows - 1) / kTileRows;
   const int64_t tiles = tiles_all - tb < a.gtiles ? tiles_all - tb : a.gtiles;
-  if (c >= tiles) return;                            // a last group with fewer tiles than G
+  if (c >= tiles) {                                  // a last group with fewer tiles than G
+    if (a.keys && tid < 32) a.keys[(int64_t)blockIdx.x * 32 + tid] = 0;
+    return;
+  }
   const uint32_t nkb = (uint32_t)(a.k / kTileCols);
   const uint32_t kbp = a.kbp;
   const int nph = a.nph;
@@ -486,6 +491,11 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   const auto owner = [&](uint32_t u) {               // the wave whose range holds unit u
     return (int)(((uint64_t)W * (u + 1) + U - 1) / U) - 1;
   };
+  // top-1 mode: the lane's best key per x row over its tiles (value order of the float bits, NaN
+  // above +Inf; ties to the lowest row index), in place of the stores
+  uint64_t best[NX];
+#pragma unroll
+  for (int cc = 0; cc < NX; ++cc) best[cc] = 0;
 #pragma unroll
   for (int f = 0; f < FT; ++f) {
     if (!fin[f]) break;
@@ -543,8 +553,45 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
       if (m >= a.mrows) continue;
       float v = P[cc];
       if constexpr (kEsc) v = FT == 1 ? fmaf(sc, P[cc] + dP[cc], Qe[f][cc]) : fmaf(sc, P[cc], Qe[f][cc]);
-      if (a.y16) a.y16[m * a.ldy + row] = float_to_bf16_rne(v);
-      else a.y[m * a.ldy + row] = v;
+      if (a.keys) {
+        const uint32_t u = __float_as_uint(v);
+        const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        const uint64_t key = ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
+        best[cc] = key > best[cc] ? key : best[cc];
+      } else if (a.y16) {
+        a.y16[m * a.ldy + row] = float_to_bf16_rne(v);
+      } else {
+        a.y[m * a.ldy + row] = v;
+      }
+    }
+  }
+  if (a.keys) {
+    // the best over the lane's 16 rows (lanes r16 of one g), then over the waves through LDS:
+    // wave w's 32 keys at word w * 32 of the escape-copy area, unused by now (every wave walked
+    // its last phase before the barrier ahead of the partial sums; the area holds at least
+    // 256 bytes per wave)
+    uint64_t* s_key = reinterpret_cast<uint64_t*>(lds + a.eoff) + w * 32;
+#pragma unroll
+    for (int cc = 0; cc < NX; ++cc) {
+      uint64_t b = best[cc];
+#pragma unroll
+      for (int sh = 1; sh < 16; sh *= 2) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)b, sh, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(b >> 32), sh, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        b = o > b ? o : b;
+      }
+      if (r16 == 0 && xm(cc) < 32) s_key[xm(cc)] = b;
+    }
+    if (MR < 32 && lane >= MR && lane < 32) s_key[lane] = 0;
+    lds_barrier();
+    if (w == 0 && lane < 32) {
+      uint64_t b = 0;
+      for (int wv = 0; wv < W; ++wv) {
+        const uint64_t o = reinterpret_cast<const uint64_t*>(lds + a.eoff)[wv * 32 + lane];
+        b = o > b ? o : b;
+      }
+      a.keys[(int64_t)blockIdx.x * 32 + lane] = b;
     }
   }
 }
@@ -682,7 +729,7 @@ bool stream_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k) {
 }
 
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                         YOut y, hipStream_t s) {
+                         YOut y, hipStream_t s, uint64_t* keys, int* key_groups) {
   DevInfo di;
   hipError_t err = dev_info(&di);
   if (err != hipSuccess) return err;
@@ -709,6 +756,12 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
     a.kbp = pl.kbp; a.nph = pl.nph; a.rs = pl.rs; a.xwords = pl.xwords; a.eoff = pl.eoff;
     a.gtiles = gr / kTileRows;                         // (the last group may be smaller)
     a.G = pl.G;
+    a.keys = keys;
+    if (keys) {
+      // top-1 mode: one pass of at most 32 rows, keys [grid][32]
+      if (m > 32) return hipErrorInvalidValue;
+      *key_groups = (int)(groups * pl.G);
+    }
     hipLaunchKernelGGL(stream_kernel(f, pl.mr, pl.ft), dim3((unsigned)(groups * pl.G)), dim3(64 * pl.waves), pl.lds, s, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -716,18 +769,12 @@ hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, i
   return hipSuccess;
 }
 
-constexpr size_t kTop1KeyBytes = size_t(128) << 10;   // keys at the start of the workspace
-
-// Only shapes of one row group: with several, the matrix cores' top-1 mode, which writes no
-// outputs, can be faster than the streaming GEMM plus the scan (LM head [152064, 5120], 16 rows,
-// W12 in three row groups: 207.7 vs 199-203 us; the Q pass in one group: 139.6 vs 147.6).
 bool stream_top1_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k) {
-  if (m < 1 || m > 32 || (uint64_t)m * (uint64_t)n * 4u > kWorkspaceBytes - kTop1KeyBytes ||
-      !stream_fits(di, f, m, n, k))
-    return false;
-  const int mr = stream_rows(m);
+  if (m < 1 || m > 32 || !stream_fits(di, f, m, n, k)) return false;
   const int64_t tiles = (n + kTileRows - 1) / kTileRows;
-  return stream_group_rows(di, m, n, stream_ft(di, f, mr, tiles)) >= n;
+  const int64_t gr = stream_group_rows(di, m, n, stream_ft(di, f, stream_rows(m), tiles));
+  const int64_t grid = (n + gr - 1) / gr * (tiles < di.cus ? tiles : di.cus);
+  return (uint64_t)grid * 32u * 8u <= kWorkspaceBytes;
 }
 
 hipError_t launch_stream_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
@@ -741,14 +788,9 @@ hipError_t launch_stream_top1(Fmt f, const uint16_t* x, int64_t m, const Planes&
   float* ws = nullptr;
   err = sc.get(&ws);
   if (err != hipSuccess) return err;
-  uint64_t* keys = reinterpret_cast<uint64_t*>(ws);                 // [<= 256][32]
-  float* yb = ws + kTop1KeyBytes / sizeof(float);                   // [m][n]
-  YOut yo;
-  yo.f = yb;
-  err = launch_stream(f, x, m, p, n, k, yo, s);
-  if (err != hipSuccess) return err;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws);                 // [grid][32]
   int groups = 0;
-  err = launch_top1_chunks(yb, (int)m, n, keys, &groups, s);
+  err = launch_stream(f, x, m, p, n, k, YOut{}, s, keys, &groups);
   if (err != hipSuccess) return err;
   return launch_top1_final(keys, groups, (int)m, idx, val, s);
 }

@@ -79,11 +79,8 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t rows, int6
 
 // best key of each row of y [m][cols] (row index row0 + column), into keys[0 .. m)
 hipError_t launch_top1_rows(const float* y, int m, int64_t cols, int64_t row0, uint64_t* keys, hipStream_t s);
-// best key of each row j < m (<= 32) of y [m][n] per chunk of columns, into keys[c * 32 + j];
-// *groups = the number of chunks (<= 256)
-hipError_t launch_top1_chunks(const float* y, int m, int64_t n, uint64_t* keys, int* groups, hipStream_t s);
-// top-1 per x row from per-group keys [groups][32] (the matrix-core kernel's top-1 mode, or the
-// chunks above)
+// top-1 per x row from per-workgroup keys [groups][32] (the top-1 modes of the matrix-core and
+// streaming kernels)
 hipError_t launch_top1_final(const uint64_t* part, int groups, int m, int32_t* idx, float* val,
                              hipStream_t s);
 
@@ -153,11 +150,13 @@ hipError_t launch_gemv(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
 // per wave of the chip (three for 3..16 rows) in equal groups of rows, one launch
 // for all; stream_fits says whether a shape can run it; no SiLU pairing
 bool stream_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k);
+// keys (top-1 mode, m <= 32): y is not written; workgroup b's best key of x row j goes to
+// keys[32 b + j] and *key_groups = the grid size
 hipError_t launch_stream(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
-                         YOut y, hipStream_t s);
-// Top-1 per row of x through the streaming kernel: the float outputs into the workspace, then a
-// chunked scan and the per-row reduction; m <= 32 and m n floats within the workspace past its
-// first 128 KiB (stream_top1_fits)
+                         YOut y, hipStream_t s, uint64_t* keys = nullptr, int* key_groups = nullptr);
+// Top-1 per row of x through the streaming kernel: its workgroups reduce their outputs to one key
+// per x row, then the per-row reduction over the workgroups; m <= 32 and the keys within the
+// workspace (stream_top1_fits)
 bool stream_top1_fits(const DevInfo& di, Fmt f, int64_t m, int64_t n, int64_t k);
 hipError_t launch_stream_top1(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int64_t n, int64_t k,
                               int32_t* idx, float* val, hipStream_t s);

@@ -456,6 +456,35 @@ def test_top1_streaming_route(m):
         assert np.all(y64[rows, idx] + bound[rows, idx] >= y64.max(axis=1) - bound.max(axis=1)), name
 
 
+def test_top1_streaming_route_row_groups():
+    """The streaming top-1 mode on a shape that runs in two row groups (200003 rows: 12501 tiles,
+    more than three per wave at 4 rows; ragged last tile): per row exactly the first maximum of
+    the automatic path's full outputs and its value, bit for bit, and within the bound of the
+    oracle's maximum."""
+    w12 = _w12()
+    n, k, m = 200003, 128, 4
+    rng = np.random.default_rng(77)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    w[rng.random((n, k)) < 0.01] = 0
+    w[[11, 150000, 200002], 3] = 0x4000                # an exact tie for x = e_3 across the groups
+    rec = w12.encode(to_dev(w))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    x[1] = 0
+    x[1, 3] = 0x3F80
+    xd = to_dev(x)
+    rows = np.arange(m)
+    say("top1 streaming route, row groups")
+    y = w12.gemm(xd, rec).cpu().numpy()
+    idx, val = (t.cpu().numpy() for t in w12.gemm_top1(xd, rec))
+    want = np.argmax(y, axis=1)
+    assert np.array_equal(idx, want)
+    assert np.array_equal(val.view(np.uint32), y[rows, want].view(np.uint32))
+    assert idx[1] == 11
+    y64 = oracle.gemm64(x, w)
+    bound = 1e-3 * oracle.abs_bound64(x, w)
+    assert np.all(y64[rows, idx] + bound[rows, idx] >= y64.max(axis=1) - bound.max(axis=1))
+
+
 def test_graph_capture_replays_match_eager():
     """Split-k GEMMs (workspace), the three kernel families (the streaming kernel with float and
     bfloat16 outputs), the Q pass and the top-1 entry points captured in one HIP graph on a fresh
