@@ -487,8 +487,9 @@ def test_top1_streaming_route_row_groups():
 
 def test_graph_capture_replays_match_eager():
     """Split-k GEMMs (workspace), the three kernel families (the streaming kernel with float and
-    bfloat16 outputs), the Q pass and the top-1 entry points captured in one HIP graph on a fresh
-    stream (its workspace is allocated inside the capture):
+    bfloat16 outputs), the Q pass and the top-1 entry points (the matrix cores' and the streaming
+    kernel's top-1 modes) captured in one HIP graph on a fresh stream (its workspace is allocated
+    inside the capture):
     every replay, with eager work and cleared outputs in between, equals the eager launches bit
     for bit."""
     w12 = _w12()
@@ -505,6 +506,14 @@ def test_graph_capture_replays_match_eager():
             torch.empty((16, n), dtype=torch.float32, device="cuda"),
             torch.empty((16, n), dtype=torch.bfloat16, device="cuda")]
     t1 = (torch.empty(16, dtype=torch.int32, device="cuda"), torch.empty(16, dtype=torch.float32, device="cuda"))
+    # 400 tiles: the automatic path and the top-1 entry points take the streaming kernel at 16 rows
+    n2, k2 = 6400, 256
+    w2 = synth.f32_to_bf16_bits((rng.standard_normal((n2, k2)) * 0.02).astype(np.float32))
+    w2[rng.random((n2, k2)) < 0.01] = 0
+    rec2 = w12.encode(to_dev(w2))
+    x16b = to_dev(synth.f32_to_bf16_bits(rng.standard_normal((16, k2)).astype(np.float32)))
+    t2 = tuple(torch.empty(16, dtype=d, device="cuda") for d in (torch.int32, torch.float32))
+    t3 = tuple(torch.empty(16, dtype=d, device="cuda") for d in (torch.int32, torch.float32))
 
     def run():
         w12.gemm(x1, rec, path="gemv", out=outs[0])
@@ -513,10 +522,14 @@ def test_graph_capture_replays_match_eager():
         w12.gemm(x16, rec, path="stream", out=outs[3])
         w12.gemm(x16, rec, path="stream", out=outs[4])
         w12.q8_top1(x16, rec, out=t1)
+        w12.q8_top1(x16b, rec2, out=t2)
+        w12.gemm_top1(x16b, rec2, out=t3)
 
     run()
     torch.cuda.synchronize()
-    want = [o.clone() for o in outs] + [t.clone() for t in t1]
+    want = [o.clone() for o in outs] + [t.clone() for t in t1 + t2 + t3]
+    y2 = w12.gemm(x16b, rec2).cpu().numpy()
+    assert np.array_equal(t3[0].cpu().numpy(), np.argmax(y2, axis=1))
     check_gemm(outs[0].cpu().numpy(), to_host_bits(x1), w, "graph eager gemv")
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -525,13 +538,13 @@ def test_graph_capture_replays_match_eager():
             run()
     torch.cuda.synchronize()
     for rep in range(4):
-        for o in outs + list(t1):
+        for o in outs + list(t1 + t2 + t3):
             o.zero_()
         torch.mm(torch.ones(64, 64, device="cuda"), torch.ones(64, 64, device="cuda"))   # eager work
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = outs + list(t1)
+        got = outs + list(t1 + t2 + t3)
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (rep, i)
 
