@@ -81,13 +81,15 @@ extern "C" {
 #define W12_PATH_AUTO 0u  /* the family measured fastest for the shape: the streaming kernel for
                            * 3 <= m <= 16 on shapes of at least 1.5 16-row tiles per compute unit
                            * and k <= 8192, for 17 <= m <= 32 on 2 to 12 tiles per unit
-                           * (the dense baseline: at most 6 tiles per unit), and for
-                           * 33 <= m <= 64 on at most 3 tiles per unit (the dense baseline:
-                           * every shape); otherwise the GEMV
+                           * (the dense baseline: at most 6 tiles per unit), for
+                           * 33 <= m <= 64 on 1.5 to 3 tiles per unit (the dense baseline:
+                           * every shape), and above 64 rows on 1.5 to 2.5 (the dense baseline:
+                           * at most 3); otherwise the GEMV
                            * with wave reductions for m <= 2, and for m <= 5 on shapes of at most
                            * 1024 tiles and k <= 8192; bf16 MFMA otherwise */
 #define W12_PATH_GEMV 1u  /* force the GEMV (m > 8 runs as several passes of <= 8 rows) */
-#define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16) */
+#define W12_PATH_MFMA 2u  /* force the MFMA kernel (any m; columns padded to 16; passes of 32
+                           * rows above 32 on shapes of fewer than 1.5 tiles per unit) */
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
                             * tiles, every wave of it an equal share of their 128-column blocks;
                             * passes of <= 64 rows of x; a wave finalises up to three tiles at

@@ -87,17 +87,25 @@ w12::Planes planes_of(const w12_weight* wt) {
 // 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 183.1 vs 206.7 at 16 rows; at 32 rows (one tile per wave, row groups) 179.3 vs 165.8 and 227.9 vs 220.2, so above
 // 16 rows only shapes of one group do.
 // At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
-// the matrix cores, which do not split k there, on shapes of up to 3 tiles per CU (W12, 64
-// rows: [1024, 5120] 28.2 vs 46.7, [6144, 5120] 37.1 vs 48.7, [5120, 6144] 41.0 vs 63.5,
-// [5120, 17408] 98.0 vs 209.0, [12288, 5120] 44.8 vs 51.0; at 40 rows the last ties, 44.5 vs
-// 44.1); above that the matrix cores ([34816, 5120]: W12 69.7 vs 80.8 with up to two tiles per
-// wave, [17408, 5120] 54.8 vs 55.1).  The dense baseline takes it at every size ([17408, 5120]:
-// 40.5 vs 48.4, [34816, 5120] 65.5 vs 65.6, [152064, 5120] 277.6 vs 312.4).
+// the matrix cores' three/four-tile kernel, which does not split k, on shapes of 1.5 to 3 tiles
+// per CU (W12, 64 rows: [6144, 5120] 37.1 vs 48.7, [12288, 5120] 44.8 vs 51.0; at 40 rows the
+// last ties, 44.5 vs 44.1); below 1.5 tiles per CU the matrix cores run passes of 32 rows that
+// split k and win (64 rows: [5120, 17408] 70.7 vs 97.3, [1024, 5120] 24.0 vs 28.1, [5120, 6144]
+// 41.0 vs 40.9); above 3 the three/four-tile kernel ([34816, 5120]: W12 69.7 vs 80.8 with up to
+// two tiles per wave, [17408, 5120] 54.8 vs 55.1).  The dense baseline takes the streaming
+// kernel at every size ([17408, 5120]: 40.5 vs 48.4, [34816, 5120] 65.5 vs 65.6, [152064, 5120]
+// 277.6 vs 312.4, [5120, 17408] 60.3 vs 70.9).  Above 64 rows (passes of 64) the streaming
+// kernel wins on 1.5 to 2.5 tiles per CU (128 rows: [6144, 5120] 73.1 vs 85.3, [8192, 5120] 74.7
+// vs 85.2; [12288, 5120] ties, 87.1 vs 86.4), the dense baseline's up to 3 ([5120, 17408] 121.2
+// vs 140.9, [5120, 6144] 55.6 vs 73.9, [8192, 5120] 54.7 vs 69.3, [12288, 5120] 68.6 vs 70.8).
 bool stream_auto_pick(w12::Fmt f, int64_t m, int64_t tiles, int64_t k, int64_t cus) {
-  return (k <= 8192 && (f != w12::kFmtBF16 || tiles <= 6 * cus) &&
-          ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) ||
-           (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus))) ||
-         (m >= 33 && m <= 64 && (f == w12::kFmtBF16 || tiles <= 3 * cus));
+  const bool dense = f == w12::kFmtBF16;
+  if (m <= 32)
+    return k <= 8192 && (!dense || tiles <= 6 * cus) &&
+           ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) ||
+            (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus));
+  if (m <= 64) return dense || (2 * tiles >= 3 * cus && tiles <= 3 * cus);
+  return dense ? tiles <= 3 * cus : 2 * tiles >= 3 * cus && 2 * tiles <= 5 * cus;
 }
 
 // Top-1 on the family the GEMM's automatic path takes for the shape: the streaming kernel's

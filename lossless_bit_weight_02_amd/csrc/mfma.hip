@@ -761,6 +761,11 @@ hipError_t launch_mfma(Fmt f, const uint16_t* x, int64_t m, const Planes& p, int
   const int64_t max_step = wide_ok ? 128 : 64;
   for (int64_t m0 = 0, step = 0; m0 < m; m0 += step) {
     step = (m - m0) < max_step ? (m - m0) : max_step;
+    // Fewer than 1.5 tiles per CU: passes of 32 rows, which split k over the chip's waves, instead
+    // of the wider kernels, which give each wave a whole tile (W12 at 64 / 128 rows, us: [5120,
+    // 17408] 70.7 / 141.1 against 207.5 / 254.8, [1024, 5120] 24.0 / 47.2 against 46.8 / 81.1,
+    // [5120, 6144] 41.0 / 79.5 against 64.9 / 98.8).
+    if (step > 32 && 2 * tiles < 3 * (int64_t)di.cus) step = 32;
     const int mb = (int)step;
     // A shape with more tiles than the chip's waves runs in rounds of one tile per wave; when the
     // last round would keep at most half of the waves busy (the LM head: 9504 tiles = 3 rounds

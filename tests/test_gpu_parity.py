@@ -264,11 +264,18 @@ def test_gemm_special_values():
     ref = oracle.encode(w)
     assert_records_equal(record_numpy(rec), ref, "special")
     x_all = synth.f32_to_bf16_bits(rng.standard_normal((100, k)).astype(np.float32) * 1e-3)
-    # 100 rows: the eight-tile matrix-core kernel, whose escapes are patched in the epilogue
-    for path, m in (("gemv", 3), ("mfma", 3), ("mfma", 100)):
-        say(f"special values path={path} m={m}")
+    # 100 rows: passes of 32 rows on this one-tile record; the same rows stacked over 6152 more
+    # (385 tiles) run the eight-tile matrix-core kernel, whose escapes are patched in the epilogue
+    w_big = np.concatenate([w, synth.f32_to_bf16_bits((rng.standard_normal((6152, k)) * 0.05).astype(np.float32))])
+    rec_big = w12.encode(to_dev(w_big))
+    for path, m, rr, ww in (("gemv", 3, rec, w), ("mfma", 3, rec, w), ("mfma", 100, rec, w),
+                            ("mfma", 100, rec_big, w_big)):
+        say(f"special values path={path} m={m} n={ww.shape[0]}")
         x = x_all[:m]
-        y = w12.gemm(to_dev(x), rec, path=path).cpu().numpy().astype(np.float64)
+        y_all = w12.gemm(to_dev(x), rr, path=path).cpu().numpy().astype(np.float64)
+        if ww.shape[0] > 8:
+            check_gemm(y_all[:, 8:], x, ww[8:], f"special values stacked rows {path} m={m}")
+        y = y_all[:, :8]
         y64 = oracle.gemm64(x, w)
         assert np.isinf(y[:, 0]).all() and np.array_equal(np.sign(y[:, 0]), np.sign(y64[:, 0]))
         assert np.isnan(y[:, 1]).all()
@@ -576,15 +583,19 @@ def test_q8_midpoint_gemm(n, k, ms):
         assert np.array_equal(y, oracle.bf16_to_f64(qm[:, cols]).T), path
 
 
-@pytest.mark.parametrize("n,k,m", [(4099, 640, 128), (300, 1152, 200), (64, 5120, 100), (16, 128, 65)])
+@pytest.mark.parametrize("n,k,m", [(4099, 640, 128), (300, 1152, 200), (64, 5120, 100), (16, 128, 65),
+                                   (6151, 384, 100), (6151, 384, 200)])
 def test_gemm_more_than_64_rows(n, k, m):
-    """65..128 rows of x per weight read (eight activation tiles; escapes patched in the
-    epilogue, from LDS and, past its 384 entries in a crowded tile, from memory), passes of 128
-    above that; every format against the oracle."""
+    """More than 32 rows of x on the matrix cores: shapes of fewer than 1.5 tiles per CU in passes
+    of 32 rows (split k); 385 tiles and more on the eight-tile kernel, 65..128 rows per weight read
+    (escapes patched in the epilogue, from LDS and, past its 384 entries in the crowded first
+    tile, from memory), passes of 128 above that; every format against the oracle."""
     rng = np.random.default_rng(n + k + m)
     w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     w[rng.random((n, k)) < 0.01] = 0
     w[rng.random((n, k)) < 1e-3] = 0x4480                                # outliers far above the window
+    if n >= 6144:
+        w[:16][rng.random((16, k)) < 0.5] = 0                            # a crowded tile: ~3000 escapes
     x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
     _gemm_case(w, x, f"m>64 {n}x{k}", paths=("mfma",))
     w12 = _w12()
@@ -594,18 +605,18 @@ def test_gemm_more_than_64_rows(n, k, m):
 
 
 def test_gemm_more_than_64_rows_one_hot_exact():
-    """x = e_c for 100 columns (escaped ones included) through the eight-tile path: every output
-    is exactly one weight, on the exact pass and both Q passes."""
+    """x = e_c for 100 columns (escaped ones included) through the eight-tile path (385 tiles): every
+    output is exactly one weight, on the exact pass and both Q passes."""
     w12 = _w12()
-    n, k = 256, 1024
+    n, k = 6160, 256
     rng = np.random.default_rng(21)
     w = synth.f32_to_bf16_bits((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     w[rng.random((n, k)) < 0.02] = 0
     w[5, 17] = 0x4500
-    w[9, 700] = 0x0001                                                   # subnormal escape
+    w[9, 200] = 0x0001                                                   # subnormal escape
     rec = w12.encode(to_dev(w))
     ref = oracle.encode(w)
-    cols = sorted(set(rng.choice(k, 97, replace=False).tolist()) | {17, 700, 0})[:100]
+    cols = sorted(set(rng.choice(k, 97, replace=False).tolist()) | {17, 200, 0})[:100]
     x = np.zeros((len(cols), k), np.uint16)
     for i, c in enumerate(cols):
         x[i, c] = 0x3F80
