@@ -79,7 +79,8 @@ def _interleaved(gate_bits, up_bits, what):
 
 @pytest.mark.parametrize("i,k,ms,paths", [
     (40, 256, (1, 2, 5, 8), ("gemv", "auto")),             # GEMV, ragged tile count
-    (200, 1152, (1, 16, 20, 32, 40, 64, 100), ("mfma", "auto")),   # every matrix-core width
+    (200, 1152, (1, 16, 20, 32, 40, 64, 100), ("mfma", "auto")),   # 25 tiles: passes of 32 above 32
+    (3080, 256, (40, 64, 100, 128), ("mfma", "auto")),     # 385 tiles: three/four- and eight-tile
     (32, 5120, (1, 16, 32), ("gemv", "mfma")),             # split k (few tiles)
     (160, 17408, (1, 32), ("gemv", "mfma")),               # split k, long rows
     (64, 6144, (8,), ("gemv",)),                           # GEMV over two k slices (float sums)
