@@ -81,7 +81,9 @@ def test_i8_tiny_config():
 
 
 @pytest.mark.parametrize("n,k,ms", [
-    (300, 1152, (1, 2, 5, 8, 17, 32, 40, 64, 100)),   # every kernel family and width, ragged tiles
+    (300, 1152, (1, 2, 5, 8, 17, 32, 40, 64, 100)),   # every kernel family, ragged tiles (passes
+                                                       # of 32 above 32 rows on 19 tiles)
+    (6160, 256, (40, 64, 100)),                        # 385 tiles: the three/four-tile kernel
     (64, 5120, (1, 16, 32)),                           # split k (few tiles)
     (320, 17408, (1, 32)),                             # split k, long rows
     (1037, 640, (4, 33)),
