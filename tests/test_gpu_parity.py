@@ -172,8 +172,8 @@ def test_gemm_attn_m1():
 
 def _seeded_shapes(count, seed):
     """Shapes drawn once from a fixed seed: ragged n, k a multiple of 128, m up to 260 (so the
-    GEMV, the one-, two-, three/four- and eight-tile matrix-core kernels, split k and passes of
-    128 rows all occur)."""
+    GEMV, the one- and two-tile matrix-core kernels, split k and, above 32 rows on these few-tile
+    shapes, passes of 32 rows and the dense baseline's streaming kernel all occur)."""
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(count):
@@ -658,8 +658,9 @@ def _check_bf16_out(y16, y32, x_bits, w_bits, what):
     (320, 2048, 16, "mfma", True),         # matrix-core split k
     (24593, 256, 20, "mfma", False),       # matrix-core, one k range: the epilogue rounds (n % 4 = 1:
                                            # 2-byte stores)
-    (300, 1152, 40, "mfma", True),         # three activation tiles
-    (300, 1152, 100, "mfma", True),        # eight activation tiles
+    (300, 1152, 40, "mfma", True),         # passes of 32 rows (few tiles)
+    (6160, 256, 40, "mfma", True),         # three activation tiles (385 tiles)
+    (6160, 256, 100, "mfma", True),        # eight activation tiles (385 tiles)
     (50752, 128, 16, "mfma", False),       # full rounds (8-byte stores) + the split tail launch
 ])
 def test_gemm_bf16_output(n, k, m, path, oracle_check):
