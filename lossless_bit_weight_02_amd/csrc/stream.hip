@@ -4,10 +4,11 @@
 // One workgroup of W waves per CU (W = 16 up to 16 rows of x, 12 with 168 VGPRs and a deeper ring
 // for 17..32 rows, 8 with 256 VGPRs for 33..64, whose ranges may touch three tiles).  Workgroup c
 // owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so every CU gets the same number
-// of tiles to within one.  Each wave finalises up to FT of the CU's tiles (FT = 3 for 3..16 rows
-// of x on shapes with more tiles than waves on the chip, W12 up to 8 rows; else 1); a shape with
+// of tiles to within one.  Each wave finalises up to FT of the CU's tiles (on shapes with more
+// tiles than waves on the chip FT = 3 for 3..16 rows of x and 2 for 33..64; else 1); a shape with
 // more tiles than FT W per CU runs as row groups of such workgroups in one launch (workgroup b:
-// group b / G).
+// group b / G).  In top-1 mode each workgroup reduces its outputs to one key per x row instead of
+// storing them.
 // Inside the CU the work is dealt by (tile, 128-column block) units rather than by tiles, so no
 // wave idles while others stream:
 //
@@ -24,7 +25,8 @@
 // keeps one running sum per touched tile in registers over all phases and adds them into LDS at
 // the end.  Tile j of the CU is then finalised by wave j % W: the partial sums of the waves that
 // touch it, added in wave order (deterministic), plus its escape corrections, collected during
-// each phase from x in LDS.
+// each phase from x in LDS (the first 384 entries of a tile, 128 with FT > 1, copied to the
+// wave's LDS slot at the start; entries past the copy are read at the end).
 //
 // Decode and arithmetic as in the GEMV: 1-2 rows by dot2 (lane r16 + 16 g computes row r16 over
 // columns 32 g .. +31 of each block); 3-64 rows on the matrix cores, the decoded block as operand
@@ -34,8 +36,8 @@
 
 namespace w12 {
 
-// escapes of a finalised tile copied to LDS (more: read at the end), with one and with three
-// tiles finalised per wave; value slots 128 more (copied as 4-byte pairs from an even entry)
+// escapes of a finalised tile copied to LDS (more: read at the end), with one and with two or
+// three tiles finalised per wave; value slots 128 more (copied as 4-byte pairs from an even entry)
 constexpr int kSECap = 384, kSECap3 = 128;
 constexpr int kSPieces = 80;    // x pieces (1 KiB) per phase buffer at most
 
