@@ -80,8 +80,8 @@ extern "C" {
 /* flags for the GEMM calls: which kernel family runs */
 #define W12_PATH_AUTO 0u  /* the family measured fastest for the shape: the streaming kernel for
                            * 3 <= m <= 16 on shapes of at least 1.5 16-row tiles per compute unit
-                           * and k <= 8192, for 17 <= m <= 32 on 2 to 12 tiles per unit
-                           * (the dense baseline: at most 6 tiles per unit), for
+                           * and k <= 8192, for 17 <= m <= 32 on at least 2 tiles per unit
+                           * (the 8-bit passes: 2 to 24; the dense baseline: 2 to 6), for
                            * 33 <= m <= 64 on 1.5 to 3 tiles per unit (the dense baseline:
                            * every shape), and above 64 rows on 1.5 to 2.5 (the dense baseline:
                            * at most 3); otherwise the GEMV
@@ -93,7 +93,7 @@ extern "C" {
 #define W12_PATH_STREAM 3u /* force the streaming kernel (one workgroup per CU owning whole 16-row
                             * tiles, every wave of it an equal share of their 128-column blocks;
                             * passes of <= 64 rows of x; a wave finalises up to three tiles at
-                            * 3..16 rows and two at 33..64 rows, and shapes with more tiles than
+                            * 3..16 rows and two at 17..64 rows, and shapes with more tiles than
                             * that in equal row groups, all in one launch; W12_ERR_SHAPE when k is
                             * 2^26 or more or no phase length fits the LDS) */
 /* w12_q8_gemm only, or-ed with a path: read the dropped B nibble as 8 (the midpoint of the 16

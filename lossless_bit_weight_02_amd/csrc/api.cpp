@@ -82,10 +82,12 @@ w12::Planes planes_of(const w12_weight* wt) {
 // 37.4, [8192, 5120]: 25.0 vs 26.2; [6144, 5120]: 24.1 vs 23.0, not taken).  Long rows
 // ([5120, 17408]) and shapes of 1.25 tiles per CU or fewer run the other families, and so does
 // the dense baseline above 6 tiles per CU (its own measurement: [34816, 5120], 4 rows 56.9 vs
-// 55.8, 32 rows 59.5 vs 57.8).  Up to 16 rows a wave finalises up to three tiles (with more,
-// row groups in one launch): the LM-head-like [152064, 5120] takes 133.3 vs 138.8 (Q pass) and
-// 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 183.1 vs 206.7 at 16 rows; at 32 rows (one tile per wave, row groups) 179.3 vs 165.8 and 227.9 vs 220.2, so above
-// 16 rows only shapes of one group do.
+// 55.8, 32 rows 59.5 vs 57.8).  Up to 16 rows a wave finalises up to three tiles, at 17..32 two
+// (with more, row groups in one launch): the LM-head-like [152064, 5120] takes 133.3 vs 138.8
+// (Q pass) and 181.2 vs 193.5 (exact) at 4 rows, 131.1 vs 148.8 and 183.1 vs 206.7 at 16 rows,
+// 164.4 vs 164.7 and 209.8 vs 219.4 at 32 rows (two groups); [65536, 5120] at 32 rows 75.6 vs
+// 88.3 and 90.9 vs 111.3 (one group).  So at 17..32 rows the 8-bit passes take it up to 24 tiles
+// per CU (one group), the exact pass on every size from 2 tiles per CU.
 // At 33..64 rows (one pass of the 64-row instance, 8 waves per CU) the streaming kernel beats
 // the matrix cores' three/four-tile kernel, which does not split k, on shapes of 1.5 to 3 tiles
 // per CU (W12, 64 rows: [6144, 5120] 37.1 vs 48.7, [12288, 5120] 44.8 vs 51.0; at 40 rows the
@@ -103,7 +105,7 @@ bool stream_auto_pick(w12::Fmt f, int64_t m, int64_t tiles, int64_t k, int64_t c
   if (m <= 32)
     return k <= 8192 && (!dense || tiles <= 6 * cus) &&
            ((m >= 3 && m <= 16 && 2 * tiles >= 3 * cus) ||
-            (m >= 17 && m <= 32 && tiles >= 2 * cus && tiles <= 12 * cus));
+            (m >= 17 && m <= 32 && tiles >= 2 * cus && (f == w12::kFmtW12 || tiles <= 24 * cus)));
   if (m <= 64) return dense || (2 * tiles >= 3 * cus && tiles <= 3 * cus);
   return dense ? tiles <= 3 * cus : 2 * tiles >= 3 * cus && 2 * tiles <= 5 * cus;
 }

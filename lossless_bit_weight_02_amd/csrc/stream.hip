@@ -5,7 +5,7 @@
 // for 17..32 rows, 8 with 256 VGPRs for 33..64, whose ranges may touch three tiles).  Workgroup c
 // owns the 16-row tiles c, c + G, c + 2 G, ... (G workgroups), so every CU gets the same number
 // of tiles to within one.  Each wave finalises up to FT of the CU's tiles (on shapes with more
-// tiles than waves on the chip FT = 3 for 3..16 rows of x and 2 for 33..64; else 1); a shape with
+// tiles than waves on the chip FT = 3 for 3..16 rows of x and 2 for 17..64; else 1); a shape with
 // more tiles than FT W per CU runs as row groups of such workgroups in one launch (workgroup b:
 // group b / G).  In top-1 mode each workgroup reduces its outputs to one key per x row instead of
 // storing them.
@@ -21,9 +21,9 @@
 // phase change costs one barrier; the weight ring (D blocks in flight per wave) runs on across
 // phases.
 //
-// Partial sums.  A wave's range touches at most two tiles (three at 64 rows, four with FT = 3); it
-// keeps one running sum per touched tile in registers over all phases and adds them into LDS at
-// the end.  Tile j of the CU is then finalised by wave j % W: the partial sums of the waves that
+// Partial sums.  A wave's range touches at most two tiles (three at 64 rows or with FT = 2, four
+// with FT = 3); it keeps one running sum per touched tile in registers over all phases and adds
+// them into LDS at the end.  Tile j of the CU is then finalised by wave j % W: the partial sums of the waves that
 // touch it, added in wave order (deterministic), plus its escape corrections, collected during
 // each phase from x in LDS (the first 384 entries of a tile, 128 with FT > 1, copied to the
 // wave's LDS slot at the start; entries past the copy are read at the end).
@@ -125,10 +125,10 @@ __global__ __launch_bounds__(64 * W) void k_stream(StreamArgs a) {
   // us against 198.7 in row groups of one tile per wave)
   constexpr int D = (FMT == kFmtW12 && FT == 3 && MR >= 8) ? 2 : StreamShape<W>::D;
   constexpr int FW = StreamShape<W>::FW;
-  static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16) || (FT == 2 && W == 8 && MR == 64),
+  static_assert(FT == 1 || (FT == 3 && W == 16 && MR <= 16) || (FT == 2 && ((W == 8 && MR == 64) || (W == 12 && MR == 32))),
                 "FT 3: up to 16 rows, 16 waves; FT 2: 64 rows, 8 waves");
   // tiles one wave's range touches at most: its length is at most FT kbp units + 1
-  constexpr int SL = FT == 3 ? 4 : MR > 32 ? 3 : 2;
+  constexpr int SL = FT == 3 ? 4 : (MR > 32 || FT == 2) ? 3 : 2;
   constexpr bool kMF = MR > 2;                       // matrix cores for 3..64 rows
   constexpr int NT = (MR + 15) / 16;                 // 16-row activation tiles
   constexpr int NACC = kMF ? 4 * NT : MR;            // running sums per lane
@@ -605,7 +605,7 @@ typedef void (*StreamKernel)(StreamArgs);
 
 template <int FMT>
 static StreamKernel stream_pick(int mr, int ft) {
-  if (ft == 2) return k_stream<FMT, 64, 8, 2>;
+  if (ft == 2) return mr == 32 ? k_stream<FMT, 32, 12, 2> : k_stream<FMT, 64, 8, 2>;
   if (ft == 3) {
     switch (mr) {
       case 4: return k_stream<FMT, 4, 16, 3>;
@@ -642,13 +642,14 @@ static int stream_rows(int64_t mb) {
 }
 static int stream_waves(int mr) { return mr > 32 ? 8 : mr > 16 ? 12 : 16; }
 // tiles a wave finalises on shapes with more tiles than waves on the chip: 3 for 3..16 rows
-// (instances for 4, 8 and 16 rows), 2 for 33..64 rows (each row group re-reads all of x through
-// the CU, as much as the CU's weights at 64 rows); else 1
+// (instances for 4, 8 and 16 rows), 2 for 17..64 rows (each row group re-reads all of x through
+// the CU, as much as the CU's weights at 64 rows; at 32 rows the LM-head-like [152064, 5120] takes
+// 209.8 us instead of 229.6 in four groups); else 1
 static int stream_ft(const DevInfo& di, Fmt, int mr, int64_t tiles) {
   if (tiles <= (int64_t)stream_waves(mr) * di.cus) return 1;
-  return mr >= 3 && mr <= 16 ? 3 : mr > 32 ? 2 : 1;
+  return mr >= 3 && mr <= 16 ? 3 : mr > 16 ? 2 : 1;
 }
-static int stream_slots(int mr, int ft) { return ft == 3 ? 4 : mr > 32 ? 3 : 2; }
+static int stream_slots(int mr, int ft) { return ft == 3 ? 4 : (mr > 32 || ft == 2) ? 3 : 2; }
 
 struct StreamPlan {
   int mr = 0, waves = 0, nph = 0, ft = 1;

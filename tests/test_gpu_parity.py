@@ -824,10 +824,11 @@ def test_stream_path(n, k, ms):
     (66000, 2816, (8, 16)),               # 4125 tiles; 16 rows: two k phases of 11 blocks
     (40000, 640, (40, 64)),               # 2500 tiles, 64-row instance: up to 2 tiles per wave
     (70000, 128, (33,)),                  # 4375 tiles: two row groups of up to 2 tiles per wave
+    (100000, 128, (24,)),                 # 6250 tiles at 24 rows: two row groups of up to 2 tiles
 ])
 def test_stream_several_tiles_per_wave(n, k, ms):
     """The streaming kernel on shapes with more tiles than waves on the chip (3..16 rows: up to
-    three tiles finalised per wave; 33..64 rows: up to two), every wave walking the escapes of all
+    three tiles finalised per wave; 17..64 rows: up to two), every wave walking the escapes of all
     its tiles phase by phase: W12 and the dense baseline against the oracle product (the plain
     definition), bfloat16 outputs the rounding of the float outputs, a second call the same bits."""
     w12 = _w12()
